@@ -1,0 +1,153 @@
+"""CPU oracle for the DSA hot path -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The library (``sparse_attention_03_amd``)
+never does, and this package imports nothing from the library.
+
+Thin ctypes wrapper over ``liboracle.so`` (plain C, double precision, built by
+``oracle/build.py``).  Element formats are passed as raw storage:
+``float32`` arrays, ``uint16`` bfloat16 bit patterns, or ``uint8`` OCP E4M3FN
+codes, with the matching dtype code.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+ACT_RELU, ACT_GELU = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = ctypes.CDLL(_LIB_PATH)
+        p, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        L.dsa_oracle_e4m3_value.argtypes = [i32]
+        L.dsa_oracle_e4m3_value.restype = dbl
+        L.dsa_oracle_indexer.argtypes = [i32, p, p, i32, p, p, p, i32, p, i32, i32, i32, p, i64]
+        L.dsa_oracle_topk.argtypes = [i32, p, p, i32, p, p, i64, i32, p]
+        L.dsa_oracle_sparse_mla.argtypes = [i32, p, p, i32, p, p, p, i32, p, i32, i32, i32, i32, dbl, p, p]
+        L.dsa_oracle_forward.argtypes = [i32, p, p, i32, p, p, p, i32, p, i32, i32, i32,
+                                         p, p, i32, i32, i32, i32, dbl, i32, i64, p, p, p, p]
+        for f in (L.dsa_oracle_indexer, L.dsa_oracle_topk, L.dsa_oracle_sparse_mla, L.dsa_oracle_forward):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def _dtype_code(a):
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.uint8:
+        return FP8_E4M3
+    raise TypeError(f"unsupported storage dtype {a.dtype}")
+
+
+def _rows(rows, cu_q):
+    if rows is None:
+        return np.arange(int(cu_q[-1]), dtype=np.int32)
+    return _c(rows, np.int32)
+
+
+def e4m3_value(code: int) -> float:
+    return lib().dsa_oracle_e4m3_value(int(code))
+
+
+def indexer(cu_q, cu_k, q_idx, k_idx, w, act=ACT_RELU, ld=None, rows=None):
+    """Scores [nrows, ld] float64; entries s > pos are left at 0."""
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    rows = _rows(rows, cu_q)
+    q_idx, k_idx = np.ascontiguousarray(q_idx), np.ascontiguousarray(k_idx)
+    dt = _dtype_code(q_idx)
+    assert _dtype_code(k_idx) == dt
+    nrows, H_I, d_I = q_idx.shape
+    assert nrows == len(rows) and k_idx.shape[1] == d_I
+    w = _c(w, np.float32)
+    assert w.shape == (nrows, H_I)
+    if ld is None:
+        ld = int(np.max(np.diff(cu_k)))
+    out = np.zeros((nrows, ld), dtype=np.float64)
+    rc = lib().dsa_oracle_indexer(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), nrows, _ptr(rows),
+                                  _ptr(q_idx), _ptr(k_idx), dt, _ptr(w), H_I, d_I, act, _ptr(out), ld)
+    if rc != 0:
+        raise ValueError("oracle indexer: invalid batch / rows")
+    return out
+
+
+def topk(cu_q, cu_k, scores, k, rows=None):
+    """Selected positions [nrows, k] int32, ascending, -1 padded."""
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    rows = _rows(rows, cu_q)
+    scores = _c(scores, np.float32)
+    nrows, ld = scores.shape
+    assert nrows == len(rows)
+    idx = np.empty((nrows, k), dtype=np.int32)
+    rc = lib().dsa_oracle_topk(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), nrows, _ptr(rows),
+                               _ptr(scores), ld, k, _ptr(idx))
+    if rc != 0:
+        raise ValueError("oracle topk: invalid batch / rows")
+    return idx
+
+
+def sparse_mla(cu_q, cu_k, q, kv, idx, d_v, scale, rows=None):
+    """(out [nrows, H, d_v] float64, lse [nrows, H] float64)."""
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    rows = _rows(rows, cu_q)
+    q, kv = np.ascontiguousarray(q), np.ascontiguousarray(kv)
+    dt = _dtype_code(q)
+    assert _dtype_code(kv) == dt
+    nrows, H, d_qk = q.shape
+    assert nrows == len(rows) and kv.shape[1] == d_qk
+    idx = _c(idx, np.int32)
+    k = idx.shape[1]
+    out = np.zeros((nrows, H, d_v), dtype=np.float64)
+    lse = np.zeros((nrows, H), dtype=np.float64)
+    rc = lib().dsa_oracle_sparse_mla(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), nrows, _ptr(rows),
+                                     _ptr(q), _ptr(kv), dt, _ptr(idx), k, H, d_qk, d_v, float(scale),
+                                     _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle sparse_mla: invalid batch / rows / indices")
+    return out, lse
+
+
+def forward(cu_q, cu_k, q_idx, k_idx, w, q, kv, k, d_v, scale, act=ACT_RELU, rows=None, ld=None):
+    """Indexer -> fp32 rounding -> top-k -> sparse attention.
+
+    Returns (out, lse, scores_f32, idx)."""
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    rows = _rows(rows, cu_q)
+    q_idx, k_idx, q, kv = (np.ascontiguousarray(a) for a in (q_idx, k_idx, q, kv))
+    nrows, H_I, d_I = q_idx.shape
+    _, H, d_qk = q.shape
+    w = _c(w, np.float32)
+    if ld is None:
+        ld = int(np.max(np.diff(cu_k)))
+    out = np.zeros((nrows, H, d_v), dtype=np.float64)
+    lse = np.zeros((nrows, H), dtype=np.float64)
+    sc = np.zeros((nrows, ld), dtype=np.float32)
+    idx = np.empty((nrows, k), dtype=np.int32)
+    rc = lib().dsa_oracle_forward(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), nrows, _ptr(rows),
+                                  _ptr(q_idx), _ptr(k_idx), _dtype_code(q_idx), _ptr(w), H_I, d_I, act,
+                                  _ptr(q), _ptr(kv), _dtype_code(q), H, d_qk, d_v, float(scale), k, ld,
+                                  _ptr(out), _ptr(lse), _ptr(sc), _ptr(idx))
+    if rc != 0:
+        raise ValueError("oracle forward failed")
+    return out, lse, sc, idx

@@ -1,0 +1,366 @@
+"""Pins for the CPU oracle, independent of the oracle's own code.
+
+Each test checks the oracle against something other than itself: a library
+routine (numpy matmul / lexsort, torch's fp8 decoding, torch's scaled-dot-
+product attention), a closed form, an invariant, or brute force on tiny
+inputs.  Mistakes these are built to catch: a dropped weight or head, a wrong
+sign in the activation, a transposed operand, a wrong key row or causal bound,
+a wrong tie rule, a wrong value slice or softmax scale.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_03_amd import inputs as gen
+
+
+def _ragged(seq_ctx, seq_q):
+    cu_q = np.concatenate([[0], np.cumsum(seq_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(seq_ctx)]).astype(np.int32)
+    return cu_q, cu_k
+
+
+def _positions(cu_q, cu_k):
+    pos, base = [], []
+    for b in range(len(cu_q) - 1):
+        qb, ctx = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        for r in range(qb):
+            pos.append(ctx - qb + r)
+            base.append(cu_k[b])
+    return np.array(pos), np.array(base)
+
+
+# ---------------------------------------------------------------- formats
+
+def test_e4m3_table_matches_torch_decoding():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.e4m3_value(c) for c in range(256)])
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+    # spot values of the OCP E4M3FN definition
+    assert oracle.e4m3_value(0x7E) == 448.0
+    assert oracle.e4m3_value(0x01) == 2.0 ** -9
+    assert oracle.e4m3_value(0x08) == 2.0 ** -6
+    assert oracle.e4m3_value(0x38) == 1.0
+    assert math.isnan(oracle.e4m3_value(0x7F)) and math.isnan(oracle.e4m3_value(0xFF))
+    assert math.copysign(1.0, oracle.e4m3_value(0x80)) == -1.0
+
+
+def test_bf16_and_fp8_storage_decode_like_fp32():
+    """The same values stored as bf16 / e4m3 / fp32 give identical results."""
+    g = torch.Generator().manual_seed(3)
+    vals = torch.randint(-4, 5, (40, 2, 16), generator=g).to(torch.float32)
+    keys = torch.randint(-4, 5, (40, 16), generator=g).to(torch.float32)
+    w = torch.rand(40, 2, generator=g)
+    cu_q, cu_k = _ragged([40], [40])
+    s32 = oracle.indexer(cu_q, cu_k, vals.numpy(), keys.numpy(), w.numpy())
+    s8 = oracle.indexer(cu_q, cu_k, gen.storage_numpy(vals.to(torch.float8_e4m3fn)),
+                        gen.storage_numpy(keys.to(torch.float8_e4m3fn)), w.numpy())
+    assert np.array_equal(s32, s8)
+    q = torch.randn(40, 3, 16, generator=g).to(torch.bfloat16)
+    kv = torch.randn(40, 16, generator=g).to(torch.bfloat16)
+    idx = np.tile(np.arange(8, dtype=np.int32), (40, 1))
+    idx[:8] = -1
+    for r in range(8):
+        idx[r, :r + 1] = np.arange(r + 1)
+    o16, l16 = oracle.sparse_mla(cu_q, cu_k, gen.storage_numpy(q), gen.storage_numpy(kv), idx, 8, 0.3)
+    o32, l32 = oracle.sparse_mla(cu_q, cu_k, q.float().numpy(), kv.float().numpy(), idx, 8, 0.3)
+    assert np.array_equal(o16, o32) and np.array_equal(l16, l32)
+
+
+# ---------------------------------------------------------------- indexer
+
+def _indexer_case(seed, seq_ctx, seq_q, H_I, d_I, integer=False):
+    rng = np.random.default_rng(seed)
+    cu_q, cu_k = _ragged(seq_ctx, seq_q)
+    T, K = cu_q[-1], cu_k[-1]
+    if integer:
+        q = rng.integers(-4, 5, (T, H_I, d_I)).astype(np.float32)
+        k = rng.integers(-4, 5, (K, d_I)).astype(np.float32)
+        w = (rng.integers(0, 9, (T, H_I)) * 0.25).astype(np.float32)
+    else:
+        q = rng.standard_normal((T, H_I, d_I)).astype(np.float32)
+        k = rng.standard_normal((K, d_I)).astype(np.float32)
+        w = rng.uniform(-1, 1, (T, H_I)).astype(np.float32)
+    return cu_q, cu_k, q, k, w
+
+
+@pytest.mark.parametrize("act", [oracle.ACT_RELU, oracle.ACT_GELU])
+@pytest.mark.parametrize("integer", [False, True])
+def test_indexer_antisymmetric_part_is_a_matmul(act, integer):
+    """relu(x) - relu(-x) = x and gelu(x) - gelu(-x) = x, so
+    I(q) - I(-q) = sum_j w_j q_j . k_s = ((w q) summed over heads) @ k^T."""
+    cu_q, cu_k, q, k, w = _indexer_case(1, [37, 50, 9], [37, 4, 1], 3, 8, integer)
+    ld = 50
+    plus = oracle.indexer(cu_q, cu_k, q, k, w, act=act, ld=ld)
+    minus = oracle.indexer(cu_q, cu_k, -q, k, w, act=act, ld=ld)
+    pos, base = _positions(cu_q, cu_k)
+    wq = np.einsum("tj,tjd->td", w.astype(np.float64), q.astype(np.float64))
+    for i in range(len(pos)):
+        keys = k[base[i]: base[i] + pos[i] + 1].astype(np.float64)
+        want = keys @ wq[i]
+        got = plus[i, :pos[i] + 1] - minus[i, :pos[i] + 1]
+        if integer and act == oracle.ACT_RELU:
+            assert np.array_equal(got, want)
+        else:
+            np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+        assert np.all(plus[i, pos[i] + 1:] == 0.0)  # beyond the causal bound: untouched
+
+
+def test_indexer_relu_symmetric_part_is_abs():
+    """relu(x) + relu(-x) = |x|: I(q) + I(-q) = sum_j w_j |q_j . k_s|; with w >= 0
+    every score is >= 0 and a row whose dot products are all <= 0 scores 0."""
+    cu_q, cu_k, q, k, w = _indexer_case(2, [64], [64], 4, 16, integer=True)
+    w = np.abs(w)
+    plus = oracle.indexer(cu_q, cu_k, q, k, w)
+    minus = oracle.indexer(cu_q, cu_k, -q, k, w)
+    dots = np.einsum("tjd,sd->tjs", q.astype(np.float64), k.astype(np.float64))
+    want = np.einsum("tj,tjs->ts", w.astype(np.float64), np.abs(dots))
+    mask = np.tril(np.ones((64, 64), dtype=bool))
+    assert np.array_equal((plus + minus)[mask], want[mask])
+    assert np.all(plus >= 0.0)
+    # all dot products negative -> zero score
+    qq = -np.abs(q)
+    kk = np.abs(k)
+    assert np.all(oracle.indexer(cu_q, cu_k, qq, kk, w)[mask] == 0.0)
+
+
+def test_indexer_gelu_value_is_x_times_normal_cdf():
+    from scipy.stats import norm
+    xs = np.array([-2.5, -1.0, -0.3, 0.0, 0.7, 1.0, 3.0], dtype=np.float32)
+    n = len(xs)
+    cu_q, cu_k = _ragged([n], [n])
+    q = np.ones((n, 1, 1), dtype=np.float32)
+    k = xs.reshape(n, 1)
+    w = np.ones((n, 1), dtype=np.float32)
+    got = oracle.indexer(cu_q, cu_k, q, k, w, act=oracle.ACT_GELU)
+    want = xs.astype(np.float64) * norm.cdf(xs.astype(np.float64))
+    assert abs(got[n - 1, 5] - 0.8413447460685429) < 1e-15   # GELU(1) = Phi(1)
+    for s in range(n):
+        assert abs(got[n - 1, s] - want[s]) < 1e-14
+
+
+def test_indexer_heads_are_weighted_independently():
+    """w = e_j isolates head j: the score is relu(q_j . k_s)."""
+    cu_q, cu_k, q, k, _ = _indexer_case(5, [20], [20], 3, 4, integer=True)
+    for j in range(3):
+        w = np.zeros((20, 3), dtype=np.float32)
+        w[:, j] = 1.0
+        got = oracle.indexer(cu_q, cu_k, q, k, w)
+        dots = q[:, j, :].astype(np.float64) @ k.T.astype(np.float64)
+        want = np.where(np.tril(np.ones((20, 20), bool)), np.maximum(dots, 0.0), 0.0)
+        assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- top-k
+
+def _brute_force_topk(scores, n, k):
+    """The unique k-subset S with: for s in S, u not in S: s beats u."""
+    def beats(a, b):
+        sa, sb = scores[a], scores[b]
+        if np.isnan(sa) or np.isnan(sb):
+            if np.isnan(sa) and np.isnan(sb):
+                return a < b
+            return np.isnan(sb)
+        return sa > sb or (sa == sb and a < b)
+    found = []
+    for S in itertools.combinations(range(n), k):
+        rest = [u for u in range(n) if u not in S]
+        if all(beats(s, u) for s in S for u in rest):
+            found.append(list(S))
+    assert len(found) == 1
+    return found[0]
+
+
+def test_topk_matches_subset_brute_force():
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        n = int(rng.integers(1, 11))
+        k = int(rng.integers(1, 6))
+        vals = rng.integers(-3, 4, n).astype(np.float32)   # many ties
+        if trial % 5 == 0:
+            vals[rng.integers(0, n)] = np.nan
+        if trial % 3 == 0:
+            vals[vals == 0] = -0.0
+        cu_q, cu_k = _ragged([n], [1])
+        got = oracle.topk(cu_q, cu_k, vals.reshape(1, n), k)[0]
+        if n <= k:
+            want = list(range(n)) + [-1] * (k - n)
+        else:
+            want = _brute_force_topk(vals, n, k)
+        assert list(got) == want, (vals, k)
+
+
+def test_topk_matches_lexsort_on_ragged_rows():
+    rng = np.random.default_rng(8)
+    cu_q, cu_k = _ragged([300, 17, 129], [300, 5, 2])
+    pos, _ = _positions(cu_q, cu_k)
+    ld = 300
+    scores = rng.integers(0, 50, (len(pos), ld)).astype(np.float32)   # ties everywhere
+    k = 32
+    got = oracle.topk(cu_q, cu_k, scores, k)
+    for i, p in enumerate(pos):
+        n = p + 1
+        row = scores[i, :n]
+        order = np.lexsort((np.arange(n), -row))    # score desc, then position asc
+        want = np.sort(order[:k]) if n > k else np.arange(n)
+        want = np.concatenate([want, -np.ones(k - len(want), np.int64)])
+        assert np.array_equal(got[i], want)
+
+
+def test_topk_invariants():
+    rng = np.random.default_rng(9)
+    n, k = 500, 64
+    cu_q, cu_k = _ragged([n], [1])
+    row = rng.standard_normal(n).astype(np.float32)
+    base = oracle.topk(cu_q, cu_k, row.reshape(1, n), k)[0]
+    # strictly increasing transform: same selection
+    mono = (np.exp(row.astype(np.float64)) * 3.0 + 1.0).astype(np.float32)
+    assert np.array_equal(oracle.topk(cu_q, cu_k, mono.reshape(1, n), k)[0], base)
+    # permuting positions maps the selection (distinct scores)
+    perm = rng.permutation(n)
+    permuted = np.empty_like(row)
+    permuted[perm] = row
+    sel = oracle.topk(cu_q, cu_k, permuted.reshape(1, n), k)[0]
+    assert np.array_equal(np.sort(perm[base]), sel)
+    # all-equal row: the first k positions
+    assert np.array_equal(oracle.topk(cu_q, cu_k, np.full((1, n), 0.5, np.float32), k)[0], np.arange(k))
+    # -0 and +0 tie: lower index wins
+    z = np.zeros((1, n), np.float32)
+    z[0, ::2] = -0.0
+    assert np.array_equal(oracle.topk(cu_q, cu_k, z, k)[0], np.arange(k))
+
+
+# ---------------------------------------------------------------- attention
+
+def _dense_causal_mqa_torch(q, kv, d_v, scale):
+    """Library reference: torch SDPA in float64, causal, all heads sharing the
+    one latent as key (all columns) and value (first d_v columns)."""
+    qt = torch.from_numpy(q.astype(np.float64)).permute(1, 0, 2)         # [H, L, d]
+    k = torch.from_numpy(kv.astype(np.float64)).unsqueeze(0).expand(q.shape[1], -1, -1)
+    v = torch.from_numpy(kv[:, :d_v].astype(np.float64)).unsqueeze(0).expand(q.shape[1], -1, -1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, k, v, is_causal=True, scale=scale)
+    return o.permute(1, 0, 2).numpy()
+
+
+def test_attention_with_all_candidates_equals_dense_causal_mqa():
+    rng = np.random.default_rng(11)
+    L, H, d_qk, d_v, k = 48, 4, 24, 16, 64     # k >= L: every candidate selected
+    q = rng.standard_normal((L, H, d_qk)).astype(np.float32)
+    kv = rng.standard_normal((L, d_qk)).astype(np.float32)
+    cu_q, cu_k = _ragged([L], [L])
+    idx = oracle.topk(cu_q, cu_k, rng.standard_normal((L, L)).astype(np.float32), k)
+    scale = 0.37
+    out, lse = oracle.sparse_mla(cu_q, cu_k, q, kv, idx, d_v, scale)
+    ref = _dense_causal_mqa_torch(q, kv, d_v, scale)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    # lse from a library logsumexp
+    logits = scale * np.einsum("thd,sd->ths", q.astype(np.float64), kv.astype(np.float64))
+    mask = np.tril(np.ones((L, L), bool))[:, None, :]
+    ref_lse = torch.logsumexp(torch.from_numpy(np.where(mask, logits, -np.inf)), dim=-1).numpy()
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(12)
+    L, H, d_qk, d_v = 30, 3, 10, 6
+    q = rng.standard_normal((L, H, d_qk)).astype(np.float32)
+    kv = rng.standard_normal((L, d_qk)).astype(np.float32)
+    cu_q, cu_k = _ragged([L], [L])
+    # one selected entry: o = v_s exactly, lse = z_s
+    idx = -np.ones((L, 4), np.int32)
+    idx[:, 0] = np.arange(L) // 2
+    out, lse = oracle.sparse_mla(cu_q, cu_k, q, kv, idx, d_v, 0.5)
+    for t in range(L):
+        s = t // 2
+        assert np.array_equal(out[t], np.tile(kv[s, :d_v].astype(np.float64), (H, 1)))
+        z = 0.5 * (q[t].astype(np.float64) @ kv[s].astype(np.float64))
+        np.testing.assert_allclose(lse[t], z, rtol=0, atol=1e-13)
+    # q = 0: mean of the selected value rows, lse = log(count)
+    idx = np.tile(np.array([0, 3, 7, -1], np.int32), (L, 1))
+    idx[:8] = np.array([0, -1, -1, -1])
+    out, lse = oracle.sparse_mla(cu_q, cu_k, np.zeros_like(q), kv, idx, d_v, 0.5)
+    mean = kv[[0, 3, 7], :d_v].astype(np.float64).mean(0)
+    np.testing.assert_allclose(out[10], np.tile(mean, (H, 1)), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse[10], np.log(3.0), rtol=0, atol=1e-14)
+    # two entries: o = sigmoid(z1 - z2) v1 + sigmoid(z2 - z1) v2
+    idx = np.tile(np.array([1, 4], np.int32), (L, 1))
+    idx[:5] = np.array([0, -1])
+    out, _ = oracle.sparse_mla(cu_q, cu_k, q, kv, idx, d_v, 0.9)
+    t = 20
+    z = 0.9 * (q[t].astype(np.float64) @ kv[[1, 4]].astype(np.float64).T)   # [H, 2]
+    sig = 1.0 / (1.0 + np.exp(-(z[:, 0] - z[:, 1])))
+    want = sig[:, None] * kv[1, :d_v] + (1 - sig)[:, None] * kv[4, :d_v]
+    np.testing.assert_allclose(out[t], want, rtol=0, atol=1e-13)
+    # empty selection
+    idx = -np.ones((L, 4), np.int32)
+    out, lse = oracle.sparse_mla(cu_q, cu_k, q, kv, idx, d_v, 0.5)
+    assert np.all(out == 0.0) and np.all(np.isneginf(lse))
+
+
+def test_attention_invariants():
+    rng = np.random.default_rng(13)
+    L, H, d_qk, d_v, k = 64, 4, 16, 8, 12
+    q = rng.standard_normal((L, H, d_qk)).astype(np.float32)
+    kv = rng.standard_normal((L, d_qk)).astype(np.float32)
+    cu_q, cu_k = _ragged([L], [L])
+    idx = oracle.topk(cu_q, cu_k, rng.standard_normal((L, L)).astype(np.float32), k)
+    out, lse = oracle.sparse_mla(cu_q, cu_k, q, kv, idx, d_v, 0.25)
+    # order of the index list is irrelevant
+    perm_idx = idx[:, rng.permutation(k)]
+    out2, lse2 = oracle.sparse_mla(cu_q, cu_k, q, kv, perm_idx, d_v, 0.25)
+    np.testing.assert_allclose(out2, out, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse, rtol=0, atol=1e-13)
+    # rows that no query selected are irrelevant
+    used = np.zeros(L, bool)
+    used[idx[idx >= 0]] = True
+    garbage = kv.copy()
+    garbage[~used] = 1e6
+    out3, lse3 = oracle.sparse_mla(cu_q, cu_k, q, garbage, idx, d_v, 0.25)
+    assert np.array_equal(out3, out) and np.array_equal(lse3, lse)
+    # heads with identical queries give identical outputs
+    q4 = q.copy()
+    q4[:, 1] = q4[:, 0]
+    out4, _ = oracle.sparse_mla(cu_q, cu_k, q4, kv, idx, d_v, 0.25)
+    assert np.array_equal(out4[:, 0], out4[:, 1])
+
+
+# ---------------------------------------------------------------- end to end
+
+def test_forward_composes_the_steps_and_is_causal():
+    p = gen.make_problem("t", [96, 40], [96, 3], H_I=2, d_I=8, H=2, d_qk=16, d_v=8, k=16,
+                         idx_dtype=torch.float32, dtype=torch.float32, seed=4)
+    a = dict(q_idx=gen.storage_numpy(p.q_idx), k_idx=gen.storage_numpy(p.k_idx), w=gen.storage_numpy(p.w),
+             q=gen.storage_numpy(p.q), kv=gen.storage_numpy(p.kv))
+    out, lse, sc, idx = oracle.forward(p.cu_q_host, p.cu_k_host, a["q_idx"], a["k_idx"], a["w"], a["q"], a["kv"],
+                                       p.k, p.d_v, p.scale)
+    s_sep = oracle.indexer(p.cu_q_host, p.cu_k_host, a["q_idx"], a["k_idx"], a["w"], ld=sc.shape[1])
+    i_sep = oracle.topk(p.cu_q_host, p.cu_k_host, s_sep.astype(np.float32), p.k)
+    o_sep, l_sep = oracle.sparse_mla(p.cu_q_host, p.cu_k_host, a["q"], a["kv"], i_sep, p.d_v, p.scale)
+    assert np.array_equal(idx, i_sep) and np.array_equal(out, o_sep) and np.array_equal(lse, l_sep)
+    # perturb every token after position 50 of sequence 0: rows <= 50 unchanged
+    kv2, kidx2 = a["kv"].copy(), a["k_idx"].copy()
+    kv2[51:96] += 3.0
+    kidx2[51:96] *= -2.0
+    out2, lse2, _, idx2 = oracle.forward(p.cu_q_host, p.cu_k_host, a["q_idx"], kidx2, a["w"], a["q"], kv2,
+                                         p.k, p.d_v, p.scale)
+    assert np.array_equal(out2[:51], out[:51]) and np.array_equal(idx2[:51], idx[:51])
+    assert np.array_equal(out2[96:], out[96:])   # the other sequence is independent
+    assert not np.array_equal(out2[51:96], out[51:96])
+
+
+def test_forward_rows_subset_matches_full():
+    p = gen.make_problem("t", [70], [70], H_I=2, d_I=8, H=2, d_qk=16, d_v=8, k=16,
+                         idx_dtype=torch.float32, dtype=torch.float32, seed=6)
+    arr = [gen.storage_numpy(t) for t in (p.q_idx, p.k_idx, p.w, p.q, p.kv)]
+    full = oracle.forward(p.cu_q_host, p.cu_k_host, *arr, p.k, p.d_v, p.scale)
+    rows = np.array([0, 15, 16, 69], np.int32)
+    sub = oracle.forward(p.cu_q_host, p.cu_k_host, arr[0][rows], arr[1], arr[2][rows], arr[3][rows], arr[4],
+                         p.k, p.d_v, p.scale, rows=rows, ld=70)
+    for a, b in zip(sub, full):
+        assert np.array_equal(a, b[rows])

@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA hot path on one MI355X.
+
+One step = one dsa_forward over the 131072-token prefill (lightning indexer in
+FP8 + causal top-k 2048 + sparse MLA attention over 128 heads, processed in
+4096-query chunks), inputs resident in HBM.  Prints one JSON line:
+
+  value            tokens/s of the 128K prefill (whole job, one GPU)
+  roofline         dominant kernel: algorithmic work per step / its time per
+                   step, against the MI355X dense MFMA peak of its dtype
+  cpu_baseline     the CPU oracle on a bounded sample of the same workload,
+                   extrapolated with the per-row cost model
+  decode           the 64 x 32K decode batch: microseconds per token
+
+Per-kernel times come from a second, instrumented pass that issues the same
+per-chunk launches through the individual C entry points with HIP events
+between them on the launch stream.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"fp8": 5.0e15, "bf16": 2.5e15}   # MI355X dense MFMA, FLOP/s
+HBM_PEAK = 8.0e12                         # bytes/s
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(p):
+    """Per step: indexer MFMA flops over the causal pairs of rows with n > k,
+    attention flops over (query, selected entry) pairs, top-k bytes."""
+    pos = p.positions().astype(np.int64)
+    n = pos + 1
+    big = n > p.k
+    idx_pairs = int(n[big].sum())
+    attn_pairs = int(np.minimum(n, p.k).sum())
+    return dict(
+        indexer_flops=idx_pairs * 2 * p.H_I * p.d_I,
+        attention_flops=attn_pairs * 2 * p.H * (p.d_qk + p.d_v),
+        topk_bytes=int((4 * n[big]).sum() + 4 * p.k * len(n)),
+        indexer_pairs=idx_pairs, attention_pairs=attn_pairs)
+
+
+def chunk_problem(p, r0, r1, skip_short):
+    """The rows [r0, r1) of a one-sequence prefill as their own batch (same
+    kernels and grids as a dsa_forward chunk).  With skip_short, rows whose
+    candidates are all selected are left out, as dsa_forward does."""
+    import torch
+    from sparse_attention_03_amd import inputs as gen
+    if skip_short:
+        r0 = max(r0, p.k)
+    c = gen.DSAInputs(name="chunk", cu_q=torch.tensor([0, r1 - r0], dtype=torch.int32, device=p.q.device),
+                      cu_k=torch.tensor([0, r1], dtype=torch.int32, device=p.q.device),
+                      cu_q_host=np.array([0, r1 - r0], np.int32), cu_k_host=np.array([0, r1], np.int32),
+                      q_idx=p.q_idx[r0:r1], k_idx=p.k_idx, w=p.w[r0:r1], q=p.q[r0:r1], kv=p.kv, k=p.k, d_v=p.d_v,
+                      scale=p.scale)
+    return c
+
+
+def kernel_times(p, reps=1):
+    """Milliseconds per step spent in each step's kernels (HIP events)."""
+    import torch
+    from sparse_attention_03_amd import dsa, libdsa as L
+    qb = p.q_block or 4096
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    tot = {"indexer": 0.0, "topk": 0.0, "attention": 0.0}
+    ld = dsa.score_ld(p.max_ctx)
+    scores = torch.empty((qb, ld), dtype=torch.float32, device=p.q.device)
+    for _ in range(reps):
+        for r0 in range(0, p.total_q, qb):
+            r1 = min(p.total_q, r0 + qb)
+            c_idx = chunk_problem(p, r0, r1, skip_short=True) if r1 > p.k else None
+            c_all = chunk_problem(p, r0, r1, skip_short=False)
+            e = [ev() for _ in range(4)]
+            e[0].record()
+            if c_idx is not None:
+                L.dsa_indexer_scores(L.batch_of(c_idx), c_idx.q_idx, c_idx.k_idx, c_idx.w, scores)
+            e[1].record()
+            idx = torch.empty((r1 - r0, p.k), dtype=torch.int32, device=p.q.device)
+            L.dsa_topk(L.batch_of(c_all), scores, p.k, idx)
+            e[2].record()
+            out, lse = dsa.sparse_mla_attn(c_all, idx)
+            e[3].record()
+            torch.cuda.synchronize()
+            tot["indexer"] += e[0].elapsed_time(e[1])
+            tot["topk"] += e[1].elapsed_time(e[2])
+            tot["attention"] += e[2].elapsed_time(e[3])
+    return {k: v / reps for k, v in tot.items()}
+
+
+def cpu_baseline(p, work, n_rows=32, seed=0):
+    """Time the oracle on `n_rows` sampled rows of the same prefill and
+    extrapolate to the whole step with the per-row cost model
+    (t+1)*H_I*d_I (rows with n > k) + min(t+1, k)*H*(d_qk + d_v) MACs."""
+    import oracle
+    import torch
+    from sparse_attention_03_amd import inputs as gen
+    rng = np.random.default_rng(seed)
+    T = p.total_q
+    rows = np.sort(rng.choice(np.arange(T), n_rows, replace=False)).astype(np.int32)
+    ri = torch.as_tensor(rows, dtype=torch.long, device=p.q.device)
+    h = gen.storage_numpy
+    args = (h(p.q_idx[ri]), h(p.k_idx), h(p.w[ri]), h(p.q[ri]), h(p.kv))
+
+    def cost(t):
+        t = np.asarray(t, np.int64)
+        n = t + 1
+        return np.where(n > p.k, n * p.H_I * p.d_I, 0) + np.minimum(n, p.k) * p.H * (p.d_qk + p.d_v)
+
+    t0 = time.perf_counter()
+    oracle.forward(p.cu_q_host, p.cu_k_host, *args, p.k, p.d_v, p.scale, rows=rows)
+    dt = time.perf_counter() - t0
+    rate = float(cost(rows).sum()) / dt                      # MAC/s of the oracle
+    full = float(cost(np.arange(T)).sum()) / rate             # seconds for the whole step
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": T / full, "unit": "tokens/s", "cores": min(threads, os.cpu_count() or threads),
+            "kind": "oracle",
+            "sample": f"{n_rows} random rows of the 131072-token prefill (seed {seed}), {dt:.1f} s on the host; "
+                      f"extrapolated to all rows with the per-row MAC cost model ({full:.0f} s per step)"}
+
+
+def decode_us_per_token(steps=20, warmup=3):
+    import torch
+    from sparse_attention_03_amd import dsa, inputs as gen
+    p = gen.make_config("decode_64x32k", device="cuda")
+    f = dsa.Forward(p)
+    for _ in range(warmup):
+        f()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        f()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / steps
+    return {"workload": "decode_64x32k: 64 sequences x 32768 cached tokens, 1 query each, k=2048",
+            "us_per_token": step_s * 1e6 / p.total_q, "us_per_step": step_s * 1e6}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-kernel-times", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_attention_03_amd import dsa, inputs as gen
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    log("generating prefill_128k inputs on the GPU")
+    p = gen.make_config("prefill_128k", device="cuda")
+    f = dsa.Forward(p)
+    work = algorithmic_work(p)
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        f()
+    torch.cuda.synchronize()
+    log("timing", args.steps, "steps")
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        f()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / args.steps
+    log(f"{ms_step:.2f} ms/step (wall {wall / args.steps * 1e3:.2f} ms/step)")
+    tokens_s = p.total_q / (ms_step / 1e3)
+
+    result = {
+        "metric": "DSA tokens/s (indexer+top-k+sparse MLA) at 128K prefill; decode us/token",
+        "value": tokens_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3 indexer / bf16 attention (fp32 accumulate)",
+        "data": "synthetic, seeded (prefill_128k recipe)",
+        "config": {"workload": "prefill_128k: 1 sequence, L=131072, H_I=64, d_I=128 fp8, k=2048, "
+                               "H=128, d_qk=576, d_v=512 bf16, q_block=4096",
+                   "seq_len": p.total_q, "q_block": p.q_block, "k": p.k},
+    }
+    if not args.no_kernel_times:
+        log("instrumented pass (per-kernel HIP events)")
+        kt = kernel_times(p)
+        fl = {"indexer": (work["indexer_flops"], "fp8"), "attention": (work["attention_flops"], "bf16")}
+        rows = {}
+        for name, (flops, dt) in fl.items():
+            ach = flops / (kt[name] / 1e3)
+            rows[name] = {"ms_per_step": kt[name], "achieved_TFLOPs": ach / 1e12, "peak_TFLOPs": PEAK[dt] / 1e12,
+                          "frac": ach / PEAK[dt]}
+        tk_bw = work["topk_bytes"] / (kt["topk"] / 1e3)
+        rows["topk"] = {"ms_per_step": kt["topk"], "achieved_GBs": tk_bw / 1e9, "peak_GBs": HBM_PEAK / 1e9,
+                        "frac": tk_bw / HBM_PEAK}
+        dom = max(("indexer", "attention"), key=lambda n: kt[n])
+        d = rows[dom]
+        result["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": d["achieved_TFLOPs"],
+                              "peak": d["peak_TFLOPs"], "unit": "TFLOP/s", "frac": d["frac"], "traffic": None}
+        result["kernels"] = rows
+        log(json.dumps(rows))
+    if not args.no_decode:
+        log("decode_64x32k")
+        result["decode"] = decode_us_per_token()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on sampled rows)")
+        result["cpu_baseline"] = cpu_baseline(p, work)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * libdsa.h -- C interface of the MI355X (gfx950) DeepSeek Sparse Attention
+ * hot path: lightning-indexer scores, causal top-k selection, and sparse MLA
+ * attention in MQA mode, plus the three fused into one call.
+ *
+ * Sources (web pages on DeepSeek-V3.2-Exp, cited by title and section):
+ *   [P1] blog "Deepseek v3.2 exp 加班快樂 ... 論文原文" (hdetylss.com), sections
+ *        "Lightning indexer / Step 1", "Step 2", "在MLA下實例化DSA".
+ *   [P2] "DeepSeek 发布新模型 V3.2-Exp：基于DSA稀疏注意力机制的长上下文优化"
+ *        (gamebaike.com), items 【闪电索引器】, 【细粒度Token选择机制】,
+ *        【MLA架构集成】, 【推理成本评估】.
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless stated otherwise; tensors are
+ *     row-major with the innermost dimension contiguous.
+ *   - The caller owns every buffer, the workspace and the stream.  The library
+ *     never allocates, frees or synchronises, and keeps no pointer after the
+ *     call returns; buffers must stay alive until the stream work completes.
+ *   - Calls are asynchronous: DSA_OK means "enqueued on `stream`".
+ *   - All argument checks run on the host before anything is enqueued; on an
+ *     error nothing is enqueued, outputs are untouched, and dsa_last_error()
+ *     holds a description (thread-local).  A failed kernel launch returns
+ *     DSA_ERR_HIP.  Device array CONTENTS (cu_q/cu_k consistent with the host
+ *     totals, selected positions in [0, pos] or -1) are the caller's contract
+ *     and are not checked.
+ *   - The library is stateless apart from a per-device property cache and is
+ *     safe to call from several threads.
+ */
+#ifndef LIBDSA_H
+#define LIBDSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* dsa_stream_t; /* a hipStream_t; NULL = default stream */
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1,  /* null / misaligned pointer, inconsistent sizes */
+  DSA_ERR_UNSUPPORTED = 2,  /* a valid shape / dtype this build does not implement */
+  DSA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the size query */
+  DSA_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} dsa_status;
+
+typedef enum {
+  DSA_F32 = 0,
+  DSA_BF16 = 1,
+  DSA_FP8_E4M3 = 2          /* OCP E4M3FN: bias 7, max 448, no infinities */
+} dsa_dtype;
+
+typedef enum {
+  DSA_ACT_RELU = 0,         /* [P1] "Lightning indexer / Step 1": ReLU, chosen for throughput */
+  DSA_ACT_GELU = 1          /* [P2] 【闪电索引器】 names GELU: x * Phi(x), erf form */
+} dsa_act;
+
+/*
+ * Ragged batch of B sequences (a HOST struct; the arrays it points to are on
+ * the device).  Query row r of sequence b (cu_q[b] <= r < cu_q[b+1]) sits at
+ * position pos = ctx_b - q_b + (r - cu_q[b]), where q_b = cu_q[b+1]-cu_q[b]
+ * and ctx_b = cu_k[b+1]-cu_k[b] (the context includes the query rows).  Its
+ * candidates are the positions s in [0, pos]: "a preceding token" of [P1]
+ * "Lightning indexer / Step 1", read inclusively.  Key / latent row of
+ * position s is cu_k[b] + s.  Prefill: q_b = ctx_b.  Decode: q_b = 1.
+ */
+typedef struct {
+  int32_t num_seqs;         /* B >= 1 */
+  const int32_t* cu_q;      /* device [B+1], cu_q[0] = 0, non-decreasing */
+  const int32_t* cu_k;      /* device [B+1], cu_k[0] = 0, non-decreasing */
+  int32_t total_q;          /* host copy of cu_q[B] (>= 0) */
+  int32_t total_k;          /* host copy of cu_k[B] (>= 1) */
+  int32_t max_ctx;          /* host: max over b of ctx_b (an upper bound is fine) */
+} dsa_batch;
+
+/* Human-readable name of a status code (static string). */
+const char* dsa_status_string(dsa_status s);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* dsa_last_error(void);
+
+/* Library version string, e.g. "libdsa 0.1 gfx950". */
+const char* dsa_version(void);
+
+/*
+ * Lightning-indexer scores.  [P1] "Lightning indexer / Step 1", [P2] 【闪电索引器】:
+ *   I[r, s] = sum_{j < H_I} w[r, j] * act(q_idx[r, j, :] . k_idx[kbase + s, :])
+ * for every query row r and every candidate s in [0, pos_r].
+ *   q_idx   [total_q, H_I, d_I]   idx_dtype (FP8_E4M3 or F32), 16-B aligned
+ *   k_idx   [total_k, d_I]        idx_dtype, 16-B aligned (one key per token,
+ *                                 shared by all indexer heads)
+ *   w       [total_q, H_I]        fp32, 16-B aligned
+ *   scores  [total_q, ld_scores]  fp32 output, 16-B aligned; only s <= pos_r
+ *                                 is written; ld_scores >= max_ctx, % 4 == 0
+ * Arithmetic: FP8 x FP8 products are exact in fp32; dot products accumulate in
+ * fp32 (MFMA); act and the weighted head sum are fp32 in a fixed head order.
+ * Supported: FP8 with d_I = 128 and H_I in {16, 32, 48, 64}; F32 with
+ * d_I <= 256, H_I <= 64 and H_I * d_I <= 8192.
+ */
+dsa_status dsa_indexer_scores(const dsa_batch* batch,
+                              const void* q_idx, const void* k_idx, dsa_dtype idx_dtype,
+                              const float* w, int32_t H_I, int32_t d_I, dsa_act act,
+                              float* scores, int64_t ld_scores, dsa_stream_t stream);
+
+/*
+ * Causal top-k selection.  [P1] "Step 2", [P2] 【细粒度Token选择机制】: for each
+ * query keep only the candidates whose index scores rank in the top k.
+ * Order: score descending, ties to the lower position; -0 equals +0; NaN
+ * ranks below every number.  With n = pos_r + 1 candidates:
+ *   n <= k: idx[r] = 0, 1, ..., n-1 followed by -1 (every candidate);
+ *   n >  k: the k best positions in ascending order.
+ *   scores [total_q, ld_scores] fp32 (only s <= pos_r is read), 16-B aligned,
+ *          ld_scores >= max_ctx, % 4 == 0
+ *   idx    [total_q, k] int32 output, 16-B aligned
+ * Integer / bit operations only: the result is exact.  Supported: 1 <= k <= 2048.
+ * Workspace: none (ws may be NULL when dsa_topk_workspace_size gives 0).
+ */
+dsa_status dsa_topk_workspace_size(const dsa_batch* batch, int32_t k, size_t* bytes /* host */);
+dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores, int32_t k,
+                    int32_t* idx, void* ws, size_t ws_bytes, dsa_stream_t stream);
+
+/*
+ * Sparse MLA attention in MQA mode.  [P1] "Step 2" (attention between the
+ * query and the selected latent entries only) and "在MLA下實例化DSA" / [P2]
+ * 【MLA架构集成】 (one latent vector shared by all query heads).  For every
+ * query row r and head h, over S_r = the entries of idx[r, :] that are >= 0:
+ *   z_s = softmax_scale * q[r, h, :] . kv[kbase + s, :]        (all d_qk columns)
+ *   out[r, h, :] = sum_s softmax(z)_s * kv[kbase + s, 0:d_v]    (value = first d_v)
+ *   lse[r, h] = log sum_s exp(z_s)
+ * An empty S_r gives out = 0 and lse = -inf.
+ *   q    [total_q, H, d_qk]  dtype (BF16 or F32), 16-B aligned
+ *   kv   [total_k, d_qk]     dtype, 16-B aligned
+ *   idx  [total_q, k]        int32 positions within the sequence, or -1
+ *   out  [total_q, H, d_v]   dtype output, 16-B aligned
+ *   lse  [total_q, H]        fp32 output, or NULL
+ * Arithmetic (BF16): bf16 MFMA with fp32 accumulation, fp32 softmax
+ * statistics, probabilities rounded to bf16 for the value product, output
+ * rounded to nearest even.  Supported: BF16 with d_qk = 576, d_v = 512,
+ * H in {32, 64, 128}; F32 with d_qk <= 1024, d_v <= d_qk, H <= 128;
+ * 1 <= k <= 2048.  The workspace (possibly 0 bytes) holds split partials.
+ */
+dsa_status dsa_sparse_mla_attn_workspace_size(const dsa_batch* batch, dsa_dtype dtype, int32_t H,
+                                              int32_t k, int32_t d_v, size_t* bytes /* host */);
+dsa_status dsa_sparse_mla_attn(const dsa_batch* batch,
+                               const void* q, const void* kv, dsa_dtype dtype,
+                               const int32_t* idx, int32_t k,
+                               int32_t H, int32_t d_qk, int32_t d_v, float softmax_scale,
+                               void* out, float* lse,
+                               void* ws, size_t ws_bytes, dsa_stream_t stream);
+
+/*
+ * The three steps fused in one call, on one stream, with no host
+ * synchronisation.  Query rows are processed in chunks of q_block rows
+ * (bounded score workspace).  Rows with pos + 1 <= k skip the indexer and the
+ * selection: every candidate is selected, which is the masked dense-equivalent
+ * mode [P2] 【推理成本评估】 describes for short prefill.  The indices equal
+ * those of dsa_topk(dsa_indexer_scores(...)) bit for bit.
+ */
+typedef struct {
+  const dsa_batch* batch;
+  /* indexer */
+  const void* q_idx; const void* k_idx; dsa_dtype idx_dtype;
+  const float* w; int32_t H_I; int32_t d_I; dsa_act act;
+  /* attention */
+  const void* q; const void* kv; dsa_dtype dtype;
+  int32_t H; int32_t d_qk; int32_t d_v; float softmax_scale;
+  int32_t k;                /* tokens selected per query (2048 in the pages) */
+  int32_t q_block;          /* query rows per chunk; 0 = library default (4096) */
+  void* out; float* lse;    /* lse may be NULL */
+  int32_t* out_idx;         /* [total_q, k] selected positions, or NULL */
+} dsa_forward_params;
+
+dsa_status dsa_forward_workspace_size(const dsa_forward_params* p, size_t* bytes /* host */);
+dsa_status dsa_forward(const dsa_forward_params* p, void* ws, size_t ws_bytes, dsa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBDSA_H */

@@ -1,0 +1,326 @@
+// api.hip -- the libdsa C interface: host-side argument checks, workspace
+// layout and kernel launches.  Every check runs before the first HIP call, so
+// invalid calls never touch the device (and work without one).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/libdsa.h"
+#include "dsa_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dsa_status fail(dsa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+dsa_status hip_fail(hipError_t e, const char* what) {
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxDevices = 64;
+int g_cus[kMaxDevices];
+std::once_flag g_once[kMaxDevices];
+
+dsa_status device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DSA_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+  std::call_once(g_once[dev], [dev] {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_cus[dev] = n;
+  });
+  *cus = g_cus[dev];
+  return DSA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+dsa_status check_batch(const dsa_batch* b) {
+  if (!b) return fail(DSA_ERR_INVALID_ARG, "batch is NULL");
+  if (b->num_seqs < 1) return fail(DSA_ERR_INVALID_ARG, "num_seqs = %d, need >= 1", b->num_seqs);
+  if (!b->cu_q || !b->cu_k) return fail(DSA_ERR_INVALID_ARG, "cu_q / cu_k is NULL");
+  if (b->total_q < 0) return fail(DSA_ERR_INVALID_ARG, "total_q = %d < 0", b->total_q);
+  if (b->total_k < 1) return fail(DSA_ERR_INVALID_ARG, "total_k = %d, need >= 1", b->total_k);
+  if (b->max_ctx < 1 || b->max_ctx > b->total_k)
+    return fail(DSA_ERR_INVALID_ARG, "max_ctx = %d outside [1, total_k = %d]", b->max_ctx, b->total_k);
+  if (b->total_q > b->total_k) return fail(DSA_ERR_INVALID_ARG, "total_q %d > total_k %d", b->total_q, b->total_k);
+  return DSA_OK;
+}
+
+dsa::BatchView view(const dsa_batch* b, int32_t r0, int32_t r1) {
+  return dsa::BatchView{b->cu_q, b->cu_k, b->num_seqs, r0, r1, b->max_ctx};
+}
+
+dsa_status check_indexer(const dsa_batch* b, const void* q_idx, const void* k_idx, dsa_dtype dt, const float* w,
+                         int32_t H_I, int32_t d_I, dsa_act act) {
+  if (!q_idx || !k_idx || !w) return fail(DSA_ERR_INVALID_ARG, "indexer input pointer is NULL");
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w))
+    return fail(DSA_ERR_INVALID_ARG, "indexer inputs must be 16-byte aligned");
+  if (act != DSA_ACT_RELU && act != DSA_ACT_GELU) return fail(DSA_ERR_INVALID_ARG, "unknown activation %d", (int)act);
+  if (H_I < 1 || d_I < 1) return fail(DSA_ERR_INVALID_ARG, "H_I = %d, d_I = %d", H_I, d_I);
+  if (dt == DSA_FP8_E4M3) {
+    if (d_I != 128) return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer needs d_I = 128 (got %d)", d_I);
+    if (H_I % 16 != 0 || H_I > 64) return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer needs H_I in {16,32,48,64} (got %d)", H_I);
+  } else if (dt == DSA_F32) {
+    if (d_I > 256 || H_I > 64 || H_I * d_I > 8192)
+      return fail(DSA_ERR_UNSUPPORTED, "F32 indexer needs d_I <= 256, H_I <= 64, H_I * d_I <= 8192");
+  } else {
+    return fail(DSA_ERR_UNSUPPORTED, "indexer dtype must be FP8_E4M3 or F32");
+  }
+  (void)b;
+  return DSA_OK;
+}
+
+dsa_status check_scores(const dsa_batch* b, const void* scores, int64_t ld) {
+  if (!scores) return fail(DSA_ERR_INVALID_ARG, "scores is NULL");
+  if (!aligned16(scores)) return fail(DSA_ERR_INVALID_ARG, "scores must be 16-byte aligned");
+  if (ld < b->max_ctx || ld % 4 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "ld_scores = %lld must be >= max_ctx (%d) and a multiple of 4", (long long)ld,
+                b->max_ctx);
+  return DSA_OK;
+}
+
+dsa_status check_k(int32_t k) {
+  if (k < 1 || k > 2048) return fail(DSA_ERR_UNSUPPORTED, "k = %d outside [1, 2048]", k);
+  return DSA_OK;
+}
+
+dsa_status check_attention(const void* q, const void* kv, dsa_dtype dt, const int32_t* idx, int32_t k, int32_t H,
+                           int32_t d_qk, int32_t d_v, float scale, const void* out, const float* lse) {
+  if (!q || !kv || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "attention pointer is NULL");
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || !aligned16(idx))
+    return fail(DSA_ERR_INVALID_ARG, "attention buffers must be 16-byte aligned");
+  (void)lse;
+  if (dsa_status s = check_k(k)) return s;
+  if (!(scale == scale)) return fail(DSA_ERR_INVALID_ARG, "softmax_scale is NaN");
+  if (H < 1 || d_qk < 1 || d_v < 1 || d_v > d_qk) return fail(DSA_ERR_INVALID_ARG, "bad H / d_qk / d_v");
+  if (dt == DSA_BF16) {
+    if (d_qk != 576 || d_v != 512) return fail(DSA_ERR_UNSUPPORTED, "BF16 attention needs d_qk = 576, d_v = 512");
+    if (H != 32 && H != 64 && H != 128) return fail(DSA_ERR_UNSUPPORTED, "BF16 attention needs H in {32, 64, 128}");
+  } else if (dt == DSA_F32) {
+    if (d_qk > 1024 || H > 128) return fail(DSA_ERR_UNSUPPORTED, "F32 attention needs d_qk <= 1024, H <= 128");
+  } else {
+    return fail(DSA_ERR_UNSUPPORTED, "attention dtype must be BF16 or F32");
+  }
+  return DSA_OK;
+}
+
+size_t attention_ws_bytes(int32_t rows, int splits, int32_t H, int32_t d_v) {
+  if (splits <= 1) return 0;
+  return round_up((size_t)rows * splits * H * d_v * sizeof(float), 256) +
+         round_up((size_t)rows * splits * H * sizeof(float), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP";
+  }
+  return "DSA_ERR_UNKNOWN";
+}
+
+const char* dsa_last_error(void) { return g_err; }
+
+const char* dsa_version(void) { return "libdsa 0.1 gfx950"; }
+
+dsa_status dsa_indexer_scores(const dsa_batch* batch, const void* q_idx, const void* k_idx, dsa_dtype idx_dtype,
+                              const float* w, int32_t H_I, int32_t d_I, dsa_act act, float* scores,
+                              int64_t ld_scores, dsa_stream_t stream) {
+  g_err[0] = 0;
+  if (dsa_status s = check_batch(batch)) return s;
+  if (dsa_status s = check_indexer(batch, q_idx, k_idx, idx_dtype, w, H_I, d_I, act)) return s;
+  if (dsa_status s = check_scores(batch, scores, ld_scores)) return s;
+  if (batch->total_q == 0) return DSA_OK;
+  int cus = 0;
+  if (dsa_status s = device_cus(&cus)) return s;
+  dsa::IndexerLaunch L{view(batch, 0, batch->total_q), 0, q_idx, k_idx, w, scores, ld_scores, H_I, d_I, (int32_t)act,
+                       idx_dtype == DSA_FP8_E4M3, cus};
+  hipError_t e = dsa::launch_indexer(L, (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "indexer launch");
+}
+
+dsa_status dsa_topk_workspace_size(const dsa_batch* batch, int32_t k, size_t* bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is NULL");
+  if (dsa_status s = check_batch(batch)) return s;
+  if (dsa_status s = check_k(k)) return s;
+  *bytes = 0;
+  return DSA_OK;
+}
+
+dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores, int32_t k, int32_t* idx,
+                    void* ws, size_t ws_bytes, dsa_stream_t stream) {
+  g_err[0] = 0;
+  (void)ws;
+  (void)ws_bytes;
+  if (dsa_status s = check_batch(batch)) return s;
+  if (dsa_status s = check_scores(batch, scores, ld_scores)) return s;
+  if (dsa_status s = check_k(k)) return s;
+  if (!idx || !aligned16(idx)) return fail(DSA_ERR_INVALID_ARG, "idx is NULL or not 16-byte aligned");
+  if (batch->total_q == 0) return DSA_OK;
+  dsa::TopkLaunch L{view(batch, 0, batch->total_q), scores, ld_scores, k, idx};
+  hipError_t e = dsa::launch_topk(L, (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "topk launch");
+}
+
+dsa_status dsa_sparse_mla_attn_workspace_size(const dsa_batch* batch, dsa_dtype dtype, int32_t H, int32_t k,
+                                              int32_t d_v, size_t* bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is NULL");
+  if (dsa_status s = check_batch(batch)) return s;
+  if (dsa_status s = check_k(k)) return s;
+  if (H < 1 || d_v < 1) return fail(DSA_ERR_INVALID_ARG, "bad H / d_v");
+  int cus = 0;
+  if (dsa_status s = device_cus(&cus)) return s;
+  const int splits = dsa::attention_splits(batch->total_q, k, dtype == DSA_BF16, cus);
+  *bytes = attention_ws_bytes(batch->total_q, splits, H, d_v);
+  return DSA_OK;
+}
+
+dsa_status dsa_sparse_mla_attn(const dsa_batch* batch, const void* q, const void* kv, dsa_dtype dtype,
+                               const int32_t* idx, int32_t k, int32_t H, int32_t d_qk, int32_t d_v,
+                               float softmax_scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                               dsa_stream_t stream) {
+  g_err[0] = 0;
+  if (dsa_status s = check_batch(batch)) return s;
+  if (dsa_status s = check_attention(q, kv, dtype, idx, k, H, d_qk, d_v, softmax_scale, out, lse)) return s;
+  if (batch->total_q == 0) return DSA_OK;
+  int cus = 0;
+  if (dsa_status s = device_cus(&cus)) return s;
+  const int splits = dsa::attention_splits(batch->total_q, k, dtype == DSA_BF16, cus);
+  const size_t need = attention_ws_bytes(batch->total_q, splits, H, d_v);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
+    return fail(DSA_ERR_WORKSPACE, "attention workspace: need %zu bytes (got %zu)", need, ws_bytes);
+  dsa::AttnLaunch L{view(batch, 0, batch->total_q), q, kv, idx, k, H, d_qk, d_v, softmax_scale, out, lse,
+                    dtype == DSA_BF16, splits, nullptr, nullptr};
+  if (splits > 1) {
+    L.ws_o = (float*)ws;
+    L.ws_lse = (float*)((char*)ws + round_up((size_t)batch->total_q * splits * H * d_v * sizeof(float), 256));
+  }
+  hipError_t e = dsa::launch_attention(L, (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "attention launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+struct ForwardPlan {
+  int32_t qb;       // rows per chunk
+  int64_t ld;       // score row stride
+  size_t off_scores, off_idx, off_attn, total;
+  int max_splits;
+};
+
+dsa_status check_forward(const dsa_forward_params* p) {
+  if (!p) return fail(DSA_ERR_INVALID_ARG, "params is NULL");
+  if (dsa_status s = check_batch(p->batch)) return s;
+  if (dsa_status s = check_indexer(p->batch, p->q_idx, p->k_idx, p->idx_dtype, p->w, p->H_I, p->d_I, p->act)) return s;
+  if (p->q_block < 0) return fail(DSA_ERR_INVALID_ARG, "q_block = %d < 0", p->q_block);
+  if (p->out_idx && !aligned16(p->out_idx)) return fail(DSA_ERR_INVALID_ARG, "out_idx must be 16-byte aligned");
+  // idx pointer is internal (workspace or out_idx); check the rest with a placeholder
+  static const int32_t kDummy[4] = {0, 0, 0, 0};
+  return check_attention(p->q, p->kv, p->dtype, kDummy, p->k, p->H, p->d_qk, p->d_v, p->softmax_scale, p->out,
+                         p->lse);
+}
+
+dsa_status plan_forward(const dsa_forward_params* p, int cus, ForwardPlan* f) {
+  const dsa_batch* b = p->batch;
+  f->qb = p->q_block > 0 ? p->q_block : 4096;
+  if (f->qb > b->total_q) f->qb = b->total_q > 0 ? b->total_q : 1;
+  f->ld = (int64_t)round_up((size_t)b->max_ctx, 64);
+  size_t off = 0;
+  f->off_scores = off;
+  off += round_up((size_t)f->qb * (size_t)f->ld * sizeof(float), 256);
+  f->off_idx = off;
+  if (!p->out_idx) off += round_up((size_t)f->qb * p->k * sizeof(int32_t), 256);
+  f->off_attn = off;
+  const int32_t last = b->total_q % f->qb;
+  const int s_full = dsa::attention_splits(f->qb, p->k, p->dtype == DSA_BF16, cus);
+  const int s_last = last ? dsa::attention_splits(last, p->k, p->dtype == DSA_BF16, cus) : 1;
+  const size_t a_full = attention_ws_bytes(f->qb, s_full, p->H, p->d_v);
+  const size_t a_last = last ? attention_ws_bytes(last, s_last, p->H, p->d_v) : 0;
+  off += a_full > a_last ? a_full : a_last;
+  f->max_splits = s_full > s_last ? s_full : s_last;
+  f->total = off;
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_forward_workspace_size(const dsa_forward_params* p, size_t* bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is NULL");
+  if (dsa_status s = check_forward(p)) return s;
+  int cus = 0;
+  if (dsa_status s = device_cus(&cus)) return s;
+  ForwardPlan f;
+  if (dsa_status s = plan_forward(p, cus, &f)) return s;
+  *bytes = f.total;
+  return DSA_OK;
+}
+
+dsa_status dsa_forward(const dsa_forward_params* p, void* ws, size_t ws_bytes, dsa_stream_t stream) {
+  g_err[0] = 0;
+  if (dsa_status s = check_forward(p)) return s;
+  const dsa_batch* b = p->batch;
+  if (b->total_q == 0) return DSA_OK;
+  int cus = 0;
+  if (dsa_status s = device_cus(&cus)) return s;
+  ForwardPlan f;
+  if (dsa_status s = plan_forward(p, cus, &f)) return s;
+  if (!ws || ws_bytes < f.total || !aligned16(ws))
+    return fail(DSA_ERR_WORKSPACE, "forward workspace: need %zu bytes (got %zu)", f.total, ws_bytes);
+  hipStream_t st = (hipStream_t)stream;
+  char* base = (char*)ws;
+  float* scores = (float*)(base + f.off_scores);
+  for (int32_t r0 = 0; r0 < b->total_q; r0 += f.qb) {
+    const int32_t r1 = r0 + f.qb < b->total_q ? r0 + f.qb : b->total_q;
+    const dsa::BatchView v = view(b, r0, r1);
+    int32_t* idx = p->out_idx ? p->out_idx + (int64_t)r0 * p->k : (int32_t*)(base + f.off_idx);
+    // rows with pos + 1 <= k select every candidate: their scores are never read
+    dsa::IndexerLaunch IL{v, p->k, p->q_idx, p->k_idx, p->w, scores, f.ld, p->H_I, p->d_I, (int32_t)p->act,
+                          p->idx_dtype == DSA_FP8_E4M3, cus};
+    hipError_t e = dsa::launch_indexer(IL, st);
+    if (e != hipSuccess) return hip_fail(e, "forward indexer launch");
+    dsa::TopkLaunch TL{v, scores, f.ld, p->k, idx};
+    e = dsa::launch_topk(TL, st);
+    if (e != hipSuccess) return hip_fail(e, "forward topk launch");
+    const int splits = dsa::attention_splits(r1 - r0, p->k, p->dtype == DSA_BF16, cus);
+    dsa::AttnLaunch AL{v, p->q, p->kv, idx, p->k, p->H, p->d_qk, p->d_v, p->softmax_scale, p->out, p->lse,
+                       p->dtype == DSA_BF16, splits, nullptr, nullptr};
+    if (splits > 1) {
+      AL.ws_o = (float*)(base + f.off_attn);
+      AL.ws_lse = (float*)(base + f.off_attn +
+                           round_up((size_t)(r1 - r0) * splits * p->H * p->d_v * sizeof(float), 256));
+    }
+    e = dsa::launch_attention(AL, st);
+    if (e != hipSuccess) return hip_fail(e, "forward attention launch");
+  }
+  return DSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// dsa_common.h -- device helpers shared by the libdsa kernels (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define DSA_LDS __attribute__((address_space(3)))
+
+namespace dsa {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+
+constexpr int kWave = 64;
+
+// Where a query row sits in the ragged batch: position of the query, first
+// key/latent row of its sequence.  Query row r of sequence b has position
+// ctx_b - q_b + (r - cu_q[b]) and sees the candidates [0, pos].
+struct RowInfo {
+  int32_t pos;
+  int32_t kbase;
+};
+
+__device__ inline RowInfo locate_row(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+                                     int num_seqs, int32_t r) {
+  int lo = 0, hi = num_seqs;  // invariant: cu_q[lo] <= r < cu_q[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (cu_q[mid] <= r) lo = mid; else hi = mid;
+  }
+  const int32_t q0 = cu_q[lo], q1 = cu_q[lo + 1];
+  const int32_t k0 = cu_k[lo], k1 = cu_k[lo + 1];
+  RowInfo ri;
+  ri.pos = (k1 - k0) - (q1 - q0) + (r - q0);
+  ri.kbase = k0;
+  return ri;
+}
+
+__device__ inline float wave_max(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ inline float wave_sum(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Inclusive prefix sum over a wave (lane order).
+__device__ inline int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ inline unsigned ballot_lo(bool p) { return (unsigned)__ballot(p); }
+
+}  // namespace dsa

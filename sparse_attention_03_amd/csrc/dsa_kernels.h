@@ -1,0 +1,66 @@
+// dsa_kernels.h -- internal launch interface between the C ABI layer and the
+// kernels.  Not installed; the public interface is include/libdsa.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// Rows [row_begin, row_end) of the global query-row space are processed; row
+// r's outputs go to row (r - row_begin) of the output arrays, except the
+// query-side inputs, which are always indexed by the global row.
+struct BatchView {
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t num_seqs;
+  int32_t row_begin;
+  int32_t row_end;
+  int32_t max_ctx;
+};
+
+struct IndexerLaunch {
+  BatchView b;
+  int32_t skip_n;          // rows with pos + 1 <= skip_n are not computed
+  const void* q_idx;       // [total_q, H_I, d_I]
+  const void* k_idx;       // [total_k, d_I]
+  const float* w;          // [total_q, H_I]
+  float* scores;           // [row_end - row_begin, ld]
+  int64_t ld;
+  int32_t H_I, d_I;
+  int32_t act;             // 0 relu, 1 gelu
+  bool fp8;
+  int32_t num_cus;
+};
+
+struct TopkLaunch {
+  BatchView b;
+  const float* scores;     // [row_end - row_begin, ld]
+  int64_t ld;
+  int32_t k;
+  int32_t* idx;            // [row_end - row_begin, k]
+};
+
+struct AttnLaunch {
+  BatchView b;
+  const void* q;           // [total_q, H, d_qk]
+  const void* kv;          // [total_k, d_qk]
+  const int32_t* idx;      // [row_end - row_begin, k]
+  int32_t k;
+  int32_t H, d_qk, d_v;
+  float scale;
+  void* out;               // [total_q, H, d_v] (global rows)
+  float* lse;              // [total_q, H] or null (global rows)
+  bool bf16;
+  int32_t splits;          // >1: partials in ws, then a merge
+  float* ws_o;             // [rows, splits, H, d_v]
+  float* ws_lse;           // [rows, splits, H]
+};
+
+hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s);
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
+hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
+
+// Number of key-splits the attention uses for `rows` query rows.
+int attention_splits(int rows, int k, bool bf16, int num_cus);
+
+}  // namespace dsa

@@ -1,0 +1,150 @@
+"""The C interface without a GPU: the library loads, exports every entry point
+the header declares, and rejects invalid calls on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libdsa.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    lib = os.path.join(ROOT, "sparse_attention_03_amd", "lib", "libdsa.so")
+    if not os.path.exists(lib):
+        from sparse_attention_03_amd import build
+        build.build()
+    from sparse_attention_03_amd import libdsa
+    return libdsa
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(L.EXPORTED)
+
+
+def test_status_strings_and_version(L):
+    assert L._lib.dsa_status_string(L.DSA_OK) == b"DSA_OK"
+    assert L._lib.dsa_status_string(L.DSA_ERR_WORKSPACE) == b"DSA_ERR_WORKSPACE"
+    assert L.version().startswith("libdsa")
+
+
+class FakeTensor:
+    """Just enough of a tensor for the binding: a pointer, a shape, a dtype."""
+
+    def __init__(self, ptr, shape, dtype, stride0=None):
+        import torch
+        self._ptr, self.shape, self.dtype = ptr, shape, dtype
+        self._stride0 = stride0 if stride0 is not None else (shape[1] if len(shape) > 1 else 1)
+        self._torch = torch
+
+    def data_ptr(self):
+        return self._ptr
+
+    def stride(self, i):
+        return self._stride0
+
+    def numel(self):
+        n = 1
+        for s in self.shape:
+            n *= s
+        return n
+
+    def element_size(self):
+        return 1
+
+
+def _batch(L, cu=0x1000, total_q=8, total_k=8, max_ctx=8, nseq=1):
+    b = L.DsaBatch(nseq, cu, cu + 0x100, total_q, total_k, max_ctx)
+    return b
+
+
+def _call_indexer(L, b, q=0x10000, k=0x20000, w=0x30000, s=0x40000, H_I=64, d_I=128, dt=2, act=0, ld=64):
+    return L._lib.dsa_indexer_scores(ctypes.byref(b), q, k, dt, w, H_I, d_I, act, s, ld, None)
+
+
+def test_indexer_validation(L):
+    b = _batch(L)
+    assert _call_indexer(L, b, q=0) == L.DSA_ERR_INVALID_ARG
+    assert b"NULL" in L._lib.dsa_last_error()
+    assert _call_indexer(L, b, q=0x10004) == L.DSA_ERR_INVALID_ARG        # misaligned
+    assert _call_indexer(L, b, d_I=64) == L.DSA_ERR_UNSUPPORTED           # fp8 needs d_I 128
+    assert _call_indexer(L, b, H_I=20) == L.DSA_ERR_UNSUPPORTED
+    assert _call_indexer(L, b, dt=1) == L.DSA_ERR_UNSUPPORTED             # bf16 indexer
+    assert _call_indexer(L, b, act=7) == L.DSA_ERR_INVALID_ARG
+    assert _call_indexer(L, b, ld=4) == L.DSA_ERR_INVALID_ARG             # ld < max_ctx
+    assert _call_indexer(L, b, ld=66) == L.DSA_ERR_INVALID_ARG            # ld % 4
+    assert _call_indexer(L, _batch(L, nseq=0)) == L.DSA_ERR_INVALID_ARG
+    assert _call_indexer(L, _batch(L, cu=0)) == L.DSA_ERR_INVALID_ARG
+    assert _call_indexer(L, _batch(L, max_ctx=9)) == L.DSA_ERR_INVALID_ARG  # > total_k
+    assert _call_indexer(L, _batch(L, total_q=9)) == L.DSA_ERR_INVALID_ARG  # more queries than keys
+    assert L._lib.dsa_indexer_scores(None, 0x10000, 0x20000, 2, 0x30000, 64, 128, 0, 0x40000, 64, None) \
+        == L.DSA_ERR_INVALID_ARG
+
+
+def test_topk_validation(L):
+    b = _batch(L)
+    f = L._lib.dsa_topk
+    assert f(ctypes.byref(b), 0x40000, 64, 0, 0x50000, None, 0, None) == L.DSA_ERR_UNSUPPORTED     # k = 0
+    assert f(ctypes.byref(b), 0x40000, 64, 4096, 0x50000, None, 0, None) == L.DSA_ERR_UNSUPPORTED  # k > 2048
+    assert f(ctypes.byref(b), 0x40000, 64, 32, 0, None, 0, None) == L.DSA_ERR_INVALID_ARG
+    assert f(ctypes.byref(b), 0, 64, 32, 0x50000, None, 0, None) == L.DSA_ERR_INVALID_ARG
+    n = ctypes.c_size_t(123)
+    assert L._lib.dsa_topk_workspace_size(ctypes.byref(b), 32, ctypes.byref(n)) == L.DSA_OK and n.value == 0
+
+
+def test_attention_validation(L):
+    b = _batch(L)
+    f = L._lib.dsa_sparse_mla_attn
+
+    def call(q=0x10000, kv=0x20000, dt=1, idx=0x30000, k=32, H=128, dqk=576, dv=512, scale=0.1, out=0x40000):
+        return f(ctypes.byref(b), q, kv, dt, idx, k, H, dqk, dv, scale, out, None, None, 0, None)
+
+    assert call(q=0) == L.DSA_ERR_INVALID_ARG
+    assert call(out=0x40008) == L.DSA_ERR_INVALID_ARG
+    assert call(dqk=512) == L.DSA_ERR_UNSUPPORTED
+    assert call(H=96) == L.DSA_ERR_UNSUPPORTED
+    assert call(dt=2) == L.DSA_ERR_UNSUPPORTED
+    assert call(k=3000) == L.DSA_ERR_UNSUPPORTED
+    assert call(dv=600) == L.DSA_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == L.DSA_ERR_INVALID_ARG
+    assert call(dt=0, dqk=2048) == L.DSA_ERR_UNSUPPORTED
+
+
+def test_forward_validation(L):
+    import torch
+    b = _batch(L)
+    t8 = FakeTensor(0x10000, (8, 64, 128), torch.float8_e4m3fn)
+    k8 = FakeTensor(0x20000, (8, 128), torch.float8_e4m3fn)
+    w = FakeTensor(0x30000, (8, 64), torch.float32)
+    q = FakeTensor(0x40000, (8, 128, 576), torch.bfloat16)
+    kv = FakeTensor(0x50000, (8, 576), torch.bfloat16)
+    out = FakeTensor(0x60000, (8, 128, 512), torch.bfloat16)
+    p = L.forward_params(b, t8, k8, w, q, kv, 2048, 512, 0.07, out)
+    p.q_block = -1
+    assert L._lib.dsa_forward(ctypes.byref(p), None, 0, None) == L.DSA_ERR_INVALID_ARG
+    p.q_block = 0
+    p.d_v = 500
+    assert L._lib.dsa_forward(ctypes.byref(p), None, 0, None) == L.DSA_ERR_UNSUPPORTED
+    p.d_v = 512
+    p.w = 0
+    assert L._lib.dsa_forward(ctypes.byref(p), None, 0, None) == L.DSA_ERR_INVALID_ARG
+    assert L._lib.dsa_forward(None, None, 0, None) == L.DSA_ERR_INVALID_ARG
+    n = ctypes.c_size_t(0)
+    assert L._lib.dsa_forward_workspace_size(ctypes.byref(p), None) == L.DSA_ERR_INVALID_ARG

@@ -1,0 +1,114 @@
+"""Parity of dsa_sparse_mla_attn (HIP) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dsa_check import TOL_ATTN_BF16, TOL_ATTN_F32, announce, host, oracle_attention_on, row_norm_err
+from sparse_attention_03_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    from sparse_attention_03_amd import dsa as d
+    return d
+
+
+def random_selection(p, k, seed):
+    """Ascending distinct positions in [0, pos] per row (min(n, k) of them), -1 padded."""
+    rng = np.random.default_rng(seed)
+    pos = p.positions()
+    idx = -np.ones((p.total_q, k), np.int32)
+    for i, ps in enumerate(pos):
+        n = ps + 1
+        if n <= k:
+            idx[i, :n] = np.arange(n)
+        else:
+            idx[i] = np.sort(rng.choice(n, k, replace=False))
+    return idx
+
+
+def _compare(dsa, p, idx_np, tol):
+    idx = torch.from_numpy(idx_np).to(DEV)
+    out, lse = dsa.sparse_mla_attn(p, idx)
+    ref_o, ref_l = oracle_attention_on(p, idx_np)
+    got = out.float().cpu().numpy()
+    err = row_norm_err(got, ref_o)
+    lse_g = lse.cpu().numpy()
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(np.isfinite(lse_g), fin)
+    lerr = float(np.max(np.abs(lse_g[fin] - ref_l[fin]))) if fin.any() else 0.0
+    print(f"row-normalised error {err:.3e}, lse abs error {lerr:.3e}")
+    assert err <= tol
+    assert lerr <= 1e-2 if tol >= 1e-3 else lerr <= 1e-4
+    return out, lse
+
+
+@pytest.mark.parametrize("H", [32, 64, 128])
+def test_bf16_prefill_rows(dsa, H):
+    announce("attention bf16 prefill", H)
+    p = gen.make_problem("attn", [700], [700], H_I=16, H=H, k=256, device=DEV, seed=H)
+    _compare(dsa, p, random_selection(p, 256, H), TOL_ATTN_BF16)
+
+
+def test_bf16_decode_rows_use_key_splits(dsa):
+    announce("attention bf16 decode split")
+    p = gen.make_problem("attn", [5000, 3000, 2100, 2048, 700, 4500], [1] * 6, H_I=16, H=128, k=2048, device=DEV,
+                         seed=7)
+    _compare(dsa, p, random_selection(p, 2048, 7), TOL_ATTN_BF16)
+
+
+def test_bf16_padding_holes_and_empty_rows(dsa):
+    announce("attention bf16 padding")
+    p = gen.make_problem("attn", [300], [300], H_I=16, H=128, k=192, device=DEV, seed=9)
+    idx = random_selection(p, 192, 9)
+    idx[5] = -1                       # empty: out 0, lse -inf
+    idx[200, ::3] = -1                # holes anywhere in the list
+    idx[201, 64:128] = -1             # a whole tile of padding in the middle
+    out, lse = _compare(dsa, p, idx, TOL_ATTN_BF16)
+    assert torch.all(out[5] == 0) and torch.all(torch.isneginf(lse[5]))
+
+
+def test_bf16_only_selected_rows_matter(dsa):
+    announce("attention bf16 non-selected rows")
+    p = gen.make_problem("attn", [400, 300], [50, 300], H_I=16, H=64, k=128, device=DEV, seed=11)
+    idx_np = random_selection(p, 128, 11)
+    idx = torch.from_numpy(idx_np).to(DEV)
+    out1, lse1 = dsa.sparse_mla_attn(p, idx)
+    used = np.zeros(p.total_k, bool)
+    pos = p.positions()
+    base = np.repeat(p.cu_k_host[:-1], np.diff(p.cu_q_host))
+    for i in range(p.total_q):
+        sel = idx_np[i][idx_np[i] >= 0]
+        used[base[i] + sel] = True
+    garbage = torch.from_numpy(~used).to(DEV)
+    p.kv[garbage] = torch.tensor(300.0, dtype=torch.bfloat16, device=DEV)
+    out2, lse2 = dsa.sparse_mla_attn(p, idx)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_bf16_heads_share_the_latent(dsa):
+    announce("attention bf16 identical heads")
+    p = gen.make_problem("attn", [500], [500], H_I=16, H=128, k=256, device=DEV, seed=12)
+    p.q[:, 77] = p.q[:, 3]
+    out, _ = dsa.sparse_mla_attn(p, torch.from_numpy(random_selection(p, 256, 12)).to(DEV))
+    assert torch.equal(out[:, 77], out[:, 3])
+
+
+def test_fp32_tiny_config(dsa):
+    announce("attention tiny_fp32")
+    p = gen.make_config("tiny_fp32", device=DEV)
+    rng = np.random.default_rng(0)
+    scores = rng.standard_normal((p.total_q, 256)).astype(np.float32)
+    idx = oracle.topk(p.cu_q_host, p.cu_k_host, scores, p.k)
+    _compare(dsa, p, idx, TOL_ATTN_F32)
+
+
+def test_fp32_with_splits_not_used(dsa):
+    announce("attention fp32 ragged")
+    p = gen.make_problem("attn", [90, 40], [3, 40], H_I=4, d_I=32, H=5, d_qk=48, d_v=40, k=24,
+                         idx_dtype=torch.float32, dtype=torch.float32, device=DEV, seed=13)
+    _compare(dsa, p, random_selection(p, 24, 13), TOL_ATTN_F32)

@@ -1,0 +1,129 @@
+"""Parity of dsa_indexer_scores (HIP) against the CPU oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dsa_check import (TOL_SCORES_F32, TOL_SCORES_FP8, announce, causal_mask, host, row_norm_err, rows_of)
+from sparse_attention_03_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    from sparse_attention_03_amd import dsa as d
+    return d
+
+
+def _oracle_scores(p, act=0, rows=None, ld=None):
+    q_idx, w, _ = rows_of(p, rows)
+    return oracle.indexer(p.cu_q_host, p.cu_k_host, q_idx, host(p.k_idx), w, act=act, ld=ld, rows=rows)
+
+
+def _ragged(H_I, integer, seed, dtype=gen.E4M3):
+    return gen.make_problem("ragged", [300, 77, 1000, 129], [300, 5, 3, 64], H_I=H_I, H=32, k=64,
+                            idx_dtype=dtype, integer=integer, device=DEV, seed=seed)
+
+
+@pytest.mark.parametrize("H_I", [16, 32, 48, 64])
+def test_fp8_integer_inputs_bit_exact(dsa, H_I):
+    announce("indexer fp8 integer", H_I)
+    p = _ragged(H_I, True, 1)
+    got = dsa.indexer_scores(p).cpu().numpy()
+    ld = got.shape[1]
+    ref = _oracle_scores(p, ld=ld)
+    mask = causal_mask(p, None, ld)
+    assert np.array_equal(got[mask], ref[mask].astype(np.float32))
+    assert np.all(np.isnan(got[~mask]))   # nothing written beyond the causal bound
+
+
+@pytest.mark.parametrize("H_I", [16, 64])
+@pytest.mark.parametrize("act", [0, 1])
+def test_fp8_random_inputs(dsa, H_I, act):
+    announce("indexer fp8 random", H_I, act)
+    p = _ragged(H_I, False, 2)
+    got = dsa.indexer_scores(p, act=act).cpu().numpy()
+    ld = got.shape[1]
+    ref = _oracle_scores(p, act=act, ld=ld)
+    mask = causal_mask(p, None, ld)
+    err = row_norm_err(got, ref, mask)
+    print("row-normalised error", err)
+    assert err <= TOL_SCORES_FP8
+    assert err <= 1e-4   # exact fp8 products, MFMA fp32 accumulation: far inside the bar
+
+
+def test_fp8_every_code_decodes_like_the_format(dsa):
+    """Keys carry every finite e4m3 code in one column; a one-hot query reads it."""
+    announce("indexer fp8 code table")
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    n = len(codes)
+    L = n + 2
+    k_idx = np.zeros((L, 128), np.uint8)
+    k_idx[2:, 5] = codes
+    q_idx = np.zeros((L, 16, 128), np.uint8)
+    q_idx[:, 3, 5] = 0x38          # +1.0, head 3
+    q_idx[1::2, 3, 5] = 0xB8       # -1.0 on odd rows: negative codes become positive
+    w = np.zeros((L, 16), np.float32)
+    w[:, 3] = 1.0
+    p = gen.make_problem("codes", [L], [L], H_I=16, H=32, k=64, device=DEV)
+    p.q_idx = torch.from_numpy(q_idx).to(DEV).view(torch.float8_e4m3fn)
+    p.k_idx = torch.from_numpy(k_idx).to(DEV).view(torch.float8_e4m3fn)
+    p.w = torch.from_numpy(w).to(DEV)
+    got = dsa.indexer_scores(p).cpu().numpy()
+    vals = np.array([oracle.e4m3_value(c) for c in codes])
+    for row in (L - 2, L - 1):
+        sign = -1.0 if row % 2 else 1.0
+        want = np.maximum(sign * vals, 0.0).astype(np.float32)
+        assert np.array_equal(got[row, 2:L], want)
+
+
+def test_fp32_tiny_config(dsa):
+    announce("indexer tiny_fp32")
+    p = gen.make_config("tiny_fp32", device=DEV)
+    got = dsa.indexer_scores(p).cpu().numpy()
+    ld = got.shape[1]
+    ref = _oracle_scores(p, ld=ld)
+    mask = causal_mask(p, None, ld)
+    err = row_norm_err(got, ref, mask)
+    print("row-normalised error", err)
+    assert err <= TOL_SCORES_F32
+
+
+def test_fp32_gelu_and_ragged(dsa):
+    announce("indexer fp32 gelu ragged")
+    p = gen.make_problem("f32", [130, 40], [130, 2], H_I=3, d_I=20, H=8, d_qk=80, d_v=64, k=32,
+                         idx_dtype=torch.float32, dtype=torch.float32, w_scale=1.0, device=DEV, seed=3)
+    for act in (0, 1):
+        got = dsa.indexer_scores(p, act=act).cpu().numpy()
+        ref = _oracle_scores(p, act=act, ld=got.shape[1])
+        mask = causal_mask(p, None, got.shape[1])
+        assert row_norm_err(got, ref, mask) <= TOL_SCORES_F32
+
+
+def test_prefill_8k_sampled_rows(dsa):
+    announce("indexer prefill_8k sampled")
+    p = gen.make_config("prefill_8k", device=DEV)
+    got = dsa.indexer_scores(p)
+    rows = np.array([0, 1, 63, 64, 2047, 2048, 4095, 5000, 8190, 8191], np.int32)
+    ref = _oracle_scores(p, rows=rows, ld=got.shape[1])
+    g = got[torch.as_tensor(rows, dtype=torch.long, device=DEV)].cpu().numpy()
+    mask = causal_mask(p, rows, got.shape[1])
+    err = row_norm_err(g, ref, mask)
+    print("row-normalised error", err)
+    assert err <= TOL_SCORES_FP8 and err <= 1e-4
+
+
+def test_decode_64x32k_sampled_rows(dsa):
+    announce("indexer decode_64x32k sampled")
+    p = gen.make_config("decode_64x32k", device=DEV)
+    got = dsa.indexer_scores(p)
+    rows = np.array([0, 17, 63], np.int32)
+    ref = _oracle_scores(p, rows=rows, ld=got.shape[1])
+    g = got[torch.as_tensor(rows, dtype=torch.long, device=DEV)].cpu().numpy()
+    err = row_norm_err(g, ref, causal_mask(p, rows, got.shape[1]))
+    print("row-normalised error", err)
+    assert err <= 1e-4

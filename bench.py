@@ -98,7 +98,7 @@ def kernel_times(p, reps=1):
     return {k: v / reps for k, v in tot.items()}
 
 
-def cpu_baseline(p, work, n_rows=32, seed=0):
+def cpu_baseline(p, work, n_rows=256, seed=0):
     """Time the oracle on `n_rows` sampled rows of the same prefill and
     extrapolate to the whole step with the per-row cost model
     (t+1)*H_I*d_I (rows with n > k) + min(t+1, k)*H*(d_qk + d_v) MACs."""
@@ -154,6 +154,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true")
+    ap.add_argument("--decode-only", action="store_true", help="time only the 64 x 32K decode batch")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -164,6 +165,9 @@ def main():
     from sparse_attention_03_amd import dsa, inputs as gen
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.decode_only:
+        print(json.dumps({"decode": decode_us_per_token(steps=args.steps, warmup=args.warmup)}), flush=True)
+        return
     log("generating prefill_128k inputs on the GPU")
     p = gen.make_config("prefill_128k", device="cuda")
     f = dsa.Forward(p)

@@ -57,28 +57,28 @@ def test_fp8_random_inputs(dsa, H_I, act):
 
 
 def test_fp8_every_code_decodes_like_the_format(dsa):
-    """Keys carry every finite e4m3 code in one column; a one-hot query reads it."""
+    """Keys carry every finite e4m3 code in one column; a one-hot query (+1 in
+    the first sequence, -1 in the second) reads each code through the MFMA."""
     announce("indexer fp8 code table")
     codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
-    n = len(codes)
-    L = n + 2
-    k_idx = np.zeros((L, 128), np.uint8)
-    k_idx[2:, 5] = codes
-    q_idx = np.zeros((L, 16, 128), np.uint8)
-    q_idx[:, 3, 5] = 0x38          # +1.0, head 3
-    q_idx[1::2, 3, 5] = 0xB8       # -1.0 on odd rows: negative codes become positive
-    w = np.zeros((L, 16), np.float32)
+    L = len(codes)
+    k_idx = np.zeros((2 * L, 128), np.uint8)
+    k_idx[:L, 5] = codes
+    k_idx[L:, 5] = codes
+    q_idx = np.zeros((2, 16, 128), np.uint8)
+    q_idx[0, 3, 5] = 0x38          # +1.0, head 3
+    q_idx[1, 3, 5] = 0xB8          # -1.0: negative codes become positive
+    w = np.zeros((2, 16), np.float32)
     w[:, 3] = 1.0
-    p = gen.make_problem("codes", [L], [L], H_I=16, H=32, k=64, device=DEV)
+    p = gen.make_problem("codes", [L, L], [1, 1], H_I=16, H=32, k=64, device=DEV)
     p.q_idx = torch.from_numpy(q_idx).to(DEV).view(torch.float8_e4m3fn)
     p.k_idx = torch.from_numpy(k_idx).to(DEV).view(torch.float8_e4m3fn)
     p.w = torch.from_numpy(w).to(DEV)
     got = dsa.indexer_scores(p).cpu().numpy()
     vals = np.array([oracle.e4m3_value(c) for c in codes])
-    for row in (L - 2, L - 1):
-        sign = -1.0 if row % 2 else 1.0
+    for row, sign in ((0, 1.0), (1, -1.0)):
         want = np.maximum(sign * vals, 0.0).astype(np.float32)
-        assert np.array_equal(got[row, 2:L], want)
+        assert np.array_equal(got[row, :L], want)
 
 
 def test_fp32_tiny_config(dsa):

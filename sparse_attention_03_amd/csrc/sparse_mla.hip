@@ -18,9 +18,11 @@
 //     rows (K fragments read from LDS with ds_read_b128), heads the columns (Q
 //     fragments resident in VGPRs for the whole row), so each lane ends up
 //     holding 16 keys of one head;
-//   * softmax: fp32, base-2 exponent with the scale folded in, running max
-//     updated only when a tile's max exceeds it by more than 8 (so the
-//     accumulator rescale is rare), row sums kept per lane and reduced once;
+//   * softmax: fp32, base-2 exponent with the scale folded in, against a
+//     per-head reference max fixed by the first tile (the accumulators are
+//     only touched by MFMAs; a row whose later max overflows the headroom is
+//     recomputed once with its true max), row sums kept per lane and reduced
+//     once;
 //   * values: O^T = V^T P^T.  The lane's 8 probabilities of one head are
 //     exactly the B fragment of the next MFMA (K index permuted consistently),
 //     and the V^T A fragment comes from two ds_read_b64_tr_b16 transposed LDS
@@ -35,11 +37,13 @@ constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kRowBytes = kDqk * 2;        // 1152
 constexpr int kChunksPerRow = kRowBytes / 16;  // 72
-constexpr int kTile = 64;                  // selected entries per tile
-constexpr int kTileBytes = kTile * kRowBytes;  // 73728
+constexpr int kTile = 32;                  // selected entries per tile
+constexpr int kTileBytes = kTile * kRowBytes;  // 36864
+constexpr int kNumBuf = 4;                 // LDS tile buffers (147456 bytes)
+constexpr int kMaxSel = 2048;              // selected entries staged in LDS per row
 constexpr int kQkSteps = kDqk / 32;        // 18
 constexpr int kDvTiles = kDv / 16;         // 32
-constexpr float kLazy = 8.0f;              // log2 headroom before a rescale
+constexpr float kHeadroom = 32.0f;         // log2 headroom above the reference max
 
 struct MlaArgs {
   const int32_t* cu_q;
@@ -65,34 +69,75 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
+// Wait until at most N vector-memory instructions of this wave are in flight
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup rendezvous for the tile loop that does not drain vector memory:
+// this wave's LDS operations complete (lgkmcnt 0), then every wave meets.
+// The HBM -> LDS copies in flight are left alone; their completion is tracked
+// by the counted vmcnt waits before this barrier.  (__syncthreads() carries a
+// release fence, which would wait for every outstanding copy.)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Issue the HBM -> LDS copy of tile t (the latent rows of selected entries
+// 32t .. 32t+31).  The tile is 32 x 72 16-byte chunks = 36 lane-contiguous
+// 1-KB copy instructions; copy q fills LDS slots [64q, 64q + 64) and wave w
+// issues q = w, w + NW, ...  Every wave issues the same number of copies (so
+// the counted waits are uniform): a wave short of that count repeats one of
+// its copies, which writes the same bytes to the same slots again.  A lane's
+// source chunk is the swizzled chunk that belongs at its LDS slot.  Invalid
+// entries (-1) copy row 0 of the sequence, always in bounds, masked later.
+constexpr int kTileCopies = kTile * kChunksPerRow / 64;  // 36
+
 template <int NW>
-__device__ __forceinline__ void gather_tile(const MlaArgs& a, int32_t kbase, int32_t idx_lane, uint8_t* buf) {
-  constexpr int RPW = kTile / NW;                      // rows gathered by one wave
-  constexpr int NINS = RPW * kChunksPerRow / 64;       // wave instructions
+constexpr int copies_per_wave() { return (kTileCopies + NW - 1) / NW; }
+
+template <int NW>
+__device__ __forceinline__ void gather_tile(const MlaArgs& a, int32_t kbase, const DSA_LDS int32_t* sel, int t,
+                                            uint8_t* buf) {
+  constexpr int NINS = copies_per_wave<NW>();
   const int wave = threadIdx.x >> 6;
   int lane = threadIdx.x & 63;
   // keep the per-lane address arithmetic inside the tile loop (cheap integer
   // ops) instead of letting it be hoisted into registers for the whole kernel
   asm volatile("" : "+v"(lane));
-  DSA_LDS uint8_t* lbase = (DSA_LDS uint8_t*)buf + (size_t)wave * RPW * kRowBytes;
 #pragma unroll
-  for (int q = 0; q < NINS; ++q) {
+  for (int i = 0; i < NINS; ++i) {
+    int q = wave + NW * i;
+    if (q >= kTileCopies) q = wave;  // repeat this wave's first copy
     const int slot = 64 * q + lane;
-    const int riw = slot / kChunksPerRow;
-    const int c_lds = slot - riw * kChunksPerRow;
-    const int row = wave * RPW + riw;
-    int32_t p = __shfl(idx_lane, row);
+    const int row = slot / kChunksPerRow;
+    const int c_lds = slot - row * kChunksPerRow;
+    int32_t p = sel[t * kTile + row];
     p = p < 0 ? 0 : p;
     const int c_src = chunk_at(c_lds, row);
     const uint8_t* src = a.kv + ((int64_t)(kbase + p) * kChunksPerRow + c_src) * 16;
-    __builtin_amdgcn_global_load_lds((const void*)src, (DSA_LDS void*)(lbase + 64 * q * 16), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)src, (DSA_LDS void*)((DSA_LDS uint8_t*)buf + 64 * q * 16), 16,
+                                     0, 0);
   }
 }
 
 template <int HPW, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   constexpr int NT = HPW / 16;
+  constexpr int NINS = copies_per_wave<NW>();  // copy instructions per tile per wave
+  // tiles whose copies are issued ahead of the one being computed; the counted
+  // wait below needs (AHEAD - 1) * NINS to fit the 6-bit vmcnt
+  constexpr int AHEAD = 2 * NINS < 64 ? 3 : 1;
+  static_assert(AHEAD + 1 <= kNumBuf, "not enough LDS buffers");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  DSA_LDS int32_t* sel = (DSA_LDS int32_t*)((DSA_LDS uint8_t*)smem + kNumBuf * kTileBytes);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, li = lane & 15;
   const int32_t r = a.row_begin + blockIdx.x;
@@ -102,11 +147,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   const int ntiles = (a.k + kTile - 1) / kTile;
   const int t0 = sp * a.tiles_per_split;
   const int t1 = min(ntiles, t0 + a.tiles_per_split);
+
+  // the row's selected positions, -1 padded to whole tiles
   const int32_t* idx_row = a.idx + (int64_t)rl * a.k;
-  auto load_idx = [&](int t) -> int32_t {
-    const int e = t * kTile + lane;
-    return (t < t1 && e < a.k) ? idx_row[e] : -1;
-  };
+  for (int e = threadIdx.x; e < ntiles * kTile; e += NW * 64) sel[e] = e < a.k ? idx_row[e] : -1;
 
   // query fragments: B operand of S^T = K Q^T (lane: head li of column tile nt, d = 32c + 8g .. +7)
   bf16x8 qf[NT][kQkSteps];
@@ -117,139 +161,149 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
 #pragma unroll
     for (int c = 0; c < kQkSteps; ++c) qf[nt][c] = *(const bf16x8*)(qrow + 32 * c);
   }
+  __syncthreads();  // sel[] visible
 
+  // Softmax reference point: the first tile's max of each head, fixed for the
+  // whole row so that the accumulator is only ever touched by the MFMA.  A
+  // later tile whose max exceeds it by more than kHeadroom (log2 units) would
+  // overflow; then the row is recomputed once with the true max, collected in
+  // the first pass.  Exact either way; the second pass practically never runs.
+  float m_fix[NT], m_all[NT], l_run[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) { m_fix[nt] = -INFINITY; m_all[nt] = -INFINITY; }
   f32x4 oacc[kDvTiles][NT];
-#pragma unroll
-  for (int dt = 0; dt < kDvTiles; ++dt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) oacc[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[NT], l_run[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) { m_run[nt] = -INFINITY; l_run[nt] = 0.0f; }
 
-  int32_t idx_cur = load_idx(t0);
-  int32_t idx_nxt = load_idx(t0 + 1);
-  if (t0 < t1) gather_tile<NW>(a, ri.kbase, idx_cur, smem);
+  // per-lane LDS byte offsets inside a tile (see the decompositions below)
+  const int sw = swz(li);
+  const int koff0 = li * kRowBytes + 16 * ((sw & 4) + (g ^ (sw & 3)));
+  const int koff1 = li * kRowBytes + 16 * (((sw & 4) ^ 4) + (g ^ (sw & 3)));
+  const int e4 = li >> 2, r4 = li & 3;
+  const int voff = (4 * g + e4) * kRowBytes + 16 * ((r4 >> 1) ^ (g & 1)) + 8 * (r4 & 1);
 
-  for (int t = t0; t < t1; ++t) {
-    uint8_t* buf = smem + (size_t)((t - t0) & 1) * kTileBytes;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    int32_t idx_nn = -1;
-    if (t + 1 < t1) {
-      gather_tile<NW>(a, ri.kbase, idx_nxt, smem + (size_t)((t + 1 - t0) & 1) * kTileBytes);
-      idx_nn = load_idx(t + 2);
-    }
-    const uint64_t vmask = __ballot(idx_cur >= 0);
-    if (vmask != 0) {
-      const DSA_LDS uint8_t* lb = (const DSA_LDS uint8_t*)buf;
-      // ---- scores: sacc[mt][nt] = S^T[keys 16mt.., heads 16nt..]
-      f32x4 sacc[4][NT];
+  for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+    for (int dt = 0; dt < kDvTiles; ++dt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // K fragment of (key row 16mt + li, chunk 4c + g).  The swizzle of a row
-      // with li = row mod 16 only depends on li, and chunk 4c + g = 8(c>>1) +
-      // (4(c&1) | g), so the byte address is a per-lane base chosen by the
-      // parity of c plus the compile-time offset 16*1152*mt + 128*(c>>1).
-      const int sw = swz(li);
-      const int vk0 = ((sw & 4)) + (g ^ (sw & 3));
-      const int vk1 = ((sw & 4) ^ 4) + (g ^ (sw & 3));
-      const DSA_LDS uint8_t* kbase0 = lb + li * kRowBytes + 16 * vk0;
-      const DSA_LDS uint8_t* kbase1 = lb + li * kRowBytes + 16 * vk1;
-      auto load_k = [&](int c, bf16x8 (&kf)[4]) {
-        const DSA_LDS uint8_t* kb = (c & 1) ? kbase1 : kbase0;
+      for (int nt = 0; nt < NT; ++nt) oacc[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          kf[mt] = *(const DSA_LDS bf16x8*)(kb + (16 * kRowBytes * mt + 128 * (c >> 1)));
-      };
-      bf16x8 kcur[4], knxt[4];
-      load_k(0, kcur);
+    for (int nt = 0; nt < NT; ++nt) l_run[nt] = 0.0f;
+    bool overflow = false;
+
+    __syncthreads();  // the previous pass is done with every buffer
 #pragma unroll
-      for (int c = 0; c < kQkSteps; ++c) {
-        if (c + 1 < kQkSteps) load_k(c + 1, knxt);
+    for (int j = 0; j < AHEAD; ++j)
+      if (t0 + j < t1) gather_tile<NW>(a, ri.kbase, sel, t0 + j, smem + (size_t)j * kTileBytes);
+
+    for (int t = t0; t < t1; ++t) {
+      // Tile t has landed once at most (copies issued after it) x NINS of this
+      // wave's copy instructions are still in flight; the barrier then covers
+      // the other waves' copies.
+      const int issued_after = min(AHEAD - 1, t1 - 1 - t);
+      if (issued_after >= 2) wait_vmcnt<(2 * NINS < 64 ? 2 * NINS : 0)>();
+      else if (issued_after == 1) wait_vmcnt<(NINS < 64 ? NINS : 0)>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (t + AHEAD < t1)
+        gather_tile<NW>(a, ri.kbase, sel, t + AHEAD, smem + (size_t)((t + AHEAD - t0) % kNumBuf) * kTileBytes);
+      const int32_t myidx = lane < kTile ? sel[t * kTile + lane] : -1;
+      const uint32_t vmask = (uint32_t)__ballot(myidx >= 0);
+      if (vmask != 0) {
+        const DSA_LDS uint8_t* lb = (const DSA_LDS uint8_t*)smem + (size_t)((t - t0) % kNumBuf) * kTileBytes;
+        // ---- scores: sacc[mt][nt] = S^T[keys 16mt.., heads 16nt..]
+        // K fragment of (key row 16mt + li, chunk 4c + g).  The swizzle of a row
+        // with li = row mod 16 only depends on li, and chunk 4c + g = 8(c>>1) +
+        // (4(c&1) | g), so the byte address is a per-lane base chosen by the
+        // parity of c plus the compile-time offset 16*1152*mt + 128*(c>>1).
+        f32x4 sacc[2][NT];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const DSA_LDS uint8_t* kb0 = lb + koff0;
+        const DSA_LDS uint8_t* kb1 = lb + koff1;
+        auto load_k = [&](int c, bf16x8 (&kf)[2]) {
+          const DSA_LDS uint8_t* kb = (c & 1) ? kb1 : kb0;
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            kf[mt] = *(const DSA_LDS bf16x8*)(kb + (16 * kRowBytes * mt + 128 * (c >> 1)));
+        };
+        bf16x8 kcur[2], knxt[2];
+        load_k(0, kcur);
+#pragma unroll
+        for (int c = 0; c < kQkSteps; ++c) {
+          if (c + 1 < kQkSteps) load_k(c + 1, knxt);
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              sacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kcur[mt], qf[nt][c], sacc[mt][nt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          kcur[0] = knxt[0];
+          kcur[1] = knxt[1];
+        }
+        // ---- softmax (base 2) against the fixed reference; the lane's 8
+        //      probabilities of one head are the B fragment of the value product
+        //      (MFMA K index 8g + e <-> key 4g + e for e < 4, 16 + 4g + e - 4 otherwise)
+        bf16x8 pf[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          float x[2][4];
+          float mx = -INFINITY;
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int e = 16 * mt + 4 * g + rr;
+              const bool v = (vmask >> e) & 1u;
+              x[mt][rr] = v ? sacc[mt][nt][rr] * a.scale_log2 : -INFINITY;
+              mx = fmaxf(mx, x[mt][rr]);
+            }
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          m_all[nt] = fmaxf(m_all[nt], mx);
+          if (m_fix[nt] == -INFINITY) m_fix[nt] = mx;  // first tile with a valid entry
+          overflow |= mx > m_fix[nt] + kHeadroom;
+          float ps = 0.0f;
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              x[mt][rr] = exp2f(x[mt][rr] - m_fix[nt]);
+              ps += x[mt][rr];
+            }
+          l_run[nt] += ps;
+          pf[nt] = bf16x8{(__bf16)x[0][0], (__bf16)x[0][1], (__bf16)x[0][2], (__bf16)x[0][3],
+                          (__bf16)x[1][0], (__bf16)x[1][1], (__bf16)x[1][2], (__bf16)x[1][3]};
+        }
+        // ---- values: O^T[d, h] += V^T[d, keys] P^T[keys, h], one V^T fragment ahead.
+        // V^T fragment rows 4g + e4 (+16), columns 16dt + 4r4 .. +3.  With
+        // row mod 8 = 4(g&1) + e4, the swizzled chunk of column chunk 2dt + (r4>>1)
+        // is 8(dt>>2) + 2((dt&3) ^ e4) + ((r4>>1) ^ (g&1)): a per-lane base chosen
+        // by dt&3 plus the compile-time offset 128*(dt>>2).
+        const DSA_LDS uint8_t* vrow = lb + voff;
+        auto load_v = [&](int dt) -> bf16x8 {
+          const DSA_LDS uint8_t* p = vrow + 32 * ((dt & 3) ^ e4) + 128 * (dt >> 2);
+          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS i16x4*)p);
+          const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS i16x4*)(p + 16 * kRowBytes));
+          return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+              v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]});
+        };
+        bf16x8 vcur = load_v(0), vnxt;
+#pragma unroll
+        for (int dt = 0; dt < kDvTiles; ++dt) {
+          if (dt + 1 < kDvTiles) vnxt = load_v(dt + 1);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
-            sacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kcur[mt], qf[nt][c], sacc[mt][nt], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) kcur[mt] = knxt[mt];
-      }
-      // ---- softmax (base 2), probabilities as the B fragments of the value product
-      bf16x8 pf[2][NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float x[4][4];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int e = 16 * mt + 4 * g + rr;
-            const bool v = (vmask >> e) & 1ull;
-            x[mt][rr] = v ? sacc[mt][nt][rr] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, x[mt][rr]);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const bool need = mx > m_run[nt] + kLazy;
-        if (__ballot(need) != 0) {
-          const float alpha = need ? exp2f(m_run[nt] - mx) : 1.0f;
-          if (need) m_run[nt] = mx;
-          l_run[nt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < kDvTiles; ++dt) oacc[dt][nt] *= alpha;
+            oacc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcur, pf[nt], oacc[dt][nt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          vcur = vnxt;
         }
-        float ps = 0.0f;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            x[mt][rr] = exp2f(x[mt][rr] - m_run[nt]);
-            ps += x[mt][rr];
-          }
-        l_run[nt] += ps;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          pf[ks][nt] = bf16x8{(__bf16)x[2 * ks][0], (__bf16)x[2 * ks][1], (__bf16)x[2 * ks][2], (__bf16)x[2 * ks][3],
-                              (__bf16)x[2 * ks + 1][0], (__bf16)x[2 * ks + 1][1], (__bf16)x[2 * ks + 1][2],
-                              (__bf16)x[2 * ks + 1][3]};
-      }
-      // ---- values: O^T[d, h] += V^T[d, keys] P^T[keys, h], one step of V^T fragments ahead
-      // V^T fragment rows 32ks + 4g + e4 (+16), columns 16dt + 4r4 .. +3.  With
-      // row mod 8 = 4(g&1) + e4, the swizzled chunk of column chunk 2dt + (r4>>1)
-      // is 8(dt>>2) + 2((dt&3) ^ e4) + ((r4>>1) ^ (g&1)): a per-lane base chosen
-      // by dt&3 plus the compile-time offset 32*1152*ks + 128*(dt>>2).
-      const int e4 = li >> 2, r4 = li & 3;
-      const DSA_LDS uint8_t* vrow = lb + (4 * g + e4) * kRowBytes + 16 * ((r4 >> 1) ^ (g & 1)) + 8 * (r4 & 1);
-      const DSA_LDS uint8_t* vb[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vb[j] = vrow + 32 * (j ^ e4);
-      auto load_v = [&](int step) -> bf16x8 {
-        const int ks = step / kDvTiles, dt = step % kDvTiles;
-        const DSA_LDS uint8_t* p = vb[dt & 3] + (32 * kRowBytes * ks + 128 * (dt >> 2));
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS i16x4*)p);
-        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS i16x4*)(p + 16 * kRowBytes));
-        return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
-            v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]});
-      };
-      bf16x8 vcur = load_v(0), vnxt;
-#pragma unroll
-      for (int step = 0; step < 2 * kDvTiles; ++step) {
-        const int ks = step / kDvTiles, dt = step % kDvTiles;
-        if (step + 1 < 2 * kDvTiles) vnxt = load_v(step + 1);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          oacc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcur, pf[ks][nt], oacc[dt][nt], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        vcur = vnxt;
       }
     }
-    idx_cur = idx_nxt;
-    idx_nxt = idx_nn;
+    // every wave agrees on whether the row is recomputed (the buffers are shared)
+    if (!__syncthreads_or(overflow)) break;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) m_fix[nt] = m_all[nt];
   }
 
   // ---- epilogue
@@ -261,7 +315,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
     const int h = head0 + 16 * nt + li;
     const bool empty = !(l > 0.0f);
     const float inv = empty ? 0.0f : 1.0f / l;
-    const float lse_v = empty ? -INFINITY : (m_run[nt] + log2f(l)) * 0.69314718055994531f;
+    const float lse_v = empty ? -INFINITY : (m_fix[nt] + log2f(l)) * 0.69314718055994531f;
     if (a.splits == 1) {
       uint16_t* orow = a.out + ((int64_t)r * a.H + h) * kDv + 4 * g;
 #pragma unroll
@@ -283,32 +337,43 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
 }
 
 // Combine key-split partials: o = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M).
+// One workgroup per (row, head); each thread owns 4 consecutive value columns.
 template <bool BF16>
-__global__ __launch_bounds__(256) void merge_kernel(MlaArgs a, int d_v) {
-  const int32_t rl = blockIdx.x;
-  const int32_t r = a.row_begin + rl;
+__global__ __launch_bounds__(128) void merge_kernel(MlaArgs a, int d_v) {
+  __shared__ float wsh[64];
+  __shared__ float norm[2];
+  const int32_t rl = blockIdx.x, r = a.row_begin + rl;
+  const int h = blockIdx.y;
   const int S = a.splits;
-  for (int e = threadIdx.x; e < a.H * d_v; e += blockDim.x) {
-    const int h = e / d_v, d = e - h * d_v;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, a.ws_lse[((int64_t)rl * S + s) * a.H + h]);
-    float num = 0.0f, den = 0.0f;
-    if (M > -INFINITY) {
-      for (int s = 0; s < S; ++s) {
-        const int64_t slot = ((int64_t)rl * S + s) * a.H + h;
-        const float ls = a.ws_lse[slot];
-        if (ls == -INFINITY) continue;
-        const float wgt = expf(ls - M);
-        num = fmaf(wgt, a.ws_o[slot * d_v + d], num);
-        den += wgt;
-      }
-    }
-    const float o = den > 0.0f ? num / den : 0.0f;
-    const int64_t oi = ((int64_t)r * a.H + h) * d_v + d;
-    if constexpr (BF16) a.out[oi] = to_bf16_bits(o);
-    else ((float*)a.out)[oi] = o;
-    if (d == 0 && a.lse) a.lse[(int64_t)r * a.H + h] = den > 0.0f ? M + logf(den) : -INFINITY;
+  const int64_t slot0 = (int64_t)rl * S * a.H + h;  // split s: slot0 + s * H
+  if (threadIdx.x < 64) {
+    float ls = threadIdx.x < S ? a.ws_lse[slot0 + (int64_t)threadIdx.x * a.H] : -INFINITY;
+    const float M = wave_max(ls);
+    const float wgt = (M == -INFINITY || ls == -INFINITY) ? 0.0f : expf(ls - M);
+    if (threadIdx.x < S) wsh[threadIdx.x] = wgt;
+    const float den = wave_sum(wgt);
+    if (threadIdx.x == 0) { norm[0] = den > 0.0f ? 1.0f / den : 0.0f; norm[1] = den > 0.0f ? M + logf(den) : -INFINITY; }
   }
+  __syncthreads();
+  const float inv = norm[0];
+  for (int d = 4 * threadIdx.x; d < d_v; d += 4 * blockDim.x) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s) {
+      const float wgt = wsh[s];
+      if (wgt == 0.0f) continue;
+      acc += wgt * *(const f32x4*)(a.ws_o + (slot0 + (int64_t)s * a.H) * d_v + d);
+    }
+    acc *= inv;
+    const int64_t oi = ((int64_t)r * a.H + h) * d_v + d;
+    if constexpr (BF16) {
+      const uint32_t lo = (uint32_t)to_bf16_bits(acc[0]) | ((uint32_t)to_bf16_bits(acc[1]) << 16);
+      const uint32_t hi = (uint32_t)to_bf16_bits(acc[2]) | ((uint32_t)to_bf16_bits(acc[3]) << 16);
+      *(uint2*)(a.out + oi) = make_uint2(lo, hi);
+    } else {
+      *(f32x4*)((float*)a.out + oi) = acc;
+    }
+  }
+  if (threadIdx.x == 0 && a.lse) a.lse[(int64_t)r * a.H + h] = norm[1];
 }
 
 // fp32 inputs: plain two-pass softmax per (row, head) on the VALU.
@@ -370,7 +435,7 @@ __global__ __launch_bounds__(256) void mla_f32_kernel(MlaArgs a, int d_qk, int d
 
 template <int HPW, int NW>
 hipError_t launch_bf16(const MlaArgs& a, int rows, hipStream_t s) {
-  const size_t lds = 2 * (size_t)kTileBytes;
+  const size_t lds = (size_t)kNumBuf * kTileBytes + kMaxSel * sizeof(int32_t);
   static bool attr_set = false;  // benign race: idempotent attribute call
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)mla_bf16_kernel<HPW, NW>,
@@ -429,7 +494,7 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL((merge_kernel<true>), dim3((unsigned)rows), dim3(256), 0, s, a, kDv);
+  hipLaunchKernelGGL((merge_kernel<true>), dim3((unsigned)rows, (unsigned)a.H), dim3(128), 0, s, a, kDv);
   return hipGetLastError();
 }
 

@@ -27,10 +27,17 @@ constexpr int kIdxThreads = 256;
 constexpr int kRowsPerWave = 2;
 constexpr int kRowsPerBlock = 4 * kRowsPerWave;
 
+// ReLU on the bit pattern: a float is >= +0 exactly when its int32 image is
+// >= 0, so max(bits, 0) is max(x, 0) with -0 -> +0, in one integer op and
+// without the NaN canonicalisation a float max would add.
+__device__ __forceinline__ float relu(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
 template <int ACT>
 __device__ __forceinline__ float activation(float x) {
   if constexpr (ACT == 0) {
-    return fmaxf(x, 0.0f);
+    return relu(x);
   } else {
     return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
   }
@@ -87,20 +94,26 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
     if (s0 + 64 < kend) load_keys(s0 + 64, kn);
     float part[NR][4];
 #pragma unroll
-    for (int i = 0; i < NR; ++i)
-#pragma unroll
-      for (int st = 0; st < 4; ++st) part[i][st] = 0.0f;
-#pragma unroll
     for (int st = 0; st < 4; ++st) {
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
+        // NHT independent MFMAs, then one accumulator chain per head tile
+        f32x4 x[NHT];
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht)
+          x[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[i][ht], kf[st], f32x4{0.f, 0.f, 0.f, 0.f}, 0,
+                                                                   0, 0, 127, 0, 127);
+        float acc[NHT];
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) {
-          f32x4 x = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[i][ht], kf[st], f32x4{0.f, 0.f, 0.f, 0.f},
-                                                                      0, 0, 0, 127, 0, 127);
+          acc[ht] = wv[i][ht][0] * activation<ACT>(x[ht][0]);
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) part[i][st] = fmaf(wv[i][ht][rr], activation<ACT>(x[rr]), part[i][st]);
+          for (int rr = 1; rr < 4; ++rr) acc[ht] = fmaf(wv[i][ht][rr], activation<ACT>(x[ht][rr]), acc[ht]);
         }
+        float sum = acc[0];
+#pragma unroll
+        for (int ht = 1; ht < NHT; ++ht) sum += acc[ht];
+        part[i][st] = sum;
       }
     }
     // transpose-reduce over the four lane groups: group g ends with sub-tile g

@@ -165,21 +165,26 @@ dsa_status dsa_topk_workspace_size(const dsa_batch* batch, int32_t k, size_t* by
   if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is NULL");
   if (dsa_status s = check_batch(batch)) return s;
   if (dsa_status s = check_k(k)) return s;
-  *bytes = 0;
+  int cus = 0;
+  if (dsa_status s = device_cus(&cus)) return s;
+  *bytes = dsa::topk_workspace_bytes(batch->total_q, batch->max_ctx, k, cus);
   return DSA_OK;
 }
 
 dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores, int32_t k, int32_t* idx,
                     void* ws, size_t ws_bytes, dsa_stream_t stream) {
   g_err[0] = 0;
-  (void)ws;
-  (void)ws_bytes;
   if (dsa_status s = check_batch(batch)) return s;
   if (dsa_status s = check_scores(batch, scores, ld_scores)) return s;
   if (dsa_status s = check_k(k)) return s;
   if (!idx || !aligned16(idx)) return fail(DSA_ERR_INVALID_ARG, "idx is NULL or not 16-byte aligned");
   if (batch->total_q == 0) return DSA_OK;
-  dsa::TopkLaunch L{view(batch, 0, batch->total_q), scores, ld_scores, k, idx};
+  int cus = 0;
+  if (dsa_status s = device_cus(&cus)) return s;
+  const size_t need = dsa::topk_workspace_bytes(batch->total_q, batch->max_ctx, k, cus);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
+    return fail(DSA_ERR_WORKSPACE, "top-k workspace: need %zu bytes (got %zu)", need, ws_bytes);
+  dsa::TopkLaunch L{view(batch, 0, batch->total_q), scores, ld_scores, k, idx, ws, cus};
   hipError_t e = dsa::launch_topk(L, (hipStream_t)stream);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "topk launch");
 }
@@ -229,7 +234,7 @@ namespace {
 struct ForwardPlan {
   int32_t qb;       // rows per chunk
   int64_t ld;       // score row stride
-  size_t off_scores, off_idx, off_attn, total;
+  size_t off_scores, off_idx, off_topk, off_attn, total;
   int max_splits;
 };
 
@@ -255,6 +260,13 @@ dsa_status plan_forward(const dsa_forward_params* p, int cus, ForwardPlan* f) {
   off += round_up((size_t)f->qb * (size_t)f->ld * sizeof(float), 256);
   f->off_idx = off;
   if (!p->out_idx) off += round_up((size_t)f->qb * p->k * sizeof(int32_t), 256);
+  f->off_topk = off;
+  {
+    const int32_t last_rows = b->total_q % f->qb;
+    const size_t t_full = dsa::topk_workspace_bytes(f->qb, b->max_ctx, p->k, cus);
+    const size_t t_last = last_rows ? dsa::topk_workspace_bytes(last_rows, b->max_ctx, p->k, cus) : 0;
+    off += round_up(t_full > t_last ? t_full : t_last, 256);
+  }
   f->off_attn = off;
   const int32_t last = b->total_q % f->qb;
   const int s_full = dsa::attention_splits(f->qb, p->k, p->dtype == DSA_BF16, cus);
@@ -306,7 +318,7 @@ dsa_status dsa_forward(const dsa_forward_params* p, void* ws, size_t ws_bytes, d
                           p->idx_dtype == DSA_FP8_E4M3, cus};
     hipError_t e = dsa::launch_indexer(IL, st);
     if (e != hipSuccess) return hip_fail(e, "forward indexer launch");
-    dsa::TopkLaunch TL{v, scores, f.ld, p->k, idx};
+    dsa::TopkLaunch TL{v, scores, f.ld, p->k, idx, base + f.off_topk, cus};
     e = dsa::launch_topk(TL, st);
     if (e != hipSuccess) return hip_fail(e, "forward topk launch");
     const int splits = dsa::attention_splits(r1 - r0, p->k, p->dtype == DSA_BF16, cus);

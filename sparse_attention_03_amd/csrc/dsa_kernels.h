@@ -38,6 +38,8 @@ struct TopkLaunch {
   int64_t ld;
   int32_t k;
   int32_t* idx;            // [row_end - row_begin, k]
+  void* ws;                // topk_workspace_bytes(...) bytes, or null when that is 0
+  int32_t num_cus;
 };
 
 struct AttnLaunch {
@@ -59,6 +61,9 @@ struct AttnLaunch {
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s);
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
+
+// Workspace of the segmented top-k for `rows` rows (0: single pass per row).
+size_t topk_workspace_bytes(int rows, int max_ctx, int k, int num_cus);
 
 // Number of key-splits the attention uses for `rows` query rows.
 int attention_splits(int rows, int k, bool bf16, int num_cus);

@@ -89,3 +89,15 @@ def test_decode_64x32k_rows(dsa):
     s = (0.14 + 0.03 * rng.standard_normal((p.total_q, _ld(p)))).astype(np.float32)   # clustered scores
     got, ref = _run(dsa, p, s, k)
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("k", [100, 2048])
+def test_few_long_rows_use_segments(dsa, k):
+    """Few rows: each row is split into segments whose winners are merged."""
+    announce("topk segmented", k)
+    p = _problem([40000, 3000, 9000, 1000, 70000], [1, 1, 1, 1, 1], k)
+    rng = np.random.default_rng(k + 1)
+    s = rng.integers(-5, 6, (p.total_q, _ld(p))).astype(np.float32)   # ties across segment borders
+    s[4, :] = np.arange(_ld(p), dtype=np.float32) % 977                # periodic: many exact ties
+    got, ref = _run(dsa, p, s, k)
+    assert np.array_equal(got, ref)

@@ -12,8 +12,8 @@
 //   * gather: the 64 selected latent rows of a tile are copied HBM -> LDS with
 //     global_load_lds_dwordx4 (16 B per lane, no register staging), double
 //     buffered, each row stored as 72 16-byte chunks with an XOR swizzle of
-//     the chunk index inside each group of 8 (bank spreading for both the
-//     row-wise and the transposed reads);
+//     the chunk index inside each group of 8 (no bank conflicts for either
+//     the row-wise or the transposed reads);
 //   * scores: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 -- keys are the MFMA
 //     rows (K fragments read from LDS with ds_read_b128), heads the columns (Q
 //     fragments resident in VGPRs for the whole row), so each lane ends up
@@ -61,7 +61,12 @@ struct MlaArgs {
   float* ws_lse;
 };
 
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// LDS has 64 banks of 4 bytes and a 1152-byte row shifts odd rows by half of
+// them, so the chunk swizzle is keyed on (row >> 1) & 7: the 16 rows read by
+// one K fragment instruction and the 8 rows of one transposed V read then hit
+// disjoint banks.
+__device__ __forceinline__ int swz3(int m) { return ((m & 3) << 1) | ((m >> 2) & 1); }
+__device__ __forceinline__ int swz(int row) { return swz3((row >> 1) & 7); }
 __device__ __forceinline__ int chunk_at(int chunk, int row) { return (chunk & ~7) | ((chunk & 7) ^ swz(row)); }
 
 __device__ __forceinline__ uint16_t to_bf16_bits(float f) {
@@ -164,23 +169,30 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   __syncthreads();  // sel[] visible
 
   // Softmax reference point: the first tile's max of each head, fixed for the
-  // whole row so that the accumulator is only ever touched by the MFMA.  A
-  // later tile whose max exceeds it by more than kHeadroom (log2 units) would
-  // overflow; then the row is recomputed once with the true max, collected in
-  // the first pass.  Exact either way; the second pass practically never runs.
-  float m_fix[NT], m_all[NT], l_run[NT];
+  // whole row, so the accumulators are only ever touched by MFMAs and the
+  // steady state needs no cross-lane reduction.  If a later score exceeds it by
+  // more than kHeadroom (log2 units) the row would overflow: then a max-only
+  // pass rebuilds m_fix as the true max and the row is recomputed against it
+  // (exact either way; practically never taken).
+  float m_fix[NT], l_run[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) { m_fix[nt] = -INFINITY; m_all[nt] = -INFINITY; }
+  for (int nt = 0; nt < NT; ++nt) m_fix[nt] = -INFINITY;
   f32x4 oacc[kDvTiles][NT];
 
   // per-lane LDS byte offsets inside a tile (see the decompositions below)
-  const int sw = swz(li);
+  const int sw = swz(li);  // rows 16mt + li share li's swizzle
   const int koff0 = li * kRowBytes + 16 * ((sw & 4) + (g ^ (sw & 3)));
   const int koff1 = li * kRowBytes + 16 * (((sw & 4) ^ 4) + (g ^ (sw & 3)));
   const int e4 = li >> 2, r4 = li & 3;
-  const int voff = (4 * g + e4) * kRowBytes + 16 * ((r4 >> 1) ^ (g & 1)) + 8 * (r4 & 1);
+  const int vsw = swz(4 * g + e4);  // rows 4g + e4 and 4g + e4 + 16 share it
+  const int voff = (4 * g + e4) * kRowBytes + 16 * ((r4 >> 1) ^ (vsw & 1)) + 8 * (r4 & 1);
 
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < 3; ++pass) {
+    const bool max_only = pass == 1;
+    if (max_only) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) m_fix[nt] = -INFINITY;  // rebuilt as the running max
+    }
 #pragma unroll
     for (int dt = 0; dt < kDvTiles; ++dt)
 #pragma unroll
@@ -210,10 +222,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
       if (vmask != 0) {
         const DSA_LDS uint8_t* lb = (const DSA_LDS uint8_t*)smem + (size_t)((t - t0) % kNumBuf) * kTileBytes;
         // ---- scores: sacc[mt][nt] = S^T[keys 16mt.., heads 16nt..]
-        // K fragment of (key row 16mt + li, chunk 4c + g).  The swizzle of a row
-        // with li = row mod 16 only depends on li, and chunk 4c + g = 8(c>>1) +
-        // (4(c&1) | g), so the byte address is a per-lane base chosen by the
-        // parity of c plus the compile-time offset 16*1152*mt + 128*(c>>1).
+        // K fragment of (key row 16mt + li, chunk 4c + g).  The swizzle of row
+        // 16mt + li only depends on li, and chunk 4c + g = 8(c>>1) + (4(c&1) | g),
+        // so the byte address is a per-lane base chosen by the parity of c plus
+        // the compile-time offset 16*1152*mt + 128*(c>>1).
         f32x4 sacc[2][NT];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -244,45 +256,56 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
         // ---- softmax (base 2) against the fixed reference; the lane's 8
         //      probabilities of one head are the B fragment of the value product
         //      (MFMA K index 8g + e <-> key 4g + e for e < 4, 16 + 4g + e - 4 otherwise)
+        const bool full = vmask == 0xffffffffu;
+        if (max_only || m_fix[0] == -INFINITY) {
+          // reference max of every head (first valid tile, or the max-only pass)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                const bool v = (vmask >> (16 * mt + 4 * g + rr)) & 1u;
+                mx = fmaxf(mx, v ? sacc[mt][nt][rr] * a.scale_log2 : -INFINITY);
+              }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            m_fix[nt] = fmaxf(m_fix[nt], mx);
+          }
+          if (max_only) continue;
+        }
         bf16x8 pf[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          float x[2][4];
-          float mx = -INFINITY;
+          float x[8];
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
+          for (int e = 0; e < 8; ++e) x[e] = fmaf(sacc[e >> 2][nt][e & 3], a.scale_log2, -m_fix[nt]);
+          if (!full) {
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              const int e = 16 * mt + 4 * g + rr;
-              const bool v = (vmask >> e) & 1u;
-              x[mt][rr] = v ? sacc[mt][nt][rr] * a.scale_log2 : -INFINITY;
-              mx = fmaxf(mx, x[mt][rr]);
-            }
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          m_all[nt] = fmaxf(m_all[nt], mx);
-          if (m_fix[nt] == -INFINITY) m_fix[nt] = mx;  // first tile with a valid entry
-          overflow |= mx > m_fix[nt] + kHeadroom;
+            for (int e = 0; e < 8; ++e)
+              if (!((vmask >> (16 * (e >> 2) + 4 * g + (e & 3))) & 1u)) x[e] = -INFINITY;
+          }
+          const float xm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+          overflow |= xm > kHeadroom;
           float ps = 0.0f;
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              x[mt][rr] = exp2f(x[mt][rr] - m_fix[nt]);
-              ps += x[mt][rr];
-            }
+          for (int e = 0; e < 8; ++e) {
+            x[e] = __builtin_amdgcn_exp2f(x[e]);  // v_exp_f32; exp2(-inf) = 0
+            ps += x[e];
+          }
           l_run[nt] += ps;
-          pf[nt] = bf16x8{(__bf16)x[0][0], (__bf16)x[0][1], (__bf16)x[0][2], (__bf16)x[0][3],
-                          (__bf16)x[1][0], (__bf16)x[1][1], (__bf16)x[1][2], (__bf16)x[1][3]};
+          pf[nt] = bf16x8{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3],
+                          (__bf16)x[4], (__bf16)x[5], (__bf16)x[6], (__bf16)x[7]};
         }
         // ---- values: O^T[d, h] += V^T[d, keys] P^T[keys, h], one V^T fragment ahead.
-        // V^T fragment rows 4g + e4 (+16), columns 16dt + 4r4 .. +3.  With
-        // row mod 8 = 4(g&1) + e4, the swizzled chunk of column chunk 2dt + (r4>>1)
-        // is 8(dt>>2) + 2((dt&3) ^ e4) + ((r4>>1) ^ (g&1)): a per-lane base chosen
-        // by dt&3 plus the compile-time offset 128*(dt>>2).
+        // V^T fragment rows 4g + e4 (+16), columns 16dt + 4r4 .. +3.  With s the
+        // rows' swizzle, the swizzled chunk of column chunk 2dt + (r4>>1) is
+        // 8(dt>>2) + 2((dt&3) ^ (s>>1)) + ((r4>>1) ^ (s&1)): a per-lane base
+        // chosen by dt&3 plus the compile-time offset 128*(dt>>2).
         const DSA_LDS uint8_t* vrow = lb + voff;
         auto load_v = [&](int dt) -> bf16x8 {
-          const DSA_LDS uint8_t* p = vrow + 32 * ((dt & 3) ^ e4) + 128 * (dt >> 2);
+          const DSA_LDS uint8_t* p = vrow + 32 * ((dt & 3) ^ (vsw >> 1)) + 128 * (dt >> 2);
           const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS i16x4*)p);
           const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS i16x4*)(p + 16 * kRowBytes));
           return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
@@ -300,10 +323,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
         }
       }
     }
-    // every wave agrees on whether the row is recomputed (the buffers are shared)
-    if (!__syncthreads_or(overflow)) break;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) m_fix[nt] = m_all[nt];
+    if (pass == 0) {
+      // every wave agrees on whether the row is recomputed (the buffers are shared)
+      if (!__syncthreads_or(overflow)) break;
+    }  // after the max-only pass m_fix holds the true max: the recompute cannot overflow
   }
 
   // ---- epilogue

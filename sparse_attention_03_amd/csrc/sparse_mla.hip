@@ -8,12 +8,12 @@
 // (512 latent + 64 rope columns) and the value is its first 512 columns.
 //
 // BF16 kernel, one workgroup per (query row, key split), NW waves each owning
-// HPW query heads:
-//   * gather: the 64 selected latent rows of a tile are copied HBM -> LDS with
-//     global_load_lds_dwordx4 (16 B per lane, no register staging), double
-//     buffered, each row stored as 72 16-byte chunks with an XOR swizzle of
-//     the chunk index inside each group of 8 (no bank conflicts for either
-//     the row-wise or the transposed reads);
+// HPW = 32 query heads (one wave per SIMD; every K / V fragment read from LDS
+// feeds two MFMAs, which halves LDS traffic against 16 heads per wave):
+//   * gather: the 32 selected latent rows of a tile are copied HBM -> LDS with
+//     global_load_lds_dwordx4 (16 B per lane, no register staging) into one of
+//     four buffers, up to three tiles ahead, in a chunk-major layout that
+//     makes both the K and the transposed V reads bank-conflict free;
 //   * scores: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 -- keys are the MFMA
 //     rows (K fragments read from LDS with ds_read_b128), heads the columns (Q
 //     fragments resident in VGPRs for the whole row), so each lane ends up
@@ -41,6 +41,8 @@ constexpr int kTile = 32;                  // selected entries per tile
 constexpr int kTileBytes = kTile * kRowBytes;  // 36864
 constexpr int kNumBuf = 4;                 // LDS tile buffers (147456 bytes)
 constexpr int kMaxSel = 2048;              // selected entries staged in LDS per row
+constexpr int kQkAhead = 3;                // K fragment steps read ahead of their MFMAs
+constexpr int kPvAhead = 8;                // V^T fragments read ahead of their MFMAs
 constexpr int kQkSteps = kDqk / 32;        // 18
 constexpr int kDvTiles = kDv / 16;         // 32
 constexpr float kHeadroom = 32.0f;         // log2 headroom above the reference max
@@ -61,14 +63,15 @@ struct MlaArgs {
   float* ws_lse;
 };
 
-// LDS has 64 banks of 4 bytes and a 1152-byte row shifts odd rows by half of
-// them, so the chunk swizzle is keyed on (row >> 1) & 7: the 16 rows read by
-// one K fragment instruction and the 8 rows of one transposed V read then hit
-// disjoint banks.
-__device__ __forceinline__ int swz3(int m) { return ((m & 3) << 1) | ((m >> 2) & 1); }
-__device__ __forceinline__ int swz(int row) { return swz3((row >> 1) & 7); }
-__device__ __forceinline__ int chunk_at(int chunk, int row) { return (chunk & ~7) | ((chunk & 7) ^ swz(row)); }
-
+// Tile layout in LDS: chunk-major.  Chunk c (16 bytes = 8 values, c < 72) of
+// tile row r sits at byte (32 c + (r ^ 8 (c & 1))) * 16.  Properties:
+//   * one 64-lane copy instruction fills two whole chunk columns, and a lane's
+//     source row (lane mod 32, XOR 8 for the odd column) is the same for every
+//     copy of the tile: one address per lane per tile, immediate offsets after;
+//   * a K fragment read (16 consecutive rows of one chunk per lane group) is one
+//     contiguous 256-byte span: all 64 banks once;
+//   * a transposed V read (8 rows x 2 chunks per 32 lanes) hits each bank once
+//     because odd chunks keep their rows 8 apart from even chunks.
 __device__ __forceinline__ uint16_t to_bf16_bits(float f) {
   __bf16 b = (__bf16)f;  // round to nearest even
   return __builtin_bit_cast(uint16_t, b);
@@ -96,13 +99,12 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Issue the HBM -> LDS copy of tile t (the latent rows of selected entries
-// 32t .. 32t+31).  The tile is 32 x 72 16-byte chunks = 36 lane-contiguous
-// 1-KB copy instructions; copy q fills LDS slots [64q, 64q + 64) and wave w
-// issues q = w, w + NW, ...  Every wave issues the same number of copies (so
-// the counted waits are uniform): a wave short of that count repeats one of
-// its copies, which writes the same bytes to the same slots again.  A lane's
-// source chunk is the swizzled chunk that belongs at its LDS slot.  Invalid
-// entries (-1) copy row 0 of the sequence, always in bounds, masked later.
+// 32t .. 32t+31).  The tile is 36 lane-contiguous 1-KB copy instructions; copy
+// q fills chunk columns 2q and 2q + 1, and wave w issues q = w, w + NW, ...
+// Every wave issues the same number of copies (so the counted waits are
+// uniform): a wave short of that count repeats its first copy, which writes
+// the same bytes to the same place again.  Invalid entries (-1) copy row 0 of
+// the sequence, always in bounds, and are masked later.
 constexpr int kTileCopies = kTile * kChunksPerRow / 64;  // 36
 
 template <int NW>
@@ -112,24 +114,18 @@ template <int NW>
 __device__ __forceinline__ void gather_tile(const MlaArgs& a, int32_t kbase, const DSA_LDS int32_t* sel, int t,
                                             uint8_t* buf) {
   constexpr int NINS = copies_per_wave<NW>();
-  const int wave = threadIdx.x >> 6;
-  int lane = threadIdx.x & 63;
-  // keep the per-lane address arithmetic inside the tile loop (cheap integer
-  // ops) instead of letting it be hoisted into registers for the whole kernel
-  asm volatile("" : "+v"(lane));
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int odd = lane >> 5;                     // this lane fills odd chunk columns
+  const int row = (lane & 31) ^ (8 * odd);       // the tile row it copies from
+  int32_t p = sel[t * kTile + row];
+  p = p < 0 ? 0 : p;
+  const uint8_t* src = a.kv + ((int64_t)(kbase + p) * kChunksPerRow + odd + 2 * wave) * 16;
 #pragma unroll
   for (int i = 0; i < NINS; ++i) {
-    int q = wave + NW * i;
-    if (q >= kTileCopies) q = wave;  // repeat this wave's first copy
-    const int slot = 64 * q + lane;
-    const int row = slot / kChunksPerRow;
-    const int c_lds = slot - row * kChunksPerRow;
-    int32_t p = sel[t * kTile + row];
-    p = p < 0 ? 0 : p;
-    const int c_src = chunk_at(c_lds, row);
-    const uint8_t* src = a.kv + ((int64_t)(kbase + p) * kChunksPerRow + c_src) * 16;
-    __builtin_amdgcn_global_load_lds((const void*)src, (DSA_LDS void*)((DSA_LDS uint8_t*)buf + 64 * q * 16), 16,
-                                     0, 0);
+    const bool dup = wave + NW * i >= kTileCopies;
+    const int q = dup ? wave : wave + NW * i;
+    __builtin_amdgcn_global_load_lds((const void*)(dup ? src : src + 32 * NW * i),
+                                     (DSA_LDS void*)((DSA_LDS uint8_t*)buf + 1024 * q), 16, 0, 0);
   }
 }
 
@@ -179,13 +175,12 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   for (int nt = 0; nt < NT; ++nt) m_fix[nt] = -INFINITY;
   f32x4 oacc[kDvTiles][NT];
 
-  // per-lane LDS byte offsets inside a tile (see the decompositions below)
-  const int sw = swz(li);  // rows 16mt + li share li's swizzle
-  const int koff0 = li * kRowBytes + 16 * ((sw & 4) + (g ^ (sw & 3)));
-  const int koff1 = li * kRowBytes + 16 * (((sw & 4) ^ 4) + (g ^ (sw & 3)));
+  // per-lane LDS byte offsets inside a tile (chunk-major layout, see above):
+  //   K fragment (row 16mt + li, chunk 4c + g): koff + 2048 c + 256 mt
+  //   V^T rows 4g + e4 (+16), chunk 2dt + (r4>>1), half r4&1: voff + 1024 dt (+256)
+  const int koff = g * 512 + (li ^ (8 * (g & 1))) * 16;
   const int e4 = li >> 2, r4 = li & 3;
-  const int vsw = swz(4 * g + e4);  // rows 4g + e4 and 4g + e4 + 16 share it
-  const int voff = (4 * g + e4) * kRowBytes + 16 * ((r4 >> 1) ^ (vsw & 1)) + 8 * (r4 & 1);
+  const int voff = (r4 >> 1) * 512 + ((4 * g + e4) ^ (8 * (r4 >> 1))) * 16 + 8 * (r4 & 1);
 
   for (int pass = 0; pass < 3; ++pass) {
     const bool max_only = pass == 1;
@@ -222,36 +217,31 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
       if (vmask != 0) {
         const DSA_LDS uint8_t* lb = (const DSA_LDS uint8_t*)smem + (size_t)((t - t0) % kNumBuf) * kTileBytes;
         // ---- scores: sacc[mt][nt] = S^T[keys 16mt.., heads 16nt..]
-        // K fragment of (key row 16mt + li, chunk 4c + g).  The swizzle of row
-        // 16mt + li only depends on li, and chunk 4c + g = 8(c>>1) + (4(c&1) | g),
-        // so the byte address is a per-lane base chosen by the parity of c plus
-        // the compile-time offset 16*1152*mt + 128*(c>>1).
         f32x4 sacc[2][NT];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const DSA_LDS uint8_t* kb0 = lb + koff0;
-        const DSA_LDS uint8_t* kb1 = lb + koff1;
+        const DSA_LDS uint8_t* kb = lb + koff;
         auto load_k = [&](int c, bf16x8 (&kf)[2]) {
-          const DSA_LDS uint8_t* kb = (c & 1) ? kb1 : kb0;
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-            kf[mt] = *(const DSA_LDS bf16x8*)(kb + (16 * kRowBytes * mt + 128 * (c >> 1)));
+          for (int mt = 0; mt < 2; ++mt) kf[mt] = *(const DSA_LDS bf16x8*)(kb + (2048 * c + 256 * mt));
         };
-        bf16x8 kcur[2], knxt[2];
-        load_k(0, kcur);
+        // K fragments kQkAhead steps ahead of the MFMAs (one wave per SIMD: the
+        // wave itself must cover the LDS latency)
+        bf16x8 kring[kQkAhead][2];
+#pragma unroll
+        for (int i = 0; i < kQkAhead; ++i) load_k(i, kring[i]);
 #pragma unroll
         for (int c = 0; c < kQkSteps; ++c) {
-          if (c + 1 < kQkSteps) load_k(c + 1, knxt);
+          const bf16x8 kc0 = kring[c % kQkAhead][0], kc1 = kring[c % kQkAhead][1];
+          if (c + kQkAhead < kQkSteps) load_k(c + kQkAhead, kring[c % kQkAhead]);
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-              sacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kcur[mt], qf[nt][c], sacc[mt][nt], 0, 0, 0);
+          for (int nt = 0; nt < NT; ++nt) {
+            sacc[0][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc0, qf[nt][c], sacc[0][nt], 0, 0, 0);
+            sacc[1][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc1, qf[nt][c], sacc[1][nt], 0, 0, 0);
+          }
           __builtin_amdgcn_sched_barrier(0);
-          kcur[0] = knxt[0];
-          kcur[1] = knxt[1];
         }
         // ---- softmax (base 2) against the fixed reference; the lane's 8
         //      probabilities of one head are the B fragment of the value product
@@ -299,27 +289,25 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
                           (__bf16)x[4], (__bf16)x[5], (__bf16)x[6], (__bf16)x[7]};
         }
         // ---- values: O^T[d, h] += V^T[d, keys] P^T[keys, h], one V^T fragment ahead.
-        // V^T fragment rows 4g + e4 (+16), columns 16dt + 4r4 .. +3.  With s the
-        // rows' swizzle, the swizzled chunk of column chunk 2dt + (r4>>1) is
-        // 8(dt>>2) + 2((dt&3) ^ (s>>1)) + ((r4>>1) ^ (s&1)): a per-lane base
-        // chosen by dt&3 plus the compile-time offset 128*(dt>>2).
-        const DSA_LDS uint8_t* vrow = lb + voff;
+        const DSA_LDS uint8_t* vb = lb + voff;
         auto load_v = [&](int dt) -> bf16x8 {
-          const DSA_LDS uint8_t* p = vrow + 32 * ((dt & 3) ^ (vsw >> 1)) + 128 * (dt >> 2);
+          const DSA_LDS uint8_t* p = vb + 1024 * dt;
           const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS i16x4*)p);
-          const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS i16x4*)(p + 16 * kRowBytes));
+          const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS i16x4*)(p + 256));
           return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
               v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]});
         };
-        bf16x8 vcur = load_v(0), vnxt;
+        bf16x8 vring[kPvAhead];
+#pragma unroll
+        for (int i = 0; i < kPvAhead; ++i) vring[i] = load_v(i);
 #pragma unroll
         for (int dt = 0; dt < kDvTiles; ++dt) {
-          if (dt + 1 < kDvTiles) vnxt = load_v(dt + 1);
+          const bf16x8 vc = vring[dt % kPvAhead];
+          if (dt + kPvAhead < kDvTiles) vring[dt % kPvAhead] = load_v(dt + kPvAhead);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
-            oacc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcur, pf[nt], oacc[dt][nt], 0, 0, 0);
+            oacc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vc, pf[nt], oacc[dt][nt], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
-          vcur = vnxt;
         }
       }
     }
@@ -511,9 +499,9 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t s) {
   }
   hipError_t e;
   switch (L.H) {
-    case 32: e = launch_bf16<16, 2>(a, rows, s); break;
-    case 64: e = launch_bf16<16, 4>(a, rows, s); break;
-    case 128: e = launch_bf16<16, 8>(a, rows, s); break;
+    case 32: e = launch_bf16<32, 1>(a, rows, s); break;
+    case 64: e = launch_bf16<32, 2>(a, rows, s); break;
+    case 128: e = launch_bf16<32, 4>(a, rows, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || a.splits == 1) return e;

@@ -17,9 +17,12 @@ per-chunk launches through the individual C entry points with HIP events
 between them on the launch stream.
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
-import math
 import os
+import re
 import sys
 import time
 
@@ -30,6 +33,28 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"fp8": 5.0e15, "bf16": 2.5e15}   # MI355X dense MFMA, FLOP/s
 HBM_PEAK = 8.0e12                         # bytes/s
+CSRC = os.path.join(ROOT, "sparse_attention_03_amd", "csrc")
+KERNEL_SOURCE = {"attention": "sparse_mla.hip", "indexer": "indexer.hip", "topk": "topk.hip"}
+KERNEL_SYMBOL = {"attention": "mla_bf16_kernel", "indexer": "indexer_fp8_kernel", "topk": "topk_kernel"}
+COPY_BYTES = 1 << 30                      # the calibration copy moves this many bytes each way
+
+
+def source_sha(step):
+    with open(os.path.join(CSRC, KERNEL_SOURCE[step]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(step):
+    """HBM bytes per launch measured by the FETCH_SIZE / WRITE_SIZE counter runs
+    (profiles/traffic_<step>.json), or None if the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{step}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha") != source_sha(step):
+        return None
+    return t["bytes_per_launch"]
 
 
 def log(*a):
@@ -98,7 +123,7 @@ def kernel_times(p, reps=1):
     return {k: v / reps for k, v in tot.items()}
 
 
-def cpu_baseline(p, work, n_rows=256, seed=0):
+def cpu_baseline(p, work, n_rows=640, seed=0):
     """Time the oracle on `n_rows` sampled rows of the same prefill and
     extrapolate to the whole step with the per-row cost model
     (t+1)*H_I*d_I (rows with n > k) + min(t+1, k)*H*(d_qk + d_v) MACs."""
@@ -146,6 +171,64 @@ def decode_us_per_token(steps=20, warmup=3):
             "us_per_token": step_s * 1e6 / p.total_q, "us_per_step": step_s * 1e6}
 
 
+def _short(name):
+    m = re.search(r"dsa::\(anonymous namespace\)::(\w+)", name)
+    if m:
+        return m.group(1)
+    name = name[5:] if name.startswith("void ") else name
+    name = name.replace("(anonymous namespace)::", "")
+    return re.split(r"[<(]", name, maxsplit=1)[0][-40:]
+
+
+def summarize(dirs, command):
+    """Print a text summary of rocprofv3 output in `dirs` (kernel stats and, if
+    present, FETCH_SIZE / WRITE_SIZE counter collections, where the files named
+    copy_* come from `--copy-calibration`); for counter runs also write
+    profiles/traffic_<step>.json for the kernels of the path."""
+    out = []
+    if command:
+        out.append(f"command: {command}")
+    files = lambda pat: sorted(f for d in dirs for f in glob.glob(os.path.join(d, "**", pat), recursive=True))
+    for f in files("*kernel_stats.csv"):
+        out.append(f"kernel stats ({os.path.basename(f)}):")
+        out.append(f"  {'kernel':28s} {'calls':>6s} {'total ms':>10s} {'avg ms':>9s} {'min ms':>9s} {'max ms':>9s}")
+        for r in csv.DictReader(open(f)):
+            out.append(f"  {_short(r['Name']):28s} {int(r['Calls']):6d} {float(r['TotalDurationNs']) / 1e6:10.3f} "
+                       f"{float(r['AverageNs']) / 1e6:9.4f} {float(r['MinNs']) / 1e6:9.4f} {float(r['MaxNs']) / 1e6:9.4f}")
+    counters = {}
+    for f in files("*counter_collection.csv"):
+        calib = os.path.basename(f).startswith("copy")
+        for r in csv.DictReader(open(f)):
+            name = r["Kernel_Name"]
+            if calib and "MulFunctor" not in name:
+                continue
+            key = "copy" if calib else _short(name)
+            counters.setdefault((key, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    if counters:
+        fac = {}
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            vals = counters.get(("copy", c), [])
+            big = [v for v in vals if v * 1024 > COPY_BYTES / 2]
+            if big:
+                fac[c] = COPY_BYTES / (sum(big) / len(big) * 1024)
+        out.append("counters (KiB per dispatch, mean over dispatches; copy calibration factor applied for bytes):")
+        for step, sym in KERNEL_SYMBOL.items():
+            fetch = counters.get((sym, "FETCH_SIZE"))
+            write = counters.get((sym, "WRITE_SIZE"))
+            if not fetch or not write:
+                continue
+            fk, wk = sum(fetch) / len(fetch), sum(write) / len(write)
+            ff, wf = fac.get("FETCH_SIZE", 1.0), fac.get("WRITE_SIZE", 1.0)
+            per_launch = fk * 1024 * ff + wk * 1024 * wf
+            out.append(f"  {sym:28s} FETCH {fk:12.1f} KiB  WRITE {wk:12.1f} KiB  -> {per_launch / 1e9:8.3f} GB per launch")
+            with open(os.path.join(ROOT, "profiles", f"traffic_{step}.json"), "w") as f:
+                json.dump({"kernel": sym, "source_sha": source_sha(step), "bytes_per_launch": per_launch,
+                           "fetch_kib_per_launch": fk, "write_kib_per_launch": wk, "fetch_factor": ff,
+                           "write_factor": wf, "dispatches": len(fetch), "command": command}, f, indent=1)
+        out.append(f"  copy calibration factors: {json.dumps(fac)} (bytes moved / counter bytes, 1 GiB copy)")
+    print("\n".join(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,7 +238,14 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true")
     ap.add_argument("--decode-only", action="store_true", help="time only the 64 x 32K decode batch")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy 3 times (counter calibration under rocprofv3)")
+    ap.add_argument("--summarize", metavar="DIR", nargs="+", help="summarise rocprofv3 CSV output in DIR... and exit")
+    ap.add_argument("--summary-command", default="", help="the command that produced DIR (recorded)")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, args.summary_command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -167,6 +257,16 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.decode_only:
         print(json.dumps({"decode": decode_us_per_token(steps=args.steps, warmup=args.warmup)}), flush=True)
+        return
+    if args.copy_calibration:
+        # an elementwise kernel (not hipMemcpy, which the counters do not see)
+        # that reads COPY_BYTES and writes COPY_BYTES
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES}), flush=True)
         return
     log("generating prefill_128k inputs on the GPU")
     p = gen.make_config("prefill_128k", device="cuda")
@@ -214,8 +314,12 @@ def main():
                         "frac": tk_bw / HBM_PEAK}
         dom = max(("indexer", "attention"), key=lambda n: kt[n])
         d = rows[dom]
-        result["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": d["achieved_TFLOPs"],
-                              "peak": d["peak_TFLOPs"], "unit": "TFLOP/s", "frac": d["frac"], "traffic": None}
+        launches = (p.total_q + (p.q_block or 4096) - 1) // (p.q_block or 4096)
+        result["roofline"] = {"kernel": KERNEL_SYMBOL[dom], "bound": "mfma", "achieved": d["achieved_TFLOPs"],
+                              "peak": d["peak_TFLOPs"], "unit": "TFLOP/s", "frac": d["frac"],
+                              "traffic": stored_traffic(dom), "launches_per_step": launches,
+                              "avg_launch_ms": kt[dom] / launches,
+                              "flop_per_launch": fl[dom][0] / launches}
         result["kernels"] = rows
         log(json.dumps(rows))
     if not args.no_decode:

@@ -115,7 +115,13 @@ dsa_status dsa_indexer_scores(const dsa_batch* batch,
  *          ld_scores >= max_ctx, % 4 == 0
  *   idx    [total_q, k] int32 output, 16-B aligned
  * Integer / bit operations only: the result is exact.  Supported: 1 <= k <= 2048.
- * Workspace: none (ws may be NULL when dsa_topk_workspace_size gives 0).
+ * Workspace: dsa_topk_workspace_size bytes, 16-B aligned, for batches with
+ * fewer rows than the device has compute units and max_ctx >= 8 k: each row is
+ * then split into segments whose own top-k candidates are merged (same
+ * result).  The size depends on the current device's compute-unit count, so
+ * query it on the device the call will run on (DSA_ERR_HIP if none is usable;
+ * batches with max_ctx < 8 k need no device and get 0).  ws may be NULL when
+ * the size is 0; a smaller workspace gives DSA_ERR_WORKSPACE.
  */
 dsa_status dsa_topk_workspace_size(const dsa_batch* batch, int32_t k, size_t* bytes /* host */);
 dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores, int32_t k,

@@ -165,6 +165,10 @@ dsa_status dsa_topk_workspace_size(const dsa_batch* batch, int32_t k, size_t* by
   if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is NULL");
   if (dsa_status s = check_batch(batch)) return s;
   if (dsa_status s = check_k(k)) return s;
+  if (!dsa::topk_may_segment(batch->max_ctx, k)) {
+    *bytes = 0;
+    return DSA_OK;
+  }
   int cus = 0;
   if (dsa_status s = device_cus(&cus)) return s;
   *bytes = dsa::topk_workspace_bytes(batch->total_q, batch->max_ctx, k, cus);

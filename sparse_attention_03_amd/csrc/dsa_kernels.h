@@ -64,6 +64,9 @@ hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
 
 // Workspace of the segmented top-k for `rows` rows (0: single pass per row).
 size_t topk_workspace_bytes(int rows, int max_ctx, int k, int num_cus);
+// False when no batch with this max_ctx and k is ever split into segments
+// (then the workspace is 0 bytes on every device).
+bool topk_may_segment(int max_ctx, int k);
 
 // Number of key-splits the attention uses for `rows` query rows.
 int attention_splits(int rows, int k, bool bf16, int num_cus);

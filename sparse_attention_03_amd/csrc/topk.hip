@@ -364,8 +364,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(const int32_t* _
 
 }  // namespace
 
+bool topk_may_segment(int max_ctx, int k) { return max_ctx / (4 * k) > 1; }
+
 int topk_segments(int rows, int max_ctx, int k, int num_cus) {
-  if (rows <= 0 || rows >= num_cus) return 1;
+  if (rows <= 0 || rows >= num_cus || !topk_may_segment(max_ctx, k)) return 1;
   // enough workgroups for the machine, but segments of at least 4k entries so
   // that phase 1 actually discards most of each segment
   int nseg = (2 * num_cus + rows - 1) / rows;

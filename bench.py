@@ -101,6 +101,8 @@ def kernel_times(p, reps=1):
     tot = {"indexer": 0.0, "topk": 0.0, "attention": 0.0}
     ld = dsa.score_ld(p.max_ctx)
     scores = torch.empty((qb, ld), dtype=torch.float32, device=p.q.device)
+    n_ws = L.dsa_indexer_workspace_size(L.batch_of(chunk_problem(p, 0, min(p.total_q, qb), skip_short=False)), p.q_idx)
+    idx_ws = torch.empty(max(n_ws, 16), dtype=torch.uint8, device=p.q.device)
     for _ in range(reps):
         for r0 in range(0, p.total_q, qb):
             r1 = min(p.total_q, r0 + qb)
@@ -109,7 +111,7 @@ def kernel_times(p, reps=1):
             e = [ev() for _ in range(4)]
             e[0].record()
             if c_idx is not None:
-                L.dsa_indexer_scores(L.batch_of(c_idx), c_idx.q_idx, c_idx.k_idx, c_idx.w, scores)
+                L.dsa_indexer_scores(L.batch_of(c_idx), c_idx.q_idx, c_idx.k_idx, c_idx.w, scores, ws=idx_ws)
             e[1].record()
             idx = torch.empty((r1 - r0, p.k), dtype=torch.int32, device=p.q.device)
             L.dsa_topk(L.batch_of(c_all), scores, p.k, idx)

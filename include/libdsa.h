@@ -95,14 +95,24 @@ const char* dsa_version(void);
  *   scores  [total_q, ld_scores]  fp32 output, 16-B aligned; only s <= pos_r
  *                                 is written; ld_scores >= max_ctx, % 4 == 0
  * Arithmetic: FP8 x FP8 products are exact in fp32; dot products accumulate in
- * fp32 (MFMA); act and the weighted head sum are fp32 in a fixed head order.
- * Supported: FP8 with d_I = 128 and H_I in {16, 32, 48, 64}; F32 with
- * d_I <= 256, H_I <= 64 and H_I * d_I <= 8192.
+ * fp32 (MFMA); the weighted head sum is fp32 in a fixed order.  With ReLU and
+ * FP8 inputs the score is evaluated as 1/2 (qt . k + sum_j w[r,j] |q_idx[r,j,:] . k|)
+ * with qt = sum_j w[r,j] q_idx[r,j,:] (the same function, since
+ * ReLU(x) = (x + |x|) / 2); qt is carried as four E4M3 terms with power-of-two
+ * scales per 32 elements, within about 2^-16 of each block's largest value.
+ * Workspace: dsa_indexer_workspace_size bytes (528 per query row for FP8 with
+ * ReLU, else 0), 16-B aligned; ws may be NULL when that is 0; a smaller
+ * workspace gives DSA_ERR_WORKSPACE.  The size needs no device.
+ * Supported: FP8 with d_I = 128, H_I in {16, 32, 48, 64} and max_ctx <= 2^24;
+ * F32 with d_I <= 256, H_I <= 64 and H_I * d_I <= 8192.
  */
+dsa_status dsa_indexer_workspace_size(const dsa_batch* batch, dsa_dtype idx_dtype, int32_t H_I, int32_t d_I,
+                                      dsa_act act, size_t* bytes /* host */);
 dsa_status dsa_indexer_scores(const dsa_batch* batch,
                               const void* q_idx, const void* k_idx, dsa_dtype idx_dtype,
                               const float* w, int32_t H_I, int32_t d_I, dsa_act act,
-                              float* scores, int64_t ld_scores, dsa_stream_t stream);
+                              float* scores, int64_t ld_scores,
+                              void* ws, size_t ws_bytes, dsa_stream_t stream);
 
 /*
  * Causal top-k selection.  [P1] "Step 2", [P2] 【细粒度Token选择机制】: for each

@@ -75,13 +75,13 @@ dsa_status check_indexer(const dsa_batch* b, const void* q_idx, const void* k_id
   if (dt == DSA_FP8_E4M3) {
     if (d_I != 128) return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer needs d_I = 128 (got %d)", d_I);
     if (H_I % 16 != 0 || H_I > 64) return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer needs H_I in {16,32,48,64} (got %d)", H_I);
+    if (b->max_ctx > (1 << 24)) return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer needs max_ctx <= 2^24 (got %d)", b->max_ctx);
   } else if (dt == DSA_F32) {
     if (d_I > 256 || H_I > 64 || H_I * d_I > 8192)
       return fail(DSA_ERR_UNSUPPORTED, "F32 indexer needs d_I <= 256, H_I <= 64, H_I * d_I <= 8192");
   } else {
     return fail(DSA_ERR_UNSUPPORTED, "indexer dtype must be FP8_E4M3 or F32");
   }
-  (void)b;
   return DSA_OK;
 }
 
@@ -144,18 +144,32 @@ const char* dsa_last_error(void) { return g_err; }
 
 const char* dsa_version(void) { return "libdsa 0.1 gfx950"; }
 
+dsa_status dsa_indexer_workspace_size(const dsa_batch* batch, dsa_dtype idx_dtype, int32_t H_I, int32_t d_I,
+                                      dsa_act act, size_t* bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is NULL");
+  if (dsa_status s = check_batch(batch)) return s;
+  static const uint8_t kDummy[16] __attribute__((aligned(16))) = {};
+  if (dsa_status s = check_indexer(batch, kDummy, kDummy, idx_dtype, (const float*)kDummy, H_I, d_I, act)) return s;
+  *bytes = dsa::indexer_workspace_bytes(batch->total_q, idx_dtype == DSA_FP8_E4M3, (int)act);
+  return DSA_OK;
+}
+
 dsa_status dsa_indexer_scores(const dsa_batch* batch, const void* q_idx, const void* k_idx, dsa_dtype idx_dtype,
                               const float* w, int32_t H_I, int32_t d_I, dsa_act act, float* scores,
-                              int64_t ld_scores, dsa_stream_t stream) {
+                              int64_t ld_scores, void* ws, size_t ws_bytes, dsa_stream_t stream) {
   g_err[0] = 0;
   if (dsa_status s = check_batch(batch)) return s;
   if (dsa_status s = check_indexer(batch, q_idx, k_idx, idx_dtype, w, H_I, d_I, act)) return s;
   if (dsa_status s = check_scores(batch, scores, ld_scores)) return s;
+  const size_t need = dsa::indexer_workspace_bytes(batch->total_q, idx_dtype == DSA_FP8_E4M3, (int)act);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
+    return fail(DSA_ERR_WORKSPACE, "indexer workspace: need %zu bytes (got %zu)", need, ws_bytes);
   if (batch->total_q == 0) return DSA_OK;
   int cus = 0;
   if (dsa_status s = device_cus(&cus)) return s;
   dsa::IndexerLaunch L{view(batch, 0, batch->total_q), 0, q_idx, k_idx, w, scores, ld_scores, H_I, d_I, (int32_t)act,
-                       idx_dtype == DSA_FP8_E4M3, cus};
+                       idx_dtype == DSA_FP8_E4M3, cus, need > 0 ? ws : nullptr};
   hipError_t e = dsa::launch_indexer(L, (hipStream_t)stream);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "indexer launch");
 }
@@ -238,7 +252,7 @@ namespace {
 struct ForwardPlan {
   int32_t qb;       // rows per chunk
   int64_t ld;       // score row stride
-  size_t off_scores, off_idx, off_topk, off_attn, total;
+  size_t off_scores, off_idx, off_topk, off_attn, off_lin, total;
   int max_splits;
 };
 
@@ -277,8 +291,10 @@ dsa_status plan_forward(const dsa_forward_params* p, int cus, ForwardPlan* f) {
   const int s_last = last ? dsa::attention_splits(last, p->k, p->dtype == DSA_BF16, cus) : 1;
   const size_t a_full = attention_ws_bytes(f->qb, s_full, p->H, p->d_v);
   const size_t a_last = last ? attention_ws_bytes(last, s_last, p->H, p->d_v) : 0;
-  off += a_full > a_last ? a_full : a_last;
+  off += round_up(a_full > a_last ? a_full : a_last, 256);
   f->max_splits = s_full > s_last ? s_full : s_last;
+  f->off_lin = off;
+  off += dsa::indexer_workspace_bytes(f->qb, p->idx_dtype == DSA_FP8_E4M3, (int)p->act);
   f->total = off;
   return DSA_OK;
 }
@@ -319,7 +335,7 @@ dsa_status dsa_forward(const dsa_forward_params* p, void* ws, size_t ws_bytes, d
     int32_t* idx = p->out_idx ? p->out_idx + (int64_t)r0 * p->k : (int32_t*)(base + f.off_idx);
     // rows with pos + 1 <= k select every candidate: their scores are never read
     dsa::IndexerLaunch IL{v, p->k, p->q_idx, p->k_idx, p->w, scores, f.ld, p->H_I, p->d_I, (int32_t)p->act,
-                          p->idx_dtype == DSA_FP8_E4M3, cus};
+                          p->idx_dtype == DSA_FP8_E4M3, cus, base + f.off_lin};
     hipError_t e = dsa::launch_indexer(IL, st);
     if (e != hipSuccess) return hip_fail(e, "forward indexer launch");
     dsa::TopkLaunch TL{v, scores, f.ld, p->k, idx, base + f.off_topk, cus};

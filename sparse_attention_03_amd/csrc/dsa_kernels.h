@@ -30,6 +30,7 @@ struct IndexerLaunch {
   int32_t act;             // 0 relu, 1 gelu
   bool fp8;
   int32_t num_cus;
+  void* ws;                // indexer_workspace_bytes(rows, fp8, act) bytes, or null when that is 0
 };
 
 struct TopkLaunch {
@@ -59,6 +60,10 @@ struct AttnLaunch {
 };
 
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s);
+
+// Workspace of the indexer for `rows` query rows (the FP8 ReLU path keeps the
+// linear-term fragments of every row there).
+size_t indexer_workspace_bytes(int rows, bool fp8, int act);
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
 

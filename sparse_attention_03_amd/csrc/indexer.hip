@@ -7,16 +7,28 @@
 // FP8.  GELU (named instead of ReLU on the gamebaike.com summary,
 // 【闪电索引器】) is a template switch.
 //
-// FP8 path: one v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 x E4M3, unit scales)
-// computes a whole d_I = 128 dot product for 16 heads x 16 keys.  A wave holds
-// the query fragments of two query rows (all heads) in VGPRs and streams key
-// fragments straight from global memory (a 16-key fragment is 2 KB
-// contiguous); the four waves of a workgroup sweep the same keys so the L1
-// serves three of the four reads.  Epilogue per MFMA output element: max and
-// fma with the head weight (fp32), accumulated in a fixed head order; the
-// cross-lane head sum uses a transpose-reduce so that each lane group ends up
-// owning one 16-key sub-tile and a 64-key slab is stored as one contiguous
-// 256-byte row segment.
+// FP8 path: one v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 x E4M3) computes a
+// whole d_I = 128 dot product for 16 heads x 16 keys.  A wave holds the query
+// fragments of two query rows (all heads) in VGPRs and streams key fragments
+// straight from global memory (a 16-key fragment is 2 KB contiguous; the four
+// waves of a workgroup sweep the same keys so the L1 serves most reads).
+//
+// ReLU epilogue.  With ReLU(x) = (x + |x|) / 2 the score splits into
+//   I = 1/2 * qt . k  +  1/2 * sum_j w_j |x_j|,   qt = sum_j w_j q_I[j],
+// a linear term and a term that costs one fma per head (|x| is a free source
+// modifier), instead of a max and an fma.  The linear term runs on the MFMA
+// too: a pre-pass writes qt per row as four E4M3 terms, each with E8M0 scales
+// per 32-element K block of the MFMA (the residual after four terms is about
+// 2^-16 of the block maximum; six would represent the fp32 qt exactly).  The terms of row i
+// sit in MFMA rows {i, i+4, i+8, i+12}, so every lane group holds one term per
+// key and the cross-lane head sum adds the terms up for free.  The GELU
+// epilogue applies the activation per head.
+//
+// Cross-lane head sum: a transpose-reduce with the gfx950 permlane swaps, so
+// that each lane group ends up owning one 16-key sub-tile and a 64-key slab is
+// one contiguous 256-byte store per row.  Key loads and score stores are
+// buffer instructions whose range check replaces per-lane clamps: keys past
+// the chunk read as zero, scores past the causal bound are dropped.
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
@@ -26,18 +38,15 @@ namespace {
 constexpr int kIdxThreads = 256;
 constexpr int kRowsPerWave = 2;
 constexpr int kRowsPerBlock = 4 * kRowsPerWave;
-
-// ReLU on the bit pattern: a float is >= +0 exactly when its int32 image is
-// >= 0, so max(bits, 0) is max(x, 0) with -0 -> +0, in one integer op and
-// without the NaN canonicalisation a float max would add.
-__device__ __forceinline__ float relu(float x) {
-  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
-}
+constexpr int kLinTerms = 4;
+constexpr int kLinScaleOff = kLinTerms * 128;                 // E8M0 scales [term][32-dim block]
+constexpr int kLinRowBytes = kLinScaleOff + kLinTerms * 4;    // 528
+constexpr uint32_t kBufFlags = 0x00020000;                    // raw buffer, dword data format
 
 template <int ACT>
 __device__ __forceinline__ float activation(float x) {
   if constexpr (ACT == 0) {
-    return relu(x);
+    return fmaxf(x, 0.0f);
   } else {
     return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
   }
@@ -54,12 +63,86 @@ struct IdxArgs {
   int64_t ld;
   int32_t key_chunk;
   int32_t H_I;
+  const uint8_t* lin;      // [row_end - row_begin, kLinRowBytes] linear-term fragments (ReLU)
+  uint8_t* lin_out;
 };
+
+__device__ __forceinline__ float bits_f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// Sum over the four lane groups of part[st], leaving sub-tile g's total in lane
+// group g: a permlane32 swap pairs groups {0,2} and {1,3}, a permlane16 swap
+// then pairs {0,1} and {2,3}.
+__device__ __forceinline__ float transpose_reduce(float p0, float p1, float p2, float p3) {
+  auto a = __builtin_amdgcn_permlane32_swap(f_bits(p0), f_bits(p2), false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(f_bits(p1), f_bits(p3), false, false);
+  const float ka = bits_f(a[0]) + bits_f(a[1]);  // groups 0,1: sub-tile 0; groups 2,3: sub-tile 2
+  const float kb = bits_f(b[0]) + bits_f(b[1]);  // groups 0,1: sub-tile 1; groups 2,3: sub-tile 3
+  auto c = __builtin_amdgcn_permlane16_swap(f_bits(ka), f_bits(kb), false, false);
+  return bits_f(c[0]) + bits_f(c[1]);
+}
+
+// Linear-term pre-pass, one wave per query row: qt = sum_j w[j] q_I[j] in
+// fp32, then four E4M3 terms with per-32-block power-of-two scales, each the
+// rounding of what the previous ones left.
+__global__ __launch_bounds__(256) void indexer_lin_kernel(IdxArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int32_t r = a.row_begin + blockIdx.x * 4 + wave;
+  if (r >= a.row_end) return;
+  const uint8_t* qrow = a.q_idx + (int64_t)r * a.H_I * 128 + 2 * lane;
+  const float* wr = a.w + (int64_t)r * a.H_I;
+  float q0 = 0.0f, q1 = 0.0f;
+  for (int h = 0; h < a.H_I; h += 16) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const uint32_t two = *(const uint16_t*)(qrow + (h + u) * 128);
+      const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)two, false);
+      const float wh = wr[h + u];
+      q0 = fmaf(wh, f[0], q0);
+      q1 = fmaf(wh, f[1], q1);
+    }
+  }
+  uint8_t* out = a.lin_out + (int64_t)(r - a.row_begin) * kLinRowBytes;
+  // The MFMA reads a lane's 32 fragment bytes as K = 16 g + (0..15) and
+  // 64 + 16 g + (0..15) (g = lane / 16), and lane group b's E8M0 scale covers
+  // K = 32 b .. 32 b + 31.  In memory order (fragment bytes = dims 32 g ..
+  // 32 g + 31) scale block b is therefore dims {0-15, 32-47} (b = 0),
+  // {64-79, 96-111} (1), {16-31, 48-63} (2), {80-95, 112-127} (3): for this
+  // lane's dims 2 lane, 2 lane + 1:
+  const int blk = ((lane >> 5) & 1) + 2 * ((lane >> 3) & 1);
+#pragma unroll
+  for (int t = 0; t < kLinTerms; ++t) {
+    float m = fmaxf(fabsf(q0), fabsf(q1));
+    // max over the 16 lanes of this scale block (lane bits 0-2 and 4 vary)
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    int e = 0;
+    if (m > 0.0f) {
+      int E;
+      (void)frexpf(m, &E);
+      e = E - 8;  // m * 2^-e in [128, 256): below the E4M3 maximum 448
+      e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    }
+    const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(q0, -e), ldexpf(q1, -e), 0, false);
+    const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(pk, false);
+    q0 -= ldexpf(back[0], e);
+    q1 -= ldexpf(back[1], e);
+    *(uint16_t*)(out + t * 128 + 2 * lane) = (uint16_t)pk;
+    if ((lane & 0x17) == 0) out[kLinScaleOff + t * 4 + blk] = (uint8_t)(127 + e);
+  }
+}
 
 // NR query rows of one sequence against keys [kstart, kend).
 template <int NR, int NHT, int ACT>
 __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)[NR], const int32_t (&pos)[NR],
                                          int32_t kbase, int32_t kstart, int32_t kend) {
+  constexpr bool LIN = ACT == 0;
+  constexpr int NST = 4;                          // 16-key sub-tiles per 64-key slab
+  constexpr int NPS = (LIN ? 1 : 0) + NR * NHT;   // MFMAs per sub-tile
+  constexpr int NM = NST * NPS;                   // MFMAs per slab
+  constexpr int LAG = 2;                          // epilogue of MFMA j follows MFMA j + LAG
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, li = lane & 15;
   i32x8 qf[NR][NHT];
@@ -76,72 +159,107 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
       wv[i][ht][0] = wq[0]; wv[i][ht][1] = wq[1]; wv[i][ht][2] = wq[2]; wv[i][ht][3] = wq[3];
     }
   }
-  const uint8_t* kb = a.k_idx + (int64_t)kbase * 128 + 32 * g;
-
-  auto load_keys = [&](int32_t s0, i32x8 (&kf)[4]) {
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      int32_t s = min(s0 + 16 * st + li, kend - 1);
-      const i32x4* p = (const i32x4*)(kb + (int64_t)s * 128);
+  // linear-term A fragment: MFMA row li holds term li / 4 of row li % 4
+  i32x8 lf = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  int lscale = 127;
+  if constexpr (LIN) {
+    const int i = li & 3, t = li >> 2;
+    if (i < NR) {
+      const int32_t row = i == 0 ? rows[0] : rows[NR - 1];
+      const uint8_t* src = a.lin + (int64_t)(row - a.row_begin) * kLinRowBytes;
+      const i32x4* p = (const i32x4*)(src + t * 128 + 32 * g);
       i32x4 lo = p[0], hi = p[1];
+      lf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      lscale = src[kLinScaleOff + t * 4 + g];
+    }
+  }
+  // keys: [kbase, kbase + kend) in range, everything past it reads as zero
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_idx + (int64_t)kbase * 128), 0, kend * 128, kBufFlags);
+  const int kvo = li * 128 + 32 * g;
+  __amdgpu_buffer_rsrc_t srs[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int32_t lim = min(kend, pos[i] + 1);
+    srs[i] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.scores + (int64_t)(rows[i] - a.row_begin) * a.ld), 0,
+                                               lim * 4, kBufFlags);
+  }
+  const int svo = (16 * g + li) * 4;
+
+  auto load_keys = [&](int32_t s0, i32x8 (&kf)[NST]) {
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const i32x4 lo = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, kvo + st * 2048, s0 * 128, 0));
+      const i32x4 hi = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, kvo + st * 2048 + 16, s0 * 128, 0));
       kf[st] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   };
 
-  i32x8 kf[4], kn[4];
-  load_keys(kstart, kf);
-  for (int32_t s0 = kstart; s0 < kend; s0 += 64) {
-    if (s0 + 64 < kend) load_keys(s0 + 64, kn);
-    float part[NR][4];
+  // One 64-key slab with the keys in kf; the next slab's keys go to kn.
+  auto slab = [&](int32_t s0, const i32x8 (&kf)[NST], i32x8 (&kn)[NST]) {
+    load_keys(s0 + 64, kn);  // unconditional: a conditional load would make every wait drain it
+    float acc[NST][NR];
+    f32x4 x[LAG + 1];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        // NHT independent MFMAs, then one accumulator chain per head tile
-        f32x4 x[NHT];
-#pragma unroll
-        for (int ht = 0; ht < NHT; ++ht)
-          x[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[i][ht], kf[st], f32x4{0.f, 0.f, 0.f, 0.f}, 0,
-                                                                   0, 0, 127, 0, 127);
-        float acc[NHT];
-#pragma unroll
-        for (int ht = 0; ht < NHT; ++ht) {
-          acc[ht] = wv[i][ht][0] * activation<ACT>(x[ht][0]);
-#pragma unroll
-          for (int rr = 1; rr < 4; ++rr) acc[ht] = fmaf(wv[i][ht][rr], activation<ACT>(x[ht][rr]), acc[ht]);
+    for (int j = 0; j < NM + LAG; ++j) {
+      if (j < NM) {
+        const int st = j / NPS, u = j % NPS;
+        if (LIN && u == 0) {
+          x[j % (LAG + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(lf, kf[st], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                              0, 0, 0, lscale, 0, 127);
+        } else {
+          const int v = u - (LIN ? 1 : 0), i = v / NHT, ht = v % NHT;
+          x[j % (LAG + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[i][ht], kf[st],
+                                                                              f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127,
+                                                                              0, 127);
         }
-        float sum = acc[0];
+      }
+      if (j >= LAG) {
+        const int e = j - LAG;
+        const int st = e / NPS, u = e % NPS;
+        const f32x4 xv = x[e % (LAG + 1)];
+        if (LIN && u == 0) {
 #pragma unroll
-        for (int ht = 1; ht < NHT; ++ht) sum += acc[ht];
-        part[i][st] = sum;
+          for (int i = 0; i < NR; ++i) acc[st][i] = xv[i];  // this lane group's term of row i
+        } else {
+          const int v = u - (LIN ? 1 : 0), i = v / NHT, ht = v % NHT;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if constexpr (LIN) {
+              acc[st][i] = fmaf(wv[i][ht][r], fabsf(xv[r]), acc[st][i]);
+            } else {
+              const float av = activation<ACT>(xv[r]);
+              acc[st][i] = (ht == 0 && r == 0) ? wv[i][ht][r] * av : fmaf(wv[i][ht][r], av, acc[st][i]);
+            }
+          }
+        }
       }
     }
-    // transpose-reduce over the four lane groups: group g ends with sub-tile g
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const bool hi2 = g >= 2;
-      float keep0 = hi2 ? part[i][2] : part[i][0];
-      float keep1 = hi2 ? part[i][3] : part[i][1];
-      float send0 = hi2 ? part[i][0] : part[i][2];
-      float send1 = hi2 ? part[i][1] : part[i][3];
-      keep0 += __shfl_xor(send0, 32);
-      keep1 += __shfl_xor(send1, 32);
-      const bool odd = g & 1;
-      float keep = odd ? keep1 : keep0;
-      float send = odd ? keep0 : keep1;
-      keep += __shfl_xor(send, 16);
-      const int32_t s = s0 + 16 * g + li;
-      if (s < kend && s <= pos[i]) a.scores[(int64_t)(rows[i] - a.row_begin) * a.ld + s] = keep;
+    for (int j = 0; j < NM; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, LIN ? 4 : 8, 0);   // then the epilogue VALU work
     }
 #pragma unroll
-    for (int st = 0; st < 4; ++st) kf[st] = kn[st];
+    for (int i = 0; i < NR; ++i) {
+      float v = transpose_reduce(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
+      if constexpr (LIN) v *= 0.5f;
+      __builtin_amdgcn_raw_buffer_store_b32(f_bits(v), srs[i], svo, s0 * 4, 0);
+    }
+  };
+
+  i32x8 k0[NST], k1[NST];
+  load_keys(kstart, k0);
+  for (int32_t s0 = kstart; s0 < kend; s0 += 128) {
+    slab(s0, k0, k1);
+    if (s0 + 64 < kend) slab(s0 + 64, k1, k0);
   }
 }
 
 template <int NHT, int ACT>
 __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(IdxArgs a) {
   const int wave = threadIdx.x >> 6;
-  const int32_t r0 = a.row_begin + blockIdx.x * kRowsPerBlock + wave * kRowsPerWave;
+  const int32_t r0 = __builtin_amdgcn_readfirstlane(a.row_begin + blockIdx.x * kRowsPerBlock + wave * kRowsPerWave);
   const int32_t kstart = blockIdx.y * a.key_chunk;
   int32_t rows[2] = {r0, r0 + 1};
   int32_t pos[2];
@@ -154,9 +272,11 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(IdxArgs a) {
     kbase[i] = 0;
     if (valid[i]) {
       RowInfo ri = locate_row(a.cu_q, a.cu_k, a.num_seqs, rows[i]);
-      pos[i] = ri.pos;
-      kbase[i] = ri.kbase;
-      valid[i] = ri.pos + 1 > a.skip_n && ri.pos >= kstart;
+      // wave-uniform by construction; say so, so that the buffer descriptors
+      // built from them live in scalar registers
+      pos[i] = __builtin_amdgcn_readfirstlane(ri.pos);
+      kbase[i] = __builtin_amdgcn_readfirstlane(ri.kbase);
+      valid[i] = pos[i] + 1 > a.skip_n && pos[i] >= kstart;
     }
   }
   const int32_t kchunk_end = kstart + a.key_chunk;
@@ -212,6 +332,11 @@ hipError_t launch_fp8(const IdxArgs& a, int act, dim3 grid, hipStream_t s) {
 
 }  // namespace
 
+size_t indexer_workspace_bytes(int rows, bool fp8, int act) {
+  if (!fp8 || act != 0 || rows <= 0) return 0;
+  return ((size_t)rows * kLinRowBytes + 255) / 256 * 256;
+}
+
 hipError_t launch_indexer(const IndexerLaunch& L, hipStream_t s) {
   const int32_t rows = L.b.row_end - L.b.row_begin;
   if (rows <= 0) return hipSuccess;
@@ -228,7 +353,15 @@ hipError_t launch_indexer(const IndexerLaunch& L, hipStream_t s) {
   a.scores = L.scores;
   a.ld = L.ld;
   a.H_I = L.H_I;
+  a.lin = (const uint8_t*)L.ws;
+  a.lin_out = (uint8_t*)L.ws;
   if (L.fp8) {
+    if (L.act == 0) {
+      if (!L.ws) return hipErrorInvalidValue;
+      hipLaunchKernelGGL(indexer_lin_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     // key chunk: enough workgroups to cover every CU several times over
     const int64_t row_blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
     int32_t chunk = 4096;

@@ -20,7 +20,9 @@ def indexer_scores(p, act=L.DSA_ACT_RELU, ld=None, fill=float("nan")):
     """Scores [total_q, ld] fp32; entries beyond each row's causal bound keep `fill`."""
     ld = score_ld(p.max_ctx) if ld is None else ld
     scores = torch.full((p.total_q, ld), fill, dtype=torch.float32, device=p.q_idx.device)
-    L.dsa_indexer_scores(L.batch_of(p), p.q_idx, p.k_idx, p.w, scores, act=act)
+    b = L.batch_of(p)
+    n = L.dsa_indexer_workspace_size(b, p.q_idx, act)
+    L.dsa_indexer_scores(b, p.q_idx, p.k_idx, p.w, scores, act=act, ws=_ws(n, scores.device) if n else None)
     return scores
 
 

@@ -48,7 +48,9 @@ _SIGS = {
     "dsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "dsa_last_error": ([], ctypes.c_char_p),
     "dsa_version": ([], ctypes.c_char_p),
-    "dsa_indexer_scores": ([_BP, _p, _p, ctypes.c_int, _p, _i32, _i32, ctypes.c_int, _p, _i64, _p], ctypes.c_int),
+    "dsa_indexer_workspace_size": ([_BP, ctypes.c_int, _i32, _i32, ctypes.c_int, ctypes.POINTER(_sz)], ctypes.c_int),
+    "dsa_indexer_scores": ([_BP, _p, _p, ctypes.c_int, _p, _i32, _i32, ctypes.c_int, _p, _i64, _p, _sz, _p],
+                           ctypes.c_int),
     "dsa_topk_workspace_size": ([_BP, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
     "dsa_topk": ([_BP, _p, _i64, _i32, _p, _p, _sz, _p], ctypes.c_int),
     "dsa_sparse_mla_attn_workspace_size": ([_BP, ctypes.c_int, _i32, _i32, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
@@ -107,10 +109,18 @@ def batch_of(p) -> DsaBatch:
     return make_batch(p.cu_q, p.cu_k, p.total_q, p.total_k, p.max_ctx)
 
 
-def dsa_indexer_scores(batch: DsaBatch, q_idx, k_idx, w, scores, act=DSA_ACT_RELU, stream=None):
+def dsa_indexer_workspace_size(batch: DsaBatch, q_idx, act=DSA_ACT_RELU) -> int:
+    n = _sz(0)
+    _check(_lib.dsa_indexer_workspace_size(ctypes.byref(batch), _dtype_code(q_idx), q_idx.shape[1], q_idx.shape[2],
+                                           act, ctypes.byref(n)), "dsa_indexer_workspace_size")
+    return n.value
+
+
+def dsa_indexer_scores(batch: DsaBatch, q_idx, k_idx, w, scores, act=DSA_ACT_RELU, ws=None, stream=None):
     _check(_lib.dsa_indexer_scores(ctypes.byref(batch), _ptr(q_idx), _ptr(k_idx), _dtype_code(q_idx), _ptr(w),
-                                   q_idx.shape[1], q_idx.shape[2], act, _ptr(scores), scores.stride(0),
-                                   _stream(stream)), "dsa_indexer_scores")
+                                   q_idx.shape[1], q_idx.shape[2], act, _ptr(scores), scores.stride(0), _ptr(ws),
+                                   0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "dsa_indexer_scores")
 
 
 def dsa_topk_workspace_size(batch: DsaBatch, k: int) -> int:

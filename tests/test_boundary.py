@@ -76,7 +76,7 @@ def _batch(L, cu=0x1000, total_q=8, total_k=8, max_ctx=8, nseq=1):
 
 
 def _call_indexer(L, b, q=0x10000, k=0x20000, w=0x30000, s=0x40000, H_I=64, d_I=128, dt=2, act=0, ld=64):
-    return L._lib.dsa_indexer_scores(ctypes.byref(b), q, k, dt, w, H_I, d_I, act, s, ld, None)
+    return L._lib.dsa_indexer_scores(ctypes.byref(b), q, k, dt, w, H_I, d_I, act, s, ld, 0x50000, 1 << 20, None)
 
 
 def test_indexer_validation(L):
@@ -94,8 +94,22 @@ def test_indexer_validation(L):
     assert _call_indexer(L, _batch(L, cu=0)) == L.DSA_ERR_INVALID_ARG
     assert _call_indexer(L, _batch(L, max_ctx=9)) == L.DSA_ERR_INVALID_ARG  # > total_k
     assert _call_indexer(L, _batch(L, total_q=9)) == L.DSA_ERR_INVALID_ARG  # more queries than keys
-    assert L._lib.dsa_indexer_scores(None, 0x10000, 0x20000, 2, 0x30000, 64, 128, 0, 0x40000, 64, None) \
+    assert L._lib.dsa_indexer_scores(None, 0x10000, 0x20000, 2, 0x30000, 64, 128, 0, 0x40000, 64, None, 0, None) \
         == L.DSA_ERR_INVALID_ARG
+    # FP8 + ReLU keeps 528 bytes per query row in the workspace; GELU and F32 need none
+    f = L._lib.dsa_indexer_scores
+    assert f(ctypes.byref(b), 0x10000, 0x20000, 2, 0x30000, 64, 128, 0, 0x40000, 64, None, 0, None) \
+        == L.DSA_ERR_WORKSPACE
+    assert f(ctypes.byref(b), 0x10000, 0x20000, 2, 0x30000, 64, 128, 0, 0x40000, 64, 0x50000, 100, None) \
+        == L.DSA_ERR_WORKSPACE
+    n = ctypes.c_size_t(123)
+    assert L._lib.dsa_indexer_workspace_size(ctypes.byref(b), 2, 64, 128, 0, ctypes.byref(n)) == L.DSA_OK
+    assert n.value >= 8 * 528 and n.value % 256 == 0
+    assert L._lib.dsa_indexer_workspace_size(ctypes.byref(b), 2, 64, 128, 1, ctypes.byref(n)) == L.DSA_OK
+    assert n.value == 0
+    assert L._lib.dsa_indexer_workspace_size(ctypes.byref(b), 0, 8, 32, 0, ctypes.byref(n)) == L.DSA_OK
+    assert n.value == 0
+    assert L._lib.dsa_indexer_workspace_size(ctypes.byref(b), 2, 20, 128, 0, ctypes.byref(n)) == L.DSA_ERR_UNSUPPORTED
 
 
 def test_topk_validation(L):

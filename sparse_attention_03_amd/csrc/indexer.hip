@@ -38,6 +38,8 @@ namespace {
 constexpr int kIdxThreads = 256;
 constexpr int kRowsPerWave = 2;
 constexpr int kRowsPerBlock = 4 * kRowsPerWave;
+constexpr int kSlabBytes = 64 * 128;                         // 64 keys
+constexpr int kRing = 3;                                      // LDS slabs: one read, two in flight
 constexpr int kLinTerms = 4;
 constexpr int kLinScaleOff = kLinTerms * 128;                 // E8M0 scales [term][32-dim block]
 constexpr int kLinRowBytes = kLinScaleOff + kLinTerms * 4;    // 528
@@ -134,10 +136,19 @@ __global__ __launch_bounds__(256) void indexer_lin_kernel(IdxArgs a) {
   }
 }
 
-// NR query rows of one sequence against keys [kstart, kend).
-template <int NR, int NHT, int ACT>
-__device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)[NR], const int32_t (&pos)[NR],
-                                         int32_t kbase, int32_t kstart, int32_t kend) {
+// Where the keys come from.
+enum KeySource {
+  kKeysShared = 0,    // the four waves run the same key range and take the keys from an LDS ring
+                      // that they fill together (one 8-KB slab per barrier)
+  kKeysPrefetch = 1,  // each wave streams its keys, the next slab in flight
+  kKeysPlain = 2,     // each wave streams its keys, one slab at a time (fewest registers)
+};
+
+// NR query rows of one sequence against keys [kstart, kend); lim[i]: row i's
+// scores are stored for keys below lim[i] only.
+template <int NR, int NHT, int ACT, int KEYS>
+__device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)[NR], const int32_t (&lim)[NR],
+                                         int32_t kbase, int32_t kstart, int32_t kend, DSA_LDS uint8_t* ring) {
   constexpr bool LIN = ACT == 0;
   constexpr int NST = 4;                          // 16-key sub-tiles per 64-key slab
   constexpr int NPS = (LIN ? 1 : 0) + NR * NHT;   // MFMAs per sub-tile
@@ -179,25 +190,51 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
   const int kvo = li * 128 + 32 * g;
   __amdgpu_buffer_rsrc_t srs[NR];
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    const int32_t lim = min(kend, pos[i] + 1);
+  for (int i = 0; i < NR; ++i)
     srs[i] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.scores + (int64_t)(rows[i] - a.row_begin) * a.ld), 0,
-                                               lim * 4, kBufFlags);
-  }
+                                               lim[i] * 4, kBufFlags);
   const int svo = (16 * g + li) * 4;
 
-  auto load_keys = [&](int32_t s0, i32x8 (&kf)[NST]) {
+  // LDS ring (SHARED): copy instruction q of a slab fills key rows 8q .. 8q+7,
+  // lane i writing 16-byte slot i % 8 of row 8q + i / 8; the slot holds chunk
+  // (i % 8) ^ ((row / 2) % 8) of the key, so that the 16 lanes of a fragment
+  // read (16 consecutive rows, one chunk) hit 16 different 16-byte bank groups.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cr0 = 8 * wave + (lane >> 3), cr1 = cr0 + 32;
+  const int cc0 = ((lane & 7) ^ ((cr0 >> 1) & 7)) * 16, cc1 = ((lane & 7) ^ ((cr1 >> 1) & 7)) * 16;
+  const uint8_t* kglob = a.k_idx + (int64_t)kbase * 128;
+  auto copy_slab = [&](int32_t s0, int slot) {
+    DSA_LDS uint8_t* dst = ring + slot * kSlabBytes;
+    const int32_t r0 = min(s0 + cr0, kend - 1), r1 = min(s0 + cr1, kend - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(kglob + (int64_t)r0 * 128 + cc0),
+                                     (DSA_LDS void*)(dst + 1024 * wave), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(kglob + (int64_t)r1 * 128 + cc1),
+                                     (DSA_LDS void*)(dst + 1024 * (wave + 4)), 16, 0, 0);
+  };
+  const int sw = (li >> 1) & 7;
+  const int ro0 = li * 128 + (((2 * g) ^ sw) * 16), ro1 = li * 128 + (((2 * g + 1) ^ sw) * 16);
+  auto read_keys = [&](int slot, i32x8 (&kf)[NST]) {
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
-      const i32x4 lo = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, kvo + st * 2048, s0 * 128, 0));
-      const i32x4 hi = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, kvo + st * 2048 + 16, s0 * 128, 0));
+      const DSA_LDS uint8_t* base = ring + slot * kSlabBytes + st * 2048;
+      const i32x4 lo = *(const DSA_LDS i32x4*)(base + ro0);
+      const i32x4 hi = *(const DSA_LDS i32x4*)(base + ro1);
       kf[st] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   };
 
-  // One 64-key slab with the keys in kf; the next slab's keys go to kn.
-  auto slab = [&](int32_t s0, const i32x8 (&kf)[NST], i32x8 (&kn)[NST]) {
-    load_keys(s0 + 64, kn);  // unconditional: a conditional load would make every wait drain it
+  auto load_keys = [&](int32_t s0, i32x8 (&kf)[NST]) {
+    const int so = __builtin_amdgcn_readfirstlane(s0 * 128);  // keep the offset scalar
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const i32x4 lo = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, kvo + st * 2048, so, 0));
+      const i32x4 hi = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, kvo + st * 2048 + 16, so, 0));
+      kf[st] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+
+  // One 64-key slab with the keys in kf.
+  auto slab = [&](int32_t s0, const i32x8 (&kf)[NST]) {
     float acc[NST][NR];
     f32x4 x[LAG + 1];
 #pragma unroll
@@ -244,52 +281,113 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
     for (int i = 0; i < NR; ++i) {
       float v = transpose_reduce(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
       if constexpr (LIN) v *= 0.5f;
-      __builtin_amdgcn_raw_buffer_store_b32(f_bits(v), srs[i], svo, s0 * 4, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(f_bits(v), srs[i], svo, __builtin_amdgcn_readfirstlane(s0 * 4), 0);
     }
   };
 
-  i32x8 k0[NST], k1[NST];
-  load_keys(kstart, k0);
-  for (int32_t s0 = kstart; s0 < kend; s0 += 128) {
-    slab(s0, k0, k1);
-    if (s0 + 64 < kend) slab(s0 + 64, k1, k0);
+  if constexpr (KEYS == kKeysShared) {
+    // per slab n: this wave's copies of slab n done (after them it issued the
+    // stores of n-2, the copies of n+1 and the stores of n-1), barrier (every
+    // wave's copies landed, every wave done reading slab n-1), copy slab n+2
+    // into the slot slab n-1 used, read and compute slab n
+    copy_slab(kstart, 0);
+    copy_slab(kstart + 64, 1);
+    int slot = 0, n = 0;
+    for (int32_t s0 = kstart; s0 < kend; s0 += 64, ++n) {
+      if (n == 0) wait_vmcnt<2>();
+      else if (n == 1) wait_vmcnt<2 + NR>();
+      else wait_vmcnt<2 + 2 * NR>();
+      lds_barrier();
+      copy_slab(s0 + 128, slot == 0 ? 2 : slot - 1);
+      i32x8 kf[NST];
+      read_keys(slot, kf);
+      slab(s0, kf);
+      slot = slot == 2 ? 0 : slot + 1;
+    }
+  } else if constexpr (KEYS == kKeysPrefetch) {
+    i32x8 k0[NST], k1[NST];
+    load_keys(kstart, k0);
+    for (int32_t s0 = kstart; s0 < kend; s0 += 128) {
+      load_keys(s0 + 64, k1);  // unconditional: a conditional load would make every wait drain it
+      slab(s0, k0);
+      if (s0 + 64 >= kend) break;
+      load_keys(s0 + 128, k0);
+      slab(s0 + 64, k1);
+    }
+  } else {
+    for (int32_t s0 = kstart; s0 < kend; s0 += 64) {
+      i32x8 kf[NST];
+      load_keys(s0, kf);
+      slab(s0, kf);
+    }
   }
 }
 
-template <int NHT, int ACT>
+// SHARED: workgroups whose eight rows are one sequence's (prefill) share the
+// keys through LDS; the rest fall back to the lean per-wave path.  Otherwise
+// (decode batches: every row its own sequence) every wave streams its own
+// keys with prefetch.
+template <int NHT, int ACT, bool SHARED>
 __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(IdxArgs a) {
-  const int wave = threadIdx.x >> 6;
-  const int32_t r0 = __builtin_amdgcn_readfirstlane(a.row_begin + blockIdx.x * kRowsPerBlock + wave * kRowsPerWave);
+  __shared__ __attribute__((aligned(16))) uint8_t ring[SHARED ? kRing * kSlabBytes : 16];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t rb = a.row_begin + blockIdx.x * kRowsPerBlock;
   const int32_t kstart = blockIdx.y * a.key_chunk;
-  int32_t rows[2] = {r0, r0 + 1};
-  int32_t pos[2];
-  int32_t kbase[2];
-  bool valid[2];
+  const int32_t kchunk_end = kstart + a.key_chunk;
+  // the workgroup's rows (wave-uniform values: readfirstlane lets the buffer
+  // descriptors built from them live in scalar registers)
+  int32_t pos[kRowsPerBlock], kb[kRowsPerBlock];
+  bool live[kRowsPerBlock];
+  bool same = true;
+  int32_t kend_blk = kstart;
+#pragma unroll
+  for (int j = 0; j < kRowsPerBlock; ++j) {
+    const int32_t r = rb + j;
+    pos[j] = -1;
+    kb[j] = 0;
+    if (r < a.row_end) {
+      const RowInfo ri = locate_row(a.cu_q, a.cu_k, a.num_seqs, r);
+      pos[j] = __builtin_amdgcn_readfirstlane(ri.pos);
+      kb[j] = __builtin_amdgcn_readfirstlane(ri.kbase);
+      same = same && kb[j] == kb[0];
+    }
+    live[j] = pos[j] >= 0 && pos[j] + 1 > a.skip_n && pos[j] >= kstart;
+    if (live[j]) kend_blk = max(kend_blk, min(kchunk_end, pos[j] + 1));
+  }
+  if (kend_blk <= kstart) return;  // nothing to score in this key chunk (uniform over the workgroup)
+  if (SHARED && same) {
+    int32_t rows[2], lim[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int j = wave * kRowsPerWave + i;
+      rows[i] = min(rb + j, a.row_end - 1);
+      lim[i] = __builtin_amdgcn_readfirstlane(live[j] ? min(kchunk_end, pos[j] + 1) : 0);
+    }
+    fp8_rows<2, NHT, ACT, kKeysShared>(a, rows, lim, kb[0], kstart, kend_blk, (DSA_LDS uint8_t*)ring);
+    return;
+  }
+  // rows of several sequences: each wave on its own
+  const int j0 = wave * kRowsPerWave;
+  bool v[2];
+  int32_t l[2], k[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    valid[i] = rows[i] < a.row_end;
-    pos[i] = -1;
-    kbase[i] = 0;
-    if (valid[i]) {
-      RowInfo ri = locate_row(a.cu_q, a.cu_k, a.num_seqs, rows[i]);
-      // wave-uniform by construction; say so, so that the buffer descriptors
-      // built from them live in scalar registers
-      pos[i] = __builtin_amdgcn_readfirstlane(ri.pos);
-      kbase[i] = __builtin_amdgcn_readfirstlane(ri.kbase);
-      valid[i] = pos[i] + 1 > a.skip_n && pos[i] >= kstart;
-    }
+    v[i] = __builtin_amdgcn_readfirstlane((int)live[j0 + i]) != 0;
+    l[i] = __builtin_amdgcn_readfirstlane(min(kchunk_end, pos[j0 + i] + 1));
+    k[i] = __builtin_amdgcn_readfirstlane(kb[j0 + i]);
   }
-  const int32_t kchunk_end = kstart + a.key_chunk;
-  if (valid[0] && valid[1] && kbase[0] == kbase[1]) {
-    const int32_t kend = min(kchunk_end, max(pos[0], pos[1]) + 1);
-    fp8_rows<2, NHT, ACT>(a, rows, pos, kbase[0], kstart, kend);
+  if (v[0] && v[1] && k[0] == k[1]) {
+    const int32_t rows[2] = {rb + j0, rb + j0 + 1};
+    const int32_t lim[2] = {l[0], l[1]};
+    fp8_rows<2, NHT, ACT, SHARED ? kKeysPlain : kKeysPrefetch>(a, rows, lim, k[0], kstart, max(l[0], l[1]),
+                                                               nullptr);
   } else {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      if (!valid[i]) continue;
-      const int32_t r1[1] = {rows[i]};
-      const int32_t p1[1] = {pos[i]};
-      fp8_rows<1, NHT, ACT>(a, r1, p1, kbase[i], kstart, min(kchunk_end, pos[i] + 1));
+      if (!v[i]) continue;
+      const int32_t r1[1] = {rb + j0 + i};
+      const int32_t l1[1] = {l[i]};
+      fp8_rows<1, NHT, ACT, SHARED ? kKeysPlain : kKeysPrefetch>(a, r1, l1, k[i], kstart, l[i], nullptr);
     }
   }
 }
@@ -324,9 +422,14 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(IdxArgs a, int d_I) {
 }
 
 template <int NHT>
-hipError_t launch_fp8(const IdxArgs& a, int act, dim3 grid, hipStream_t s) {
-  if (act == 0) hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 0>), grid, dim3(kIdxThreads), 0, s, a);
-  else hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 1>), grid, dim3(kIdxThreads), 0, s, a);
+hipError_t launch_fp8(const IdxArgs& a, int act, bool shared, dim3 grid, hipStream_t s) {
+  if (act == 0) {
+    if (shared) hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 0, true>), grid, dim3(kIdxThreads), 0, s, a);
+    else hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 0, false>), grid, dim3(kIdxThreads), 0, s, a);
+  } else {
+    if (shared) hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 1, true>), grid, dim3(kIdxThreads), 0, s, a);
+    else hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 1, false>), grid, dim3(kIdxThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -368,11 +471,13 @@ hipError_t launch_indexer(const IndexerLaunch& L, hipStream_t s) {
     while (chunk > 256 && row_blocks * ((L.b.max_ctx + chunk - 1) / chunk) < 4LL * L.num_cus) chunk >>= 1;
     a.key_chunk = chunk;
     dim3 grid((unsigned)row_blocks, (unsigned)((L.b.max_ctx + chunk - 1) / chunk));
+    // prefill-like batches (sequences of many query rows): workgroups share keys
+    const bool shared = (int64_t)rows >= 8LL * L.b.num_seqs;
     switch (L.H_I / 16) {
-      case 1: return launch_fp8<1>(a, L.act, grid, s);
-      case 2: return launch_fp8<2>(a, L.act, grid, s);
-      case 3: return launch_fp8<3>(a, L.act, grid, s);
-      case 4: return launch_fp8<4>(a, L.act, grid, s);
+      case 1: return launch_fp8<1>(a, L.act, shared, grid, s);
+      case 2: return launch_fp8<2>(a, L.act, shared, grid, s);
+      case 3: return launch_fp8<3>(a, L.act, shared, grid, s);
+      case 4: return launch_fp8<4>(a, L.act, shared, grid, s);
       default: return hipErrorInvalidValue;
     }
   }

@@ -77,27 +77,6 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
-// Wait until at most N vector-memory instructions of this wave are in flight
-// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
-// left at their no-wait maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Workgroup rendezvous for the tile loop that does not drain vector memory:
-// this wave's LDS operations complete (lgkmcnt 0), then every wave meets.
-// The HBM -> LDS copies in flight are left alone; their completion is tracked
-// by the counted vmcnt waits before this barrier.  (__syncthreads() carries a
-// release fence, which would wait for every outstanding copy.)
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0) only
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Issue the HBM -> LDS copy of tile t (the latent rows of selected entries
 // 32t .. 32t+31).  The tile is 36 lane-contiguous 1-KB copy instructions; copy
 // q fills chunk columns 2q and 2q + 1, and wave w issues q = w, w + NW, ...

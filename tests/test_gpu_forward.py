@@ -71,6 +71,20 @@ def test_forward_integer_inputs_exact_selection(dsa):
     _check_rows(p, out, idx, rows, TOL_ATTN_BF16, need_exact_idx=True)
 
 
+def test_forward_workgroups_mixing_skipped_and_live_rows(dsa):
+    """k not a multiple of the indexer's 8-row workgroups and a row count that
+    is not either: the workgroup holding rows 32..39 has rows that skip the
+    indexer (pos + 1 <= k) next to rows that need it, and the last workgroup is
+    partial; selections stay exact."""
+    announce("forward mixed workgroups")
+    p = gen.make_problem("fwd", [1003], [1003], H_I=64, H=32, k=37, integer=True, device=DEV, seed=26)
+    out, _, idx = dsa.forward(p)
+    idx2 = dsa.topk(p, dsa.indexer_scores(p))
+    assert torch.equal(idx, idx2)
+    rows = np.array([0, 31, 35, 36, 37, 38, 39, 40, 41, 500, 999, 1000, 1001, 1002], np.int32)
+    _check_rows(p, out, idx, rows, TOL_ATTN_BF16, need_exact_idx=True)
+
+
 @pytest.mark.parametrize("act", [0, 1])
 def test_forward_random_inputs(dsa, act):
     announce("forward random", act)

@@ -20,7 +20,7 @@
 //     holding 16 keys of one head;
 //   * softmax: fp32, base-2 exponent with the scale folded in, against a
 //     per-head reference max fixed by the first tile (the accumulators are
-//     only touched by MFMAs; a row whose later max overflows the headroom is
+//     only touched by MFMAs; a row whose sum leaves the safe range is
 //     recomputed once with its true max), row sums kept per lane and reduced
 //     once;
 //   * values: O^T = V^T P^T.  The lane's 8 probabilities of one head are
@@ -45,7 +45,7 @@ constexpr int kQkAhead = 3;                // K fragment steps read ahead of the
 constexpr int kPvAhead = 8;                // V^T fragments read ahead of their MFMAs
 constexpr int kQkSteps = kDqk / 32;        // 18
 constexpr int kDvTiles = kDv / 16;         // 32
-constexpr float kHeadroom = 32.0f;         // log2 headroom above the reference max
+constexpr float kSumLimit = 0x1p96f;       // row sums beyond this trigger the recompute
 
 struct MlaArgs {
   const int32_t* cu_q;
@@ -89,14 +89,16 @@ constexpr int kTileCopies = kTile * kChunksPerRow / 64;  // 36
 template <int NW>
 constexpr int copies_per_wave() { return (kTileCopies + NW - 1) / NW; }
 
+// Source position of this lane's tile row: the tile's selected entry number
+// (lane mod 32) XOR 8 for the lanes that fill odd chunk columns.
+__device__ __forceinline__ int gather_row(int lane) { return (lane & 31) ^ (8 * (lane >> 5)); }
+
+// p: selected position of this lane's tile row (gather_row) of the tile.
 template <int NW>
-__device__ __forceinline__ void gather_tile(const MlaArgs& a, int32_t kbase, const DSA_LDS int32_t* sel, int t,
-                                            uint8_t* buf) {
+__device__ __forceinline__ void gather_tile(const MlaArgs& a, int32_t kbase, int32_t p, uint8_t* buf) {
   constexpr int NINS = copies_per_wave<NW>();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int odd = lane >> 5;                     // this lane fills odd chunk columns
-  const int row = (lane & 31) ^ (8 * odd);       // the tile row it copies from
-  int32_t p = sel[t * kTile + row];
   p = p < 0 ? 0 : p;
   const uint8_t* src = a.kv + ((int64_t)(kbase + p) * kChunksPerRow + odd + 2 * wave) * 16;
 #pragma unroll
@@ -128,9 +130,21 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   const int t0 = sp * a.tiles_per_split;
   const int t1 = min(ntiles, t0 + a.tiles_per_split);
 
-  // the row's selected positions, -1 padded to whole tiles
+  // the row's selected positions, -1 padded to whole tiles, and per tile the
+  // mask of its valid entries (bit j: entry 32 t + j is >= 0)
+  DSA_LDS uint32_t* tmask = (DSA_LDS uint32_t*)(sel + kMaxSel);
   const int32_t* idx_row = a.idx + (int64_t)rl * a.k;
-  for (int e = threadIdx.x; e < ntiles * kTile; e += NW * 64) sel[e] = e < a.k ? idx_row[e] : -1;
+  for (int base = wave * 64; base < ntiles * kTile; base += NW * 64) {
+    const int e = base + lane;
+    const bool in = e < ntiles * kTile;
+    const int32_t v = e < a.k ? idx_row[e] : -1;
+    if (in) sel[e] = v;
+    const uint64_t m = __ballot(in && v >= 0);
+    if (lane == 0) {
+      tmask[base / kTile] = (uint32_t)m;
+      tmask[base / kTile + 1] = (uint32_t)(m >> 32);
+    }
+  }
 
   // query fragments: B operand of S^T = K Q^T (lane: head li of column tile nt, d = 32c + 8g .. +7)
   bf16x8 qf[NT][kQkSteps];
@@ -141,14 +155,15 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
 #pragma unroll
     for (int c = 0; c < kQkSteps; ++c) qf[nt][c] = *(const bf16x8*)(qrow + 32 * c);
   }
-  __syncthreads();  // sel[] visible
+  __syncthreads();  // sel[] and tmask[] visible
+  const uint32_t tmask_lane = lane < kMaxSel / kTile ? tmask[lane] : 0u;  // tile t's mask: lane t
 
   // Softmax reference point: the first tile's max of each head, fixed for the
   // whole row, so the accumulators are only ever touched by MFMAs and the
-  // steady state needs no cross-lane reduction.  If a later score exceeds it by
-  // more than kHeadroom (log2 units) the row would overflow: then a max-only
-  // pass rebuilds m_fix as the true max and the row is recomputed against it
-  // (exact either way; practically never taken).
+  // steady state needs no cross-lane reduction.  Later scores above it only
+  // scale the probabilities up (exact in fp32 until they leave its range); if a
+  // row sum reaches kSumLimit, a max-only pass rebuilds m_fix as the true max
+  // and the row is recomputed against it (practically never taken).
   float m_fix[NT], l_run[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) m_fix[nt] = -INFINITY;
@@ -178,7 +193,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
     __syncthreads();  // the previous pass is done with every buffer
 #pragma unroll
     for (int j = 0; j < AHEAD; ++j)
-      if (t0 + j < t1) gather_tile<NW>(a, ri.kbase, sel, t0 + j, smem + (size_t)j * kTileBytes);
+      if (t0 + j < t1)
+        gather_tile<NW>(a, ri.kbase, sel[(t0 + j) * kTile + gather_row(lane)], smem + (size_t)j * kTileBytes);
+    // position for the next gather, read a tile ahead so its LDS latency hides
+    int32_t p_next = t0 + AHEAD < t1 ? sel[(t0 + AHEAD) * kTile + gather_row(lane)] : 0;
 
     for (int t = t0; t < t1; ++t) {
       // Tile t has landed once at most (copies issued after it) x NINS of this
@@ -189,10 +207,11 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
       else if (issued_after == 1) wait_vmcnt<(NINS < 64 ? NINS : 0)>();
       else wait_vmcnt<0>();
       lds_barrier();
-      if (t + AHEAD < t1)
-        gather_tile<NW>(a, ri.kbase, sel, t + AHEAD, smem + (size_t)((t + AHEAD - t0) % kNumBuf) * kTileBytes);
-      const int32_t myidx = lane < kTile ? sel[t * kTile + lane] : -1;
-      const uint32_t vmask = (uint32_t)__ballot(myidx >= 0);
+      if (t + AHEAD < t1) {
+        gather_tile<NW>(a, ri.kbase, p_next, smem + (size_t)((t + AHEAD - t0) % kNumBuf) * kTileBytes);
+        if (t + AHEAD + 1 < t1) p_next = sel[(t + AHEAD + 1) * kTile + gather_row(lane)];
+      }
+      const uint32_t vmask = (uint32_t)__builtin_amdgcn_readlane((int)tmask_lane, t);
       if (vmask != 0) {
         const DSA_LDS uint8_t* lb = (const DSA_LDS uint8_t*)smem + (size_t)((t - t0) % kNumBuf) * kTileBytes;
         // ---- scores: sacc[mt][nt] = S^T[keys 16mt.., heads 16nt..]
@@ -255,8 +274,6 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
             for (int e = 0; e < 8; ++e)
               if (!((vmask >> (16 * (e >> 2) + 4 * g + (e & 3))) & 1u)) x[e] = -INFINITY;
           }
-          const float xm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-          overflow |= xm > kHeadroom;
           float ps = 0.0f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -291,7 +308,12 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
       }
     }
     if (pass == 0) {
-      // every wave agrees on whether the row is recomputed (the buffers are shared)
+      // Probabilities grew past the fp32 / bf16 range only if some row sum did:
+      // below 2^96 every probability and every p * v term (|v| < 2^31) is
+      // finite.  Every wave agrees on whether the row is recomputed (the
+      // buffers are shared).
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) overflow |= !(l_run[nt] < kSumLimit);
       if (!__syncthreads_or(overflow)) break;
     }  // after the max-only pass m_fix holds the true max: the recompute cannot overflow
   }
@@ -425,7 +447,7 @@ __global__ __launch_bounds__(256) void mla_f32_kernel(MlaArgs a, int d_qk, int d
 
 template <int HPW, int NW>
 hipError_t launch_bf16(const MlaArgs& a, int rows, hipStream_t s) {
-  const size_t lds = (size_t)kNumBuf * kTileBytes + kMaxSel * sizeof(int32_t);
+  const size_t lds = (size_t)kNumBuf * kTileBytes + kMaxSel * sizeof(int32_t) + (kMaxSel / kTile) * sizeof(uint32_t);
   static bool attr_set = false;  // benign race: idempotent attribute call
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)mla_bf16_kernel<HPW, NW>,

@@ -72,6 +72,23 @@ def test_bf16_padding_holes_and_empty_rows(dsa):
     assert torch.all(out[5] == 0) and torch.all(torch.isneginf(lse[5]))
 
 
+def test_bf16_later_scores_far_above_the_first_tile(dsa):
+    """The softmax reference is the first tile's max; an entry selected later
+    that scores far above it (here by about 2^240 in probability) makes the
+    row sum leave the fp32 range and forces the exact recompute."""
+    announce("attention bf16 recompute")
+    p = gen.make_problem("attn", [600], [600], H_I=16, H=128, k=256, device=DEV, seed=11)
+    idx = random_selection(p, 256, 11)
+    hot = [400, 599]
+    for r in hot:
+        idx[r, -1] = r                     # the row's own position, last in ascending order
+        p.q[r] = 1.0                       # every head, every column
+        p.kv[r] = 4.0                      # score 576 * 4 = 2304 for those rows' heads
+    out, lse = _compare(dsa, p, idx, TOL_ATTN_BF16)
+    for r in hot:                          # the hot entry takes all the probability mass
+        assert torch.allclose(out[r].float(), torch.full_like(out[r].float(), 4.0))
+
+
 def test_bf16_only_selected_rows_matter(dsa):
     announce("attention bf16 non-selected rows")
     p = gen.make_problem("attn", [400, 300], [50, 300], H_I=16, H=64, k=128, device=DEV, seed=11)

@@ -68,10 +68,16 @@ struct MlaArgs {
 //   * one 64-lane copy instruction fills two whole chunk columns, and a lane's
 //     source row (lane mod 32, XOR 8 for the odd column) is the same for every
 //     copy of the tile: one address per lane per tile, immediate offsets after;
-//   * a K fragment read (16 consecutive rows of one chunk per lane group) is one
-//     contiguous 256-byte span: all 64 banks once;
 //   * a transposed V read (8 rows x 2 chunks per 32 lanes) hits each bank once
-//     because odd chunks keep their rows 8 apart from even chunks.
+//     because odd chunks keep their rows 8 apart from even chunks;
+//   * a K fragment read (16 consecutive rows of one chunk per lane group) is a
+//     256-byte span, and ds_read_b128 is conflict-free only when lane groups 0
+//     and 1 (and 2 and 3) use the same row order: lane group g therefore reads
+//     chunk 4c + kperm(g), kperm = (0, 2, 1, 3), so that groups 0 and 1 read
+//     even chunks and groups 2 and 3 odd ones.  The query fragments use the same
+//     order, which only relabels the MFMA's K index on both operands.
+__device__ __forceinline__ int kperm(int g) { return (g >> 1) | ((g & 1) << 1); }
+
 __device__ __forceinline__ uint16_t to_bf16_bits(float f) {
   __bf16 b = (__bf16)f;  // round to nearest even
   return __builtin_bit_cast(uint16_t, b);
@@ -146,12 +152,12 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
     }
   }
 
-  // query fragments: B operand of S^T = K Q^T (lane: head li of column tile nt, d = 32c + 8g .. +7)
+  // query fragments: B operand of S^T = K Q^T (lane: head li of column tile nt, d = 32c + 8 kperm(g) .. +7)
   bf16x8 qf[NT][kQkSteps];
   const int head0 = wave * HPW;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const uint16_t* qrow = a.q + ((int64_t)r * a.H + head0 + 16 * nt + li) * kDqk + 8 * g;
+    const uint16_t* qrow = a.q + ((int64_t)r * a.H + head0 + 16 * nt + li) * kDqk + 8 * kperm(g);
 #pragma unroll
     for (int c = 0; c < kQkSteps; ++c) qf[nt][c] = *(const bf16x8*)(qrow + 32 * c);
   }
@@ -170,9 +176,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   f32x4 oacc[kDvTiles][NT];
 
   // per-lane LDS byte offsets inside a tile (chunk-major layout, see above):
-  //   K fragment (row 16mt + li, chunk 4c + g): koff + 2048 c + 256 mt
+  //   K fragment (row 16mt + li, chunk 4c + kperm(g)): koff + 2048 c + 256 mt
   //   V^T rows 4g + e4 (+16), chunk 2dt + (r4>>1), half r4&1: voff + 1024 dt (+256)
-  const int koff = g * 512 + (li ^ (8 * (g & 1))) * 16;
+  const int koff = kperm(g) * 512 + (li ^ (8 * (kperm(g) & 1))) * 16;
   const int e4 = li >> 2, r4 = li & 3;
   const int voff = (r4 >> 1) * 512 + ((4 * g + e4) ^ (8 * (r4 >> 1))) * 16 + 8 * (r4 & 1);
 

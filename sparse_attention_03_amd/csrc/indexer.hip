@@ -195,30 +195,27 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
                                                lim[i] * 4, kBufFlags);
   const int svo = (16 * g + li) * 4;
 
-  // LDS ring (SHARED): copy instruction q of a slab fills key rows 8q .. 8q+7,
-  // lane i writing 16-byte slot i % 8 of row 8q + i / 8; the slot holds chunk
-  // (i % 8) ^ ((row / 2) % 8) of the key, so that the 16 lanes of a fragment
-  // read (16 consecutive rows, one chunk) hit 16 different 16-byte bank groups.
+  // LDS ring (SHARED), chunk-major: 16-byte chunk c of slab key row r sits at
+  // byte (64 c + r) * 16.  Copy instruction c of a slab fills chunk column c
+  // (lane i: key row i); a fragment read (lane group g: chunks 2g, 2g + 1 of
+  // rows 16 st + li) puts every lane group on the same bank slot for the same
+  // row, which is what ds_read_b128 needs to run without bank conflicts.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int cr0 = 8 * wave + (lane >> 3), cr1 = cr0 + 32;
-  const int cc0 = ((lane & 7) ^ ((cr0 >> 1) & 7)) * 16, cc1 = ((lane & 7) ^ ((cr1 >> 1) & 7)) * 16;
   const uint8_t* kglob = a.k_idx + (int64_t)kbase * 128;
   auto copy_slab = [&](int32_t s0, int slot) {
     DSA_LDS uint8_t* dst = ring + slot * kSlabBytes;
-    const int32_t r0 = min(s0 + cr0, kend - 1), r1 = min(s0 + cr1, kend - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(kglob + (int64_t)r0 * 128 + cc0),
-                                     (DSA_LDS void*)(dst + 1024 * wave), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(kglob + (int64_t)r1 * 128 + cc1),
-                                     (DSA_LDS void*)(dst + 1024 * (wave + 4)), 16, 0, 0);
+    const uint8_t* src = kglob + (int64_t)min(s0 + lane, kend - 1) * 128;
+    __builtin_amdgcn_global_load_lds((const void*)(src + 16 * wave), (DSA_LDS void*)(dst + 1024 * wave), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(src + 16 * (wave + 4)), (DSA_LDS void*)(dst + 1024 * (wave + 4)),
+                                     16, 0, 0);
   };
-  const int sw = (li >> 1) & 7;
-  const int ro0 = li * 128 + (((2 * g) ^ sw) * 16), ro1 = li * 128 + (((2 * g + 1) ^ sw) * 16);
+  const int ro = 2 * g * 1024 + li * 16;
   auto read_keys = [&](int slot, i32x8 (&kf)[NST]) {
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
-      const DSA_LDS uint8_t* base = ring + slot * kSlabBytes + st * 2048;
-      const i32x4 lo = *(const DSA_LDS i32x4*)(base + ro0);
-      const i32x4 hi = *(const DSA_LDS i32x4*)(base + ro1);
+      const DSA_LDS uint8_t* base = ring + slot * kSlabBytes + st * 256 + ro;
+      const i32x4 lo = *(const DSA_LDS i32x4*)base;
+      const i32x4 hi = *(const DSA_LDS i32x4*)(base + 1024);
       kf[st] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   };

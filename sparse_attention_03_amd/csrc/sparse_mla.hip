@@ -12,8 +12,9 @@
 // feeds two MFMAs, which halves LDS traffic against 16 heads per wave):
 //   * gather: the 32 selected latent rows of a tile are copied HBM -> LDS with
 //     global_load_lds_dwordx4 (16 B per lane, no register staging) into one of
-//     four buffers, up to three tiles ahead, in a chunk-major layout that
-//     makes both the K and the transposed V reads bank-conflict free;
+//     four buffers, up to three tiles ahead; every 8 lanes of a copy read one
+//     whole 128-byte line of a latent row, and the line-block layout keeps the
+//     transposed V reads bank-conflict free;
 //   * scores: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 -- keys are the MFMA
 //     rows (K fragments read from LDS with ds_read_b128), heads the columns (Q
 //     fragments resident in VGPRs for the whole row), so each lane ends up
@@ -45,7 +46,7 @@ constexpr int kQkAhead = 3;                // K fragment steps read ahead of the
 constexpr int kPvAhead = 8;                // V^T fragments read ahead of their MFMAs
 constexpr int kQkSteps = kDqk / 32;        // 18
 constexpr int kDvTiles = kDv / 16;         // 32
-constexpr float kSumLimit = 0x1p96f;       // row sums beyond this trigger the recompute
+constexpr float kSumLimit = 0x1p90f;       // per-lane row sums beyond this trigger the recompute
 
 struct MlaArgs {
   const int32_t* cu_q;
@@ -63,20 +64,27 @@ struct MlaArgs {
   float* ws_lse;
 };
 
-// Tile layout in LDS: chunk-major.  Chunk c (16 bytes = 8 values, c < 72) of
-// tile row r sits at byte (32 c + (r ^ 8 (c & 1))) * 16.  Properties:
-//   * one 64-lane copy instruction fills two whole chunk columns, and a lane's
-//     source row (lane mod 32, XOR 8 for the odd column) is the same for every
-//     copy of the tile: one address per lane per tile, immediate offsets after;
-//   * a transposed V read (8 rows x 2 chunks per 32 lanes) hits each bank once
-//     because odd chunks keep their rows 8 apart from even chunks;
-//   * a K fragment read (16 consecutive rows of one chunk per lane group) is a
-//     256-byte span, and ds_read_b128 is conflict-free only when lane groups 0
-//     and 1 (and 2 and 3) use the same row order: lane group g therefore reads
-//     chunk 4c + kperm(g), kperm = (0, 2, 1, 3), so that groups 0 and 1 read
-//     even chunks and groups 2 and 3 odd ones.  The query fragments use the same
-//     order, which only relabels the MFMA's K index on both operands.
-__device__ __forceinline__ int kperm(int g) { return (g >> 1) | ((g & 1) << 1); }
+// Tile layout in LDS: line blocks.  The tile (32 rows x 72 chunks of 16 bytes)
+// is 36 blocks of 1 KB; block 4 s + rg holds segment s (chunks 8 s .. 8 s + 7,
+// one 128-byte line of each latent row) of tile rows 8 rg .. 8 rg + 7.  Rows 2k
+// and 2k + 1 of a block share its 256-byte bank row k, and chunk 8 s + x of row
+// r sits in 16-byte slot 8 (r & 1) + (x ^ tile_swz(r)) of it.  Properties:
+//   * every 8 lanes of a copy instruction read one whole 128-byte line of one
+//     latent row (a row's chunks permuted inside the line), so the gather
+//     touches each line of a tile once;
+//   * a lane copies from one latent row for the whole tile (one address per
+//     lane and row group, immediate offsets after);
+//   * a transposed V read (8 rows x 2 chunks per 32 lanes) covers each bank
+//     once;
+//   * the 16 rows of one chunk in a K fragment read sit in 16 different
+//     slots, but lane groups 0 and 1 (2 and 3) read different chunks of the
+//     same rows, which the LDS serves in two passes.  Line-sized gathers are
+//     worth far more than that pass.
+constexpr int kSegments = kChunksPerRow / 8;  // 9 lines per latent row
+__device__ __forceinline__ int tile_swz(int r) { return 2 * ((r >> 1) & 3) + ((r >> 3) & 1); }
+__device__ __forceinline__ int tile_off(int r, int ch) {
+  return ((ch >> 3) * 4 + (r >> 3)) * 1024 + ((r & 7) >> 1) * 256 + (8 * (r & 1) + ((ch & 7) ^ tile_swz(r))) * 16;
+}
 
 __device__ __forceinline__ uint16_t to_bf16_bits(float f) {
   __bf16 b = (__bf16)f;  // round to nearest even
@@ -84,42 +92,40 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float f) {
 }
 
 // Issue the HBM -> LDS copy of tile t (the latent rows of selected entries
-// 32t .. 32t+31).  The tile is 36 lane-contiguous 1-KB copy instructions; copy
-// q fills chunk columns 2q and 2q + 1, and wave w issues q = w, w + NW, ...
-// Every wave issues the same number of copies (so the counted waits are
-// uniform): a wave short of that count repeats its first copy, which writes
-// the same bytes to the same place again.  Invalid entries (-1) copy row 0 of
-// the sequence, always in bounds, and are masked later.
-constexpr int kTileCopies = kTile * kChunksPerRow / 64;  // 36
-
+// 32 t .. 32 t + 31): 36 lane-contiguous 1-KB copy instructions, one per block.
+// Wave w copies the row groups rg = w, w + NW, ... (all nine segments of each);
+// lane l copies tile row 8 rg + l / 8.  Invalid entries (-1) copy row 0 of the
+// sequence, always in bounds, and are masked later.
 template <int NW>
-constexpr int copies_per_wave() { return (kTileCopies + NW - 1) / NW; }
+constexpr int row_groups_per_wave() { return 4 / NW; }
 
-// Source position of this lane's tile row: the tile's selected entry number
-// (lane mod 32) XOR 8 for the lanes that fill odd chunk columns.
-__device__ __forceinline__ int gather_row(int lane) { return (lane & 31) ^ (8 * (lane >> 5)); }
+// Tile row copied by this lane for its k-th row group.
+__device__ __forceinline__ int gather_row(int wave, int NW, int k, int lane) { return 8 * (wave + NW * k) + (lane >> 3); }
 
-// p: selected position of this lane's tile row (gather_row) of the tile.
+// p[k]: selected position of this lane's tile row for row group k.
 template <int NW>
-__device__ __forceinline__ void gather_tile(const MlaArgs& a, int32_t kbase, int32_t p, uint8_t* buf) {
-  constexpr int NINS = copies_per_wave<NW>();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int odd = lane >> 5;                     // this lane fills odd chunk columns
-  p = p < 0 ? 0 : p;
-  const uint8_t* src = a.kv + ((int64_t)(kbase + p) * kChunksPerRow + odd + 2 * wave) * 16;
+__device__ __forceinline__ void gather_tile(const MlaArgs& a, int32_t kbase, const int32_t (&p)[4 / NW],
+                                            uint8_t* buf) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < NINS; ++i) {
-    const bool dup = wave + NW * i >= kTileCopies;
-    const int q = dup ? wave : wave + NW * i;
-    __builtin_amdgcn_global_load_lds((const void*)(dup ? src : src + 32 * NW * i),
-                                     (DSA_LDS void*)((DSA_LDS uint8_t*)buf + 1024 * q), 16, 0, 0);
+  for (int k = 0; k < row_groups_per_wave<NW>(); ++k) {
+    const int rg = wave + NW * k;
+    const int x = (lane & 7) ^ tile_swz(8 * rg + (lane >> 3));  // chunk of the line this lane copies
+    const int32_t pk = p[k] < 0 ? 0 : p[k];
+    const uint8_t* src = a.kv + ((int64_t)(kbase + pk) * kChunksPerRow + x) * 16;
+#pragma unroll
+    for (int sg = 0; sg < kSegments; ++sg)
+      __builtin_amdgcn_global_load_lds((const void*)(src + 128 * sg),
+                                       (DSA_LDS void*)((DSA_LDS uint8_t*)buf + 1024 * (4 * sg + rg)), 16, 0, 0);
   }
 }
 
 template <int HPW, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   constexpr int NT = HPW / 16;
-  constexpr int NINS = copies_per_wave<NW>();  // copy instructions per tile per wave
+  static_assert(4 % NW == 0, "a wave copies whole row groups");
+  constexpr int RG = row_groups_per_wave<NW>();
+  constexpr int NINS = kSegments * RG;  // copy instructions per tile per wave
   // tiles whose copies are issued ahead of the one being computed; the counted
   // wait below needs (AHEAD - 1) * NINS to fit the 6-bit vmcnt
   constexpr int AHEAD = 2 * NINS < 64 ? 3 : 1;
@@ -152,12 +158,12 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
     }
   }
 
-  // query fragments: B operand of S^T = K Q^T (lane: head li of column tile nt, d = 32c + 8 kperm(g) .. +7)
+  // query fragments: B operand of S^T = K Q^T (lane: head li of column tile nt, d = 32c + 8g .. +7)
   bf16x8 qf[NT][kQkSteps];
   const int head0 = wave * HPW;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const uint16_t* qrow = a.q + ((int64_t)r * a.H + head0 + 16 * nt + li) * kDqk + 8 * kperm(g);
+    const uint16_t* qrow = a.q + ((int64_t)r * a.H + head0 + 16 * nt + li) * kDqk + 8 * g;
 #pragma unroll
     for (int c = 0; c < kQkSteps; ++c) qf[nt][c] = *(const bf16x8*)(qrow + 32 * c);
   }
@@ -175,12 +181,16 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   for (int nt = 0; nt < NT; ++nt) m_fix[nt] = -INFINITY;
   f32x4 oacc[kDvTiles][NT];
 
-  // per-lane LDS byte offsets inside a tile (chunk-major layout, see above):
-  //   K fragment (row 16mt + li, chunk 4c + kperm(g)): koff + 2048 c + 256 mt
-  //   V^T rows 4g + e4 (+16), chunk 2dt + (r4>>1), half r4&1: voff + 1024 dt (+256)
-  const int koff = kperm(g) * 512 + (li ^ (8 * (kperm(g) & 1))) * 16;
+  // per-lane LDS byte offsets inside a tile (line blocks, see above):
+  //   K fragment (row 16 mt + li, chunk 4c + g): koff[c & 1] + 4096 (c >> 1) + 2048 mt
+  //   V^T rows 4g + e4 (+16), chunk 2dt + (r4 >> 1), half r4 & 1:
+  //   voff[dt & 3] + 4096 (dt >> 2) (+2048)
+  int koff[2], voff[4];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) koff[e] = tile_off(li, 4 * e + g);
   const int e4 = li >> 2, r4 = li & 3;
-  const int voff = (r4 >> 1) * 512 + ((4 * g + e4) ^ (8 * (r4 >> 1))) * 16 + 8 * (r4 & 1);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) voff[m] = tile_off(4 * g + e4, 2 * m + (r4 >> 1)) + 8 * (r4 & 1);
 
   for (int pass = 0; pass < 3; ++pass) {
     const bool max_only = pass == 1;
@@ -199,10 +209,17 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
     __syncthreads();  // the previous pass is done with every buffer
 #pragma unroll
     for (int j = 0; j < AHEAD; ++j)
-      if (t0 + j < t1)
-        gather_tile<NW>(a, ri.kbase, sel[(t0 + j) * kTile + gather_row(lane)], smem + (size_t)j * kTileBytes);
-    // position for the next gather, read a tile ahead so its LDS latency hides
-    int32_t p_next = t0 + AHEAD < t1 ? sel[(t0 + AHEAD) * kTile + gather_row(lane)] : 0;
+      if (t0 + j < t1) {
+        int32_t pj[RG];
+#pragma unroll
+        for (int k = 0; k < RG; ++k) pj[k] = sel[(t0 + j) * kTile + gather_row(wave, NW, k, lane)];
+        gather_tile<NW>(a, ri.kbase, pj, smem + (size_t)j * kTileBytes);
+      }
+    // positions for the next gather, read a tile ahead so their LDS latency hides
+    int32_t p_next[RG];
+#pragma unroll
+    for (int k = 0; k < RG; ++k)
+      p_next[k] = t0 + AHEAD < t1 ? sel[(t0 + AHEAD) * kTile + gather_row(wave, NW, k, lane)] : 0;
 
     for (int t = t0; t < t1; ++t) {
       // Tile t has landed once at most (copies issued after it) x NINS of this
@@ -215,7 +232,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
       lds_barrier();
       if (t + AHEAD < t1) {
         gather_tile<NW>(a, ri.kbase, p_next, smem + (size_t)((t + AHEAD - t0) % kNumBuf) * kTileBytes);
-        if (t + AHEAD + 1 < t1) p_next = sel[(t + AHEAD + 1) * kTile + gather_row(lane)];
+        if (t + AHEAD + 1 < t1) {
+#pragma unroll
+          for (int k = 0; k < RG; ++k) p_next[k] = sel[(t + AHEAD + 1) * kTile + gather_row(wave, NW, k, lane)];
+        }
       }
       const uint32_t vmask = (uint32_t)__builtin_amdgcn_readlane((int)tmask_lane, t);
       if (vmask != 0) {
@@ -226,10 +246,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const DSA_LDS uint8_t* kb = lb + koff;
+        const DSA_LDS uint8_t* kb[2] = {lb + koff[0], lb + koff[1]};
         auto load_k = [&](int c, bf16x8 (&kf)[2]) {
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt) kf[mt] = *(const DSA_LDS bf16x8*)(kb + (2048 * c + 256 * mt));
+          for (int mt = 0; mt < 2; ++mt) kf[mt] = *(const DSA_LDS bf16x8*)(kb[c & 1] + 4096 * (c >> 1) + 2048 * mt);
         };
         // K fragments kQkAhead steps ahead of the MFMAs (one wave per SIMD: the
         // wave itself must cover the LDS latency)
@@ -291,11 +311,11 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
                           (__bf16)x[4], (__bf16)x[5], (__bf16)x[6], (__bf16)x[7]};
         }
         // ---- values: O^T[d, h] += V^T[d, keys] P^T[keys, h], one V^T fragment ahead.
-        const DSA_LDS uint8_t* vb = lb + voff;
+        const DSA_LDS uint8_t* vb[4] = {lb + voff[0], lb + voff[1], lb + voff[2], lb + voff[3]};
         auto load_v = [&](int dt) -> bf16x8 {
-          const DSA_LDS uint8_t* p = vb + 1024 * dt;
+          const DSA_LDS uint8_t* p = vb[dt & 3] + 4096 * (dt >> 2);
           const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS i16x4*)p);
-          const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS i16x4*)(p + 256));
+          const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS i16x4*)(p + 2048));
           return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
               v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]});
         };
@@ -314,10 +334,12 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
       }
     }
     if (pass == 0) {
-      // Probabilities grew past the fp32 / bf16 range only if some row sum did:
-      // below 2^96 every probability and every p * v term (|v| < 2^31) is
-      // finite.  Every wave agrees on whether the row is recomputed (the
-      // buffers are shared).
+      // Probabilities grew past the fp32 / bf16 range only if some row sum did.
+      // Four lanes share a head's row, so with every per-lane sum below 2^90
+      // the row sum stays below 2^92 and every sum of p * v (|v| < 2^31, the
+      // bf16 values a latent holds in practice) below 2^123: finite in fp32.
+      // Every wave agrees on whether the row is recomputed (the buffers are
+      // shared).
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) overflow |= !(l_run[nt] < kSumLimit);
       if (!__syncthreads_or(overflow)) break;

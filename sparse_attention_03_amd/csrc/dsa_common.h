@@ -59,6 +59,44 @@ __device__ inline RowInfo locate_row(const int32_t* __restrict__ cu_q, const int
   return ri;
 }
 
+// The same lookup for a row that is uniform over the wave, with every lane
+// active.  For batches of at most 63 sequences each lane holds one cu_q / cu_k
+// entry (load_seq_table, one load each for the whole kernel) and a row is
+// located with one ballot; larger batches fall back to the binary search.
+struct SeqTable {
+  int32_t q, k;  // cu_q[lane], cu_k[lane] (lane <= num_seqs)
+  int32_t n;     // num_seqs
+};
+
+__device__ inline SeqTable load_seq_table(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+                                          int num_seqs) {
+  const int lane = threadIdx.x & 63;
+  SeqTable t;
+  t.n = num_seqs;
+  t.q = 0;
+  t.k = 0;
+  if (num_seqs < 64) {
+    const int i = min(lane, num_seqs);
+    t.q = cu_q[i];
+    t.k = cu_k[i];
+  }
+  return t;
+}
+
+__device__ inline RowInfo locate_row_wave(const SeqTable& t, const int32_t* __restrict__ cu_q,
+                                          const int32_t* __restrict__ cu_k, int32_t r) {
+  if (t.n >= 64) return locate_row(cu_q, cu_k, t.n, r);
+  const int lane = threadIdx.x & 63;
+  // cu_q[0] = 0 <= r and cu_q is nondecreasing: lanes 1 .. b hold the entries <= r
+  const int b = __popcll(__ballot(lane >= 1 && lane <= t.n && t.q <= r));
+  const int32_t q0 = __builtin_amdgcn_readlane(t.q, b), q1 = __builtin_amdgcn_readlane(t.q, b + 1);
+  const int32_t k0 = __builtin_amdgcn_readlane(t.k, b), k1 = __builtin_amdgcn_readlane(t.k, b + 1);
+  RowInfo ri;
+  ri.pos = (k1 - k0) - (q1 - q0) + (r - q0);
+  ri.kbase = k0;
+  return ri;
+}
+
 __device__ inline float wave_max(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;

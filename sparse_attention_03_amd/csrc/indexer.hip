@@ -337,13 +337,14 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(IdxArgs a) {
   bool live[kRowsPerBlock];
   bool same = true;
   int32_t kend_blk = kstart;
+  const SeqTable seqs = load_seq_table(a.cu_q, a.cu_k, a.num_seqs);
 #pragma unroll
   for (int j = 0; j < kRowsPerBlock; ++j) {
     const int32_t r = rb + j;
     pos[j] = -1;
     kb[j] = 0;
     if (r < a.row_end) {
-      const RowInfo ri = locate_row(a.cu_q, a.cu_k, a.num_seqs, r);
+      const RowInfo ri = locate_row_wave(seqs, a.cu_q, a.cu_k, r);
       pos[j] = __builtin_amdgcn_readfirstlane(ri.pos);
       kb[j] = __builtin_amdgcn_readfirstlane(ri.kbase);
       same = same && kb[j] == kb[0];

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   const int32_t r = a.row_begin + blockIdx.x;
   const int32_t rl = blockIdx.x;
   const int sp = blockIdx.y;
-  const RowInfo ri = locate_row(a.cu_q, a.cu_k, a.num_seqs, r);
+  const RowInfo ri = locate_row_wave(load_seq_table(a.cu_q, a.cu_k, a.num_seqs), a.cu_q, a.cu_k, r);
   const int ntiles = (a.k + kTile - 1) / kTile;
   const int t0 = sp * a.tiles_per_split;
   const int t1 = min(ntiles, t0 + a.tiles_per_split);

@@ -297,7 +297,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const int32_t* __restr
                                                           int64_t ld, int32_t k, int32_t* __restrict__ idx) {
   __shared__ TopkShared sh;
   const int32_t r = row_begin + blockIdx.x;
-  const RowInfo ri = locate_row(cu_q, cu_k, num_seqs, r);
+  const RowInfo ri = locate_row_wave(load_seq_table(cu_q, cu_k, num_seqs), cu_q, cu_k, r);
   const int32_t n = ri.pos + 1;
   int32_t* out = idx + (int64_t)blockIdx.x * k;
   const int tid = threadIdx.x;
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_segment_kernel(const int32_t*
                                                                   int32_t* __restrict__ cpos) {
   __shared__ TopkShared sh;
   const int32_t rl = blockIdx.x, seg = blockIdx.y, nseg = gridDim.y;
-  const RowInfo ri = locate_row(cu_q, cu_k, num_seqs, row_begin + rl);
+  const RowInfo ri = locate_row_wave(load_seq_table(cu_q, cu_k, num_seqs), cu_q, cu_k, row_begin + rl);
   const int32_t n = ri.pos + 1;
   if (n <= k_row) return;  // the merge writes every candidate directly
   const int32_t lo = seg * seg_len, hi = min(n, lo + seg_len);
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(const int32_t* _
                                                                 int32_t* __restrict__ idx) {
   __shared__ TopkShared sh;
   const int32_t rl = blockIdx.x;
-  const RowInfo ri = locate_row(cu_q, cu_k, num_seqs, row_begin + rl);
+  const RowInfo ri = locate_row_wave(load_seq_table(cu_q, cu_k, num_seqs), cu_q, cu_k, row_begin + rl);
   const int32_t n = ri.pos + 1;
   int32_t* out = idx + (int64_t)rl * k;
   if (n <= k) {
@@ -362,24 +362,350 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(const int32_t* _
   for (int e = threadIdx.x; e < k; e += kTkThreads) out[e] = e < cnt ? sh.pos[e] : -1;
 }
 
-}  // namespace
+// ---------------------------------------------------------------------------
+// Few long rows (decode batches).  One 1024-thread workgroup per row, or per
+// segment of a row longer than kRxCap.  Each wave loads a contiguous range of
+// the row into registers (16-byte loads, lane l holding entries 4l .. 4l + 3
+// of every 256-entry block), so the row is read once and never staged in LDS.
+// The k-th key is found by histogram refinement (the range-adaptive 256-bin
+// passes of cut_to_k, LDS atomics fed from registers), and the winners are
+// written in ascending position order: ballots order the lanes of a wave, one
+// exchange of per-wave counts orders the waves.  Rows longer than kRxCap are
+// cut into segments whose winners, (key, position) padded with position -1,
+// go to a workspace; a second launch of the same kernel selects among them.
+// A winner of the row is a winner of its segment and the candidates keep
+// their keys, so the result is identical.
+// ---------------------------------------------------------------------------
+constexpr int kRxThreads = 1024;
+constexpr int kRxWaves = kRxThreads / 64;
+constexpr int kRxRowVecs = 9;                               // 16-byte vectors of keys per lane
+constexpr int kRxCandVecs = 5;                              // ... of (key, position) candidates
+constexpr int kRxCap = kRxWaves * 256 * kRxRowVecs;         // 36864 row entries per workgroup
+constexpr int kRxCapPairs = kRxWaves * 256 * kRxCandVecs;   // 20480 candidates per workgroup
 
-bool topk_may_segment(int max_ctx, int k) { return max_ctx / (4 * k) > 1; }
+struct RadixShared {
+  int hist[256];
+  int cnt[kRxWaves];
+  int fcnt[2][kRxWaves];
+  uint32_t red[2][kRxWaves];
+  int digit;
+  int need;
+};
 
-int topk_segments(int rows, int max_ctx, int k, int num_cus) {
-  if (rows <= 0 || rows >= num_cus || !topk_may_segment(max_ctx, k)) return 1;
-  // enough workgroups for the machine, but segments of at least 4k entries so
-  // that phase 1 actually discards most of each segment
-  int nseg = (2 * num_cus + rows - 1) / rows;
-  const int by_len = max_ctx / (4 * k);
-  if (nseg > by_len) nseg = by_len;
-  return nseg > 1 ? nseg : 1;
+// IN_CAND: the entries are (key, position) candidates [rows, kp] from the
+// segment pass (position -1 = padding; launched with one segment); else the
+// scores of one row at positions [seg * seg_len, (seg + 1) * seg_len).
+// OUT_CAND: write the winners as candidates (kp slots, padded), else their
+// positions to idx (k slots, padded with -1).
+// NV: 16-byte vectors per lane, enough for the launch's longest segment
+// (m <= 4096 NV).
+template <bool IN_CAND, bool OUT_CAND, int NV>
+__global__ __launch_bounds__(kRxThreads) void topk_radix_kernel(const int32_t* __restrict__ cu_q,
+                                                                const int32_t* __restrict__ cu_k, int32_t num_seqs,
+                                                                int32_t row_begin, const float* __restrict__ scores,
+                                                                int64_t ld, int32_t k, int32_t seg_len, int32_t kp,
+                                                                uint32_t* __restrict__ ckey,
+                                                                int32_t* __restrict__ cpos,
+                                                                int32_t* __restrict__ idx) {
+  static_assert(NV <= (IN_CAND ? kRxCandVecs : kRxRowVecs), "too many vectors per lane");
+  __shared__ RadixShared sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t rl = blockIdx.x, seg = blockIdx.y, nseg = gridDim.y;
+  const RowInfo ri = locate_row_wave(load_seq_table(cu_q, cu_k, num_seqs), cu_q, cu_k, row_begin + rl);
+  const int32_t n = ri.pos + 1;
+  if (!IN_CAND && OUT_CAND && n <= k) return;  // the selection pass writes every position directly
+  if (!OUT_CAND && n <= k) {
+    int32_t* out = idx + (int64_t)rl * k;
+    for (int e = tid; e < k; e += kRxThreads) out[e] = e < n ? e : -1;
+    return;
+  }
+  // ---- load: wave w owns entries [w0, w1), L a multiple of 256
+  int32_t m, lo_pos = 0;
+  if constexpr (IN_CAND) {
+    m = kp;
+  } else {
+    lo_pos = seg * seg_len;  // seg_len is a multiple of 4
+    m = max(0, min(n, lo_pos + seg_len) - lo_pos);
+  }
+  const int L = (m + 256 * kRxWaves - 1) / (256 * kRxWaves) * 256;  // <= 256 * NV
+  const int w0 = min(wave * L, m), w1 = min(w0 + L, m);
+  uint32_t key[NV][4];
+  int32_t pos[NV][4];
+  {
+    // raw buffer loads over whole 16-byte vectors (they stay in the row:
+    // lo_pos and ld are multiples of 4, candidate lists multiples of 8);
+    // loads past the range read zero, and all are issued before the first use
+    const uint32_t bytes = (uint32_t)((m + 3) / 4 * 16);
+    const void* kbase = IN_CAND ? (const void*)(ckey + (int64_t)rl * kp)
+                                : (const void*)(scores + (int64_t)rl * ld + lo_pos);
+    const auto ks = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, bytes, 0x00020000);
+    i32x4 kv[NV], pv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = w0 + 256 * i + 4 * lane;
+      const uint32_t off = 256 * i < L ? (uint32_t)e * 4u : 0xfffffff0u;  // outside the wave's range: no access
+      kv[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(ks, off, 0, 0));
+      if constexpr (IN_CAND) {
+        const auto ps = __builtin_amdgcn_make_buffer_rsrc((void*)(cpos + (int64_t)rl * kp), 0, bytes, 0x00020000);
+        pv[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(ps, off, 0, 0));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = w0 + 256 * i + 4 * lane + j;
+        const bool in = 256 * i < L && e < w1;
+        if constexpr (IN_CAND) {
+          pos[i][j] = in ? pv[i][j] : -1;
+          key[i][j] = (uint32_t)kv[i][j];
+        } else {
+          pos[i][j] = in ? lo_pos + e : -1;
+          const int bits = kv[i][j];  // copied out first: a bit_cast of the element expression read element 0
+          key[i][j] = order_key(__int_as_float(bits));
+        }
+      }
+  }
+  // ---- valid entries: count, min and max key
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  int nv = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (pos[i][j] >= 0) {
+        mn = min(mn, key[i][j]);
+        mx = max(mx, key[i][j]);
+        ++nv;
+      }
+  for (int o = 32; o >= 1; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    nv += __shfl_xor(nv, o);
+  }
+  if (lane == 0) { sh.red[0][wave] = mn; sh.red[1][wave] = mx; sh.cnt[wave] = nv; }
+  __syncthreads();
+  uint32_t lo = sh.red[0][0], hi = sh.red[1][0];
+  int nvalid = sh.cnt[0];
+#pragma unroll
+  for (int w = 1; w < kRxWaves; ++w) {
+    lo = min(lo, sh.red[0][w]);
+    hi = max(hi, sh.red[1][w]);
+    nvalid += sh.cnt[w];
+  }
+
+  // ---- the k-th key T: entries above it are kept, and `need` of those equal to it (the earliest)
+  const int take = min((int)k, nvalid);
+  int need;
+  if (nvalid > k) {
+    need = k;
+    while (hi > lo) {
+      const uint32_t span = hi - lo;
+      const int bits = 32 - __clz(span);
+      const int shift = bits > 8 ? bits - 8 : 0;
+      const int nbins = (int)(span >> shift) + 1;  // <= 256
+      if (tid < 256) sh.hist[tid] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t kk = key[i][j];
+          if (pos[i][j] >= 0 && kk >= lo && kk <= hi) atomicAdd(&sh.hist[(kk - lo) >> shift], 1);
+        }
+      __syncthreads();
+      if (wave == 0) {
+        int c[4], sum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int b = nbins - 1 - 4 * lane - j;
+          c[j] = b >= 0 ? sh.hist[b] : 0;
+          sum += c[j];
+        }
+        const int incl = wave_inclusive_scan(sum);
+        const int excl = incl - sum;
+        if (excl < need && need <= incl) {
+          int run = excl;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (run < need && need <= run + c[j]) { sh.digit = nbins - 1 - 4 * lane - j; sh.need = need - run; }
+            run += c[j];
+          }
+        }
+      }
+      __syncthreads();
+      const uint32_t blo = lo + ((uint32_t)sh.digit << shift);
+      lo = blo;
+      hi = min(hi, blo + ((1u << shift) - 1u));
+      need = sh.need;
+    }
+  } else {
+    lo = 0u;  // every valid entry is kept
+    need = 0x7fffffff;
+  }
+  const uint32_t T = lo;
+
+  // ---- stable filter in position order
+  int gt_w = 0, eq_w = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool v = pos[i][j] >= 0;
+      gt_w += v && key[i][j] > T;
+      eq_w += v && key[i][j] == T;
+    }
+  for (int o = 32; o >= 1; o >>= 1) {
+    gt_w += __shfl_xor(gt_w, o);
+    eq_w += __shfl_xor(eq_w, o);
+  }
+  if (lane == 0) { sh.fcnt[0][wave] = eq_w; sh.fcnt[1][wave] = gt_w; }
+  __syncthreads();
+  int eqrun = 0, keeprun = 0;
+  {
+    int eq_pre = 0;
+#pragma unroll
+    for (int w = 0; w < kRxWaves; ++w) {
+      const int e_w = sh.fcnt[0][w], g_w = sh.fcnt[1][w];
+      const int keep_w = g_w + min(max(need - eq_pre, 0), e_w);
+      if (w < wave) { eqrun += e_w; keeprun += keep_w; }
+      eq_pre += e_w;
+    }
+  }
+  uint32_t* okey = nullptr;
+  int32_t* opos = nullptr;
+  int32_t* out = nullptr;
+  if constexpr (OUT_CAND) {
+    okey = ckey + ((int64_t)rl * nseg + seg) * kp;
+    opos = cpos + ((int64_t)rl * nseg + seg) * kp;
+  } else {
+    out = idx + (int64_t)rl * k;
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    int eq_l = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) eq_l += pos[i][j] >= 0 && key[i][j] == T;
+    int eq_tot;
+    int rank = eqrun + wave_excl_prefix_small<3>(eq_l, eq_tot);
+    bool kept[4];
+    int keep_l = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool v = pos[i][j] >= 0;
+      const bool is_eq = v && key[i][j] == T;
+      kept[j] = (v && key[i][j] > T) || (is_eq && rank < need);
+      rank += is_eq;
+      keep_l += kept[j];
+    }
+    int keep_tot;
+    int o = keeprun + wave_excl_prefix_small<3>(keep_l, keep_tot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (kept[j]) {
+        if constexpr (OUT_CAND) {
+          okey[o] = key[i][j];
+          opos[o] = pos[i][j];
+        } else {
+          out[o] = pos[i][j];
+        }
+        ++o;
+      }
+    }
+    eqrun += eq_tot;
+    keeprun += keep_tot;
+  }
+  if constexpr (OUT_CAND) {
+    for (int e = take + tid; e < kp; e += kRxThreads) { okey[e] = 0u; opos[e] = -1; }
+  } else {
+    for (int e = take + tid; e < k; e += kRxThreads) out[e] = -1;
+  }
 }
 
+}  // namespace
+
+namespace {
+
+// How a batch is selected:
+//   kStream:     one 256-thread workgroup streams each row (many rows: the
+//                rows fill the machine, and each is read from HBM once);
+//   kRadix:      few rows of at most kRxCap entries: LDS radix select per row;
+//   kRadixSeg:   few longer rows: radix select per segment, then over the
+//                segments' winners;
+//   kStreamSeg:  few rows too long for the radix merge: streaming selection
+//                per segment, then over the segments' winners.
+enum TopkKind { kStream, kRadix, kRadixSeg, kStreamSeg };
+struct TopkPlan {
+  TopkKind kind;
+  int nseg;
+  int32_t seg_len;
+};
+
+TopkPlan topk_plan(int rows, int max_ctx, int k, int num_cus) {
+  TopkPlan p{kStream, 1, 0};
+  if (rows <= 0 || rows >= num_cus) return p;
+  // Radix select: enough (row, segment) workgroups to cover the machine, but
+  // segments of at least 4k entries (so that the segment pass discards most of
+  // them); a segment must fit the registers, and the winners of all segments
+  // of a row must fit one more radix pass.
+  const int kp = (k + kPer - 1) / kPer * kPer;
+  const int lo = (max_ctx + kRxCap - 1) / kRxCap;
+  const int hi = kRxCapPairs / kp;
+  int nseg = min((num_cus + rows - 1) / rows, max_ctx / (4 * k));
+  nseg = max(nseg, lo);
+  if (nseg <= 1) {
+    p.kind = kRadix;
+    return p;
+  }
+  if (nseg <= hi) {
+    p.kind = kRadixSeg;
+    p.nseg = nseg;
+    p.seg_len = ((max_ctx + nseg - 1) / nseg + 3) / 4 * 4;  // <= kRxCap
+    return p;
+  }
+  // rows too long for the radix merge: streaming selection per segment
+  int ns = (2 * num_cus + rows - 1) / rows;
+  const int by_len = max_ctx / (4 * k);
+  if (ns > by_len) ns = by_len;
+  if (ns <= 1) return p;
+  p.kind = kStreamSeg;
+  p.nseg = ns;
+  const int32_t len = (max_ctx + ns - 1) / ns;
+  p.seg_len = (len + kChunk - 1) / kChunk * kChunk;
+  return p;
+}
+
+template <bool IN_CAND, bool OUT_CAND, int NV>
+hipError_t launch_radix_nv(const TopkLaunch& L, dim3 grid, int32_t seg_len, int32_t kp, uint32_t* ckey,
+                           int32_t* cpos, hipStream_t s) {
+  hipLaunchKernelGGL((topk_radix_kernel<IN_CAND, OUT_CAND, NV>), grid, dim3(kRxThreads), 0, s, L.b.cu_q, L.b.cu_k,
+                     L.b.num_seqs, L.b.row_begin, L.scores, L.ld, L.k, seg_len, kp, ckey, cpos, L.idx);
+  return hipGetLastError();
+}
+
+// m_max: the most entries one workgroup holds (a segment, or a row's candidates)
+template <bool IN_CAND, bool OUT_CAND>
+hipError_t launch_radix(const TopkLaunch& L, dim3 grid, int32_t seg_len, int32_t kp, int32_t m_max, uint32_t* ckey,
+                        int32_t* cpos, hipStream_t s) {
+  const int nv = (m_max + 256 * kRxWaves - 1) / (256 * kRxWaves);
+  if (nv <= 1) return launch_radix_nv<IN_CAND, OUT_CAND, 1>(L, grid, seg_len, kp, ckey, cpos, s);
+  if (nv <= 2) return launch_radix_nv<IN_CAND, OUT_CAND, 2>(L, grid, seg_len, kp, ckey, cpos, s);
+  if (nv <= 3) return launch_radix_nv<IN_CAND, OUT_CAND, 3>(L, grid, seg_len, kp, ckey, cpos, s);
+  if (nv <= 5) return launch_radix_nv<IN_CAND, OUT_CAND, 5>(L, grid, seg_len, kp, ckey, cpos, s);
+  if constexpr (!IN_CAND) {
+    if (nv <= 9) return launch_radix_nv<IN_CAND, OUT_CAND, 9>(L, grid, seg_len, kp, ckey, cpos, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool topk_may_segment(int max_ctx, int k) { return k > 0 && (max_ctx > kRxCap || max_ctx / (4 * k) > 1); }
+
 size_t topk_workspace_bytes(int rows, int max_ctx, int k, int num_cus) {
-  const int nseg = topk_segments(rows, max_ctx, k, num_cus);
-  if (nseg <= 1) return 0;
-  const size_t n = (size_t)rows * nseg * (size_t)((k + kPer - 1) / kPer * kPer);
+  const TopkPlan p = topk_plan(rows, max_ctx, k, num_cus);
+  if (p.kind != kRadixSeg && p.kind != kStreamSeg) return 0;
+  const size_t n = (size_t)rows * p.nseg * (size_t)((k + kPer - 1) / kPer * kPer);
   return 2 * ((n * 4 + 255) / 256 * 256);
 }
 
@@ -387,25 +713,31 @@ hipError_t launch_topk(const TopkLaunch& L, hipStream_t s) {
   const int32_t rows = L.b.row_end - L.b.row_begin;
   if (rows <= 0) return hipSuccess;
   if (L.k > kMaxK || L.k < 1) return hipErrorInvalidValue;
-  const int nseg = topk_segments(rows, L.b.max_ctx, L.k, L.num_cus);
-  if (nseg <= 1) {
+  const TopkPlan p = topk_plan(rows, L.b.max_ctx, L.k, L.num_cus);
+  if (p.kind == kStream) {
     hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(kTkThreads), 0, s, L.b.cu_q, L.b.cu_k, L.b.num_seqs,
                        L.b.row_begin, L.scores, L.ld, L.k, L.idx);
     return hipGetLastError();
   }
+  if (p.kind == kRadix)
+    return launch_radix<false, false>(L, dim3((unsigned)rows), kRxCap, 0, L.b.max_ctx, nullptr, nullptr, s);
   // candidate lists are padded to a multiple of kPer so that loads stay aligned
   const int kp = (L.k + kPer - 1) / kPer * kPer;
-  const size_t n = (size_t)rows * nseg * kp;
+  const size_t n = (size_t)rows * p.nseg * kp;
   uint32_t* ckey = (uint32_t*)L.ws;
   int32_t* cpos = (int32_t*)((char*)L.ws + (n * 4 + 255) / 256 * 256);
-  int32_t seg_len = (L.b.max_ctx + nseg - 1) / nseg;
-  seg_len = (seg_len + kChunk - 1) / kChunk * kChunk;
-  hipLaunchKernelGGL(topk_segment_kernel, dim3((unsigned)rows, (unsigned)nseg), dim3(kTkThreads), 0, s, L.b.cu_q,
-                     L.b.cu_k, L.b.num_seqs, L.b.row_begin, L.scores, L.ld, L.k, kp, seg_len, ckey, cpos);
+  if (p.kind == kRadixSeg) {
+    hipError_t e = launch_radix<false, true>(L, dim3((unsigned)rows, (unsigned)p.nseg), p.seg_len, kp,
+                                             min(p.seg_len, L.b.max_ctx), ckey, cpos, s);
+    if (e != hipSuccess) return e;
+    return launch_radix<true, false>(L, dim3((unsigned)rows), 0, p.nseg * kp, p.nseg * kp, ckey, cpos, s);
+  }
+  hipLaunchKernelGGL(topk_segment_kernel, dim3((unsigned)rows, (unsigned)p.nseg), dim3(kTkThreads), 0, s, L.b.cu_q,
+                     L.b.cu_k, L.b.num_seqs, L.b.row_begin, L.scores, L.ld, L.k, kp, p.seg_len, ckey, cpos);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)rows), dim3(kTkThreads), 0, s, L.b.cu_q, L.b.cu_k,
-                     L.b.num_seqs, L.b.row_begin, nseg, L.k, kp, ckey, cpos, L.idx);
+                     L.b.num_seqs, L.b.row_begin, p.nseg, L.k, kp, ckey, cpos, L.idx);
   return hipGetLastError();
 }
 

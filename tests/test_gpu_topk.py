@@ -101,3 +101,63 @@ def test_few_long_rows_use_segments(dsa, k):
     s[4, :] = np.arange(_ld(p), dtype=np.float32) % 977                # periodic: many exact ties
     got, ref = _run(dsa, p, s, k)
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("k", [1, 100, 2048])
+def test_few_rows_radix_select(dsa, k):
+    """Few rows that fit the LDS radix path: ties, -0/+0, NaN and a row
+    whose keys nearly all fall in one histogram bin."""
+    announce("topk radix", k)
+    p = _problem([30000, 36864, 2049, 12000, 500, 36000], [1, 1, 1, 1, 1, 1], k)
+    rng = np.random.default_rng(10 + k)
+    n = _ld(p)
+    s = rng.standard_normal((p.total_q, n)).astype(np.float32)
+    s[0] = rng.integers(-3, 4, n).astype(np.float32)                    # heavy ties
+    s[0][s[0] == 0] = np.where(rng.random((s[0] == 0).sum()) < 0.5, -0.0, 0.0)
+    s[1][rng.random(n) < 0.02] = np.nan
+    s[3] = 1.0                                                           # one bin holds almost every key
+    s[3, rng.integers(0, 12000, 40)] = rng.standard_normal(40).astype(np.float32)
+    s[5] = np.float32(0.25) + np.float32(1e-7) * np.arange(n, dtype=np.float32)        # keys a few ulps apart
+    got, ref = _run(dsa, p, s, k)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("k", [37, 2048])
+def test_radix_segments_and_winner_merge(dsa, k):
+    """Rows longer than one LDS stage: per-segment winners, then a selection
+    over them; ties straddle the segment borders and short rows ride along."""
+    announce("topk radix segments", k)
+    p = _problem([131072, 2000, 73728, 36865, 100000], [1, 1, 1, 1, 1], k)
+    rng = np.random.default_rng(20 + k)
+    n = _ld(p)
+    s = (0.14 + 0.03 * rng.standard_normal((p.total_q, n))).astype(np.float32)
+    s[2] = (np.arange(n) % 1013).astype(np.float32)                     # equal keys in every segment
+    s[3] = 0.0
+    s[3, 36864] = 1.0                                                    # the best entry is alone in the last segment
+    s[4, 50000:] = np.nan
+    got, ref = _run(dsa, p, s, k)
+    assert np.array_equal(got, ref)
+
+
+def test_rows_beyond_the_radix_merge(dsa):
+    """Few rows too long for the radix merge take the streaming segment path."""
+    announce("topk streaming segments")
+    k = 2048
+    p = _problem([340000, 5000], [1, 1], k)
+    rng = np.random.default_rng(31)
+    s = rng.standard_normal((p.total_q, _ld(p))).astype(np.float32)
+    s[0, ::3] = 2.5                                                      # ties at the cut
+    got, ref = _run(dsa, p, s, k)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("k", [5, 2048])
+def test_few_short_rows_one_radix_pass(dsa, k):
+    """Few rows too short to split: one radix workgroup per row, no workspace."""
+    announce("topk radix unsplit", k)
+    p = _problem([6000, 3000, 7000, 2048], [1, 1, 1, 2], k)
+    rng = np.random.default_rng(40 + k)
+    s = rng.standard_normal((p.total_q, _ld(p))).astype(np.float32)
+    s[1] = np.round(s[1])                                                # ties
+    got, ref = _run(dsa, p, s, k)
+    assert np.array_equal(got, ref)

@@ -40,6 +40,8 @@ constexpr int kRowsPerWave = 2;
 constexpr int kRowsPerBlock = 4 * kRowsPerWave;
 constexpr int kSlabBytes = 64 * 128;                         // 64 keys
 constexpr int kRing = 3;                                      // LDS slabs: one read, two in flight
+constexpr int kPrivSlots = 4;                                 // per-wave LDS ring of the streaming kernel
+constexpr int kStreamRows = 4;                                // rows per workgroup of the streaming kernel
 constexpr int kLinTerms = 4;
 constexpr int kLinScaleOff = kLinTerms * 128;                 // E8M0 scales [term][32-dim block]
 constexpr int kLinRowBytes = kLinScaleOff + kLinTerms * 4;    // 528
@@ -140,16 +142,19 @@ __global__ __launch_bounds__(256) void indexer_lin_kernel(IdxArgs a) {
 enum KeySource {
   kKeysShared = 0,    // the four waves run the same key range and take the keys from an LDS ring
                       // that they fill together (one 8-KB slab per barrier)
-  kKeysPrefetch = 1,  // each wave streams its keys, the next slab in flight
   kKeysPlain = 2,     // each wave streams its keys, one slab at a time (fewest registers)
+  kKeysPrivate = 3,   // each wave streams its keys through its own LDS ring (global_load_lds),
+                      // kPrivSlots - 1 slabs in flight, no register staging and no barriers
 };
 
 // NR query rows of one sequence against keys [kstart, kend); lim[i]: row i's
-// scores are stored for keys below lim[i] only.
-template <int NR, int NHT, int ACT, int KEYS>
+// scores are stored for keys below lim[i] only.  LIN: ReLU through the
+// linear-term MFMA and |x| (rows need the pre-pass fragments); otherwise the
+// activation is applied per head.
+template <int NR, int NHT, int ACT, int KEYS, bool LIN = ACT == 0>
 __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)[NR], const int32_t (&lim)[NR],
                                          int32_t kbase, int32_t kstart, int32_t kend, DSA_LDS uint8_t* ring) {
-  constexpr bool LIN = ACT == 0;
+  static_assert(!LIN || ACT == 0, "the linear-term split is ReLU's");
   constexpr int NST = 4;                          // 16-key sub-tiles per 64-key slab
   constexpr int NPS = (LIN ? 1 : 0) + NR * NHT;   // MFMAs per sub-tile
   constexpr int NM = NST * NPS;                   // MFMAs per slab
@@ -301,16 +306,35 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
       slab(s0, kf);
       slot = slot == 2 ? 0 : slot + 1;
     }
-  } else if constexpr (KEYS == kKeysPrefetch) {
-    i32x8 k0[NST], k1[NST];
-    load_keys(kstart, k0);
-    for (int32_t s0 = kstart; s0 < kend; s0 += 128) {
-      load_keys(s0 + 64, k1);  // unconditional: a conditional load would make every wait drain it
-      slab(s0, k0);
-      if (s0 + 64 >= kend) break;
-      load_keys(s0 + 128, k0);
-      slab(s0 + 64, k1);
+  } else if constexpr (KEYS == kKeysPrivate) {
+    // ring: this wave's kPrivSlots slabs.  Slab n sits in slot n % kPrivSlots;
+    // its 8 copies (chunk column c: lane i copies key row i) are issued
+    // kPrivSlots - 1 slabs ahead.  Ahead of slab n's wait, this wave issued the
+    // copies of slabs n + 1 .. n + kPrivSlots - 2 and the score stores of the
+    // (at most kPrivSlots - 1) slabs before n, all counted by vmcnt.
+    constexpr int P = kPrivSlots;
+    auto copy_own = [&](int32_t s0, int slot) {
+      const uint8_t* src = kglob + (int64_t)min(s0 + lane, kend - 1) * 128;  // rows past kend: a valid key
+      DSA_LDS uint8_t* dst = ring + slot * kSlabBytes;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        __builtin_amdgcn_global_load_lds((const void*)(src + 16 * c), (DSA_LDS void*)(dst + 1024 * c), 16, 0, 0);
+    };
+#pragma unroll
+    for (int j = 0; j < P - 1; ++j) copy_own(kstart + 64 * j, j);
+    int n = 0;
+    for (int32_t s0 = kstart; s0 < kend; s0 += 64, ++n) {
+      static_assert(P == 4, "the counted waits below assume four slots");
+      if (n == 0) wait_vmcnt<8 * (P - 2)>();
+      else if (n == 1) wait_vmcnt<8 * (P - 2) + NR>();
+      else if (n == 2) wait_vmcnt<8 * (P - 2) + 2 * NR>();
+      else wait_vmcnt<8 * (P - 2) + 3 * NR>();
+      copy_own(s0 + 64 * (P - 1), (n + P - 1) % P);  // the slot slab n - 1 used, read before this point
+      i32x8 kf[NST];
+      read_keys(n % P, kf);
+      slab(s0, kf);
     }
+    wait_vmcnt<0>();  // no copy into LDS outlives the wave
   } else {
     for (int32_t s0 = kstart; s0 < kend; s0 += 64) {
       i32x8 kf[NST];
@@ -320,13 +344,12 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
   }
 }
 
-// SHARED: workgroups whose eight rows are one sequence's (prefill) share the
-// keys through LDS; the rest fall back to the lean per-wave path.  Otherwise
-// (decode batches: every row its own sequence) every wave streams its own
-// keys with prefetch.
-template <int NHT, int ACT, bool SHARED>
+// Prefill-like batches: workgroups whose eight rows are one sequence's share
+// the keys through an LDS ring; workgroups whose rows span two sequences fall
+// back to the lean per-wave path.
+template <int NHT, int ACT>
 __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(IdxArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ring[SHARED ? kRing * kSlabBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kSlabBytes];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int32_t rb = a.row_begin + blockIdx.x * kRowsPerBlock;
   const int32_t kstart = blockIdx.y * a.key_chunk;
@@ -353,7 +376,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(IdxArgs a) {
     if (live[j]) kend_blk = max(kend_blk, min(kchunk_end, pos[j] + 1));
   }
   if (kend_blk <= kstart) return;  // nothing to score in this key chunk (uniform over the workgroup)
-  if (SHARED && same) {
+  if (same) {
     int32_t rows[2], lim[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -377,7 +400,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(IdxArgs a) {
   if (v[0] && v[1] && k[0] == k[1]) {
     const int32_t rows[2] = {rb + j0, rb + j0 + 1};
     const int32_t lim[2] = {l[0], l[1]};
-    fp8_rows<2, NHT, ACT, SHARED ? kKeysPlain : kKeysPrefetch>(a, rows, lim, k[0], kstart, max(l[0], l[1]),
+    fp8_rows<2, NHT, ACT, kKeysPlain>(a, rows, lim, k[0], kstart, max(l[0], l[1]),
                                                                nullptr);
   } else {
 #pragma unroll
@@ -385,9 +408,30 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(IdxArgs a) {
       if (!v[i]) continue;
       const int32_t r1[1] = {rb + j0 + i};
       const int32_t l1[1] = {l[i]};
-      fp8_rows<1, NHT, ACT, SHARED ? kKeysPlain : kKeysPrefetch>(a, r1, l1, k[i], kstart, l[i], nullptr);
+      fp8_rows<1, NHT, ACT, kKeysPlain>(a, r1, l1, k[i], kstart, l[i], nullptr);
     }
   }
+}
+
+// Decode-like batches (fewer than 8 query rows per sequence): one row per
+// wave, kStreamRows rows per workgroup.  Every wave streams its row's keys
+// through its own LDS ring, so it needs no barrier and returns on its own.
+// The path is bound by the key bytes, so the activation is applied per head
+// (no linear-term pre-pass).
+template <int NHT, int ACT>
+__global__ __launch_bounds__(kIdxThreads) void indexer_fp8_stream_kernel(IdxArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t pring[];  // kStreamRows x kPrivSlots slabs
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const RowInfo ri = locate_row_wave(load_seq_table(a.cu_q, a.cu_k, a.num_seqs), a.cu_q, a.cu_k,
+                                     min(a.row_begin + (int32_t)blockIdx.x * kStreamRows + wave, a.row_end - 1));
+  const int32_t r = a.row_begin + blockIdx.x * kStreamRows + wave;
+  const int32_t pos = __builtin_amdgcn_readfirstlane(ri.pos);
+  const int32_t kstart = blockIdx.y * a.key_chunk;
+  if (r >= a.row_end || pos < kstart || pos + 1 <= a.skip_n) return;
+  const int32_t kend = min(kstart + a.key_chunk, pos + 1);
+  const int32_t rows[1] = {r}, lim[1] = {kend};
+  fp8_rows<1, NHT, ACT, kKeysPrivate, false>(a, rows, lim, __builtin_amdgcn_readfirstlane(ri.kbase), kstart, kend,
+                                             (DSA_LDS uint8_t*)pring + wave * kPrivSlots * kSlabBytes);
 }
 
 // fp32 inputs: plain VALU dot products (used for small fp32 problems).
@@ -420,15 +464,29 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(IdxArgs a, int d_I) {
 }
 
 template <int NHT>
-hipError_t launch_fp8(const IdxArgs& a, int act, bool shared, dim3 grid, hipStream_t s) {
-  if (act == 0) {
-    if (shared) hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 0, true>), grid, dim3(kIdxThreads), 0, s, a);
-    else hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 0, false>), grid, dim3(kIdxThreads), 0, s, a);
-  } else {
-    if (shared) hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 1, true>), grid, dim3(kIdxThreads), 0, s, a);
-    else hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 1, false>), grid, dim3(kIdxThreads), 0, s, a);
-  }
+hipError_t launch_fp8(const IdxArgs& a, int act, dim3 grid, hipStream_t s) {
+  if (act == 0) hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 0>), grid, dim3(kIdxThreads), 0, s, a);
+  else hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 1>), grid, dim3(kIdxThreads), 0, s, a);
   return hipGetLastError();
+}
+
+template <int NHT, int ACT>
+hipError_t launch_stream_act(const IdxArgs& a, dim3 grid, hipStream_t s) {
+  constexpr size_t lds = (size_t)kStreamRows * kPrivSlots * kSlabBytes;  // 128 KB
+  static bool attr_set = false;  // benign race: idempotent attribute call
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)indexer_fp8_stream_kernel<NHT, ACT>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((indexer_fp8_stream_kernel<NHT, ACT>), grid, dim3(kIdxThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int NHT>
+hipError_t launch_stream(const IdxArgs& a, int act, dim3 grid, hipStream_t s) {
+  return act == 0 ? launch_stream_act<NHT, 0>(a, grid, s) : launch_stream_act<NHT, 1>(a, grid, s);
 }
 
 }  // namespace
@@ -457,6 +515,24 @@ hipError_t launch_indexer(const IndexerLaunch& L, hipStream_t s) {
   a.lin = (const uint8_t*)L.ws;
   a.lin_out = (uint8_t*)L.ws;
   if (L.fp8) {
+    // prefill-like batches (sequences of many query rows): workgroups of eight
+    // rows share their keys; otherwise every row streams its own
+    const bool shared = (int64_t)rows >= 8LL * L.b.num_seqs;
+    if (!shared) {
+      // one workgroup per CU (128 KB of LDS): key chunks that cover the CUs once
+      const int64_t row_blocks = (rows + kStreamRows - 1) / kStreamRows;
+      int32_t chunk = 8192;
+      while (chunk > 256 && row_blocks * ((L.b.max_ctx + chunk - 1) / chunk) < L.num_cus) chunk >>= 1;
+      a.key_chunk = chunk;
+      dim3 grid((unsigned)row_blocks, (unsigned)((L.b.max_ctx + chunk - 1) / chunk));
+      switch (L.H_I / 16) {
+        case 1: return launch_stream<1>(a, L.act, grid, s);
+        case 2: return launch_stream<2>(a, L.act, grid, s);
+        case 3: return launch_stream<3>(a, L.act, grid, s);
+        case 4: return launch_stream<4>(a, L.act, grid, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
     if (L.act == 0) {
       if (!L.ws) return hipErrorInvalidValue;
       hipLaunchKernelGGL(indexer_lin_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
@@ -469,13 +545,11 @@ hipError_t launch_indexer(const IndexerLaunch& L, hipStream_t s) {
     while (chunk > 256 && row_blocks * ((L.b.max_ctx + chunk - 1) / chunk) < 4LL * L.num_cus) chunk >>= 1;
     a.key_chunk = chunk;
     dim3 grid((unsigned)row_blocks, (unsigned)((L.b.max_ctx + chunk - 1) / chunk));
-    // prefill-like batches (sequences of many query rows): workgroups share keys
-    const bool shared = (int64_t)rows >= 8LL * L.b.num_seqs;
     switch (L.H_I / 16) {
-      case 1: return launch_fp8<1>(a, L.act, shared, grid, s);
-      case 2: return launch_fp8<2>(a, L.act, shared, grid, s);
-      case 3: return launch_fp8<3>(a, L.act, shared, grid, s);
-      case 4: return launch_fp8<4>(a, L.act, shared, grid, s);
+      case 1: return launch_fp8<1>(a, L.act, grid, s);
+      case 2: return launch_fp8<2>(a, L.act, grid, s);
+      case 3: return launch_fp8<3>(a, L.act, grid, s);
+      case 4: return launch_fp8<4>(a, L.act, grid, s);
       default: return hipErrorInvalidValue;
     }
   }

@@ -42,6 +42,7 @@ struct TopkShared {
   int32_t pos[kCap];
   int hist[256];
   int wave_sum[2][kTkWaves];   // double-buffered: one barrier per scan
+  int fcnt[2][kTkWaves];       // per-wave counts of the cut's filter
   uint32_t red[2][kTkWaves];
   int digit;
   int need;
@@ -85,19 +86,27 @@ __device__ __forceinline__ int block_excl_scan(int v, TopkShared& sh, int& parit
   return off + pre;
 }
 
-// Cut the first `cnt` (>= k) buffer entries to the k best, keeping position
-// order; returns the k-th best key (the smallest kept key).  The k-th key T is
-// located by histogram refinement over the buffer's own key range: each pass
-// splits the current interval [lo, hi] (known to hold T) into at most 256
-// equal power-of-two bins, so clustered scores still spread over the bins;
-// at most four passes, none when every key is equal.
-__device__ uint32_t cut_to_k(TopkShared& sh, int cnt, int k, int& parity) {
+// The k-th best key T of the first `cnt` (>= k) buffer entries, and in `need`
+// how many of the entries equal to T rank among the k best.  T is located by
+// histogram refinement over the buffer's own key range: each pass splits the
+// current interval [lo, hi] (known to hold T) into at most 256 equal
+// power-of-two bins, so clustered scores still spread over the bins; at most
+// four passes, none when every key is equal.
+__device__ uint32_t kth_key(TopkShared& sh, int cnt, int k, int& need) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the thread's keys (entries tid + 256 j) stay in registers for every pass
+  uint32_t kr[kSegMax];
+  bool kv[kSegMax];
   uint32_t mn = 0xffffffffu, mx = 0u;
-  for (int e = tid; e < cnt; e += kTkThreads) {
-    const uint32_t key = sh.key[e];
-    mn = min(mn, key);
-    mx = max(mx, key);
+#pragma unroll
+  for (int j = 0; j < kSegMax; ++j) {
+    const int e = tid + kTkThreads * j;
+    kv[j] = e < cnt;
+    kr[j] = kv[j] ? sh.key[e] : 0u;
+    if (kv[j]) {
+      mn = min(mn, kr[j]);
+      mx = max(mx, kr[j]);
+    }
   }
   for (int o = 32; o >= 1; o >>= 1) {
     mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
@@ -108,7 +117,7 @@ __device__ uint32_t cut_to_k(TopkShared& sh, int cnt, int k, int& parity) {
   uint32_t lo = sh.red[0][0], hi = sh.red[1][0];
 #pragma unroll
   for (int w = 1; w < kTkWaves; ++w) { lo = min(lo, sh.red[0][w]); hi = max(hi, sh.red[1][w]); }
-  int need = k;  // entries of [lo, hi] still to take, counted from the top
+  need = k;  // entries of [lo, hi] still to take, counted from the top
   while (hi > lo) {
     const uint32_t span = hi - lo;
     const int bits = 32 - __clz(span);
@@ -116,10 +125,9 @@ __device__ uint32_t cut_to_k(TopkShared& sh, int cnt, int k, int& parity) {
     const int nbins = (int)(span >> shift) + 1;  // <= 256
     sh.hist[tid] = 0;
     __syncthreads();
-    for (int e = tid; e < cnt; e += kTkThreads) {
-      const uint32_t key = sh.key[e];
-      if (key >= lo && key <= hi) atomicAdd(&sh.hist[(key - lo) >> shift], 1);
-    }
+#pragma unroll
+    for (int j = 0; j < kSegMax; ++j)
+      if (kv[j] && kr[j] >= lo && kr[j] <= hi) atomicAdd(&sh.hist[(kr[j] - lo) >> shift], 1);
     __syncthreads();
     if (wave == 0) {
       // lane l owns bins nbins-1-4l .. nbins-4-4l (descending key order)
@@ -148,37 +156,61 @@ __device__ uint32_t cut_to_k(TopkShared& sh, int cnt, int k, int& parity) {
     hi = min(hi, bhi);
     need = sh.need;
   }
-  const uint32_t T = lo;  // `need` entries equal to T are kept, the earliest ones
-  // stable filter over contiguous per-thread segments
-  const int per = (cnt + kTkThreads - 1) / kTkThreads;
-  const int seg0 = min(tid * per, cnt), seg1 = min(seg0 + per, cnt);
+  return lo;
+}
+
+// Cut the first `cnt` (>= k) buffer entries to the k best, keeping position
+// order; returns the k-th best key (the smallest kept key).  The filter: wave
+// w takes a contiguous range of 64-entry blocks (lane l: entry l of each
+// block, conflict-free LDS reads) into registers, ballots order the lanes and
+// one exchange of per-wave counts orders the waves; every read precedes the
+// barrier of that exchange, so the kept entries are written back in place.
+__device__ uint32_t cut_to_k(TopkShared& sh, int cnt, int k, int& parity) {
+  (void)parity;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int need;
+  const uint32_t T = kth_key(sh, cnt, k, need);
+  const int L = (cnt + 64 * kTkWaves - 1) / (64 * kTkWaves) * 64;  // <= 64 * kSegMax
+  const int w0 = min(wave * L, cnt), w1 = min(w0 + L, cnt);
   uint32_t kk[kSegMax];
   int32_t pp[kSegMax];
-  int eq = 0;
+  int gt = 0, eq = 0;
 #pragma unroll
   for (int j = 0; j < kSegMax; ++j) {
-    const int e = seg0 + j;
-    kk[j] = 0u;
-    pp[j] = 0;
-    if (e < seg1) { kk[j] = sh.key[e]; pp[j] = sh.pos[e]; eq += kk[j] == T; }
+    const int e = w0 + 64 * j + lane;
+    const bool in = 64 * j < L && e < w1;
+    kk[j] = in ? sh.key[e] : 0u;
+    pp[j] = in ? sh.pos[e] : -1;  // buffered positions are >= 0: -1 marks an empty slot
+    gt += __popcll(__ballot(in && kk[j] > T));
+    eq += __popcll(__ballot(in && kk[j] == T));
   }
-  int tot;
-  int rank = block_excl_scan<5>(eq, sh, parity, tot);
-  int keep = 0;
-  bool kf[kSegMax];
+  if (lane == 0) { sh.fcnt[0][wave] = eq; sh.fcnt[1][wave] = gt; }
+  __syncthreads();
+  int eqrun = 0, keeprun = 0;
+  {
+    int eq_pre = 0;
 #pragma unroll
-  for (int j = 0; j < kSegMax; ++j) {
-    const bool in = seg0 + j < seg1;
-    bool kp = in && kk[j] > T;
-    if (in && kk[j] == T) { kp = rank < need; ++rank; }
-    kf[j] = kp;
-    keep += kp;
+    for (int w = 0; w < kTkWaves; ++w) {
+      const int e_w = sh.fcnt[0][w], g_w = sh.fcnt[1][w];
+      const int keep_w = g_w + min(max(need - eq_pre, 0), e_w);
+      if (w < wave) { eqrun += e_w; keeprun += keep_w; }
+      eq_pre += e_w;
+    }
   }
-  int off = block_excl_scan<5>(keep, sh, parity, tot);
-  __syncthreads();  // every read of the buffer above precedes the writes below
 #pragma unroll
   for (int j = 0; j < kSegMax; ++j) {
-    if (kf[j]) { sh.key[off] = kk[j]; sh.pos[off] = pp[j]; ++off; }
+    const bool in = pp[j] >= 0;
+    const bool is_eq = in && kk[j] == T;
+    const uint64_t meq = __ballot(is_eq);
+    const int rank = eqrun + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(meq >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)meq, 0u));
+    const bool kept = (in && kk[j] > T) || (is_eq && rank < need);
+    const uint64_t mk = __ballot(kept);
+    const int o = keeprun + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+    if (kept) { sh.key[o] = kk[j]; sh.pos[o] = pp[j]; }
+    eqrun += __popcll(meq);
+    keeprun += __popcll(mk);
   }
   __syncthreads();
   return T;
@@ -192,12 +224,15 @@ __device__ uint32_t cut_to_k(TopkShared& sh, int cnt, int k, int& parity) {
 // decode(); three chunks of loads are kept in flight ahead of the one being
 // filtered, so the row streams at memory speed instead of load latency.
 // ---------------------------------------------------------------------------
+// tau0 (have_tau0): start with the threshold tau0 -- only keys above it are
+// admitted; *admitted: how many entries were admitted in all.
 template <class Src>
-__device__ int stream_select(TopkShared& sh, const Src& src, int32_t count, int k) {
+__device__ int stream_select(TopkShared& sh, const Src& src, int32_t count, int k, bool have_tau0 = false,
+                             uint32_t tau0 = 0, int* admitted = nullptr) {
   const int tid = threadIdx.x;
-  int cnt = 0;
-  bool have_tau = false;
-  uint32_t tau = 0;
+  int cnt = 0, adm = 0;
+  bool have_tau = have_tau0;
+  uint32_t tau = tau0;
   int parity = 0;
   typename Src::Fetch f0, f1, f2, f3;
   src.fetch(0, f0);
@@ -229,16 +264,48 @@ __device__ int stream_select(TopkShared& sh, const Src& src, int32_t count, int 
       if (ok[j] && (!have_tau || key[j] > tau)) { sh.key[off] = key[j]; sh.pos[off] = pos[j]; ++off; }
     }
     cnt += total;
+    adm += total;
     f0 = f1;
     f1 = f2;
     f2 = f3;
   }
   __syncthreads();
+  if (admitted) *admitted = adm;
   if (cnt > k) {
     cut_to_k(sh, cnt, k, parity);
     cnt = k;
   }
   return cnt;
+}
+
+// Long rows start from a sampled threshold: the key of rank ~1.5 k n_s / n
+// among n_s = 4096 entries (four contiguous blocks spread over the row), so
+// that about 1.5 k entries of the row reach it and the stream rarely needs a
+// cut.  The result stays exact: if at least k entries reach the threshold,
+// the k-th best key of the row is at least the threshold and every winner is
+// admitted; otherwise the row is selected again without it.
+constexpr int kSampleBlocks = 4;
+constexpr int kSampleBlock = 4 * kTkThreads;      // 1024 entries, one 16-byte load per thread
+constexpr int kSampleMinRow = 16384;
+static_assert(kSampleBlocks * kSampleBlock <= kCap, "the sample is staged in the candidate buffer");
+
+__device__ uint32_t sampled_threshold(TopkShared& sh, const float* row, int32_t n, int k) {
+  const int tid = threadIdx.x;
+  f32x4 v[kSampleBlocks];
+#pragma unroll
+  for (int b = 0; b < kSampleBlocks; ++b) {
+    const int32_t start = (int32_t)((int64_t)b * (n - kSampleBlock) / (kSampleBlocks - 1)) & ~3;
+    v[b] = *(const f32x4*)(row + start + 4 * tid);  // start + kSampleBlock <= n; rows are 16-byte aligned
+  }
+#pragma unroll
+  for (int b = 0; b < kSampleBlocks; ++b)
+    *(i32x4*)&sh.key[b * kSampleBlock + 4 * tid] = i32x4{(int)order_key(v[b][0]), (int)order_key(v[b][1]),
+                                                         (int)order_key(v[b][2]), (int)order_key(v[b][3])};
+  __syncthreads();
+  constexpr int m = kSampleBlocks * kSampleBlock;
+  const int rank = (int)min((int64_t)m, 3LL * k * m / (2LL * n) + 8);
+  int need;
+  return kth_key(sh, m, rank, need);
 }
 
 // Elements are the scores of one row at positions [lo, hi).
@@ -248,10 +315,11 @@ struct ScoreSrc {
   int32_t lo, hi;
   __device__ void fetch(int32_t c0, Fetch& f) const {
     const int32_t p = lo + c0 + (int32_t)threadIdx.x * kPer;  // lo is a multiple of kPer
-    f.a = f32x4{0.f, 0.f, 0.f, 0.f};
-    f.b = f.a;
-    if (p < hi) f.a = *(const f32x4*)(row + p);
-    if (p + 4 < hi) f.b = *(const f32x4*)(row + p + 4);
+    // raw buffer loads over the row's first hi entries: entries past hi read
+    // as zero (and are masked in decode), and no load is conditional
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)row, 0, (uint32_t)hi * 4, 0x00020000);
+    f.a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)p * 4, 0, 0));
+    f.b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)p * 4 + 16, 0, 0));
   }
   __device__ void decode(const Fetch& f, int32_t i0, uint32_t (&key)[kPer], int32_t (&pos)[kPer],
                          bool (&ok)[kPer]) const {
@@ -305,8 +373,17 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const int32_t* __restr
     for (int e = tid; e < k; e += kTkThreads) out[e] = e < n ? e : -1;
     return;
   }
-  const ScoreSrc src{scores + (int64_t)blockIdx.x * ld, 0, n};
-  const int cnt = stream_select(sh, src, n, k);
+  const float* row = scores + (int64_t)blockIdx.x * ld;
+  const ScoreSrc src{row, 0, n};
+  int cnt = -1;
+  if (n >= kSampleMinRow) {
+    const uint32_t ts = sampled_threshold(sh, row, n, k);
+    int admitted;
+    const int c = stream_select(sh, src, n, k, ts > 0u, ts - 1u, &admitted);  // admits keys >= ts
+    if (admitted >= k) cnt = c;
+    __syncthreads();
+  }
+  if (cnt < 0) cnt = stream_select(sh, src, n, k);
   for (int e = tid; e < k; e += kTkThreads) out[e] = e < cnt ? sh.pos[e] : -1;
 }
 

@@ -161,3 +161,26 @@ def test_few_short_rows_one_radix_pass(dsa, k):
     s[1] = np.round(s[1])                                                # ties
     got, ref = _run(dsa, p, s, k)
     assert np.array_equal(got, ref)
+
+
+def test_long_rows_sampled_threshold(dsa):
+    """Rows of 16K candidates or more start from a threshold sampled from four
+    blocks of 1024 entries spread over the row.  Rows whose blocks hold a few
+    outsized scores make the sample overestimate it (fewer than k entries reach
+    it), and those rows must fall back to the plain pass; integer rows put
+    many ties on the sampled threshold."""
+    announce("topk sampled threshold")
+    k = 2048
+    p = _problem([40000], [300], k)
+    rng = np.random.default_rng(50)
+    n_ld = _ld(p)
+    s = (0.14 + 0.03 * rng.standard_normal((p.total_q, n_ld))).astype(np.float32)
+    s[1::3] = rng.integers(-2, 3, (len(s[1::3]), n_ld)).astype(np.float32)
+    for r in range(0, p.total_q, 3):
+        n = 40000 - p.total_q + r + 1
+        rank = min(4096, 3 * k * 4096 // (2 * n) + 8)
+        for b in range(4):
+            start = (b * (n - 1024) // 3) & ~3
+            s[r, start:start + rank // 4 + 1] = 100.0                  # the sample's top ranks: too high
+    got, ref = _run(dsa, p, s, k)
+    assert np.array_equal(got, ref)

@@ -95,11 +95,13 @@ const char* dsa_version(void);
  *   scores  [total_q, ld_scores]  fp32 output, 16-B aligned; only s <= pos_r
  *                                 is written; ld_scores >= max_ctx, % 4 == 0
  * Arithmetic: FP8 x FP8 products are exact in fp32; dot products accumulate in
- * fp32 (MFMA); the weighted head sum is fp32 in a fixed order.  With ReLU and
- * FP8 inputs the score is evaluated as 1/2 (qt . k + sum_j w[r,j] |q_idx[r,j,:] . k|)
- * with qt = sum_j w[r,j] q_idx[r,j,:] (the same function, since
+ * fp32 (MFMA); the weighted head sum is fp32 in a fixed order.  With ReLU,
+ * FP8 inputs and at least 8 query rows per sequence (prefill-like batches) the
+ * score is evaluated as 1/2 (qt . k + sum_j w[r,j] |q_idx[r,j,:] . k|) with
+ * qt = sum_j w[r,j] q_idx[r,j,:] (the same function, since
  * ReLU(x) = (x + |x|) / 2); qt is carried as four E4M3 terms with power-of-two
  * scales per 32 elements, within about 2^-16 of each block's largest value.
+ * Other batches (decode) apply the activation per head.
  * Workspace: dsa_indexer_workspace_size bytes (528 per query row for FP8 with
  * ReLU, else 0), 16-B aligned; ws may be NULL when that is 0; a smaller
  * workspace gives DSA_ERR_WORKSPACE.  The size needs no device.
@@ -126,12 +128,13 @@ dsa_status dsa_indexer_scores(const dsa_batch* batch,
  *   idx    [total_q, k] int32 output, 16-B aligned
  * Integer / bit operations only: the result is exact.  Supported: 1 <= k <= 2048.
  * Workspace: dsa_topk_workspace_size bytes, 16-B aligned, for batches with
- * fewer rows than the device has compute units and max_ctx >= 8 k: each row is
- * then split into segments whose own top-k candidates are merged (same
- * result).  The size depends on the current device's compute-unit count, so
- * query it on the device the call will run on (DSA_ERR_HIP if none is usable;
- * batches with max_ctx < 8 k need no device and get 0).  ws may be NULL when
- * the size is 0; a smaller workspace gives DSA_ERR_WORKSPACE.
+ * fewer rows than the device has compute units and max_ctx >= 8 k or
+ * max_ctx > 36864: each row is then split into segments whose own top-k
+ * candidates are selected again (same result).  The size depends on the
+ * current device's compute-unit count, so query it on the device the call
+ * will run on (DSA_ERR_HIP if none is usable; batches with max_ctx < 8 k and
+ * max_ctx <= 36864 need no device and get 0).  ws may be NULL when the size is
+ * 0; a smaller workspace gives DSA_ERR_WORKSPACE.
  */
 dsa_status dsa_topk_workspace_size(const dsa_batch* batch, int32_t k, size_t* bytes /* host */);
 dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scores, int32_t k,

@@ -35,9 +35,11 @@ def lib():
         L.dsa_oracle_indexer.argtypes = [i32, p, p, i32, p, p, p, i32, p, i32, i32, i32, p, i64]
         L.dsa_oracle_topk.argtypes = [i32, p, p, i32, p, p, i64, i32, p]
         L.dsa_oracle_sparse_mla.argtypes = [i32, p, p, i32, p, p, p, i32, p, i32, i32, i32, i32, dbl, p, p]
+        L.dsa_oracle_dense_mla.argtypes = [i32, p, p, i32, p, p, p, i32, i32, i32, i32, dbl, p, p]
         L.dsa_oracle_forward.argtypes = [i32, p, p, i32, p, p, p, i32, p, i32, i32, i32,
                                          p, p, i32, i32, i32, i32, dbl, i32, i64, p, p, p, p]
-        for f in (L.dsa_oracle_indexer, L.dsa_oracle_topk, L.dsa_oracle_sparse_mla, L.dsa_oracle_forward):
+        for f in (L.dsa_oracle_indexer, L.dsa_oracle_topk, L.dsa_oracle_sparse_mla, L.dsa_oracle_dense_mla,
+                  L.dsa_oracle_forward):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -125,6 +127,25 @@ def sparse_mla(cu_q, cu_k, q, kv, idx, d_v, scale, rows=None):
                                      _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle sparse_mla: invalid batch / rows / indices")
+    return out, lse
+
+
+def dense_mla(cu_q, cu_k, q, kv, d_v, scale, rows=None):
+    """Dense causal MQA over every candidate [0, pos] (the masked mode of short
+    prefill): (out [nrows, H, d_v] float64, lse [nrows, H] float64)."""
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    rows = _rows(rows, cu_q)
+    q, kv = np.ascontiguousarray(q), np.ascontiguousarray(kv)
+    dt = _dtype_code(q)
+    assert _dtype_code(kv) == dt
+    nrows, H, d_qk = q.shape
+    assert nrows == len(rows) and kv.shape[1] == d_qk
+    out = np.zeros((nrows, H, d_v), dtype=np.float64)
+    lse = np.zeros((nrows, H), dtype=np.float64)
+    rc = lib().dsa_oracle_dense_mla(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), nrows, _ptr(rows),
+                                    _ptr(q), _ptr(kv), dt, H, d_qk, d_v, float(scale), _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle dense_mla: invalid batch / rows")
     return out, lse
 
 

@@ -240,6 +240,53 @@ int dsa_oracle_sparse_mla(int nseq, const int32_t* cu_q, const int32_t* cu_k,
 }
 
 /* ------------------------------------------------------------------ */
+/* Dense causal MQA: attention of every query row over all its candidates
+ * [0, pos], no selection.  [P2] 【推理成本评估】 describes this "masked mode"
+ * for short prefill, where DSA is emulated by a mask over the dense
+ * attention; [P1] "在MLA下實例化DSA" gives the MQA form (one latent per
+ * position, key = all columns, value = the first d_v).  Same plain
+ * definition as above with the candidate set S = [0, pos]. */
+/* ------------------------------------------------------------------ */
+int dsa_oracle_dense_mla(int nseq, const int32_t* cu_q, const int32_t* cu_k,
+                         int nrows, const int32_t* rows,
+                         const void* q, const void* kv, int dtype,
+                         int H, int d_qk, int d_v, double scale, double* out, double* lse) {
+    double table[256];
+    for (int c = 0; c < 256; ++c) table[c] = dsa_oracle_e4m3_value(c);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int i = 0; i < nrows; ++i) {
+        int64_t pos, kbase;
+        if (locate_row(nseq, cu_q, cu_k, rows[i], &pos, &kbase) != 0) { bad |= 1; continue; }
+        const int64_t n = pos + 1;
+        double* z = (double*)malloc((size_t)n * sizeof(double));
+        for (int h = 0; h < H; ++h) {
+            double* o = out + ((int64_t)i * H + h) * d_v;
+            double m = -INFINITY;
+            for (int64_t s = 0; s < n; ++s) {
+                double dot = 0.0;
+                for (int d = 0; d < d_qk; ++d)
+                    dot += load_elem(q, dtype, ((int64_t)i * H + h) * d_qk + d, table) *
+                           load_elem(kv, dtype, (kbase + s) * d_qk + d, table);
+                z[s] = scale * dot;
+                if (z[s] > m) m = z[s];
+            }
+            double l = 0.0;
+            for (int d = 0; d < d_v; ++d) o[d] = 0.0;
+            for (int64_t s = 0; s < n; ++s) {
+                double p = exp(z[s] - m);
+                l += p;
+                for (int d = 0; d < d_v; ++d) o[d] += p * load_elem(kv, dtype, (kbase + s) * d_qk + d, table);
+            }
+            for (int d = 0; d < d_v; ++d) o[d] /= l;
+            if (lse) lse[(int64_t)i * H + h] = m + log(l);
+        }
+        free(z);
+    }
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* The three steps in order for a list of rows.  The scores are rounded to
  * binary32 (round-to-nearest-even, the C cast) before selection, since the
  * score tensor the method ranks is fp32.  scores_out / idx_out may be NULL. */

@@ -330,6 +330,58 @@ def test_attention_invariants():
     assert np.array_equal(out4[:, 0], out4[:, 1])
 
 
+# ------------------------------------------------- dense (masked mode) attention
+
+def test_dense_attention_equals_masked_sdpa_on_ragged_batches():
+    """Dense causal MQA: every query row attends to all of [0, pos].  Checked
+    against torch SDPA in float64 with the causal mask written out, per
+    sequence: a prefill sequence, a decode-like one (3 queries at the end of 50
+    cached tokens) and a one-token sequence."""
+    rng = np.random.default_rng(21)
+    ctx, nq, H, d_qk, d_v = [40, 50, 1], [40, 3, 1], 3, 12, 8
+    cu_q, cu_k = _ragged(ctx, nq)
+    q = rng.standard_normal((sum(nq), H, d_qk)).astype(np.float32)
+    kv = rng.standard_normal((sum(ctx), d_qk)).astype(np.float32)
+    out, lse = oracle.dense_mla(cu_q, cu_k, q, kv, d_v, 0.31)
+    for b in range(len(ctx)):
+        qb = q[cu_q[b]:cu_q[b + 1]].astype(np.float64)
+        kb = kv[cu_k[b]:cu_k[b + 1]].astype(np.float64)
+        pos = ctx[b] - nq[b] + np.arange(nq[b])
+        mask = np.arange(ctx[b])[None, :] <= pos[:, None]                  # [nq, ctx]
+        qt = torch.from_numpy(qb).permute(1, 0, 2)
+        k = torch.from_numpy(kb).unsqueeze(0).expand(H, -1, -1)
+        v = torch.from_numpy(kb[:, :d_v].copy()).unsqueeze(0).expand(H, -1, -1)
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, k, v, attn_mask=torch.from_numpy(mask),
+                                                               scale=0.31).permute(1, 0, 2).numpy()
+        np.testing.assert_allclose(out[cu_q[b]:cu_q[b + 1]], ref, rtol=0, atol=1e-12)
+        logits = 0.31 * np.einsum("thd,sd->ths", qb, kb)
+        ref_lse = torch.logsumexp(torch.from_numpy(np.where(mask[:, None, :], logits, -np.inf)), dim=-1).numpy()
+        np.testing.assert_allclose(lse[cu_q[b]:cu_q[b + 1]], ref_lse, rtol=0, atol=1e-12)
+
+
+def test_dense_attention_closed_forms_and_causality():
+    rng = np.random.default_rng(22)
+    L, H, d_qk, d_v = 20, 2, 6, 4
+    cu_q, cu_k = _ragged([L], [L])
+    q = rng.standard_normal((L, H, d_qk)).astype(np.float32)
+    kv = rng.standard_normal((L, d_qk)).astype(np.float32)
+    # q = 0: the mean of v over [0, pos], lse = log(pos + 1)
+    out, lse = oracle.dense_mla(cu_q, cu_k, np.zeros_like(q), kv, d_v, 0.7)
+    for t in range(L):
+        np.testing.assert_allclose(out[t], np.tile(kv[:t + 1, :d_v].astype(np.float64).mean(0), (H, 1)),
+                                   rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse[t], np.log(t + 1.0), rtol=0, atol=1e-14)
+    # position 0 sees itself only
+    out, lse = oracle.dense_mla(cu_q, cu_k, q, kv, d_v, 0.7)
+    assert np.array_equal(out[0], np.tile(kv[0, :d_v].astype(np.float64), (H, 1)))
+    # future rows never matter
+    for t in (3, 11):
+        late = kv.copy()
+        late[t + 1:] = 1e6
+        o2, l2 = oracle.dense_mla(cu_q, cu_k, q, late, d_v, 0.7)
+        assert np.array_equal(o2[:t + 1], out[:t + 1]) and np.array_equal(l2[:t + 1], lse[:t + 1])
+
+
 # ---------------------------------------------------------------- end to end
 
 def test_forward_composes_the_steps_and_is_causal():

@@ -170,6 +170,29 @@ dsa_status dsa_sparse_mla_attn(const dsa_batch* batch,
                                void* ws, size_t ws_bytes, dsa_stream_t stream);
 
 /*
+ * Dense causal MQA attention: the masked mode of short prefill.  [P2]
+ * 【推理成本评估】 says short prefill runs DSA as a mask over dense attention;
+ * [P1] "在MLA下實例化DSA" gives the MQA form.  For every query row r and head h
+ * the candidate set is every position s in [0, pos_r] (no index tensor):
+ *   z_s = softmax_scale * q[r, h, :] . kv[kbase + s, :]
+ *   out[r, h, :] = sum_s softmax(z)_s * kv[kbase + s, 0:d_v],  lse[r, h] = log sum_s exp(z_s)
+ * Shapes, layouts, arithmetic and support as dsa_sparse_mla_attn.  When
+ * neither call splits rows over keys (batches with at least as many rows as
+ * the device has compute units) the result is bit-identical to
+ * dsa_sparse_mla_attn with idx[r] = 0, 1, ..., pos_r (-1 padded): the tiles
+ * and their order are the same.  batch->max_ctx must be at least every
+ * sequence's context length.
+ * F32 additionally needs max_ctx + d_qk <= 16376.  Workspace:
+ * dsa_dense_mla_attn_workspace_size bytes (split partials for batches with
+ * fewer rows than compute units), 16-B aligned; ws may be NULL when that is 0.
+ */
+dsa_status dsa_dense_mla_attn_workspace_size(const dsa_batch* batch, dsa_dtype dtype, int32_t H, int32_t d_v,
+                                             size_t* bytes /* host */);
+dsa_status dsa_dense_mla_attn(const dsa_batch* batch, const void* q, const void* kv, dsa_dtype dtype,
+                              int32_t H, int32_t d_qk, int32_t d_v, float softmax_scale,
+                              void* out, float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
+
+/*
  * The three steps fused in one call, on one stream, with no host
  * synchronisation.  Query rows are processed in chunks of q_block rows
  * (bounded score workspace).  Rows with pos + 1 <= k skip the indexer and the

@@ -245,6 +245,47 @@ dsa_status dsa_sparse_mla_attn(const dsa_batch* batch, const void* q, const void
   return e == hipSuccess ? DSA_OK : hip_fail(e, "attention launch");
 }
 
+dsa_status dsa_dense_mla_attn_workspace_size(const dsa_batch* batch, dsa_dtype dtype, int32_t H, int32_t d_v,
+                                             size_t* bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is NULL");
+  if (dsa_status s = check_batch(batch)) return s;
+  if (H < 1 || d_v < 1) return fail(DSA_ERR_INVALID_ARG, "bad H / d_v");
+  int cus = 0;
+  if (dsa_status s = device_cus(&cus)) return s;
+  const int splits = dsa::attention_splits(batch->total_q, batch->max_ctx, dtype == DSA_BF16, cus);
+  *bytes = attention_ws_bytes(batch->total_q, splits, H, d_v);
+  return DSA_OK;
+}
+
+dsa_status dsa_dense_mla_attn(const dsa_batch* batch, const void* q, const void* kv, dsa_dtype dtype, int32_t H,
+                              int32_t d_qk, int32_t d_v, float softmax_scale, void* out, float* lse, void* ws,
+                              size_t ws_bytes, dsa_stream_t stream) {
+  g_err[0] = 0;
+  if (dsa_status s = check_batch(batch)) return s;
+  // the same checks as the sparse call, with a stand-in index pointer and k
+  static const int32_t no_idx[4] __attribute__((aligned(16))) = {0, 0, 0, 0};
+  if (dsa_status s = check_attention(q, kv, dtype, no_idx, 1, H, d_qk, d_v, softmax_scale, out, lse)) return s;
+  if (dtype == DSA_F32 && (int64_t)batch->max_ctx + d_qk + 8 > 16384)
+    return fail(DSA_ERR_UNSUPPORTED, "F32 dense attention needs max_ctx + d_qk <= 16376");
+  if (batch->total_q == 0) return DSA_OK;
+  int cus = 0;
+  if (dsa_status s = device_cus(&cus)) return s;
+  const int splits = dsa::attention_splits(batch->total_q, batch->max_ctx, dtype == DSA_BF16, cus);
+  const size_t need = attention_ws_bytes(batch->total_q, splits, H, d_v);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
+    return fail(DSA_ERR_WORKSPACE, "attention workspace: need %zu bytes (got %zu)", need, ws_bytes);
+  dsa::AttnLaunch L{view(batch, 0, batch->total_q), q, kv, nullptr, batch->max_ctx, H, d_qk, d_v, softmax_scale,
+                    out, lse, dtype == DSA_BF16, splits, nullptr, nullptr};
+  L.dense = true;
+  if (splits > 1) {
+    L.ws_o = (float*)ws;
+    L.ws_lse = (float*)((char*)ws + round_up((size_t)batch->total_q * splits * H * d_v * sizeof(float), 256));
+  }
+  hipError_t e = dsa::launch_attention(L, (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "dense attention launch");
+}
+
 }  // extern "C"
 
 namespace {

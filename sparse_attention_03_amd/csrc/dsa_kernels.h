@@ -57,6 +57,7 @@ struct AttnLaunch {
   int32_t splits;          // >1: partials in ws, then a merge
   float* ws_o;             // [rows, splits, H, d_v]
   float* ws_lse;           // [rows, splits, H]
+  bool dense = false;      // every candidate [0, pos] (idx unused; k = max_ctx)
 };
 
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s);

@@ -60,6 +60,7 @@ struct MlaArgs {
   uint16_t* out;
   float* lse;
   int32_t splits, tiles_per_split;
+  int32_t dense;  // every candidate [0, pos] instead of idx (k = the longest row's candidate count)
   float* ws_o;
   float* ws_lse;
 };
@@ -120,7 +121,10 @@ __device__ __forceinline__ void gather_tile(const MlaArgs& a, int32_t kbase, con
   }
 }
 
-template <int HPW, int NW>
+// DENSE: every candidate [0, pos] in position order (the masked mode of short
+// prefill), tile t holding positions 32 t .. 32 t + 31, instead of the row's
+// selected entries.
+template <int HPW, int NW, bool DENSE>
 __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   constexpr int NT = HPW / 16;
   static_assert(4 % NW == 0, "a wave copies whole row groups");
@@ -138,7 +142,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   const int32_t rl = blockIdx.x;
   const int sp = blockIdx.y;
   const RowInfo ri = locate_row_wave(load_seq_table(a.cu_q, a.cu_k, a.num_seqs), a.cu_q, a.cu_k, r);
-  const int ntiles = (a.k + kTile - 1) / kTile;
+  const int32_t n = ri.pos + 1;  // candidates of the row (DENSE)
+  const int ntiles = DENSE ? (n + kTile - 1) / kTile : (a.k + kTile - 1) / kTile;
   const int t0 = sp * a.tiles_per_split;
   const int t1 = min(ntiles, t0 + a.tiles_per_split);
 
@@ -146,7 +151,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   // mask of its valid entries (bit j: entry 32 t + j is >= 0)
   DSA_LDS uint32_t* tmask = (DSA_LDS uint32_t*)(sel + kMaxSel);
   const int32_t* idx_row = a.idx + (int64_t)rl * a.k;
-  for (int base = wave * 64; base < ntiles * kTile; base += NW * 64) {
+  for (int base = wave * 64; !DENSE && base < ntiles * kTile; base += NW * 64) {
     const int e = base + lane;
     const bool in = e < ntiles * kTile;
     const int32_t v = e < a.k ? idx_row[e] : -1;
@@ -168,7 +173,14 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
     for (int c = 0; c < kQkSteps; ++c) qf[nt][c] = *(const bf16x8*)(qrow + 32 * c);
   }
   __syncthreads();  // sel[] and tmask[] visible
-  const uint32_t tmask_lane = lane < kMaxSel / kTile ? tmask[lane] : 0u;  // tile t's mask: lane t
+  const uint32_t tmask_lane = !DENSE && lane < kMaxSel / kTile ? tmask[lane] : 0u;  // tile t's mask: lane t
+  // position copied by this lane for tile t, row group k (DENSE: invalid
+  // entries copy position 0, always in bounds, and are masked)
+  auto pos_at = [&](int t, int k) -> int32_t {
+    const int e = t * kTile + gather_row(wave, NW, k, lane);
+    if constexpr (DENSE) return e < n ? e : 0;
+    else return sel[e];
+  };
 
   // Softmax reference point: the first tile's max of each head, fixed for the
   // whole row, so the accumulators are only ever touched by MFMAs and the
@@ -212,14 +224,14 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
       if (t0 + j < t1) {
         int32_t pj[RG];
 #pragma unroll
-        for (int k = 0; k < RG; ++k) pj[k] = sel[(t0 + j) * kTile + gather_row(wave, NW, k, lane)];
+        for (int k = 0; k < RG; ++k) pj[k] = pos_at(t0 + j, k);
         gather_tile<NW>(a, ri.kbase, pj, smem + (size_t)j * kTileBytes);
       }
     // positions for the next gather, read a tile ahead so their LDS latency hides
     int32_t p_next[RG];
 #pragma unroll
     for (int k = 0; k < RG; ++k)
-      p_next[k] = t0 + AHEAD < t1 ? sel[(t0 + AHEAD) * kTile + gather_row(wave, NW, k, lane)] : 0;
+      p_next[k] = t0 + AHEAD < t1 ? pos_at(t0 + AHEAD, k) : 0;
 
     for (int t = t0; t < t1; ++t) {
       // Tile t has landed once at most (copies issued after it) x NINS of this
@@ -234,10 +246,11 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
         gather_tile<NW>(a, ri.kbase, p_next, smem + (size_t)((t + AHEAD - t0) % kNumBuf) * kTileBytes);
         if (t + AHEAD + 1 < t1) {
 #pragma unroll
-          for (int k = 0; k < RG; ++k) p_next[k] = sel[(t + AHEAD + 1) * kTile + gather_row(wave, NW, k, lane)];
+          for (int k = 0; k < RG; ++k) p_next[k] = pos_at(t + AHEAD + 1, k);
         }
       }
-      const uint32_t vmask = (uint32_t)__builtin_amdgcn_readlane((int)tmask_lane, t);
+      const uint32_t vmask = DENSE ? (n - kTile * t >= kTile ? 0xffffffffu : (1u << (n - kTile * t)) - 1u)
+                                   : (uint32_t)__builtin_amdgcn_readlane((int)tmask_lane, t);
       if (vmask != 0) {
         const DSA_LDS uint8_t* lb = (const DSA_LDS uint8_t*)smem + (size_t)((t - t0) % kNumBuf) * kTileBytes;
         // ---- scores: sacc[mt][nt] = S^T[keys 16mt.., heads 16nt..]
@@ -427,12 +440,12 @@ __global__ __launch_bounds__(256) void mla_f32_kernel(MlaArgs a, int d_qk, int d
   float* red = z + a.k;
   const float* q = (const float*)a.q + ((int64_t)r * a.H + h) * d_qk;
   const float* kv = (const float*)a.kv;
-  const int32_t* sel = a.idx + (int64_t)rl * a.k;
+  const int32_t* sel = a.dense ? nullptr : a.idx + (int64_t)rl * a.k;
   for (int d = threadIdx.x; d < d_qk; d += blockDim.x) qs[d] = q[d];
   __syncthreads();
   float mloc = -INFINITY;
   for (int e = threadIdx.x; e < a.k; e += blockDim.x) {
-    const int32_t p = sel[e];
+    const int32_t p = a.dense ? (e <= ri.pos ? e : -1) : sel[e];
     float zz = -INFINITY;
     if (p >= 0) {
       const float* row = kv + (int64_t)(ri.kbase + p) * d_qk;
@@ -464,7 +477,7 @@ __global__ __launch_bounds__(256) void mla_f32_kernel(MlaArgs a, int d_qk, int d
   for (int d = threadIdx.x; d < d_v; d += blockDim.x) {
     float acc = 0.0f;
     for (int e = 0; e < a.k; ++e) {
-      const int32_t p = sel[e];
+      const int32_t p = a.dense ? (e <= ri.pos ? e : -1) : sel[e];
       if (p < 0) continue;
       acc = fmaf(z[e], kv[(int64_t)(ri.kbase + p) * d_qk + d], acc);
     }
@@ -473,17 +486,18 @@ __global__ __launch_bounds__(256) void mla_f32_kernel(MlaArgs a, int d_qk, int d
   if (threadIdx.x == 0 && a.lse) a.lse[(int64_t)r * a.H + h] = l > 0.0f ? m + logf(l) : -INFINITY;
 }
 
-template <int HPW, int NW>
+template <int HPW, int NW, bool DENSE>
 hipError_t launch_bf16(const MlaArgs& a, int rows, hipStream_t s) {
   const size_t lds = (size_t)kNumBuf * kTileBytes + kMaxSel * sizeof(int32_t) + (kMaxSel / kTile) * sizeof(uint32_t);
   static bool attr_set = false;  // benign race: idempotent attribute call
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)mla_bf16_kernel<HPW, NW>,
+    hipError_t e = hipFuncSetAttribute((const void*)mla_bf16_kernel<HPW, NW, DENSE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((mla_bf16_kernel<HPW, NW>), dim3((unsigned)rows, (unsigned)a.splits), dim3(NW * 64), lds, s, a);
+  hipLaunchKernelGGL((mla_bf16_kernel<HPW, NW, DENSE>), dim3((unsigned)rows, (unsigned)a.splits), dim3(NW * 64), lds,
+                     s, a);
   return hipGetLastError();
 }
 
@@ -520,6 +534,7 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t s) {
   a.tiles_per_split = (ntiles + a.splits - 1) / a.splits;
   a.ws_o = L.ws_o;
   a.ws_lse = L.ws_lse;
+  a.dense = L.dense ? 1 : 0;
   if (!L.bf16) {
     const size_t lds = (size_t)(L.d_qk + L.k + 8) * sizeof(float);
     hipLaunchKernelGGL(mla_f32_kernel, dim3((unsigned)rows, (unsigned)L.H), dim3(256), lds, s, a, L.d_qk, L.d_v,
@@ -527,10 +542,13 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t s) {
     return hipGetLastError();
   }
   hipError_t e;
-  switch (L.H) {
-    case 32: e = launch_bf16<32, 1>(a, rows, s); break;
-    case 64: e = launch_bf16<32, 2>(a, rows, s); break;
-    case 128: e = launch_bf16<32, 4>(a, rows, s); break;
+  switch (L.H * 2 + (L.dense ? 1 : 0)) {
+    case 64: e = launch_bf16<32, 1, false>(a, rows, s); break;
+    case 128: e = launch_bf16<32, 2, false>(a, rows, s); break;
+    case 256: e = launch_bf16<32, 4, false>(a, rows, s); break;
+    case 65: e = launch_bf16<32, 1, true>(a, rows, s); break;
+    case 129: e = launch_bf16<32, 2, true>(a, rows, s); break;
+    case 257: e = launch_bf16<32, 4, true>(a, rows, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || a.splits == 1) return e;

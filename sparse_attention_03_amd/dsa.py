@@ -45,6 +45,17 @@ def sparse_mla_attn(p, idx, with_lse=True):
     return out, lse
 
 
+def dense_mla_attn(p, with_lse=True):
+    """Dense causal MQA over every candidate [0, pos] (the masked mode)."""
+    b = L.batch_of(p)
+    dev = p.q.device
+    out = torch.empty((p.total_q, p.H, p.d_v), dtype=p.q.dtype, device=dev)
+    lse = torch.empty((p.total_q, p.H), dtype=torch.float32, device=dev) if with_lse else None
+    n = L.dsa_dense_mla_attn_workspace_size(b, L._dtype_code(p.q), p.H, p.d_v)
+    L.dsa_dense_mla_attn(b, p.q, p.kv, p.d_v, p.scale, out, lse, ws=_ws(n, dev) if n else None)
+    return out, lse
+
+
 class Forward:
     """A prepared dsa_forward call: outputs and workspace allocated once, so
     that repeated calls (benchmarks) allocate nothing."""

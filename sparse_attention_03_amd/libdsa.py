@@ -56,6 +56,8 @@ _SIGS = {
     "dsa_sparse_mla_attn_workspace_size": ([_BP, ctypes.c_int, _i32, _i32, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
     "dsa_sparse_mla_attn": ([_BP, _p, _p, ctypes.c_int, _p, _i32, _i32, _i32, _i32, _f32, _p, _p, _p, _sz, _p],
                             ctypes.c_int),
+    "dsa_dense_mla_attn_workspace_size": ([_BP, ctypes.c_int, _i32, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
+    "dsa_dense_mla_attn": ([_BP, _p, _p, ctypes.c_int, _i32, _i32, _i32, _f32, _p, _p, _p, _sz, _p], ctypes.c_int),
     "dsa_forward_workspace_size": ([_FP, ctypes.POINTER(_sz)], ctypes.c_int),
     "dsa_forward": ([_FP, _p, _sz, _p], ctypes.c_int),
 }
@@ -147,6 +149,20 @@ def dsa_sparse_mla_attn(batch: DsaBatch, q, kv, idx, d_v: int, softmax_scale: fl
                                     q.shape[1], q.shape[2], d_v, float(softmax_scale), _ptr(out), _ptr(lse),
                                     _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
            "dsa_sparse_mla_attn")
+
+
+def dsa_dense_mla_attn_workspace_size(batch: DsaBatch, dtype: int, H: int, d_v: int) -> int:
+    n = _sz(0)
+    _check(_lib.dsa_dense_mla_attn_workspace_size(ctypes.byref(batch), dtype, H, d_v, ctypes.byref(n)),
+           "dsa_dense_mla_attn_workspace_size")
+    return n.value
+
+
+def dsa_dense_mla_attn(batch: DsaBatch, q, kv, d_v: int, softmax_scale: float, out, lse=None, ws=None, stream=None):
+    _check(_lib.dsa_dense_mla_attn(ctypes.byref(batch), _ptr(q), _ptr(kv), _dtype_code(q), q.shape[1], q.shape[2],
+                                   d_v, float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                   0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "dsa_dense_mla_attn")
 
 
 def forward_params(batch: DsaBatch, q_idx, k_idx, w, q, kv, k: int, d_v: int, softmax_scale: float, out,

@@ -173,6 +173,45 @@ def decode_us_per_token(steps=20, warmup=3):
             "us_per_token": step_s * 1e6 / p.total_q, "us_per_step": step_s * 1e6}
 
 
+def crossover(lengths, steps=3, warmup=1):
+    """Masked mode against the sparse path on one prefill sequence of each
+    length (the prefill_8k distributions): ms per step of dsa_forward (indexer
+    + top-k + sparse attention, 4096-row chunks) and of dsa_dense_mla_attn
+    (dense causal MQA over the same rows, no indexer, no selection)."""
+    import torch
+    from sparse_attention_03_amd import dsa, inputs as gen, libdsa as L
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    rows = []
+    for n in lengths:
+        p = gen.make_problem("crossover", [n], [n], device="cuda", seed=0, q_block=4096)
+        f = dsa.Forward(p, with_idx=False, with_lse=False)
+        b = L.batch_of(p)
+        out = torch.empty((p.total_q, p.H, p.d_v), dtype=p.q.dtype, device="cuda")
+        nws = L.dsa_dense_mla_attn_workspace_size(b, L._dtype_code(p.q), p.H, p.d_v)
+        ws = torch.empty(max(nws, 256), dtype=torch.uint8, device="cuda")
+        sparse_ms = timed(f)
+        dense_ms = timed(lambda: L.dsa_dense_mla_attn(b, p.q, p.kv, p.d_v, p.scale, out, None, ws=ws))
+        row = {"seq_len": n, "sparse_ms": sparse_ms, "dense_ms": dense_ms,
+               "sparse_tokens_s": n / (sparse_ms / 1e3), "dense_tokens_s": n / (dense_ms / 1e3)}
+        log(json.dumps(row))
+        rows.append(row)
+        del p, f, out, ws
+        torch.cuda.empty_cache()
+    return rows
+
+
 def _short(name):
     m = re.search(r"dsa::\(anonymous namespace\)::(\w+)", name)
     if m:
@@ -242,6 +281,9 @@ def main():
     ap.add_argument("--decode-only", action="store_true", help="time only the 64 x 32K decode batch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy 3 times (counter calibration under rocprofv3)")
+    ap.add_argument("--crossover", metavar="L", type=int, nargs="+",
+                    help="masked mode (dense attention) against the sparse path on one prefill sequence of each "
+                         "length L, and exit")
     ap.add_argument("--summarize", metavar="DIR", nargs="+", help="summarise rocprofv3 CSV output in DIR... and exit")
     ap.add_argument("--summary-command", default="", help="the command that produced DIR (recorded)")
     args = ap.parse_args()
@@ -257,6 +299,9 @@ def main():
     from sparse_attention_03_amd import dsa, inputs as gen
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.crossover:
+        print(json.dumps({"crossover": crossover(args.crossover, steps=args.steps, warmup=args.warmup)}), flush=True)
+        return
     if args.decode_only:
         print(json.dumps({"decode": decode_us_per_token(steps=args.steps, warmup=args.warmup)}), flush=True)
         return

@@ -385,6 +385,7 @@ dsa_status dsa_forward(const dsa_forward_params* p, void* ws, size_t ws_bytes, d
     const int splits = dsa::attention_splits(r1 - r0, p->k, p->dtype == DSA_BF16, cus);
     dsa::AttnLaunch AL{v, p->q, p->kv, idx, p->k, p->H, p->d_qk, p->d_v, p->softmax_scale, p->out, p->lse,
                        p->dtype == DSA_BF16, splits, nullptr, nullptr};
+    AL.dense_short = true;  // rows with pos + 1 <= k: the masked mode, same result as their idx = 0 .. pos
     if (splits > 1) {
       AL.ws_o = (float*)(base + f.off_attn);
       AL.ws_lse = (float*)(base + f.off_attn +

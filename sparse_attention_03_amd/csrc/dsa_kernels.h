@@ -58,6 +58,7 @@ struct AttnLaunch {
   float* ws_o;             // [rows, splits, H, d_v]
   float* ws_lse;           // [rows, splits, H]
   bool dense = false;      // every candidate [0, pos] (idx unused; k = max_ctx)
+  bool dense_short = false;  // rows with pos + 1 <= k walk [0, pos] without reading idx
 };
 
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s);

@@ -60,7 +60,8 @@ struct MlaArgs {
   uint16_t* out;
   float* lse;
   int32_t splits, tiles_per_split;
-  int32_t dense;  // every candidate [0, pos] instead of idx (k = the longest row's candidate count)
+  int32_t dense;        // every candidate [0, pos] instead of idx (k = the longest row's candidate count)
+  int32_t dense_short;  // rows with n <= k walk [0, pos] directly (their idx is 0 .. pos)
   float* ws_o;
   float* ws_lse;
 };
@@ -123,7 +124,9 @@ __device__ __forceinline__ void gather_tile(const MlaArgs& a, int32_t kbase, con
 
 // DENSE: every candidate [0, pos] in position order (the masked mode of short
 // prefill), tile t holding positions 32 t .. 32 t + 31, instead of the row's
-// selected entries.
+// selected entries.  With a.dense_short, rows with n <= k (which select every
+// candidate) take the same dense walk; their tiles and tile order equal those
+// of the index walk over idx = 0 .. pos, so the result is the same.
 template <int HPW, int NW, bool DENSE>
 __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   constexpr int NT = HPW / 16;
@@ -142,8 +145,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   const int32_t rl = blockIdx.x;
   const int sp = blockIdx.y;
   const RowInfo ri = locate_row_wave(load_seq_table(a.cu_q, a.cu_k, a.num_seqs), a.cu_q, a.cu_k, r);
-  const int32_t n = ri.pos + 1;  // candidates of the row (DENSE)
-  const int ntiles = DENSE ? (n + kTile - 1) / kTile : (a.k + kTile - 1) / kTile;
+  const int32_t n = ri.pos + 1;  // candidates of the row
+  const bool dense = DENSE || (a.dense_short && n <= a.k);  // uniform over the workgroup
+  const int ntiles = dense ? (n + kTile - 1) / kTile : (a.k + kTile - 1) / kTile;
   const int t0 = sp * a.tiles_per_split;
   const int t1 = min(ntiles, t0 + a.tiles_per_split);
 
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   // mask of its valid entries (bit j: entry 32 t + j is >= 0)
   DSA_LDS uint32_t* tmask = (DSA_LDS uint32_t*)(sel + kMaxSel);
   const int32_t* idx_row = a.idx + (int64_t)rl * a.k;
-  for (int base = wave * 64; !DENSE && base < ntiles * kTile; base += NW * 64) {
+  for (int base = wave * 64; !dense && base < ntiles * kTile; base += NW * 64) {
     const int e = base + lane;
     const bool in = e < ntiles * kTile;
     const int32_t v = e < a.k ? idx_row[e] : -1;
@@ -173,13 +177,12 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
     for (int c = 0; c < kQkSteps; ++c) qf[nt][c] = *(const bf16x8*)(qrow + 32 * c);
   }
   __syncthreads();  // sel[] and tmask[] visible
-  const uint32_t tmask_lane = !DENSE && lane < kMaxSel / kTile ? tmask[lane] : 0u;  // tile t's mask: lane t
+  const uint32_t tmask_lane = !dense && lane < kMaxSel / kTile ? tmask[lane] : 0u;  // tile t's mask: lane t
   // position copied by this lane for tile t, row group k (DENSE: invalid
   // entries copy position 0, always in bounds, and are masked)
   auto pos_at = [&](int t, int k) -> int32_t {
     const int e = t * kTile + gather_row(wave, NW, k, lane);
-    if constexpr (DENSE) return e < n ? e : 0;
-    else return sel[e];
+    return dense ? (e < n ? e : 0) : sel[e];
   };
 
   // Softmax reference point: the first tile's max of each head, fixed for the
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
           for (int k = 0; k < RG; ++k) p_next[k] = pos_at(t + AHEAD + 1, k);
         }
       }
-      const uint32_t vmask = DENSE ? (n - kTile * t >= kTile ? 0xffffffffu : (1u << (n - kTile * t)) - 1u)
+      const uint32_t vmask = dense ? (n - kTile * t >= kTile ? 0xffffffffu : (1u << (n - kTile * t)) - 1u)
                                    : (uint32_t)__builtin_amdgcn_readlane((int)tmask_lane, t);
       if (vmask != 0) {
         const DSA_LDS uint8_t* lb = (const DSA_LDS uint8_t*)smem + (size_t)((t - t0) % kNumBuf) * kTileBytes;
@@ -535,6 +538,7 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t s) {
   a.ws_o = L.ws_o;
   a.ws_lse = L.ws_lse;
   a.dense = L.dense ? 1 : 0;
+  a.dense_short = L.dense_short ? 1 : 0;
   if (!L.bf16) {
     const size_t lds = (size_t)(L.d_qk + L.k + 8) * sizeof(float);
     hipLaunchKernelGGL(mla_f32_kernel, dim3((unsigned)rows, (unsigned)L.H), dim3(256), lds, s, a, L.d_qk, L.d_v,

@@ -63,6 +63,19 @@ def test_forward_equals_separate_calls(dsa):
     assert torch.equal(idx3, idx) and torch.equal(out3, out)
 
 
+def test_forward_short_rows_masked_mode_with_key_splits(dsa):
+    """Rows with pos + 1 <= k take the dense walk inside dsa_forward; with few
+    rows the attention is split over keys, and the dense rows leave their later
+    splits empty.  The outputs equal the separate calls bit for bit."""
+    announce("forward masked mode with splits")
+    p = gen.make_problem("fwd", [3000, 300, 500, 40], [1, 1, 2, 40], H_I=64, H=128, k=512, device=DEV, seed=27)
+    out, lse, idx = dsa.forward(p)
+    idx2 = dsa.topk(p, dsa.indexer_scores(p))
+    assert torch.equal(idx, idx2)
+    out2, lse2 = dsa.sparse_mla_attn(p, idx2)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
 def test_forward_integer_inputs_exact_selection(dsa):
     announce("forward integer inputs")
     p = gen.make_problem("fwd", [2500], [2500], H_I=64, H=128, k=256, integer=True, device=DEV, seed=22)

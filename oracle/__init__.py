@@ -36,10 +36,11 @@ def lib():
         L.dsa_oracle_topk.argtypes = [i32, p, p, i32, p, p, i64, i32, p]
         L.dsa_oracle_sparse_mla.argtypes = [i32, p, p, i32, p, p, p, i32, p, i32, i32, i32, i32, dbl, p, p]
         L.dsa_oracle_dense_mla.argtypes = [i32, p, p, i32, p, p, p, i32, i32, i32, i32, dbl, p, p]
+        L.dsa_oracle_quantize_keys.argtypes = [p, i32, i64, i32, i32, p, p]
         L.dsa_oracle_forward.argtypes = [i32, p, p, i32, p, p, p, i32, p, i32, i32, i32,
                                          p, p, i32, i32, i32, i32, dbl, i32, i64, p, p, p, p]
         for f in (L.dsa_oracle_indexer, L.dsa_oracle_topk, L.dsa_oracle_sparse_mla, L.dsa_oracle_dense_mla,
-                  L.dsa_oracle_forward):
+                  L.dsa_oracle_quantize_keys, L.dsa_oracle_forward):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -147,6 +148,20 @@ def dense_mla(cu_q, cu_k, q, kv, d_v, scale, rows=None):
     if rc != 0:
         raise ValueError("oracle dense_mla: invalid batch / rows")
     return out, lse
+
+
+def quantize_keys(src, scaled=False):
+    """Indexer keys [n, d] (float32, or bfloat16 bits as uint16) to E4M3FN codes
+    [n, d] uint8, plus E8M0 per-row scales [n] uint8 when `scaled`."""
+    src = np.ascontiguousarray(src)
+    dt = _dtype_code(src)
+    n, d = src.shape
+    codes = np.zeros((n, d), dtype=np.uint8)
+    scale = np.zeros(n if scaled else 1, dtype=np.uint8)
+    rc = lib().dsa_oracle_quantize_keys(_ptr(src), dt, n, d, int(scaled), _ptr(codes), _ptr(scale))
+    if rc != 0:
+        raise ValueError("oracle quantize_keys: source must be float32 or bfloat16")
+    return (codes, scale) if scaled else codes
 
 
 def forward(cu_q, cu_k, q_idx, k_idx, w, q, kv, k, d_v, scale, act=ACT_RELU, rows=None, ld=None):

@@ -240,6 +240,63 @@ int dsa_oracle_sparse_mla(int nseq, const int32_t* cu_q, const int32_t* cu_k,
 }
 
 /* ------------------------------------------------------------------ */
+/* Indexer-key quantisation to OCP E4M3FN.  [P1] "Lightning indexer": the
+ * indexer runs in FP8, so its key cache holds FP8 codes.  Rounding is to the
+ * nearest representable value, ties to the even code; magnitudes beyond the
+ * largest finite value (448) saturate to it; NaN gives 0x7F; the sign is kept
+ * (so values that round to zero give +0 or -0).
+ * With per-token scaling each key row t gets the power of two 2^e_t with the
+ * smallest e_t such that max_d |x[t,d]| <= 448 * 2^e_t (e_t = 0 for an
+ * all-zero row, clamped to [-127, 127]); the codes encode x[t,d] / 2^e_t and
+ * the scale is stored as an E8M0 byte 127 + e_t, so the key is
+ * value(code) * 2^e_t. */
+/* ------------------------------------------------------------------ */
+static int e4m3_encode(double x) {
+    if (x != x) return 0x7F;
+    const int sign = (x < 0.0 || (x == 0.0 && signbit(x))) ? 0x80 : 0;
+    double a = fabs(x);
+    if (a >= 448.0) return sign | 0x7E;
+    /* nearest of the 127 non-negative finite codes 0x00 .. 0x7E; codes are
+     * monotone in value, ties go to the even code */
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        const double d = fabs(dsa_oracle_e4m3_value(c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0)) { bd = d; best = c; }
+    }
+    return sign | best;
+}
+
+int dsa_oracle_quantize_keys(const void* src, int dtype, int64_t n, int d, int scaled,
+                             uint8_t* codes, uint8_t* scale_e8m0) {
+    double table[256];
+    for (int c = 0; c < 256; ++c) table[c] = dsa_oracle_e4m3_value(c);
+    if (dtype != OR_F32 && dtype != OR_BF16) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        int e = 0;
+        if (scaled) {
+            double amax = 0.0;
+            for (int j = 0; j < d; ++j) {
+                const double v = fabs(load_elem(src, dtype, t * d + j, table));
+                if (v > amax) amax = v;  /* NaN never compares greater */
+            }
+            if (amax > 0.0) {
+                int ex;
+                const double f = frexp(amax / 448.0, &ex);  /* amax / 448 = f 2^ex, f in [0.5, 1) */
+                e = (f == 0.5) ? ex - 1 : ex;               /* ceil(log2(amax / 448)) */
+                if (e < -127) e = -127;
+                if (e > 127) e = 127;
+            }
+            scale_e8m0[t] = (uint8_t)(127 + e);
+        }
+        for (int j = 0; j < d; ++j)
+            codes[t * d + j] = (uint8_t)e4m3_encode(ldexp(load_elem(src, dtype, t * d + j, table), -e));
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Dense causal MQA: attention of every query row over all its candidates
  * [0, pos], no selection.  [P2] 【推理成本评估】 describes this "masked mode"
  * for short prefill, where DSA is emulated by a mask over the dense

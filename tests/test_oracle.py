@@ -382,6 +382,76 @@ def test_dense_attention_closed_forms_and_causality():
         assert np.array_equal(o2[:t + 1], out[:t + 1]) and np.array_equal(l2[:t + 1], lse[:t + 1])
 
 
+# ------------------------------------------------------ indexer-key quantisation
+
+def _e4m3_values():
+    return np.array([oracle.e4m3_value(c) for c in range(256)])
+
+
+def test_quantize_every_code_round_trips_and_ties_go_even():
+    vals = _e4m3_values()
+    finite = [c for c in range(256) if np.isfinite(vals[c])]
+    x = np.array([vals[c] for c in finite], np.float32)[None, :]
+    codes = oracle.quantize_keys(x)[0]
+    want = np.array(finite, np.uint8)
+    assert np.array_equal(codes, want)                      # every finite code, -0 included
+    # midpoints between neighbouring positive values go to the even code,
+    # points just beside them to the nearer one
+    pos = np.array([vals[c] for c in range(0x7F)])
+    mids = (pos[:-1] + pos[1:]) / 2
+    codes_mid = oracle.quantize_keys(mids.astype(np.float32)[None, :])[0]
+    even = np.where(np.arange(0x7E) % 2 == 0, np.arange(0x7E), np.arange(1, 0x7F))
+    assert np.array_equal(codes_mid, even.astype(np.uint8))
+    below = oracle.quantize_keys(np.nextafter(mids.astype(np.float32), np.float32(0))[None, :])[0]
+    above = oracle.quantize_keys(np.nextafter(mids.astype(np.float32), np.float32(1e9))[None, :])[0]
+    assert np.array_equal(below, np.arange(0x7E, dtype=np.uint8))
+    assert np.array_equal(above, np.arange(1, 0x7F, dtype=np.uint8))
+
+
+def test_quantize_saturation_nan_and_library_rounding():
+    x = np.array([[448.0, 449.0, 464.0, 1e30, -500.0, np.nan, -0.0, 1e-30, -1e-30]], np.float32)
+    codes = oracle.quantize_keys(x)[0]
+    assert list(codes) == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0x7F, 0x80, 0x00, 0x80]
+    # in range, torch's conversion (round to nearest even) gives the same codes
+    rng = np.random.default_rng(31)
+    y = (rng.standard_normal((64, 128)) * np.exp(rng.uniform(-8, 5, (64, 1)))).astype(np.float32)
+    y = np.clip(y, -440, 440)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.quantize_keys(y), ref)
+    # bfloat16 sources decode exactly first
+    bits = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ref_b = torch.from_numpy(y).to(torch.bfloat16).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.quantize_keys(bits), ref_b)
+
+
+def test_quantize_per_token_scale():
+    vals = _e4m3_values()
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((6, 128)).astype(np.float32)
+    x[0] *= 1e-3
+    x[1] *= 1e3
+    x[2] = 0.0
+    x[3, :] = 0.5
+    x[3, 7] = 448.0 * 4.0            # amax exactly 448 * 2^2: e = 2
+    x[4, :] = 0.5
+    x[4, 9] = np.nextafter(np.float32(448.0 * 4.0), np.float32(1e9))  # just above: e = 3
+    codes, sc = oracle.quantize_keys(x, scaled=True)
+    e = sc.astype(np.int64) - 127
+    assert e[2] == 0 and np.all(codes[2] == 0)
+    assert e[3] == 2 and codes[3, 7] == 0x7E
+    assert e[4] == 3
+    for t in range(6):
+        amax = np.abs(x[t]).max()
+        if amax > 0:
+            assert amax <= 448.0 * 2.0 ** e[t] and amax > 448.0 * 2.0 ** (e[t] - 1)
+        deq = vals[codes[t]] * 2.0 ** e[t]
+        # the scaled codes are the unscaled quantisation of x / 2^e
+        assert np.array_equal(codes[t], oracle.quantize_keys((x[t] / np.float32(2.0 ** e[t]))[None, :])[0])
+        # relative error of normal values at most 2^-4 (3 mantissa bits, round to nearest)
+        big = np.abs(x[t]) >= 2.0 ** (e[t] - 6)
+        assert np.all(np.abs(deq[big] - x[t][big]) <= np.abs(x[t][big]) * 2.0 ** -4)
+
+
 # ---------------------------------------------------------------- end to end
 
 def test_forward_composes_the_steps_and_is_causal():

@@ -32,12 +32,12 @@ def lib():
         p, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         L.dsa_oracle_e4m3_value.argtypes = [i32]
         L.dsa_oracle_e4m3_value.restype = dbl
-        L.dsa_oracle_indexer.argtypes = [i32, p, p, i32, p, p, p, i32, p, i32, i32, i32, p, i64]
+        L.dsa_oracle_indexer.argtypes = [i32, p, p, i32, p, p, p, i32, p, p, i32, i32, i32, p, i64]
         L.dsa_oracle_topk.argtypes = [i32, p, p, i32, p, p, i64, i32, p]
         L.dsa_oracle_sparse_mla.argtypes = [i32, p, p, i32, p, p, p, i32, p, i32, i32, i32, i32, dbl, p, p]
         L.dsa_oracle_dense_mla.argtypes = [i32, p, p, i32, p, p, p, i32, i32, i32, i32, dbl, p, p]
         L.dsa_oracle_quantize_keys.argtypes = [p, i32, i64, i32, i32, p, p]
-        L.dsa_oracle_forward.argtypes = [i32, p, p, i32, p, p, p, i32, p, i32, i32, i32,
+        L.dsa_oracle_forward.argtypes = [i32, p, p, i32, p, p, p, i32, p, p, i32, i32, i32,
                                          p, p, i32, i32, i32, i32, dbl, i32, i64, p, p, p, p]
         for f in (L.dsa_oracle_indexer, L.dsa_oracle_topk, L.dsa_oracle_sparse_mla, L.dsa_oracle_dense_mla,
                   L.dsa_oracle_quantize_keys, L.dsa_oracle_forward):
@@ -74,8 +74,9 @@ def e4m3_value(code: int) -> float:
     return lib().dsa_oracle_e4m3_value(int(code))
 
 
-def indexer(cu_q, cu_k, q_idx, k_idx, w, act=ACT_RELU, ld=None, rows=None):
-    """Scores [nrows, ld] float64; entries s > pos are left at 0."""
+def indexer(cu_q, cu_k, q_idx, k_idx, w, act=ACT_RELU, ld=None, rows=None, k_scale=None):
+    """Scores [nrows, ld] float64; entries s > pos are left at 0.  `k_scale`:
+    optional E8M0 byte per key row (FP8 keys scaled by 2^(byte - 127))."""
     cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
     rows = _rows(rows, cu_q)
     q_idx, k_idx = np.ascontiguousarray(q_idx), np.ascontiguousarray(k_idx)
@@ -87,9 +88,13 @@ def indexer(cu_q, cu_k, q_idx, k_idx, w, act=ACT_RELU, ld=None, rows=None):
     assert w.shape == (nrows, H_I)
     if ld is None:
         ld = int(np.max(np.diff(cu_k)))
+    if k_scale is not None:
+        k_scale = _c(k_scale, np.uint8)
+        assert k_scale.shape == (k_idx.shape[0],)
     out = np.zeros((nrows, ld), dtype=np.float64)
     rc = lib().dsa_oracle_indexer(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), nrows, _ptr(rows),
-                                  _ptr(q_idx), _ptr(k_idx), dt, _ptr(w), H_I, d_I, act, _ptr(out), ld)
+                                  _ptr(q_idx), _ptr(k_idx), dt, _ptr(k_scale), _ptr(w), H_I, d_I, act,
+                                  _ptr(out), ld)
     if rc != 0:
         raise ValueError("oracle indexer: invalid batch / rows")
     return out
@@ -164,7 +169,7 @@ def quantize_keys(src, scaled=False):
     return (codes, scale) if scaled else codes
 
 
-def forward(cu_q, cu_k, q_idx, k_idx, w, q, kv, k, d_v, scale, act=ACT_RELU, rows=None, ld=None):
+def forward(cu_q, cu_k, q_idx, k_idx, w, q, kv, k, d_v, scale, act=ACT_RELU, rows=None, ld=None, k_scale=None):
     """Indexer -> fp32 rounding -> top-k -> sparse attention.
 
     Returns (out, lse, scores_f32, idx)."""
@@ -174,6 +179,8 @@ def forward(cu_q, cu_k, q_idx, k_idx, w, q, kv, k, d_v, scale, act=ACT_RELU, row
     nrows, H_I, d_I = q_idx.shape
     _, H, d_qk = q.shape
     w = _c(w, np.float32)
+    if k_scale is not None:
+        k_scale = _c(k_scale, np.uint8)
     if ld is None:
         ld = int(np.max(np.diff(cu_k)))
     out = np.zeros((nrows, H, d_v), dtype=np.float64)
@@ -181,7 +188,7 @@ def forward(cu_q, cu_k, q_idx, k_idx, w, q, kv, k, d_v, scale, act=ACT_RELU, row
     sc = np.zeros((nrows, ld), dtype=np.float32)
     idx = np.empty((nrows, k), dtype=np.int32)
     rc = lib().dsa_oracle_forward(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), nrows, _ptr(rows),
-                                  _ptr(q_idx), _ptr(k_idx), _dtype_code(q_idx), _ptr(w), H_I, d_I, act,
+                                  _ptr(q_idx), _ptr(k_idx), _dtype_code(q_idx), _ptr(k_scale), _ptr(w), H_I, d_I, act,
                                   _ptr(q), _ptr(kv), _dtype_code(q), H, d_qk, d_v, float(scale), k, ld,
                                   _ptr(out), _ptr(lse), _ptr(sc), _ptr(idx))
     if rc != 0:

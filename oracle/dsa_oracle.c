@@ -87,7 +87,9 @@ static int locate_row(int nseq, const int32_t* cu_q, const int32_t* cu_k, int32_
  * derived from the query token times a ReLU of the dot product of the head's
  * indexer query q_I[t,j] with the preceding token's indexer key k_I[s]; ReLU
  * was chosen for throughput.  [P2] 【闪电索引器】 names GELU instead; it is kept
- * as a switch (exact erf form).                                        */
+ * as a switch (exact erf form).  An FP8 key cache may carry a per-token
+ * power-of-two scale (E8M0 byte, see the quantisation below); the key is
+ * then value(code) * 2^(scale - 127).                                  */
 /* ------------------------------------------------------------------ */
 static double activation(double x, int act) {
     if (act == OR_ACT_GELU) return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));
@@ -96,7 +98,7 @@ static double activation(double x, int act) {
 
 int dsa_oracle_indexer(int nseq, const int32_t* cu_q, const int32_t* cu_k,
                        int nrows, const int32_t* rows,
-                       const void* q_idx, const void* k_idx, int dtype,
+                       const void* q_idx, const void* k_idx, int dtype, const uint8_t* k_scale,
                        const float* w, int H_I, int d_I, int act,
                        double* scores, int64_t ld) {
     double table[256];
@@ -108,12 +110,14 @@ int dsa_oracle_indexer(int nseq, const int32_t* cu_q, const int32_t* cu_k,
         if (locate_row(nseq, cu_q, cu_k, rows[i], &pos, &kbase) != 0 || pos + 1 > ld) { bad |= 1; continue; }
         double* out = scores + (int64_t)i * ld;
         for (int64_t s = 0; s <= pos; ++s) {
+            /* per-token key scale: the key is value(code) * 2^(scale - 127) */
+            const double ks = k_scale ? ldexp(1.0, (int)k_scale[kbase + s] - 127) : 1.0;
             double score = 0.0;
             for (int j = 0; j < H_I; ++j) {
                 double dot = 0.0;
                 for (int d = 0; d < d_I; ++d) {
                     double q = load_elem(q_idx, dtype, ((int64_t)i * H_I + j) * d_I + d, table);
-                    double k = load_elem(k_idx, dtype, (kbase + s) * d_I + d, table);
+                    double k = load_elem(k_idx, dtype, (kbase + s) * d_I + d, table) * ks;
                     dot += q * k;
                 }
                 score += (double)w[(int64_t)i * H_I + j] * activation(dot, act);
@@ -350,7 +354,7 @@ int dsa_oracle_dense_mla(int nseq, const int32_t* cu_q, const int32_t* cu_k,
 /* ------------------------------------------------------------------ */
 int dsa_oracle_forward(int nseq, const int32_t* cu_q, const int32_t* cu_k,
                        int nrows, const int32_t* rows,
-                       const void* q_idx, const void* k_idx, int idx_dtype,
+                       const void* q_idx, const void* k_idx, int idx_dtype, const uint8_t* k_scale,
                        const float* w, int H_I, int d_I, int act,
                        const void* q, const void* kv, int dtype,
                        int H, int d_qk, int d_v, double scale, int k,
@@ -362,7 +366,7 @@ int dsa_oracle_forward(int nseq, const int32_t* cu_q, const int32_t* cu_k,
     int rc = -1;
     if (!sc || !sf || !sel) goto done;
     for (int64_t e = 0; e < (int64_t)nrows * ld; ++e) sc[e] = 0.0;
-    if (dsa_oracle_indexer(nseq, cu_q, cu_k, nrows, rows, q_idx, k_idx, idx_dtype, w, H_I, d_I, act, sc, ld)) goto done;
+    if (dsa_oracle_indexer(nseq, cu_q, cu_k, nrows, rows, q_idx, k_idx, idx_dtype, k_scale, w, H_I, d_I, act, sc, ld)) goto done;
     for (int64_t e = 0; e < (int64_t)nrows * ld; ++e) sf[e] = (float)sc[e];
     if (dsa_oracle_topk(nseq, cu_q, cu_k, nrows, rows, sf, ld, k, sel)) goto done;
     if (dsa_oracle_sparse_mla(nseq, cu_q, cu_k, nrows, rows, q, kv, dtype, sel, k, H, d_qk, d_v, scale, out, lse)) goto done;

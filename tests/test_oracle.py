@@ -452,6 +452,46 @@ def test_quantize_per_token_scale():
         assert np.all(np.abs(deq[big] - x[t][big]) <= np.abs(x[t][big]) * 2.0 ** -4)
 
 
+def _fp8_keys_case(seed, n, d):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, (n, d)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C          # no NaN codes
+    return codes
+
+
+@pytest.mark.parametrize("act", [oracle.ACT_RELU, oracle.ACT_GELU])
+def test_scaled_fp8_keys_equal_their_dequantised_values(act):
+    """A key with E8M0 byte b is value(code) * 2^(b - 127): the scores of scaled
+    FP8 keys equal those of float32 keys holding exactly those values."""
+    vals = _e4m3_values()
+    cu_q, cu_k = _ragged([40, 23], [40, 5])
+    rng = np.random.default_rng(33)
+    kc = _fp8_keys_case(33, 63, 32)
+    qc = _fp8_keys_case(34, 45, 2 * 32).reshape(45, 2, 32)
+    sc = rng.integers(127 - 12, 127 + 12, 63).astype(np.uint8)
+    w = rng.standard_normal((45, 2)).astype(np.float32)
+    got = oracle.indexer(cu_q, cu_k, qc, kc, w, act=act, k_scale=sc)
+    kf = (vals[kc] * 2.0 ** (sc.astype(np.int64) - 127)[:, None]).astype(np.float32)
+    assert np.array_equal(kf.astype(np.float64), vals[kc] * 2.0 ** (sc.astype(np.int64) - 127)[:, None])
+    want = oracle.indexer(cu_q, cu_k, vals[qc].astype(np.float32), kf, w, act=act)
+    assert np.array_equal(got, want)
+    # scale byte 127 is the unscaled key
+    same = oracle.indexer(cu_q, cu_k, qc, kc, w, act=act, k_scale=np.full(63, 127, np.uint8))
+    assert np.array_equal(same, oracle.indexer(cu_q, cu_k, qc, kc, w, act=act))
+
+
+def test_relu_scores_are_homogeneous_in_the_key_scale():
+    """ReLU(2^e x) = 2^e ReLU(x): one scale for every key multiplies each score."""
+    cu_q, cu_k = _ragged([30], [30])
+    kc = _fp8_keys_case(35, 30, 16)
+    qc = _fp8_keys_case(36, 30, 3 * 16).reshape(30, 3, 16)
+    w = np.random.default_rng(36).standard_normal((30, 3)).astype(np.float32)
+    base = oracle.indexer(cu_q, cu_k, qc, kc, w)
+    for e in (-20, -1, 3, 17):
+        got = oracle.indexer(cu_q, cu_k, qc, kc, w, k_scale=np.full(30, 127 + e, np.uint8))
+        assert np.array_equal(got, base * 2.0 ** e)
+
+
 # ---------------------------------------------------------------- end to end
 
 def test_forward_composes_the_steps_and_is_causal():

@@ -250,8 +250,9 @@ int dsa_oracle_sparse_mla(int nseq, const int32_t* cu_q, const int32_t* cu_k,
  * largest finite value (448) saturate to it; NaN gives 0x7F; the sign is kept
  * (so values that round to zero give +0 or -0).
  * With per-token scaling each key row t gets the power of two 2^e_t with the
- * smallest e_t such that max_d |x[t,d]| <= 448 * 2^e_t (e_t = 0 for an
- * all-zero row, clamped to [-127, 127]); the codes encode x[t,d] / 2^e_t and
+ * smallest e_t such that max_d |x[t,d]| <= 448 * 2^e_t (NaN ignored; e_t = 0
+ * for an all-zero row; clamped to [-127, 127], so a row holding an infinity
+ * gets 127); the codes encode x[t,d] / 2^e_t and
  * the scale is stored as an E8M0 byte 127 + e_t, so the key is
  * value(code) * 2^e_t. */
 /* ------------------------------------------------------------------ */
@@ -285,7 +286,9 @@ int dsa_oracle_quantize_keys(const void* src, int dtype, int64_t n, int d, int s
                 const double v = fabs(load_elem(src, dtype, t * d + j, table));
                 if (v > amax) amax = v;  /* NaN never compares greater */
             }
-            if (amax > 0.0) {
+            if (isinf(amax)) {
+                e = 127;
+            } else if (amax > 0.0) {
                 int ex;
                 const double f = frexp(amax / 448.0, &ex);  /* amax / 448 = f 2^ex, f in [0.5, 1) */
                 e = (f == 0.5) ? ex - 1 : ex;               /* ceil(log2(amax / 448)) */

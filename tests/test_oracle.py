@@ -436,6 +436,11 @@ def test_quantize_per_token_scale():
     x[4, :] = 0.5
     x[4, 9] = np.nextafter(np.float32(448.0 * 4.0), np.float32(1e9))  # just above: e = 3
     codes, sc = oracle.quantize_keys(x, scaled=True)
+    # an infinity takes the largest scale; NaN takes no part in the maximum
+    y = np.array([[1.0, -np.inf, 2.0, np.nan], [np.nan, 448.0, -3.0, 1.0]], np.float32)
+    cy, sy = oracle.quantize_keys(y, scaled=True)
+    assert list(sy) == [127 + 127, 127] and list(cy[1]) == [0x7F, 0x7E, 0xC4, 0x38]
+    assert cy[0, 1] == 0xFE and cy[0, 3] == 0x7F and cy[0, 0] == 0x00
     e = sc.astype(np.int64) - 127
     assert e[2] == 0 and np.all(codes[2] == 0)
     assert e[3] == 2 and codes[3, 7] == 0x7E

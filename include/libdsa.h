@@ -102,6 +102,10 @@ const char* dsa_version(void);
  * ReLU(x) = (x + |x|) / 2); qt is carried as four E4M3 terms with power-of-two
  * scales per 32 elements, within about 2^-16 of each block's largest value.
  * Other batches (decode) apply the activation per head.
+ * k_idx_scale [total_k] uint8 E8M0, or NULL: FP8 keys with a per-token
+ *   power-of-two scale (as dsa_cache_append writes them); key s is then
+ *   value(k_idx[s, :]) * 2^(k_idx_scale[s] - 127).  The MFMA applies the
+ *   scale to each key's dot products, so the products stay exact.  FP8 only.
  * Workspace: dsa_indexer_workspace_size bytes (528 per query row for FP8 with
  * ReLU, else 0), 16-B aligned; ws may be NULL when that is 0; a smaller
  * workspace gives DSA_ERR_WORKSPACE.  The size needs no device.
@@ -112,6 +116,7 @@ dsa_status dsa_indexer_workspace_size(const dsa_batch* batch, dsa_dtype idx_dtyp
                                       dsa_act act, size_t* bytes /* host */);
 dsa_status dsa_indexer_scores(const dsa_batch* batch,
                               const void* q_idx, const void* k_idx, dsa_dtype idx_dtype,
+                              const uint8_t* k_idx_scale,
                               const float* w, int32_t H_I, int32_t d_I, dsa_act act,
                               float* scores, int64_t ld_scores,
                               void* ws, size_t ws_bytes, dsa_stream_t stream);
@@ -193,6 +198,39 @@ dsa_status dsa_dense_mla_attn(const dsa_batch* batch, const void* q, const void*
                               void* out, float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
 
 /*
+ * New tokens into the caches.  [P1] "Lightning indexer": the indexer runs in
+ * FP8, so the indexer key of every token is stored as E4M3 codes;
+ * "在MLA下實例化DSA": one latent row per token serves all query heads.  For
+ * each new token t < n, with d = dst_rows[t] (or t when dst_rows is NULL):
+ *   k_cache[d, :]  = E4M3FN(k_new[t, :] / 2^e_t)   (when k_new != NULL)
+ *   k_scale[d]     = 127 + e_t                      (when k_scale != NULL)
+ *   kv_cache[d, :] = kv_new[t, :]                   (when kv_new != NULL)
+ * E4M3FN(x): nearest value, ties to the even code, magnitudes above 448 give
+ * +-448, NaN gives 0x7F, the sign of x is kept (results that round to zero
+ * give +0 or -0).  e_t = 0 without k_scale; with it, e_t is the smallest
+ * integer with max_j |k_new[t, j]| <= 448 * 2^e_t (NaN ignored), clamped to
+ * [-127, 127], e_t = 0 for an all-zero row and 127 for a row holding an
+ * infinity.  Scaling by 2^-e_t is exact except for values that round to zero
+ * in E4M3 anyway.
+ *   k_new     [n, d_I]           k_dtype F32 or BF16, 16-B aligned
+ *   k_cache   [cache_rows, d_I]  uint8 E4M3FN codes, 8-B aligned
+ *   k_scale   [cache_rows]       uint8 E8M0, or NULL (unscaled codes)
+ *   kv_new    [n, d_qk]          kv_dtype (F32 or BF16), 16-B aligned; d_qk
+ *                                 times the element size a multiple of 16
+ *   kv_cache  [cache_rows, d_qk] kv_dtype, 16-B aligned
+ *   dst_rows  [n] int32 device, or NULL.  Tokens whose row lies outside
+ *             [0, cache_rows) are not written.  Two tokens with the same row
+ *             race (either result may stay).
+ * Supported: d_I in {64, 128, 256, 512}; n * d_qk * element size / 16 < 2^31.
+ * No workspace; the result is exact (bit-for-bit definition above).
+ */
+dsa_status dsa_cache_append(int64_t n, const int32_t* dst_rows, int64_t cache_rows,
+                            const void* k_new, dsa_dtype k_dtype, int32_t d_I,
+                            uint8_t* k_cache, uint8_t* k_scale,
+                            const void* kv_new, dsa_dtype kv_dtype, int32_t d_qk, void* kv_cache,
+                            dsa_stream_t stream);
+
+/*
  * The three steps fused in one call, on one stream, with no host
  * synchronisation.  Query rows are processed in chunks of q_block rows
  * (bounded score workspace).  Rows with pos + 1 <= k skip the indexer and the
@@ -204,6 +242,7 @@ typedef struct {
   const dsa_batch* batch;
   /* indexer */
   const void* q_idx; const void* k_idx; dsa_dtype idx_dtype;
+  const uint8_t* k_idx_scale;  /* [total_k] E8M0 per-token key scales (FP8), or NULL */
   const float* w; int32_t H_I; int32_t d_I; dsa_act act;
   /* attention */
   const void* q; const void* kv; dsa_dtype dtype;

@@ -156,11 +156,12 @@ dsa_status dsa_indexer_workspace_size(const dsa_batch* batch, dsa_dtype idx_dtyp
 }
 
 dsa_status dsa_indexer_scores(const dsa_batch* batch, const void* q_idx, const void* k_idx, dsa_dtype idx_dtype,
-                              const float* w, int32_t H_I, int32_t d_I, dsa_act act, float* scores,
-                              int64_t ld_scores, void* ws, size_t ws_bytes, dsa_stream_t stream) {
+                              const uint8_t* k_idx_scale, const float* w, int32_t H_I, int32_t d_I, dsa_act act,
+                              float* scores, int64_t ld_scores, void* ws, size_t ws_bytes, dsa_stream_t stream) {
   g_err[0] = 0;
   if (dsa_status s = check_batch(batch)) return s;
   if (dsa_status s = check_indexer(batch, q_idx, k_idx, idx_dtype, w, H_I, d_I, act)) return s;
+  if (k_idx_scale && idx_dtype != DSA_FP8_E4M3) return fail(DSA_ERR_INVALID_ARG, "k_idx_scale needs FP8 keys");
   if (dsa_status s = check_scores(batch, scores, ld_scores)) return s;
   const size_t need = dsa::indexer_workspace_bytes(batch->total_q, idx_dtype == DSA_FP8_E4M3, (int)act);
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
@@ -170,6 +171,7 @@ dsa_status dsa_indexer_scores(const dsa_batch* batch, const void* q_idx, const v
   if (dsa_status s = device_cus(&cus)) return s;
   dsa::IndexerLaunch L{view(batch, 0, batch->total_q), 0, q_idx, k_idx, w, scores, ld_scores, H_I, d_I, (int32_t)act,
                        idx_dtype == DSA_FP8_E4M3, cus, need > 0 ? ws : nullptr};
+  L.k_scale = k_idx_scale;
   hipError_t e = dsa::launch_indexer(L, (hipStream_t)stream);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "indexer launch");
 }
@@ -286,6 +288,48 @@ dsa_status dsa_dense_mla_attn(const dsa_batch* batch, const void* q, const void*
   return e == hipSuccess ? DSA_OK : hip_fail(e, "dense attention launch");
 }
 
+dsa_status dsa_cache_append(int64_t n, const int32_t* dst_rows, int64_t cache_rows, const void* k_new,
+                            dsa_dtype k_dtype, int32_t d_I, uint8_t* k_cache, uint8_t* k_scale, const void* kv_new,
+                            dsa_dtype kv_dtype, int32_t d_qk, void* kv_cache, dsa_stream_t stream) {
+  g_err[0] = 0;
+  if (n < 0 || cache_rows < 0) return fail(DSA_ERR_INVALID_ARG, "n = %lld, cache_rows = %lld", (long long)n,
+                                          (long long)cache_rows);
+  dsa::AppendLaunch L{};
+  L.n = n;
+  L.dst = dst_rows;
+  L.cache_rows = cache_rows;
+  if (k_new) {
+    if (k_dtype != DSA_F32 && k_dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "k_new must be F32 or BF16");
+    if (d_I != 64 && d_I != 128 && d_I != 256 && d_I != 512)
+      return fail(DSA_ERR_UNSUPPORTED, "d_I = %d not in {64, 128, 256, 512}", d_I);
+    if (!k_cache) return fail(DSA_ERR_INVALID_ARG, "k_cache is NULL");
+    if (!aligned16(k_new) || (reinterpret_cast<uintptr_t>(k_cache) & 7u))
+      return fail(DSA_ERR_INVALID_ARG, "k_new must be 16-byte and k_cache 8-byte aligned");
+    L.k_new = k_new;
+    L.k_bf16 = k_dtype == DSA_BF16;
+    L.d_I = d_I;
+    L.k_cache = k_cache;
+    L.k_scale = k_scale;
+  } else if (k_scale) {
+    return fail(DSA_ERR_INVALID_ARG, "k_scale without k_new");
+  }
+  if (kv_new) {
+    if (kv_dtype != DSA_F32 && kv_dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "kv_new must be F32 or BF16");
+    const int64_t row_bytes = (int64_t)d_qk * (kv_dtype == DSA_F32 ? 4 : 2);
+    if (d_qk < 1 || row_bytes % 16) return fail(DSA_ERR_INVALID_ARG, "latent row of %lld bytes is not a multiple of 16",
+                                                (long long)row_bytes);
+    if (!kv_cache || !aligned16(kv_new) || !aligned16(kv_cache))
+      return fail(DSA_ERR_INVALID_ARG, "kv_new / kv_cache NULL or not 16-byte aligned");
+    if (n * (row_bytes / 16) >= (1LL << 31)) return fail(DSA_ERR_UNSUPPORTED, "latent part too large for one call");
+    L.kv_new = kv_new;
+    L.kv_cache = kv_cache;
+    L.kv_row_bytes = row_bytes;
+  }
+  if (n == 0 || (!k_new && !kv_new)) return DSA_OK;
+  hipError_t e = dsa::launch_cache_append(L, (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "cache append launch");
+}
+
 }  // extern "C"
 
 namespace {
@@ -301,6 +345,8 @@ dsa_status check_forward(const dsa_forward_params* p) {
   if (!p) return fail(DSA_ERR_INVALID_ARG, "params is NULL");
   if (dsa_status s = check_batch(p->batch)) return s;
   if (dsa_status s = check_indexer(p->batch, p->q_idx, p->k_idx, p->idx_dtype, p->w, p->H_I, p->d_I, p->act)) return s;
+  if (p->k_idx_scale && p->idx_dtype != DSA_FP8_E4M3)
+    return fail(DSA_ERR_INVALID_ARG, "k_idx_scale needs FP8 keys");
   if (p->q_block < 0) return fail(DSA_ERR_INVALID_ARG, "q_block = %d < 0", p->q_block);
   if (p->out_idx && !aligned16(p->out_idx)) return fail(DSA_ERR_INVALID_ARG, "out_idx must be 16-byte aligned");
   // idx pointer is internal (workspace or out_idx); check the rest with a placeholder
@@ -377,6 +423,7 @@ dsa_status dsa_forward(const dsa_forward_params* p, void* ws, size_t ws_bytes, d
     // rows with pos + 1 <= k select every candidate: their scores are never read
     dsa::IndexerLaunch IL{v, p->k, p->q_idx, p->k_idx, p->w, scores, f.ld, p->H_I, p->d_I, (int32_t)p->act,
                           p->idx_dtype == DSA_FP8_E4M3, cus, base + f.off_lin};
+    IL.k_scale = p->k_idx_scale;
     hipError_t e = dsa::launch_indexer(IL, st);
     if (e != hipSuccess) return hip_fail(e, "forward indexer launch");
     dsa::TopkLaunch TL{v, scores, f.ld, p->k, idx, base + f.off_topk, cus};

@@ -31,6 +31,7 @@ struct IndexerLaunch {
   bool fp8;
   int32_t num_cus;
   void* ws;                // indexer_workspace_bytes(rows, fp8, act) bytes, or null when that is 0
+  const uint8_t* k_scale = nullptr;  // [total_k] E8M0 per-key scales (FP8), or null
 };
 
 struct TopkLaunch {
@@ -61,7 +62,24 @@ struct AttnLaunch {
   bool dense_short = false;  // rows with pos + 1 <= k walk [0, pos] without reading idx
 };
 
+// New tokens into the caches: indexer keys quantised to E4M3 (optionally with
+// per-token E8M0 scales), latent rows copied.  Either part may be absent.
+struct AppendLaunch {
+  int64_t n;               // new tokens
+  const int32_t* dst;      // [n] cache rows, or null (token t -> row t)
+  int64_t cache_rows;      // rows outside [0, cache_rows) are not written
+  const void* k_new;       // [n, d_I] fp32 or bf16, or null
+  bool k_bf16;
+  int32_t d_I;             // 64, 128, 256 or 512
+  uint8_t* k_cache;        // [cache_rows, d_I]
+  uint8_t* k_scale;        // [cache_rows] or null (unscaled)
+  const void* kv_new;      // [n, kv_row_bytes], or null
+  void* kv_cache;          // [cache_rows, kv_row_bytes]
+  int64_t kv_row_bytes;    // multiple of 16
+};
+
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s);
+hipError_t launch_cache_append(const AppendLaunch& a, hipStream_t s);
 
 // Workspace of the indexer for `rows` query rows (the FP8 ReLU path keeps the
 // linear-term fragments of every row there).

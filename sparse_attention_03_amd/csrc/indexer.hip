@@ -69,6 +69,7 @@ struct IdxArgs {
   int32_t H_I;
   const uint8_t* lin;      // [row_end - row_begin, kLinRowBytes] linear-term fragments (ReLU)
   uint8_t* lin_out;
+  const uint8_t* k_scale;  // [total_k] E8M0 per-key scales, or null
 };
 
 __device__ __forceinline__ float bits_f(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -150,8 +151,10 @@ enum KeySource {
 // NR query rows of one sequence against keys [kstart, kend); lim[i]: row i's
 // scores are stored for keys below lim[i] only.  LIN: ReLU through the
 // linear-term MFMA and |x| (rows need the pre-pass fragments); otherwise the
-// activation is applied per head.
-template <int NR, int NHT, int ACT, int KEYS, bool LIN = ACT == 0>
+// activation is applied per head.  SC: every key carries an E8M0 scale, which
+// goes into the MFMA's B-operand scale (lane (g, li) of sub-tile st: key
+// 16 st + li); the scales of the next slab are loaded one slab ahead.
+template <int NR, int NHT, int ACT, int KEYS, bool SC, bool LIN = ACT == 0>
 __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)[NR], const int32_t (&lim)[NR],
                                          int32_t kbase, int32_t kstart, int32_t kend, DSA_LDS uint8_t* ring) {
   static_assert(!LIN || ACT == 0, "the linear-term split is ReLU's");
@@ -199,6 +202,19 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
     srs[i] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.scores + (int64_t)(rows[i] - a.row_begin) * a.ld), 0,
                                                lim[i] * 4, kBufFlags);
   const int svo = (16 * g + li) * 4;
+  // per-key scales: [kbase, kbase + kend) in range; past it reads 0 (those scores are dropped)
+  __amdgpu_buffer_rsrc_t ksrs;
+  if constexpr (SC) ksrs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_scale + kbase), 0, kend, kBufFlags);
+  auto load_scales = [&](int32_t s0, int (&ks)[NST]) {
+    if constexpr (SC) {
+      const int so = __builtin_amdgcn_readfirstlane(s0);
+#pragma unroll
+      for (int st = 0; st < NST; ++st) ks[st] = __builtin_amdgcn_raw_buffer_load_b8(ksrs, li + 16 * st, so, 0);
+    } else {
+#pragma unroll
+      for (int st = 0; st < NST; ++st) ks[st] = 127;
+    }
+  };
 
   // LDS ring (SHARED), chunk-major: 16-byte chunk c of slab key row r sits at
   // byte (64 c + r) * 16.  Copy instruction c of a slab fills chunk column c
@@ -235,8 +251,8 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
     }
   };
 
-  // One 64-key slab with the keys in kf.
-  auto slab = [&](int32_t s0, const i32x8 (&kf)[NST]) {
+  // One 64-key slab with the keys in kf and their scales in ks.
+  auto slab = [&](int32_t s0, const i32x8 (&kf)[NST], const int (&ks)[NST]) {
     float acc[NST][NR];
     f32x4 x[LAG + 1];
 #pragma unroll
@@ -245,12 +261,12 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
         const int st = j / NPS, u = j % NPS;
         if (LIN && u == 0) {
           x[j % (LAG + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(lf, kf[st], f32x4{0.f, 0.f, 0.f, 0.f},
-                                                                              0, 0, 0, lscale, 0, 127);
+                                                                              0, 0, 0, lscale, 0, SC ? ks[st] : 127);
         } else {
           const int v = u - (LIN ? 1 : 0), i = v / NHT, ht = v % NHT;
           x[j % (LAG + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[i][ht], kf[st],
                                                                               f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127,
-                                                                              0, 127);
+                                                                              0, SC ? ks[st] : 127);
         }
       }
       if (j >= LAG) {
@@ -292,18 +308,28 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
     // stores of n-2, the copies of n+1 and the stores of n-1), barrier (every
     // wave's copies landed, every wave done reading slab n-1), copy slab n+2
     // into the slot slab n-1 used, read and compute slab n
+    // (the scale loads of slab n + 1 go out before the copies of slab n + 2,
+    // so waiting for them never waits for copies issued later)
+    int ks[NST], ksn[NST];
+    load_scales(kstart, ks);
     copy_slab(kstart, 0);
     copy_slab(kstart + 64, 1);
     int slot = 0, n = 0;
     for (int32_t s0 = kstart; s0 < kend; s0 += 64, ++n) {
+      constexpr int X = SC ? NST : 0;  // scale loads issued after the copies of slab n
       if (n == 0) wait_vmcnt<2>();
-      else if (n == 1) wait_vmcnt<2 + NR>();
-      else wait_vmcnt<2 + 2 * NR>();
+      else if (n == 1) wait_vmcnt<2 + NR + X>();
+      else wait_vmcnt<2 + 2 * NR + X>();
       lds_barrier();
+      if constexpr (SC) load_scales(s0 + 64, ksn);
       copy_slab(s0 + 128, slot == 0 ? 2 : slot - 1);
       i32x8 kf[NST];
       read_keys(slot, kf);
-      slab(s0, kf);
+      slab(s0, kf, ks);
+      if constexpr (SC) {
+#pragma unroll
+        for (int st = 0; st < NST; ++st) ks[st] = ksn[st];
+      }
       slot = slot == 2 ? 0 : slot + 1;
     }
   } else if constexpr (KEYS == kKeysPrivate) {
@@ -320,26 +346,36 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
       for (int c = 0; c < 8; ++c)
         __builtin_amdgcn_global_load_lds((const void*)(src + 16 * c), (DSA_LDS void*)(dst + 1024 * c), 16, 0, 0);
     };
+    int ks[NST], ksn[NST];
+    load_scales(kstart, ks);
 #pragma unroll
     for (int j = 0; j < P - 1; ++j) copy_own(kstart + 64 * j, j);
     int n = 0;
     for (int32_t s0 = kstart; s0 < kend; s0 += 64, ++n) {
       static_assert(P == 4, "the counted waits below assume four slots");
+      constexpr int X = SC ? NST : 0;  // scale loads per slab, issued ahead of its copies
       if (n == 0) wait_vmcnt<8 * (P - 2)>();
-      else if (n == 1) wait_vmcnt<8 * (P - 2) + NR>();
-      else if (n == 2) wait_vmcnt<8 * (P - 2) + 2 * NR>();
-      else wait_vmcnt<8 * (P - 2) + 3 * NR>();
+      else if (n == 1) wait_vmcnt<8 * (P - 2) + NR + X>();
+      else if (n == 2) wait_vmcnt<8 * (P - 2) + 2 * NR + 2 * X>();
+      else wait_vmcnt<8 * (P - 2) + 3 * NR + 2 * X>();
+      if constexpr (SC) load_scales(s0 + 64, ksn);
       copy_own(s0 + 64 * (P - 1), (n + P - 1) % P);  // the slot slab n - 1 used, read before this point
       i32x8 kf[NST];
       read_keys(n % P, kf);
-      slab(s0, kf);
+      slab(s0, kf, ks);
+      if constexpr (SC) {
+#pragma unroll
+        for (int st = 0; st < NST; ++st) ks[st] = ksn[st];
+      }
     }
     wait_vmcnt<0>();  // no copy into LDS outlives the wave
   } else {
     for (int32_t s0 = kstart; s0 < kend; s0 += 64) {
       i32x8 kf[NST];
+      int ks[NST];
       load_keys(s0, kf);
-      slab(s0, kf);
+      load_scales(s0, ks);
+      slab(s0, kf, ks);
     }
   }
 }
@@ -347,7 +383,7 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
 // Prefill-like batches: workgroups whose eight rows are one sequence's share
 // the keys through an LDS ring; workgroups whose rows span two sequences fall
 // back to the lean per-wave path.
-template <int NHT, int ACT>
+template <int NHT, int ACT, bool SC>
 __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(IdxArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kSlabBytes];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -384,7 +420,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(IdxArgs a) {
       rows[i] = min(rb + j, a.row_end - 1);
       lim[i] = __builtin_amdgcn_readfirstlane(live[j] ? min(kchunk_end, pos[j] + 1) : 0);
     }
-    fp8_rows<2, NHT, ACT, kKeysShared>(a, rows, lim, kb[0], kstart, kend_blk, (DSA_LDS uint8_t*)ring);
+    fp8_rows<2, NHT, ACT, kKeysShared, SC>(a, rows, lim, kb[0], kstart, kend_blk, (DSA_LDS uint8_t*)ring);
     return;
   }
   // rows of several sequences: each wave on its own
@@ -400,15 +436,14 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(IdxArgs a) {
   if (v[0] && v[1] && k[0] == k[1]) {
     const int32_t rows[2] = {rb + j0, rb + j0 + 1};
     const int32_t lim[2] = {l[0], l[1]};
-    fp8_rows<2, NHT, ACT, kKeysPlain>(a, rows, lim, k[0], kstart, max(l[0], l[1]),
-                                                               nullptr);
+    fp8_rows<2, NHT, ACT, kKeysPlain, SC>(a, rows, lim, k[0], kstart, max(l[0], l[1]), nullptr);
   } else {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if (!v[i]) continue;
       const int32_t r1[1] = {rb + j0 + i};
       const int32_t l1[1] = {l[i]};
-      fp8_rows<1, NHT, ACT, kKeysPlain>(a, r1, l1, k[i], kstart, l[i], nullptr);
+      fp8_rows<1, NHT, ACT, kKeysPlain, SC>(a, r1, l1, k[i], kstart, l[i], nullptr);
     }
   }
 }
@@ -418,7 +453,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(IdxArgs a) {
 // through its own LDS ring, so it needs no barrier and returns on its own.
 // The path is bound by the key bytes, so the activation is applied per head
 // (no linear-term pre-pass).
-template <int NHT, int ACT>
+template <int NHT, int ACT, bool SC>
 __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_stream_kernel(IdxArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t pring[];  // kStreamRows x kPrivSlots slabs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -430,7 +465,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_stream_kernel(IdxArgs
   if (r >= a.row_end || pos < kstart || pos + 1 <= a.skip_n) return;
   const int32_t kend = min(kstart + a.key_chunk, pos + 1);
   const int32_t rows[1] = {r}, lim[1] = {kend};
-  fp8_rows<1, NHT, ACT, kKeysPrivate, false>(a, rows, lim, __builtin_amdgcn_readfirstlane(ri.kbase), kstart, kend,
+  fp8_rows<1, NHT, ACT, kKeysPrivate, SC, false>(a, rows, lim, __builtin_amdgcn_readfirstlane(ri.kbase), kstart, kend,
                                              (DSA_LDS uint8_t*)pring + wave * kPrivSlots * kSlabBytes);
 }
 
@@ -465,28 +500,35 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(IdxArgs a, int d_I) {
 
 template <int NHT>
 hipError_t launch_fp8(const IdxArgs& a, int act, dim3 grid, hipStream_t s) {
-  if (act == 0) hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 0>), grid, dim3(kIdxThreads), 0, s, a);
-  else hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 1>), grid, dim3(kIdxThreads), 0, s, a);
+  const bool sc = a.k_scale != nullptr;
+  if (act == 0) {
+    if (sc) hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 0, true>), grid, dim3(kIdxThreads), 0, s, a);
+    else hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 0, false>), grid, dim3(kIdxThreads), 0, s, a);
+  } else {
+    if (sc) hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 1, true>), grid, dim3(kIdxThreads), 0, s, a);
+    else hipLaunchKernelGGL((indexer_fp8_kernel<NHT, 1, false>), grid, dim3(kIdxThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
-template <int NHT, int ACT>
+template <int NHT, int ACT, bool SC>
 hipError_t launch_stream_act(const IdxArgs& a, dim3 grid, hipStream_t s) {
   constexpr size_t lds = (size_t)kStreamRows * kPrivSlots * kSlabBytes;  // 128 KB
   static bool attr_set = false;  // benign race: idempotent attribute call
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)indexer_fp8_stream_kernel<NHT, ACT>,
+    hipError_t e = hipFuncSetAttribute((const void*)indexer_fp8_stream_kernel<NHT, ACT, SC>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((indexer_fp8_stream_kernel<NHT, ACT>), grid, dim3(kIdxThreads), lds, s, a);
+  hipLaunchKernelGGL((indexer_fp8_stream_kernel<NHT, ACT, SC>), grid, dim3(kIdxThreads), lds, s, a);
   return hipGetLastError();
 }
 
 template <int NHT>
 hipError_t launch_stream(const IdxArgs& a, int act, dim3 grid, hipStream_t s) {
-  return act == 0 ? launch_stream_act<NHT, 0>(a, grid, s) : launch_stream_act<NHT, 1>(a, grid, s);
+  if (a.k_scale) return act == 0 ? launch_stream_act<NHT, 0, true>(a, grid, s) : launch_stream_act<NHT, 1, true>(a, grid, s);
+  return act == 0 ? launch_stream_act<NHT, 0, false>(a, grid, s) : launch_stream_act<NHT, 1, false>(a, grid, s);
 }
 
 }  // namespace
@@ -514,6 +556,7 @@ hipError_t launch_indexer(const IndexerLaunch& L, hipStream_t s) {
   a.H_I = L.H_I;
   a.lin = (const uint8_t*)L.ws;
   a.lin_out = (uint8_t*)L.ws;
+  a.k_scale = L.fp8 ? L.k_scale : nullptr;
   if (L.fp8) {
     // prefill-like batches (sequences of many query rows): workgroups of eight
     // rows share their keys; otherwise every row streams its own

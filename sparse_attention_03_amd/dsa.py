@@ -22,7 +22,8 @@ def indexer_scores(p, act=L.DSA_ACT_RELU, ld=None, fill=float("nan")):
     scores = torch.full((p.total_q, ld), fill, dtype=torch.float32, device=p.q_idx.device)
     b = L.batch_of(p)
     n = L.dsa_indexer_workspace_size(b, p.q_idx, act)
-    L.dsa_indexer_scores(b, p.q_idx, p.k_idx, p.w, scores, act=act, ws=_ws(n, scores.device) if n else None)
+    L.dsa_indexer_scores(b, p.q_idx, p.k_idx, p.w, scores, act=act, ws=_ws(n, scores.device) if n else None,
+                         k_idx_scale=p.k_idx_scale)
     return scores
 
 
@@ -69,12 +70,20 @@ class Forward:
         self.idx = torch.empty((p.total_q, p.k), dtype=torch.int32, device=dev) if with_idx else None
         qb = p.q_block if q_block is None else q_block
         self.params = L.forward_params(self.batch, p.q_idx, p.k_idx, p.w, p.q, p.kv, p.k, p.d_v, p.scale,
-                                       self.out, self.lse, self.idx, act=act, q_block=qb)
+                                       self.out, self.lse, self.idx, act=act, q_block=qb,
+                                       k_idx_scale=p.k_idx_scale)
         self.ws = _ws(L.dsa_forward_workspace_size(self.params), dev)
 
     def __call__(self, stream=None):
         L.dsa_forward(self.params, self.ws, stream=stream)
         return self.out, self.lse, self.idx
+
+
+def cache_append(k_new=None, k_cache=None, k_scale=None, kv_new=None, kv_cache=None, dst_rows=None):
+    """Write new tokens into the caches (indexer keys quantised to E4M3, optional
+    per-token E8M0 scales; latent rows copied); see dsa_cache_append."""
+    L.dsa_cache_append(k_new=k_new, k_cache=k_cache, k_scale=k_scale, kv_new=kv_new, kv_cache=kv_cache,
+                       dst_rows=dst_rows)
 
 
 def forward(p, act=L.DSA_ACT_RELU, q_block=None):

@@ -53,6 +53,7 @@ class DSAInputs:
     scale: float
     q_block: int = 0
     meta: dict = field(default_factory=dict)
+    k_idx_scale: torch.Tensor | None = None   # uint8 [total_k] E8M0 per-token key scales, or None
 
     @property
     def total_q(self) -> int:

@@ -34,7 +34,7 @@ class DsaBatch(ctypes.Structure):
 
 class DsaForwardParams(ctypes.Structure):
     _fields_ = [("batch", ctypes.POINTER(DsaBatch)),
-                ("q_idx", _p), ("k_idx", _p), ("idx_dtype", ctypes.c_int), ("w", _p),
+                ("q_idx", _p), ("k_idx", _p), ("idx_dtype", ctypes.c_int), ("k_idx_scale", _p), ("w", _p),
                 ("H_I", _i32), ("d_I", _i32), ("act", ctypes.c_int),
                 ("q", _p), ("kv", _p), ("dtype", ctypes.c_int),
                 ("H", _i32), ("d_qk", _i32), ("d_v", _i32), ("softmax_scale", _f32),
@@ -49,7 +49,7 @@ _SIGS = {
     "dsa_last_error": ([], ctypes.c_char_p),
     "dsa_version": ([], ctypes.c_char_p),
     "dsa_indexer_workspace_size": ([_BP, ctypes.c_int, _i32, _i32, ctypes.c_int, ctypes.POINTER(_sz)], ctypes.c_int),
-    "dsa_indexer_scores": ([_BP, _p, _p, ctypes.c_int, _p, _i32, _i32, ctypes.c_int, _p, _i64, _p, _sz, _p],
+    "dsa_indexer_scores": ([_BP, _p, _p, ctypes.c_int, _p, _p, _i32, _i32, ctypes.c_int, _p, _i64, _p, _sz, _p],
                            ctypes.c_int),
     "dsa_topk_workspace_size": ([_BP, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
     "dsa_topk": ([_BP, _p, _i64, _i32, _p, _p, _sz, _p], ctypes.c_int),
@@ -58,6 +58,8 @@ _SIGS = {
                             ctypes.c_int),
     "dsa_dense_mla_attn_workspace_size": ([_BP, ctypes.c_int, _i32, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
     "dsa_dense_mla_attn": ([_BP, _p, _p, ctypes.c_int, _i32, _i32, _i32, _f32, _p, _p, _p, _sz, _p], ctypes.c_int),
+    "dsa_cache_append": ([_i64, _p, _i64, _p, ctypes.c_int, _i32, _p, _p, _p, ctypes.c_int, _i32, _p, _p],
+                         ctypes.c_int),
     "dsa_forward_workspace_size": ([_FP, ctypes.POINTER(_sz)], ctypes.c_int),
     "dsa_forward": ([_FP, _p, _sz, _p], ctypes.c_int),
 }
@@ -118,8 +120,10 @@ def dsa_indexer_workspace_size(batch: DsaBatch, q_idx, act=DSA_ACT_RELU) -> int:
     return n.value
 
 
-def dsa_indexer_scores(batch: DsaBatch, q_idx, k_idx, w, scores, act=DSA_ACT_RELU, ws=None, stream=None):
-    _check(_lib.dsa_indexer_scores(ctypes.byref(batch), _ptr(q_idx), _ptr(k_idx), _dtype_code(q_idx), _ptr(w),
+def dsa_indexer_scores(batch: DsaBatch, q_idx, k_idx, w, scores, act=DSA_ACT_RELU, ws=None, stream=None,
+                       k_idx_scale=None):
+    _check(_lib.dsa_indexer_scores(ctypes.byref(batch), _ptr(q_idx), _ptr(k_idx), _dtype_code(q_idx),
+                                   _ptr(k_idx_scale), _ptr(w),
                                    q_idx.shape[1], q_idx.shape[2], act, _ptr(scores), scores.stride(0), _ptr(ws),
                                    0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
            "dsa_indexer_scores")
@@ -166,10 +170,11 @@ def dsa_dense_mla_attn(batch: DsaBatch, q, kv, d_v: int, softmax_scale: float, o
 
 
 def forward_params(batch: DsaBatch, q_idx, k_idx, w, q, kv, k: int, d_v: int, softmax_scale: float, out,
-                   lse=None, out_idx=None, act=DSA_ACT_RELU, q_block=0) -> DsaForwardParams:
+                   lse=None, out_idx=None, act=DSA_ACT_RELU, q_block=0, k_idx_scale=None) -> DsaForwardParams:
     p = DsaForwardParams()
     p.batch = ctypes.pointer(batch)
     p.q_idx, p.k_idx, p.idx_dtype, p.w = q_idx.data_ptr(), k_idx.data_ptr(), _dtype_code(q_idx), w.data_ptr()
+    p.k_idx_scale = None if k_idx_scale is None else k_idx_scale.data_ptr()
     p.H_I, p.d_I, p.act = q_idx.shape[1], q_idx.shape[2], act
     p.q, p.kv, p.dtype = q.data_ptr(), kv.data_ptr(), _dtype_code(q)
     p.H, p.d_qk, p.d_v, p.softmax_scale = q.shape[1], q.shape[2], d_v, float(softmax_scale)
@@ -178,6 +183,23 @@ def forward_params(batch: DsaBatch, q_idx, k_idx, w, q, kv, k: int, d_v: int, so
     p.lse = None if lse is None else lse.data_ptr()
     p.out_idx = None if out_idx is None else out_idx.data_ptr()
     return p
+
+
+def dsa_cache_append(k_new=None, k_cache=None, k_scale=None, kv_new=None, kv_cache=None, dst_rows=None,
+                     stream=None):
+    """New tokens into the caches: k_new [n, d_I] (fp32/bf16) -> k_cache [rows, d_I]
+    (uint8 E4M3 codes) and k_scale [rows] (uint8 E8M0, optional); kv_new [n, d_qk]
+    -> kv_cache [rows, d_qk]; dst_rows [n] int32 (None: token t -> row t)."""
+    n = (k_new if k_new is not None else kv_new).shape[0]
+    cache_rows = (k_cache if k_new is not None else kv_cache).shape[0]
+    if k_new is not None and kv_new is not None:
+        assert kv_new.shape[0] == n and kv_cache.shape[0] == cache_rows
+    _check(_lib.dsa_cache_append(n, _ptr(dst_rows), cache_rows,
+                                 _ptr(k_new), DSA_F32 if k_new is None else _dtype_code(k_new),
+                                 0 if k_new is None else k_new.shape[1], _ptr(k_cache), _ptr(k_scale),
+                                 _ptr(kv_new), DSA_BF16 if kv_new is None else _dtype_code(kv_new),
+                                 0 if kv_new is None else kv_new.shape[1], _ptr(kv_cache), _stream(stream)),
+           "dsa_cache_append")
 
 
 def dsa_forward_workspace_size(params: DsaForwardParams) -> int:

@@ -75,8 +75,8 @@ def _batch(L, cu=0x1000, total_q=8, total_k=8, max_ctx=8, nseq=1):
     return b
 
 
-def _call_indexer(L, b, q=0x10000, k=0x20000, w=0x30000, s=0x40000, H_I=64, d_I=128, dt=2, act=0, ld=64):
-    return L._lib.dsa_indexer_scores(ctypes.byref(b), q, k, dt, w, H_I, d_I, act, s, ld, 0x50000, 1 << 20, None)
+def _call_indexer(L, b, q=0x10000, k=0x20000, w=0x30000, s=0x40000, H_I=64, d_I=128, dt=2, act=0, ld=64, ks=None):
+    return L._lib.dsa_indexer_scores(ctypes.byref(b), q, k, dt, ks, w, H_I, d_I, act, s, ld, 0x50000, 1 << 20, None)
 
 
 def test_indexer_validation(L):
@@ -94,13 +94,14 @@ def test_indexer_validation(L):
     assert _call_indexer(L, _batch(L, cu=0)) == L.DSA_ERR_INVALID_ARG
     assert _call_indexer(L, _batch(L, max_ctx=9)) == L.DSA_ERR_INVALID_ARG  # > total_k
     assert _call_indexer(L, _batch(L, total_q=9)) == L.DSA_ERR_INVALID_ARG  # more queries than keys
-    assert L._lib.dsa_indexer_scores(None, 0x10000, 0x20000, 2, 0x30000, 64, 128, 0, 0x40000, 64, None, 0, None) \
-        == L.DSA_ERR_INVALID_ARG
+    assert _call_indexer(L, b, dt=0, H_I=8, d_I=32, ks=0x60000) == L.DSA_ERR_INVALID_ARG  # scales need FP8 keys
+    assert L._lib.dsa_indexer_scores(None, 0x10000, 0x20000, 2, None, 0x30000, 64, 128, 0, 0x40000, 64, None, 0,
+                                     None) == L.DSA_ERR_INVALID_ARG
     # FP8 + ReLU keeps 528 bytes per query row in the workspace; GELU and F32 need none
     f = L._lib.dsa_indexer_scores
-    assert f(ctypes.byref(b), 0x10000, 0x20000, 2, 0x30000, 64, 128, 0, 0x40000, 64, None, 0, None) \
+    assert f(ctypes.byref(b), 0x10000, 0x20000, 2, None, 0x30000, 64, 128, 0, 0x40000, 64, None, 0, None) \
         == L.DSA_ERR_WORKSPACE
-    assert f(ctypes.byref(b), 0x10000, 0x20000, 2, 0x30000, 64, 128, 0, 0x40000, 64, 0x50000, 100, None) \
+    assert f(ctypes.byref(b), 0x10000, 0x20000, 2, None, 0x30000, 64, 128, 0, 0x40000, 64, 0x50000, 100, None) \
         == L.DSA_ERR_WORKSPACE
     n = ctypes.c_size_t(123)
     assert L._lib.dsa_indexer_workspace_size(ctypes.byref(b), 2, 64, 128, 0, ctypes.byref(n)) == L.DSA_OK
@@ -141,6 +142,31 @@ def test_attention_validation(L):
     assert call(dt=0, dqk=2048) == L.DSA_ERR_UNSUPPORTED
 
 
+def test_cache_append_validation(L):
+    f = L._lib.dsa_cache_append
+
+    def call(n=4, dst=None, rows=16, kn=0x10000, kdt=0, dI=128, kc=0x20000, ks=None, vn=0x30000, vdt=1, dqk=576,
+             vc=0x40000):
+        return f(n, dst, rows, kn, kdt, dI, kc, ks, vn, vdt, dqk, vc, None)
+
+    assert call(n=-1) == L.DSA_ERR_INVALID_ARG
+    assert call(rows=-1) == L.DSA_ERR_INVALID_ARG
+    assert call(kdt=2) == L.DSA_ERR_UNSUPPORTED              # keys come in as F32 or BF16
+    assert call(dI=96) == L.DSA_ERR_UNSUPPORTED
+    assert call(kc=0) == L.DSA_ERR_INVALID_ARG
+    assert call(kn=0x10008) == L.DSA_ERR_INVALID_ARG         # k_new 16-byte aligned
+    assert call(kc=0x20004) == L.DSA_ERR_INVALID_ARG         # k_cache 8-byte aligned
+    assert call(kn=None, ks=0x50000) == L.DSA_ERR_INVALID_ARG
+    assert call(vdt=2) == L.DSA_ERR_UNSUPPORTED
+    assert call(dqk=100) == L.DSA_ERR_INVALID_ARG            # 200-byte rows: not a multiple of 16
+    assert call(vc=0) == L.DSA_ERR_INVALID_ARG
+    assert call(vn=0x30008) == L.DSA_ERR_INVALID_ARG
+    assert call(n=1 << 40) == L.DSA_ERR_UNSUPPORTED           # latent part beyond 2^31 chunks
+    # nothing to do: no device call
+    assert call(n=0) == L.DSA_OK
+    assert call(kn=None, vn=None) == L.DSA_OK
+
+
 def test_forward_validation(L):
     import torch
     b = _batch(L)
@@ -157,6 +183,11 @@ def test_forward_validation(L):
     p.d_v = 500
     assert L._lib.dsa_forward(ctypes.byref(p), None, 0, None) == L.DSA_ERR_UNSUPPORTED
     p.d_v = 512
+    p.idx_dtype = 0
+    p.H_I, p.d_I = 8, 32
+    p.k_idx_scale = 0x70000
+    assert L._lib.dsa_forward(ctypes.byref(p), None, 0, None) == L.DSA_ERR_INVALID_ARG   # scales need FP8 keys
+    p.idx_dtype, p.H_I, p.d_I, p.k_idx_scale = 2, 64, 128, None
     p.w = 0
     assert L._lib.dsa_forward(ctypes.byref(p), None, 0, None) == L.DSA_ERR_INVALID_ARG
     assert L._lib.dsa_forward(None, None, 0, None) == L.DSA_ERR_INVALID_ARG

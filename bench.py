@@ -212,6 +212,83 @@ def crossover(lengths, steps=3, warmup=1):
     return rows
 
 
+def append_bench(steps=10, warmup=2):
+    """dsa_cache_append on a 131072-token prefill (fp32 indexer keys -> E4M3
+    codes + E8M0 scales, bf16 latent rows copied) and on a 64-token decode
+    step into a 64 x 32K cache; and the indexer's cost for per-token key
+    scales on the prefill_128k and decode_64x32k workloads."""
+    import torch
+    from sparse_attention_03_amd import dsa, inputs as gen, libdsa as L
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    res = {}
+    n, d_I, d_qk = 131072, 128, 576
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    k32 = torch.randn((n, d_I), generator=g, device="cuda") / 11.3
+    kbf = k32.to(torch.bfloat16)
+    kv_new = torch.randn((n, d_qk), generator=g, device="cuda", dtype=torch.bfloat16)
+    kc = torch.empty((n, d_I), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((n,), dtype=torch.uint8, device="cuda")
+    kv_cache = torch.empty_like(kv_new)
+    cases = {
+        "keys_f32_scaled+latent_bf16": (dict(k_new=k32, k_cache=kc, k_scale=ks, kv_new=kv_new, kv_cache=kv_cache),
+                                        n * (d_I * 4 + d_I + 1 + 2 * d_qk * 2)),
+        "keys_f32_scaled": (dict(k_new=k32, k_cache=kc, k_scale=ks), n * (d_I * 4 + d_I + 1)),
+        "keys_f32": (dict(k_new=k32, k_cache=kc), n * (d_I * 4 + d_I)),
+        "keys_bf16_scaled": (dict(k_new=kbf, k_cache=kc, k_scale=ks), n * (d_I * 2 + d_I + 1)),
+        "latent_bf16": (dict(kv_new=kv_new, kv_cache=kv_cache), n * 2 * d_qk * 2),
+    }
+    for name, (kw, nbytes) in cases.items():
+        ms = timed(lambda: dsa.cache_append(**kw))
+        res[f"prefill_{n}_{name}"] = {"ms": ms, "bytes": nbytes, "GB_s": nbytes / ms / 1e6,
+                                      "frac_hbm": nbytes / ms * 1e3 / HBM_PEAK}
+        log(name, json.dumps(res[f"prefill_{n}_{name}"]))
+    del k32, kbf, kv_new, kc, ks, kv_cache
+    torch.cuda.empty_cache()
+    # decode: one new token per sequence, written at the end of its context
+    B, ctx = 64, 32768
+    kc = torch.empty((B * ctx, d_I), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((B * ctx,), dtype=torch.uint8, device="cuda")
+    kv_cache = torch.empty((B * ctx, d_qk), dtype=torch.bfloat16, device="cuda")
+    dst = (torch.arange(1, B + 1, device="cuda", dtype=torch.int32) * ctx - 1).contiguous()
+    k_new = torch.randn((B, d_I), generator=g, device="cuda")
+    kv_new = torch.randn((B, d_qk), generator=g, device="cuda", dtype=torch.bfloat16)
+    ms = timed(lambda: dsa.cache_append(k_new=k_new, k_cache=kc, k_scale=ks, kv_new=kv_new, kv_cache=kv_cache,
+                                        dst_rows=dst))
+    res["decode_64x32k_append"] = {"us_per_step": ms * 1e3}
+    log("decode append", json.dumps(res["decode_64x32k_append"]))
+    del kc, ks, kv_cache
+    torch.cuda.empty_cache()
+    # the indexer with and without per-token key scales (same codes)
+    for cfg in ("prefill_128k", "decode_64x32k"):
+        p = gen.make_config(cfg, device="cuda")
+        ld = dsa.score_ld(p.max_ctx)
+        scores = torch.empty((p.total_q, ld), dtype=torch.float32, device="cuda")
+        b = L.batch_of(p)
+        nws = L.dsa_indexer_workspace_size(b, p.q_idx)
+        ws = torch.empty(max(nws, 256), dtype=torch.uint8, device="cuda")
+        sc = torch.full((p.total_k,), 127, dtype=torch.uint8, device="cuda")
+        t_plain = timed(lambda: L.dsa_indexer_scores(b, p.q_idx, p.k_idx, p.w, scores, ws=ws))
+        t_sc = timed(lambda: L.dsa_indexer_scores(b, p.q_idx, p.k_idx, p.w, scores, ws=ws, k_idx_scale=sc))
+        res[f"indexer_{cfg}"] = {"unscaled_ms": t_plain, "scaled_ms": t_sc}
+        log(cfg, json.dumps(res[f"indexer_{cfg}"]))
+        del p, scores, ws, sc
+        torch.cuda.empty_cache()
+    return res
+
+
 def _short(name):
     m = re.search(r"dsa::\(anonymous namespace\)::(\w+)", name)
     if m:
@@ -284,6 +361,8 @@ def main():
     ap.add_argument("--crossover", metavar="L", type=int, nargs="+",
                     help="masked mode (dense attention) against the sparse path on one prefill sequence of each "
                          "length L, and exit")
+    ap.add_argument("--append", action="store_true",
+                    help="time dsa_cache_append (prefill and decode) and the indexer with key scales, then exit")
     ap.add_argument("--summarize", metavar="DIR", nargs="+", help="summarise rocprofv3 CSV output in DIR... and exit")
     ap.add_argument("--summary-command", default="", help="the command that produced DIR (recorded)")
     args = ap.parse_args()
@@ -301,6 +380,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.crossover:
         print(json.dumps({"crossover": crossover(args.crossover, steps=args.steps, warmup=args.warmup)}), flush=True)
+        return
+    if args.append:
+        print(json.dumps({"append": append_bench(steps=args.steps, warmup=args.warmup)}), flush=True)
         return
     if args.decode_only:
         print(json.dumps({"decode": decode_us_per_token(steps=args.steps, warmup=args.warmup)}), flush=True)

@@ -42,6 +42,7 @@ constexpr int kSlabBytes = 64 * 128;                         // 64 keys
 constexpr int kRing = 3;                                      // LDS slabs: one read, two in flight
 constexpr int kPrivSlots = 4;                                 // per-wave LDS ring of the streaming kernel
 constexpr int kStreamRows = 4;                                // rows per workgroup of the streaming kernel
+constexpr int kScaleArea = 256;                               // LDS bytes per slab's key scales (a dword per key)
 constexpr int kLinTerms = 4;
 constexpr int kLinScaleOff = kLinTerms * 128;                 // E8M0 scales [term][32-dim block]
 constexpr int kLinRowBytes = kLinScaleOff + kLinTerms * 4;    // 528
@@ -153,10 +154,13 @@ enum KeySource {
 // linear-term MFMA and |x| (rows need the pre-pass fragments); otherwise the
 // activation is applied per head.  SC: every key carries an E8M0 scale, which
 // goes into the MFMA's B-operand scale (lane (g, li) of sub-tile st: key
-// 16 st + li); the scales of the next slab are loaded one slab ahead.
+// 16 st + li).  On the LDS paths a slab's scales travel with its keys: one
+// byte copy per lane into the wave's kScaleArea bytes at `sarea` (key i of the
+// slab in the low byte of dword i), counted by the same waits.
 template <int NR, int NHT, int ACT, int KEYS, bool SC, bool LIN = ACT == 0>
 __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)[NR], const int32_t (&lim)[NR],
-                                         int32_t kbase, int32_t kstart, int32_t kend, DSA_LDS uint8_t* ring) {
+                                         int32_t kbase, int32_t kstart, int32_t kend, DSA_LDS uint8_t* ring,
+                                         DSA_LDS uint8_t* sarea) {
   static_assert(!LIN || ACT == 0, "the linear-term split is ReLU's");
   constexpr int NST = 4;                          // 16-key sub-tiles per 64-key slab
   constexpr int NPS = (LIN ? 1 : 0) + NR * NHT;   // MFMAs per sub-tile
@@ -202,11 +206,12 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
     srs[i] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.scores + (int64_t)(rows[i] - a.row_begin) * a.ld), 0,
                                                lim[i] * 4, kBufFlags);
   const int svo = (16 * g + li) * 4;
-  // per-key scales: [kbase, kbase + kend) in range; past it reads 0 (those scores are dropped)
-  __amdgpu_buffer_rsrc_t ksrs;
-  if constexpr (SC) ksrs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_scale + kbase), 0, kend, kBufFlags);
+  // per-key scales (SC), straight from memory (plain path): [kbase, kbase + kend)
+  // in range, past it reads 0 (those scores are dropped)
   auto load_scales = [&](int32_t s0, int (&ks)[NST]) {
     if constexpr (SC) {
+      const __amdgpu_buffer_rsrc_t ksrs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_scale + kbase), 0, kend, kBufFlags);
       const int so = __builtin_amdgcn_readfirstlane(s0);
 #pragma unroll
       for (int st = 0; st < NST; ++st) ks[st] = __builtin_amdgcn_raw_buffer_load_b8(ksrs, li + 16 * st, so, 0);
@@ -214,6 +219,17 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
 #pragma unroll
       for (int st = 0; st < NST; ++st) ks[st] = 127;
     }
+  };
+  // ... and through LDS (ring paths): the copy of slab s0's scales into one
+  // scale area, and the read of this lane's four
+  auto copy_scales = [&](int32_t s0, DSA_LDS uint8_t* dst) {
+    if constexpr (SC)
+      __builtin_amdgcn_global_load_lds((const void*)(a.k_scale + kbase + min(s0 + lane, kend - 1)),
+                                       (DSA_LDS void*)dst, 1, 0, 0);
+  };
+  auto read_scales = [&](const DSA_LDS uint8_t* src, int (&ks)[NST]) {
+#pragma unroll
+    for (int st = 0; st < NST; ++st) ks[st] = SC ? (int)src[4 * (li + 16 * st)] : 127;
   };
 
   // LDS ring (SHARED), chunk-major: 16-byte chunk c of slab key row r sits at
@@ -224,6 +240,7 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint8_t* kglob = a.k_idx + (int64_t)kbase * 128;
   auto copy_slab = [&](int32_t s0, int slot) {
+    copy_scales(s0, sarea + slot * 4 * kScaleArea);
     DSA_LDS uint8_t* dst = ring + slot * kSlabBytes;
     const uint8_t* src = kglob + (int64_t)min(s0 + lane, kend - 1) * 128;
     __builtin_amdgcn_global_load_lds((const void*)(src + 16 * wave), (DSA_LDS void*)(dst + 1024 * wave), 16, 0, 0);
@@ -308,28 +325,22 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
     // stores of n-2, the copies of n+1 and the stores of n-1), barrier (every
     // wave's copies landed, every wave done reading slab n-1), copy slab n+2
     // into the slot slab n-1 used, read and compute slab n
-    // (the scale loads of slab n + 1 go out before the copies of slab n + 2,
-    // so waiting for them never waits for copies issued later)
-    int ks[NST], ksn[NST];
-    load_scales(kstart, ks);
+    // (each wave also copies the slab's scales into its own scale area)
+    constexpr int C = SC ? 3 : 2;  // copies per slab and wave
     copy_slab(kstart, 0);
     copy_slab(kstart + 64, 1);
     int slot = 0, n = 0;
     for (int32_t s0 = kstart; s0 < kend; s0 += 64, ++n) {
-      constexpr int X = SC ? NST : 0;  // scale loads issued after the copies of slab n
-      if (n == 0) wait_vmcnt<2>();
-      else if (n == 1) wait_vmcnt<2 + NR + X>();
-      else wait_vmcnt<2 + 2 * NR + X>();
+      if (n == 0) wait_vmcnt<C>();
+      else if (n == 1) wait_vmcnt<C + NR>();
+      else wait_vmcnt<C + 2 * NR>();
       lds_barrier();
-      if constexpr (SC) load_scales(s0 + 64, ksn);
       copy_slab(s0 + 128, slot == 0 ? 2 : slot - 1);
       i32x8 kf[NST];
+      int ks[NST];
       read_keys(slot, kf);
+      read_scales(sarea + slot * 4 * kScaleArea, ks);
       slab(s0, kf, ks);
-      if constexpr (SC) {
-#pragma unroll
-        for (int st = 0; st < NST; ++st) ks[st] = ksn[st];
-      }
       slot = slot == 2 ? 0 : slot + 1;
     }
   } else if constexpr (KEYS == kKeysPrivate) {
@@ -339,34 +350,30 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
     // copies of slabs n + 1 .. n + kPrivSlots - 2 and the score stores of the
     // (at most kPrivSlots - 1) slabs before n, all counted by vmcnt.
     constexpr int P = kPrivSlots;
+    constexpr int C = SC ? 9 : 8;  // copies per slab
     auto copy_own = [&](int32_t s0, int slot) {
+      copy_scales(s0, sarea + slot * kScaleArea);
       const uint8_t* src = kglob + (int64_t)min(s0 + lane, kend - 1) * 128;  // rows past kend: a valid key
       DSA_LDS uint8_t* dst = ring + slot * kSlabBytes;
 #pragma unroll
       for (int c = 0; c < 8; ++c)
         __builtin_amdgcn_global_load_lds((const void*)(src + 16 * c), (DSA_LDS void*)(dst + 1024 * c), 16, 0, 0);
     };
-    int ks[NST], ksn[NST];
-    load_scales(kstart, ks);
 #pragma unroll
     for (int j = 0; j < P - 1; ++j) copy_own(kstart + 64 * j, j);
     int n = 0;
     for (int32_t s0 = kstart; s0 < kend; s0 += 64, ++n) {
       static_assert(P == 4, "the counted waits below assume four slots");
-      constexpr int X = SC ? NST : 0;  // scale loads per slab, issued ahead of its copies
-      if (n == 0) wait_vmcnt<8 * (P - 2)>();
-      else if (n == 1) wait_vmcnt<8 * (P - 2) + NR + X>();
-      else if (n == 2) wait_vmcnt<8 * (P - 2) + 2 * NR + 2 * X>();
-      else wait_vmcnt<8 * (P - 2) + 3 * NR + 2 * X>();
-      if constexpr (SC) load_scales(s0 + 64, ksn);
+      if (n == 0) wait_vmcnt<C * (P - 2)>();
+      else if (n == 1) wait_vmcnt<C * (P - 2) + NR>();
+      else if (n == 2) wait_vmcnt<C * (P - 2) + 2 * NR>();
+      else wait_vmcnt<C * (P - 2) + 3 * NR>();
       copy_own(s0 + 64 * (P - 1), (n + P - 1) % P);  // the slot slab n - 1 used, read before this point
       i32x8 kf[NST];
+      int ks[NST];
       read_keys(n % P, kf);
+      read_scales(sarea + (n % P) * kScaleArea, ks);
       slab(s0, kf, ks);
-      if constexpr (SC) {
-#pragma unroll
-        for (int st = 0; st < NST; ++st) ks[st] = ksn[st];
-      }
     }
     wait_vmcnt<0>();  // no copy into LDS outlives the wave
   } else {
@@ -385,7 +392,7 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
 // back to the lean per-wave path.
 template <int NHT, int ACT, bool SC>
 __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(IdxArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kSlabBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kSlabBytes + (SC ? kRing * 4 * kScaleArea : 0)];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int32_t rb = a.row_begin + blockIdx.x * kRowsPerBlock;
   const int32_t kstart = blockIdx.y * a.key_chunk;
@@ -420,7 +427,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(IdxArgs a) {
       rows[i] = min(rb + j, a.row_end - 1);
       lim[i] = __builtin_amdgcn_readfirstlane(live[j] ? min(kchunk_end, pos[j] + 1) : 0);
     }
-    fp8_rows<2, NHT, ACT, kKeysShared, SC>(a, rows, lim, kb[0], kstart, kend_blk, (DSA_LDS uint8_t*)ring);
+    fp8_rows<2, NHT, ACT, kKeysShared, SC>(a, rows, lim, kb[0], kstart, kend_blk, (DSA_LDS uint8_t*)ring,
+                                           (DSA_LDS uint8_t*)ring + kRing * kSlabBytes + wave * kScaleArea);
     return;
   }
   // rows of several sequences: each wave on its own
@@ -436,14 +444,14 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(IdxArgs a) {
   if (v[0] && v[1] && k[0] == k[1]) {
     const int32_t rows[2] = {rb + j0, rb + j0 + 1};
     const int32_t lim[2] = {l[0], l[1]};
-    fp8_rows<2, NHT, ACT, kKeysPlain, SC>(a, rows, lim, k[0], kstart, max(l[0], l[1]), nullptr);
+    fp8_rows<2, NHT, ACT, kKeysPlain, SC>(a, rows, lim, k[0], kstart, max(l[0], l[1]), nullptr, nullptr);
   } else {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if (!v[i]) continue;
       const int32_t r1[1] = {rb + j0 + i};
       const int32_t l1[1] = {l[i]};
-      fp8_rows<1, NHT, ACT, kKeysPlain, SC>(a, r1, l1, k[i], kstart, l[i], nullptr);
+      fp8_rows<1, NHT, ACT, kKeysPlain, SC>(a, r1, l1, k[i], kstart, l[i], nullptr, nullptr);
     }
   }
 }
@@ -455,7 +463,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_kernel(IdxArgs a) {
 // (no linear-term pre-pass).
 template <int NHT, int ACT, bool SC>
 __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_stream_kernel(IdxArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t pring[];  // kStreamRows x kPrivSlots slabs
+  // kStreamRows x kPrivSlots slabs, then (SC) kStreamRows x kPrivSlots scale areas
+  extern __shared__ __attribute__((aligned(16))) uint8_t pring[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const RowInfo ri = locate_row_wave(load_seq_table(a.cu_q, a.cu_k, a.num_seqs), a.cu_q, a.cu_k,
                                      min(a.row_begin + (int32_t)blockIdx.x * kStreamRows + wave, a.row_end - 1));
@@ -466,7 +475,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_fp8_stream_kernel(IdxArgs
   const int32_t kend = min(kstart + a.key_chunk, pos + 1);
   const int32_t rows[1] = {r}, lim[1] = {kend};
   fp8_rows<1, NHT, ACT, kKeysPrivate, SC, false>(a, rows, lim, __builtin_amdgcn_readfirstlane(ri.kbase), kstart, kend,
-                                             (DSA_LDS uint8_t*)pring + wave * kPrivSlots * kSlabBytes);
+                                             (DSA_LDS uint8_t*)pring + wave * kPrivSlots * kSlabBytes,
+                                             (DSA_LDS uint8_t*)pring + kStreamRows * kPrivSlots * kSlabBytes +
+                                                 wave * kPrivSlots * kScaleArea);
 }
 
 // fp32 inputs: plain VALU dot products (used for small fp32 problems).
@@ -513,7 +524,7 @@ hipError_t launch_fp8(const IdxArgs& a, int act, dim3 grid, hipStream_t s) {
 
 template <int NHT, int ACT, bool SC>
 hipError_t launch_stream_act(const IdxArgs& a, dim3 grid, hipStream_t s) {
-  constexpr size_t lds = (size_t)kStreamRows * kPrivSlots * kSlabBytes;  // 128 KB
+  constexpr size_t lds = (size_t)kStreamRows * kPrivSlots * (kSlabBytes + (SC ? kScaleArea : 0));  // 128 (132) KB
   static bool attr_set = false;  // benign race: idempotent attribute call
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)indexer_fp8_stream_kernel<NHT, ACT, SC>,

@@ -313,6 +313,22 @@ def summarize(dirs, command):
         for r in csv.DictReader(open(f)):
             out.append(f"  {_short(r['Name']):28s} {int(r['Calls']):6d} {float(r['TotalDurationNs']) / 1e6:10.3f} "
                        f"{float(r['AverageNs']) / 1e6:9.4f} {float(r['MinNs']) / 1e6:9.4f} {float(r['MaxNs']) / 1e6:9.4f}")
+    for f in files("*kernel_trace.csv"):
+        # the library's kernels per template instance and grid (one row per launch shape)
+        shapes = {}
+        for r in csv.DictReader(open(f)):
+            name = r["Kernel_Name"]
+            if "dsa::" not in name:
+                continue
+            m = re.search(r"(\w+)(<[^()]*>)?\(", name.replace("(anonymous namespace)::", ""))
+            key = ((m.group(1) + (m.group(2) or "")) if m else name[:60], int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]),
+                   int(r["Grid_Size_Y"]))
+            shapes.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        if shapes:
+            out.append(f"launch shapes ({os.path.basename(f)}):")
+            out.append(f"  {'kernel':44s} {'grid':>14s} {'calls':>6s} {'avg us':>10s} {'min us':>10s}")
+            for (k, gx, gy), v in shapes.items():
+                out.append(f"  {k:44s} {f'{gx}x{gy}':>14s} {len(v):6d} {sum(v) / len(v):10.2f} {min(v):10.2f}")
     counters = {}
     for f in files("*counter_collection.csv"):
         calib = os.path.basename(f).startswith("copy")

@@ -37,10 +37,15 @@ def lib():
         L.dsa_oracle_sparse_mla.argtypes = [i32, p, p, i32, p, p, p, i32, p, i32, i32, i32, i32, dbl, p, p]
         L.dsa_oracle_dense_mla.argtypes = [i32, p, p, i32, p, p, p, i32, i32, i32, i32, dbl, p, p]
         L.dsa_oracle_quantize_keys.argtypes = [p, i32, i64, i32, i32, p, p]
+        L.dsa_oracle_attn_target.argtypes = [i32, p, p, i32, p, p, p, i32, p, i32, i32, i32, dbl, p]
+        L.dsa_oracle_indexer_kl.argtypes = [i32, i32, p, p, p, p, p]
+        L.dsa_oracle_indexer_backward.argtypes = [i32, p, p, i32, p, p, p, i32, p, p, i32, i32, i32, p, i32, p,
+                                                  p, p, p]
         L.dsa_oracle_forward.argtypes = [i32, p, p, i32, p, p, p, i32, p, p, i32, i32, i32,
                                          p, p, i32, i32, i32, i32, dbl, i32, i64, p, p, p, p]
         for f in (L.dsa_oracle_indexer, L.dsa_oracle_topk, L.dsa_oracle_sparse_mla, L.dsa_oracle_dense_mla,
-                  L.dsa_oracle_quantize_keys, L.dsa_oracle_forward):
+                  L.dsa_oracle_quantize_keys, L.dsa_oracle_forward, L.dsa_oracle_attn_target,
+                  L.dsa_oracle_indexer_kl, L.dsa_oracle_indexer_backward):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -167,6 +172,72 @@ def quantize_keys(src, scaled=False):
     if rc != 0:
         raise ValueError("oracle quantize_keys: source must be float32 or bfloat16")
     return (codes, scale) if scaled else codes
+
+
+def attn_target(cu_q, cu_k, q, kv, scale, idx=None, ld=None, rows=None):
+    """Indexer-alignment target p [nrows, m] float64: the main attention's
+    per-head probabilities over each row's candidates, summed over heads and
+    L1-normalised.  idx None: dense, entry e = position e (m = ld, default the
+    longest context); else entry e = position idx[i, e] (m = k)."""
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    rows = _rows(rows, cu_q)
+    q, kv = np.ascontiguousarray(q), np.ascontiguousarray(kv)
+    dt = _dtype_code(q)
+    assert _dtype_code(kv) == dt
+    nrows, H, d_qk = q.shape
+    if idx is not None:
+        idx = _c(idx, np.int32)
+        m = idx.shape[1]
+    else:
+        m = int(np.max(np.diff(cu_k))) if ld is None else ld
+    out = np.zeros((nrows, m), dtype=np.float64)
+    rc = lib().dsa_oracle_attn_target(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), nrows, _ptr(rows), _ptr(q), _ptr(kv),
+                                      dt, _ptr(idx), m, H, d_qk, float(scale), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle attn_target: invalid batch / rows")
+    return out
+
+
+def indexer_kl(I, p, cnt):
+    """(loss [nrows], dI [nrows, m]) of KL(p || softmax(I)) over each row's first
+    cnt[i] entries."""
+    I, p = _c(I, np.float64), _c(p, np.float64)
+    cnt = _c(cnt, np.int32)
+    nrows, m = I.shape
+    loss = np.zeros(nrows, dtype=np.float64)
+    dI = np.zeros((nrows, m), dtype=np.float64)
+    if lib().dsa_oracle_indexer_kl(nrows, m, _ptr(cnt), _ptr(I), _ptr(p), _ptr(loss), _ptr(dI)) != 0:
+        raise ValueError("oracle indexer_kl: bad counts")
+    return loss, dI
+
+
+def indexer_backward(cu_q, cu_k, q_idx, k_idx, w, g, act=ACT_RELU, idx=None, rows=None, k_scale=None):
+    """(dq_idx [nrows, H_I, d_I], dw [nrows, H_I], dk_idx [total_k, d_I]) float64
+    for the upstream gradient g [nrows, m] over each row's candidates (dense:
+    entry e = position e; else entry e = position idx[i, e])."""
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    rows = _rows(rows, cu_q)
+    q_idx, k_idx = np.ascontiguousarray(q_idx), np.ascontiguousarray(k_idx)
+    dt = _dtype_code(q_idx)
+    assert _dtype_code(k_idx) == dt
+    nrows, H_I, d_I = q_idx.shape
+    w = _c(w, np.float32)
+    g = _c(g, np.float64)
+    m = g.shape[1]
+    if idx is not None:
+        idx = _c(idx, np.int32)
+        assert idx.shape == g.shape
+    if k_scale is not None:
+        k_scale = _c(k_scale, np.uint8)
+    dq = np.zeros((nrows, H_I, d_I), dtype=np.float64)
+    dw = np.zeros((nrows, H_I), dtype=np.float64)
+    dk = np.zeros(k_idx.shape, dtype=np.float64)
+    rc = lib().dsa_oracle_indexer_backward(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), nrows, _ptr(rows), _ptr(q_idx),
+                                           _ptr(k_idx), dt, _ptr(k_scale), _ptr(w), H_I, d_I, act, _ptr(idx), m,
+                                           _ptr(g), _ptr(dq), _ptr(dw), _ptr(dk))
+    if rc != 0:
+        raise ValueError("oracle indexer_backward: invalid batch / rows")
+    return dq, dw, dk
 
 
 def forward(cu_q, cu_k, q_idx, k_idx, w, q, kv, k, d_v, scale, act=ACT_RELU, rows=None, ld=None, k_scale=None):

@@ -304,6 +304,152 @@ int dsa_oracle_quantize_keys(const void* src, int dtype, int64_t n, int d, int s
 }
 
 /* ------------------------------------------------------------------ */
+/* Indexer alignment, the training objective of the indexer.  [P1] training
+ * "Step 1" (dense warm-up) and [P2] 【密集预热阶段】: for query token t the main
+ * attention scores (the softmax probabilities of each head) are summed over
+ * the heads and L1-normalised along the sequence, giving the target p_t; the
+ * loss is the KL divergence from p_t to the indexer's distribution, read as
+ * softmax(I_t) over the same candidates.  [P1] "Step 2" / [P2] 【稀疏训练阶段】:
+ * in the sparse stage only the selected set S_t is considered, and the
+ * indexer's input is detached, so this loss trains the indexer alone.
+ *
+ * Candidate lists: dense (idx == NULL) entry e of row i is position e, for
+ * e <= pos; sparse: entry e is position idx[i, e] when that is >= 0.  Row i's
+ * arrays have m entries; entries that are no candidate are 0 on output. */
+/* ------------------------------------------------------------------ */
+static int cand_pos(const int32_t* idx, int m, int i, int e, int64_t pos) {
+    if (!idx) return e <= pos ? e : -1;
+    const int32_t s = idx[(int64_t)i * m + e];
+    return s >= 0 && s <= pos ? s : -1;
+}
+
+int dsa_oracle_attn_target(int nseq, const int32_t* cu_q, const int32_t* cu_k,
+                           int nrows, const int32_t* rows,
+                           const void* q, const void* kv, int dtype,
+                           const int32_t* idx, int m, int H, int d_qk, double scale, double* p) {
+    double table[256];
+    for (int c = 0; c < 256; ++c) table[c] = dsa_oracle_e4m3_value(c);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int i = 0; i < nrows; ++i) {
+        int64_t pos, kbase;
+        if (locate_row(nseq, cu_q, cu_k, rows[i], &pos, &kbase) != 0 || (!idx && pos + 1 > m)) { bad |= 1; continue; }
+        double* pr = p + (int64_t)i * m;
+        double* z = (double*)malloc((size_t)m * sizeof(double));
+        for (int e = 0; e < m; ++e) pr[e] = 0.0;
+        for (int h = 0; h < H; ++h) {
+            /* this head's attention probabilities over the candidates */
+            double mx = -INFINITY;
+            for (int e = 0; e < m; ++e) {
+                const int s = cand_pos(idx, m, i, e, pos);
+                if (s < 0) continue;
+                double dot = 0.0;
+                for (int d = 0; d < d_qk; ++d)
+                    dot += load_elem(q, dtype, ((int64_t)i * H + h) * d_qk + d, table) *
+                           load_elem(kv, dtype, (kbase + s) * d_qk + d, table);
+                z[e] = scale * dot;
+                if (z[e] > mx) mx = z[e];
+            }
+            double l = 0.0;
+            for (int e = 0; e < m; ++e)
+                if (cand_pos(idx, m, i, e, pos) >= 0) l += exp(z[e] - mx);
+            /* summed over the heads */
+            for (int e = 0; e < m; ++e)
+                if (cand_pos(idx, m, i, e, pos) >= 0) pr[e] += exp(z[e] - mx) / l;
+        }
+        /* L1-normalised along the sequence */
+        double norm = 0.0;
+        for (int e = 0; e < m; ++e) norm += fabs(pr[e]);
+        if (norm > 0.0)
+            for (int e = 0; e < m; ++e) pr[e] /= norm;
+        free(z);
+    }
+    return bad ? -1 : 0;
+}
+
+/* KL(p || softmax(I)) per row over its first cnt[i] entries, and its gradient
+ * with respect to I: d/dI_e = (sum_e' p_e') softmax(I)_e - p_e.  Terms with
+ * p_e = 0 contribute 0 (0 log 0 = 0).  Entries past cnt[i] get dI = 0. */
+int dsa_oracle_indexer_kl(int nrows, int m, const int32_t* cnt, const double* I, const double* p,
+                          double* loss, double* dI) {
+    int bad = 0;
+    for (int i = 0; i < nrows; ++i) {
+        const int n = cnt[i];
+        if (n < 0 || n > m) { bad = 1; continue; }
+        const double* Ir = I + (int64_t)i * m;
+        const double* pr = p + (int64_t)i * m;
+        double mx = -INFINITY, psum = 0.0;
+        for (int e = 0; e < n; ++e) {
+            if (Ir[e] > mx) mx = Ir[e];
+            psum += pr[e];
+        }
+        double l = 0.0;
+        for (int e = 0; e < n; ++e) l += exp(Ir[e] - mx);
+        const double lse = mx + log(l);
+        double kl = 0.0;
+        for (int e = 0; e < n; ++e)
+            if (pr[e] > 0.0) kl += pr[e] * (log(pr[e]) - (Ir[e] - lse));
+        if (loss) loss[i] = n > 0 ? kl : 0.0;
+        if (dI) {
+            double* g = dI + (int64_t)i * m;
+            for (int e = 0; e < m; ++e) g[e] = e < n ? psum * exp(Ir[e] - lse) - pr[e] : 0.0;
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* Backward of the index score (R1) for an upstream gradient g over each row's
+ * candidates: with x = q_idx[i,j,:] . k[s,:] (k scaled per token if k_scale),
+ *   dw[i,j]        += g_e act(x)
+ *   dq_idx[i,j,:]  += g_e w[i,j] act'(x) k[s,:]
+ *   dk_idx[s,:]    += g_e w[i,j] act'(x) q_idx[i,j,:]      (all rows, summed)
+ * act' of ReLU is 1 for x > 0 and 0 otherwise; of GELU Phi(x) + x phi(x).
+ * The outputs are accumulated: the caller zeroes them. */
+int dsa_oracle_indexer_backward(int nseq, const int32_t* cu_q, const int32_t* cu_k,
+                                int nrows, const int32_t* rows,
+                                const void* q_idx, const void* k_idx, int dtype, const uint8_t* k_scale,
+                                const float* w, int H_I, int d_I, int act,
+                                const int32_t* idx, int m, const double* g,
+                                double* dq_idx, double* dw, double* dk_idx) {
+    double table[256];
+    for (int c = 0; c < 256; ++c) table[c] = dsa_oracle_e4m3_value(c);
+    for (int i = 0; i < nrows; ++i) {
+        int64_t pos, kbase;
+        if (locate_row(nseq, cu_q, cu_k, rows[i], &pos, &kbase) != 0 || (!idx && pos + 1 > m)) return -1;
+        for (int e = 0; e < m; ++e) {
+            const int s = cand_pos(idx, m, i, e, pos);
+            const double ge = g[(int64_t)i * m + e];
+            if (s < 0 || ge == 0.0) continue;
+            const double ks = k_scale ? ldexp(1.0, (int)k_scale[kbase + s] - 127) : 1.0;
+            for (int j = 0; j < H_I; ++j) {
+                double x = 0.0;
+                for (int d = 0; d < d_I; ++d)
+                    x += load_elem(q_idx, dtype, ((int64_t)i * H_I + j) * d_I + d, table) *
+                         load_elem(k_idx, dtype, (kbase + s) * d_I + d, table) * ks;
+                const double wij = (double)w[(int64_t)i * H_I + j];
+                double a, da;
+                if (act == OR_ACT_GELU) {
+                    const double cdf = 0.5 * (1.0 + erf(x / sqrt(2.0)));
+                    a = x * cdf;
+                    da = cdf + x * exp(-0.5 * x * x) / sqrt(2.0 * 3.14159265358979323846);
+                } else {
+                    a = x > 0.0 ? x : 0.0;
+                    da = x > 0.0 ? 1.0 : 0.0;
+                }
+                dw[(int64_t)i * H_I + j] += ge * a;
+                const double c = ge * wij * da;
+                if (c == 0.0) continue;
+                for (int d = 0; d < d_I; ++d) {
+                    dq_idx[((int64_t)i * H_I + j) * d_I + d] += c * load_elem(k_idx, dtype, (kbase + s) * d_I + d, table) * ks;
+                    dk_idx[(kbase + s) * d_I + d] += c * load_elem(q_idx, dtype, ((int64_t)i * H_I + j) * d_I + d, table);
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Dense causal MQA: attention of every query row over all its candidates
  * [0, pos], no selection.  [P2] 【推理成本评估】 describes this "masked mode"
  * for short prefill, where DSA is emulated by a mask over the dense

@@ -497,6 +497,163 @@ def test_relu_scores_are_homogeneous_in_the_key_scale():
         assert np.array_equal(got, base * 2.0 ** e)
 
 
+# ------------------------------------------------------ indexer alignment loss
+
+def _target_case(seed, seq_ctx, seq_q, H, d):
+    rng = np.random.default_rng(seed)
+    cu_q, cu_k = _ragged(seq_ctx, seq_q)
+    q = (rng.standard_normal((int(cu_q[-1]), H, d)) * 0.7).astype(np.float32)
+    kv = rng.standard_normal((int(cu_k[-1]), d)).astype(np.float32)
+    return cu_q, cu_k, q, kv
+
+
+def test_attn_target_dense_is_the_head_mean_of_softmax():
+    """Summing the heads' softmax rows and L1-normalising is the head mean of
+    torch's softmax over the causal candidates."""
+    cu_q, cu_k, q, kv = _target_case(60, [37, 50, 9], [37, 4, 1], 3, 16)
+    scale = 0.3
+    p = oracle.attn_target(cu_q, cu_k, q, kv, scale)
+    pos, base = _positions(cu_q, cu_k)
+    assert p.shape == (len(pos), 50)
+    for i in range(len(pos)):
+        n = pos[i] + 1
+        z = scale * torch.from_numpy(q[i]).double() @ torch.from_numpy(kv[base[i]: base[i] + n]).double().T
+        want = torch.softmax(z, dim=-1).mean(0).numpy()
+        np.testing.assert_allclose(p[i, :n], want, rtol=1e-12, atol=1e-15)
+        assert np.all(p[i, n:] == 0.0)
+        assert abs(p[i].sum() - 1.0) < 1e-12
+
+
+def test_attn_target_over_a_selected_set():
+    cu_q, cu_k, q, kv = _target_case(61, [40, 33], [40, 2], 2, 8)
+    scale = 0.5
+    pos, base = _positions(cu_q, cu_k)
+    rng = np.random.default_rng(62)
+    k = 12
+    idx = np.full((len(pos), k), -1, np.int32)
+    for i in range(len(pos)):
+        n = pos[i] + 1
+        sel = np.sort(rng.choice(n, min(n, k), replace=False)) if n > k else np.arange(n)
+        idx[i, :len(sel)] = sel
+    p = oracle.attn_target(cu_q, cu_k, q, kv, scale, idx=idx)
+    for i in range(len(pos)):
+        sel = idx[i][idx[i] >= 0]
+        z = scale * torch.from_numpy(q[i]).double() @ torch.from_numpy(kv[base[i] + sel]).double().T
+        want = torch.softmax(z, dim=-1).mean(0).numpy()
+        np.testing.assert_allclose(p[i, :len(sel)], want, rtol=1e-12, atol=1e-15)
+        assert np.all(p[i, len(sel):] == 0.0)
+    # selecting every candidate is the dense target
+    cu_q2, cu_k2, q2, kv2 = _target_case(63, [20], [20], 3, 8)
+    all_idx = np.where(np.arange(20)[None, :] <= np.arange(20)[:, None], np.arange(20)[None, :], -1).astype(np.int32)
+    np.testing.assert_allclose(oracle.attn_target(cu_q2, cu_k2, q2, kv2, 0.4, idx=all_idx),
+                               oracle.attn_target(cu_q2, cu_k2, q2, kv2, 0.4), rtol=0, atol=1e-15)
+
+
+def test_indexer_kl_matches_torch_autograd():
+    rng = np.random.default_rng(64)
+    nrows, m = 9, 30
+    cnt = np.array([30, 1, 5, 17, 0, 29, 2, 30, 11], np.int32)
+    I = rng.standard_normal((nrows, m)) * 3
+    p = rng.random((nrows, m)) ** 3
+    p[:, ::4] = 0.0                                       # zero targets: 0 log 0 = 0
+    for i in range(nrows):
+        p[i, cnt[i]:] = 0.0
+        if p[i].sum() > 0:
+            p[i] /= p[i].sum()
+    loss, dI = oracle.indexer_kl(I, p, cnt)
+    for i in range(nrows):
+        n = cnt[i]
+        if n == 0:
+            assert loss[i] == 0.0 and np.all(dI[i] == 0.0)
+            continue
+        Iv = torch.tensor(I[i, :n], dtype=torch.float64, requires_grad=True)
+        pv = torch.tensor(p[i, :n], dtype=torch.float64)
+        ref = torch.nn.functional.kl_div(torch.log_softmax(Iv, 0), pv, reduction="sum")
+        ref.backward()
+        assert abs(loss[i] - ref.item()) <= 1e-12 * max(1.0, abs(ref.item()))
+        np.testing.assert_allclose(dI[i, :n], Iv.grad.numpy(), rtol=1e-11, atol=1e-14)
+        assert np.all(dI[i, n:] == 0.0)
+    # closed forms: p = softmax(I) gives 0 and no gradient; a one-hot p gives -log softmax(I)_e
+    row = rng.standard_normal(7)
+    sm = np.exp(row - row.max()) / np.exp(row - row.max()).sum()
+    l0, g0 = oracle.indexer_kl(row[None, :], sm[None, :], [7])
+    assert abs(l0[0]) < 1e-15 and np.max(np.abs(g0)) < 1e-15
+    onehot = np.zeros(7)
+    onehot[3] = 1.0
+    l1, g1 = oracle.indexer_kl(row[None, :], onehot[None, :], [7])
+    assert abs(l1[0] + np.log(sm[3])) < 1e-13
+    np.testing.assert_allclose(g1[0], sm - onehot, atol=1e-15)
+
+
+def _torch_index_grads(cu_q, cu_k, q_idx, k_idx, w, g, act, idx=None):
+    """Gradients of sum_i sum_e g[i, e] I[i, s_e] through torch's autograd, the
+    index score built from torch ops in float64."""
+    pos, base = _positions(cu_q, cu_k)
+    qt = torch.tensor(q_idx, dtype=torch.float64, requires_grad=True)
+    wt = torch.tensor(w, dtype=torch.float64, requires_grad=True)
+    kt = torch.tensor(k_idx, dtype=torch.float64, requires_grad=True)
+    total = torch.zeros((), dtype=torch.float64)
+    for i in range(len(pos)):
+        if idx is None:
+            sel = np.arange(pos[i] + 1)
+            gi = g[i, :pos[i] + 1]
+        else:
+            keep = idx[i] >= 0
+            sel = idx[i][keep]
+            gi = g[i][keep]
+        x = qt[i] @ kt[torch.from_numpy(base[i] + sel)].T
+        a = torch.relu(x) if act == oracle.ACT_RELU else torch.nn.functional.gelu(x)
+        total = total + (torch.from_numpy(gi) * (wt[i] @ a)).sum()
+    total.backward()
+    return qt.grad.numpy(), wt.grad.numpy(), kt.grad.numpy()
+
+
+@pytest.mark.parametrize("act,integer", [(oracle.ACT_RELU, True), (oracle.ACT_RELU, False), (oracle.ACT_GELU, False)])
+def test_indexer_backward_matches_torch_autograd(act, integer):
+    cu_q, cu_k, q, k, w = _indexer_case(65, [23, 30], [23, 3], 3, 8, integer)
+    pos, _ = _positions(cu_q, cu_k)
+    rng = np.random.default_rng(66)
+    g = rng.standard_normal((len(pos), 30))
+    for i in range(len(pos)):
+        g[i, pos[i] + 1:] = 0.0
+    dq, dw, dk = oracle.indexer_backward(cu_q, cu_k, q, k, w, g, act=act)
+    rq, rw, rk = _torch_index_grads(cu_q, cu_k, q, k, w, g, act)
+    for got, ref in ((dq, rq), (dw, rw), (dk, rk)):
+        np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-10)
+    if integer:
+        # integer inputs put many dot products exactly at 0, where both take ReLU's slope as 0
+        assert np.any(np.einsum("tjd,sd->tjs", q, k) == 0)
+    # over a selected set (ascending, -1 padded)
+    m = 6
+    idx = np.full((len(pos), m), -1, np.int32)
+    for i in range(len(pos)):
+        n = pos[i] + 1
+        sel = np.sort(rng.choice(n, min(n, m), replace=False))
+        idx[i, :len(sel)] = sel
+    gs = rng.standard_normal((len(pos), m))
+    dq, dw, dk = oracle.indexer_backward(cu_q, cu_k, q, k, w, gs, act=act, idx=idx)
+    rq, rw, rk = _torch_index_grads(cu_q, cu_k, q, k, w, gs, act, idx=idx)
+    for got, ref in ((dq, rq), (dw, rw), (dk, rk)):
+        np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-10)
+
+
+def test_indexer_backward_with_key_scales():
+    """FP8 codes with per-token scales give the gradients of float32 keys
+    holding the dequantised values (dk with respect to the dequantised key)."""
+    vals = _e4m3_values()
+    cu_q, cu_k = _ragged([25], [25])
+    kc = _fp8_keys_case(67, 25, 16)
+    qc = _fp8_keys_case(68, 25, 2 * 16).reshape(25, 2, 16)
+    sc = np.random.default_rng(69).integers(120, 134, 25).astype(np.uint8)
+    w = np.random.default_rng(70).standard_normal((25, 2)).astype(np.float32)
+    g = np.tril(np.random.default_rng(71).standard_normal((25, 25)))
+    got = oracle.indexer_backward(cu_q, cu_k, qc, kc, w, g, k_scale=sc)
+    kf = (vals[kc] * 2.0 ** (sc.astype(np.int64) - 127)[:, None]).astype(np.float32)
+    want = oracle.indexer_backward(cu_q, cu_k, vals[qc].astype(np.float32), kf, w, g)
+    for a_, b_ in zip(got, want):
+        np.testing.assert_allclose(a_, b_, rtol=1e-13, atol=1e-300)
+
+
 # ---------------------------------------------------------------- end to end
 
 def test_forward_composes_the_steps_and_is_causal():

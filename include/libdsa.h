@@ -198,6 +198,50 @@ dsa_status dsa_dense_mla_attn(const dsa_batch* batch, const void* q, const void*
                               void* out, float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
 
 /*
+ * Indexer-alignment target.  [P1] training "Step 1" (dense warm-up) and
+ * "Step 2" (sparse training), [P2] 【密集预热阶段】 / 【稀疏训练阶段】: for each
+ * query row the main attention's probabilities of every head are summed over
+ * the heads and L1-normalised along the candidates, giving the distribution
+ * the indexer is trained to follow.  With lse the main attention's log-sum-exp
+ * over the same candidates (as dsa_sparse_mla_attn / dsa_dense_mla_attn return
+ * it) each head's probabilities sum to 1, so
+ *   p[r, e] = (1/H) sum_h exp(softmax_scale * q[r, h, :] . kv[kbase + s_e, :] - lse[r, h])
+ * (sum_e p[r, e] = 1 up to rounding).  Candidates: idx == NULL, every
+ * position s_e = e <= pos_r (dense warm-up); else s_e = idx[r, e] for the
+ * entries >= 0 (the selected set of the sparse stage).
+ *   q, kv   as dsa_sparse_mla_attn (BF16: d_qk = 576, H in {32, 64, 128};
+ *           F32: d_qk <= 1024, H <= 128)
+ *   idx     [total_q, k] int32 or NULL; k as dsa_sparse_mla_attn (ignored when NULL)
+ *   lse     [total_q, H] fp32 (natural log); a head with lse = -inf adds nothing
+ *   p       [total_q, ld_p] fp32 output, 16-B aligned.  Entries that are no
+ *           candidate are written as 0, up to the walk's whole 32-entry tiles
+ *           (dense: positions up to pos_r rounded up; selected: k rounded up),
+ *           so ld_p >= 32 * ceil(m / 32) with m = max_ctx (dense) or k.
+ * Arithmetic: bf16 MFMA scores, fp32 exponent and head sums.  F32 needs
+ * m + d_qk <= 16384.  No workspace.
+ */
+dsa_status dsa_attn_target(const dsa_batch* batch, const void* q, const void* kv, dsa_dtype dtype,
+                           const int32_t* idx, int32_t k, int32_t H, int32_t d_qk, float softmax_scale,
+                           const float* lse, float* p, int64_t ld_p, dsa_stream_t stream);
+
+/*
+ * Indexer-alignment loss and its gradient.  [P1] training "Step 1": a KL
+ * divergence between the target p and the indexer's output, read as
+ * softmax(I) over the same candidates; "Step 2": over the selected set only.
+ * For each query row r, with candidates s_e as in dsa_attn_target:
+ *   loss[r] = sum_e p[r, e] (log p[r, e] - log softmax(I)_e)       (0 log 0 = 0)
+ *   dI[r, e] = (sum_e' p[r, e']) softmax(I)_e - p[r, e]             (d loss[r] / d I[r, s_e])
+ * where I_e = scores[r, s_e] (dense: s_e = e, so dI is by position; selected:
+ * dI is by entry, aligned with idx; entries that are no candidate get 0).
+ *   scores [total_q, ld_scores] fp32 (the indexer's output), 16-B aligned
+ *   p      [total_q, ld_p] fp32; dI [total_q, ld_p] fp32 output or NULL;
+ *   loss   [total_q] fp32 output or NULL
+ * Arithmetic: fp32, row sums as trees.  No workspace.
+ */
+dsa_status dsa_indexer_kl(const dsa_batch* batch, const float* scores, int64_t ld_scores, const int32_t* idx,
+                          int32_t k, const float* p, int64_t ld_p, float* loss, float* dI, dsa_stream_t stream);
+
+/*
  * New tokens into the caches.  [P1] "Lightning indexer": the indexer runs in
  * FP8, so the indexer key of every token is stored as E4M3 codes;
  * "在MLA下實例化DSA": one latent row per token serves all query heads.  For

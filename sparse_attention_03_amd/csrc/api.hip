@@ -288,6 +288,54 @@ dsa_status dsa_dense_mla_attn(const dsa_batch* batch, const void* q, const void*
   return e == hipSuccess ? DSA_OK : hip_fail(e, "dense attention launch");
 }
 
+dsa_status dsa_attn_target(const dsa_batch* batch, const void* q, const void* kv, dsa_dtype dtype,
+                           const int32_t* idx, int32_t k, int32_t H, int32_t d_qk, float softmax_scale,
+                           const float* lse, float* p, int64_t ld_p, dsa_stream_t stream) {
+  g_err[0] = 0;
+  if (dsa_status s = check_batch(batch)) return s;
+  static const int32_t no_idx[4] __attribute__((aligned(16))) = {0, 0, 0, 0};
+  const bool dense = idx == nullptr;
+  // the attention's checks (d_v is the value width; the target has none: pass a valid one)
+  const int32_t d_v = dtype == DSA_BF16 ? 512 : d_qk;
+  if (dsa_status s = check_attention(q, kv, dtype, dense ? no_idx : idx, dense ? 1 : k, H, d_qk, d_v, softmax_scale,
+                                     p, lse))
+    return s;
+  if (!lse || !p) return fail(DSA_ERR_INVALID_ARG, "lse / p is NULL");
+  const int64_t m = dense ? batch->max_ctx : k;
+  if (ld_p < (m + 31) / 32 * 32 || ld_p % 4 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "ld_p = %lld must be >= %lld (whole 32-entry tiles) and a multiple of 4",
+                (long long)ld_p, (long long)((m + 31) / 32 * 32));
+  if (dtype == DSA_F32 && m + d_qk > 16384) return fail(DSA_ERR_UNSUPPORTED, "F32 target needs m + d_qk <= 16384");
+  if (batch->total_q == 0) return DSA_OK;
+  int cus = 0;
+  if (dsa_status s = device_cus(&cus)) return s;
+  dsa::AttnLaunch L{view(batch, 0, batch->total_q), q, kv, idx, dense ? batch->max_ctx : k, H, d_qk, d_v,
+                    softmax_scale, nullptr, nullptr, dtype == DSA_BF16, 1, nullptr, nullptr};
+  L.splits = dsa::attention_splits(batch->total_q, L.k, dtype == DSA_BF16, cus);
+  L.dense = dense;
+  L.target = true;
+  L.lse_in = lse;
+  L.p_out = p;
+  L.ld_p = ld_p;
+  hipError_t e = dsa::launch_attention(L, (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "target launch");
+}
+
+dsa_status dsa_indexer_kl(const dsa_batch* batch, const float* scores, int64_t ld_scores, const int32_t* idx,
+                          int32_t k, const float* p, int64_t ld_p, float* loss, float* dI, dsa_stream_t stream) {
+  g_err[0] = 0;
+  if (dsa_status s = check_batch(batch)) return s;
+  if (dsa_status s = check_scores(batch, scores, ld_scores)) return s;
+  if (!p || !aligned16(p) || (dI && !aligned16(dI))) return fail(DSA_ERR_INVALID_ARG, "p / dI NULL or misaligned");
+  const int64_t m = idx ? k : batch->max_ctx;
+  if (idx && (k < 1 || !aligned16(idx))) return fail(DSA_ERR_INVALID_ARG, "idx misaligned or k < 1");
+  if (ld_p < m) return fail(DSA_ERR_INVALID_ARG, "ld_p = %lld < %lld", (long long)ld_p, (long long)m);
+  if (batch->total_q == 0) return DSA_OK;
+  dsa::KlLaunch L{view(batch, 0, batch->total_q), scores, ld_scores, idx, k, p, ld_p, loss, dI};
+  hipError_t e = dsa::launch_indexer_kl(L, (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "indexer kl launch");
+}
+
 dsa_status dsa_cache_append(int64_t n, const int32_t* dst_rows, int64_t cache_rows, const void* k_new,
                             dsa_dtype k_dtype, int32_t d_I, uint8_t* k_cache, uint8_t* k_scale, const void* kv_new,
                             dsa_dtype kv_dtype, int32_t d_qk, void* kv_cache, dsa_stream_t stream) {

@@ -60,6 +60,11 @@ struct AttnLaunch {
   float* ws_lse;           // [rows, splits, H]
   bool dense = false;      // every candidate [0, pos] (idx unused; k = max_ctx)
   bool dense_short = false;  // rows with pos + 1 <= k walk [0, pos] without reading idx
+  // alignment target instead of attention: p_out[row, e] = sum_h exp(z_h,e - lse_in[row, h]) / H
+  bool target = false;
+  const float* lse_in = nullptr;  // [total_q, H] (global rows)
+  float* p_out = nullptr;         // [rows, ld_p]
+  int64_t ld_p = 0;
 };
 
 // New tokens into the caches: indexer keys quantised to E4M3 (optionally with
@@ -78,7 +83,21 @@ struct AppendLaunch {
   int64_t kv_row_bytes;    // multiple of 16
 };
 
+// KL(p || softmax(I)) per row over its candidates and dI (indexer alignment).
+struct KlLaunch {
+  BatchView b;
+  const float* scores;     // [rows, ld_s] index scores by position
+  int64_t ld_s;
+  const int32_t* idx;      // [rows, k] selected positions, or null (dense: entry e = position e)
+  int32_t k;
+  const float* p;          // [rows, ld_p] target by entry
+  int64_t ld_p;
+  float* loss;             // [rows] or null
+  float* dI;               // [rows, ld_p] by entry, or null
+};
+
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s);
+hipError_t launch_indexer_kl(const KlLaunch& a, hipStream_t s);
 hipError_t launch_cache_append(const AppendLaunch& a, hipStream_t s);
 
 // Workspace of the indexer for `rows` query rows (the FP8 ReLU path keeps the

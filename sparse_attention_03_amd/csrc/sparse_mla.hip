@@ -64,6 +64,9 @@ struct MlaArgs {
   int32_t dense_short;  // rows with n <= k walk [0, pos] directly (their idx is 0 .. pos)
   float* ws_o;
   float* ws_lse;
+  const float* lse_in;  // target: the main attention's lse per (row, head)
+  float* p_out;         // target: [rows, ld_p]
+  int64_t ld_p;
 };
 
 // Tile layout in LDS: line blocks.  The tile (32 rows x 72 chunks of 16 bytes)
@@ -392,6 +395,176 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   }
 }
 
+// Indexer-alignment target (blog "Deepseek v3.2 exp ..." training "Step 1"
+// and "Step 2"): per query row and candidate entry e, the heads' attention
+// probabilities exp(z_h,e - lse_h) summed over the heads and L1-normalised
+// along the candidates.  With the main attention's lse given, each head's
+// probabilities sum to 1, so the L1 norm of the head sum is H and the target
+// is the head sum / H.  Same walk, gather and score MFMAs as mla_bf16_kernel,
+// no value product.  Per tile, each wave reduces its heads within the lane
+// groups and leaves a 32-entry partial in LDS; after the next barrier wave 0
+// adds the waves' partials and stores the tile's 32 entries (0 for entries
+// that are no candidate).
+template <int HPW, int NW, bool DENSE>
+__global__ __launch_bounds__(NW * 64, 1) void mla_target_kernel(MlaArgs a) {
+  constexpr int NT = HPW / 16;
+  static_assert(4 % NW == 0, "a wave copies whole row groups");
+  constexpr int RG = row_groups_per_wave<NW>();
+  constexpr int NINS = kSegments * RG;
+  constexpr int AHEAD = 2 * NINS < 64 ? 3 : 1;
+  static_assert(AHEAD + 1 <= kNumBuf, "not enough LDS buffers");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  DSA_LDS int32_t* sel = (DSA_LDS int32_t*)((DSA_LDS uint8_t*)smem + kNumBuf * kTileBytes);
+  DSA_LDS uint32_t* tmask = (DSA_LDS uint32_t*)(sel + kMaxSel);
+  DSA_LDS float* psum = (DSA_LDS float*)(tmask + kMaxSel / kTile);  // [2][NW][kTile]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, li = lane & 15;
+  const int32_t r = a.row_begin + blockIdx.x;
+  const int32_t rl = blockIdx.x;
+  const int sp = blockIdx.y;
+  const RowInfo ri = locate_row_wave(load_seq_table(a.cu_q, a.cu_k, a.num_seqs), a.cu_q, a.cu_k, r);
+  const int32_t n = ri.pos + 1;
+  const bool dense = DENSE;
+  const int ntiles = dense ? (n + kTile - 1) / kTile : (a.k + kTile - 1) / kTile;
+  const int t0 = sp * a.tiles_per_split;
+  const int t1 = min(ntiles, t0 + a.tiles_per_split);
+  const int32_t* idx_row = a.idx + (int64_t)rl * a.k;
+  for (int base = wave * 64; !dense && base < ntiles * kTile; base += NW * 64) {
+    const int e = base + lane;
+    const bool in = e < ntiles * kTile;
+    const int32_t v = e < a.k ? idx_row[e] : -1;
+    if (in) sel[e] = v;
+    const uint64_t m = __ballot(in && v >= 0);
+    if (lane == 0) {
+      tmask[base / kTile] = (uint32_t)m;
+      tmask[base / kTile + 1] = (uint32_t)(m >> 32);
+    }
+  }
+  bf16x8 qf[NT][kQkSteps];
+  float lse2[NT];
+  const int head0 = wave * HPW;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int h = head0 + 16 * nt + li;
+    const uint16_t* qrow = a.q + ((int64_t)r * a.H + h) * kDqk + 8 * g;
+#pragma unroll
+    for (int c = 0; c < kQkSteps; ++c) qf[nt][c] = *(const bf16x8*)(qrow + 32 * c);
+    lse2[nt] = a.lse_in[(int64_t)r * a.H + h] * 1.4426950408889634f;  // -inf: the head adds nothing
+  }
+  __syncthreads();
+  const uint32_t tmask_lane = !dense && lane < kMaxSel / kTile ? tmask[lane] : 0u;
+  auto pos_at = [&](int t, int k) -> int32_t {
+    const int e = t * kTile + gather_row(wave, NW, k, lane);
+    return dense ? (e < n ? e : 0) : sel[e];
+  };
+  auto tile_mask = [&](int t) -> uint32_t {
+    return dense ? (n - kTile * t >= kTile ? 0xffffffffu : (1u << (n - kTile * t)) - 1u)
+                 : (uint32_t)__builtin_amdgcn_readlane((int)tmask_lane, t);
+  };
+  const float inv_h = 1.0f / (float)a.H;
+  float* prow = a.p_out + (int64_t)rl * a.ld_p;
+  // wave 0 stores tile t from the waves' partials (every wave wrote its part
+  // before the barrier that precedes this)
+  auto finish = [&](int t) {
+    if (wave == 0 && lane < kTile) {
+      const uint32_t vm = tile_mask(t);
+      float v = 0.0f;
+      if ((vm >> lane) & 1u) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) v += psum[((t & 1) * NW + w) * kTile + lane];
+        v *= inv_h;
+      }
+      prow[kTile * t + lane] = v;
+    }
+  };
+  int koff[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) koff[e] = tile_off(li, 4 * e + g);
+
+#pragma unroll
+  for (int j = 0; j < AHEAD; ++j)
+    if (t0 + j < t1) {
+      int32_t pj[RG];
+#pragma unroll
+      for (int k = 0; k < RG; ++k) pj[k] = pos_at(t0 + j, k);
+      gather_tile<NW>(a, ri.kbase, pj, smem + (size_t)j * kTileBytes);
+    }
+  int32_t p_next[RG];
+#pragma unroll
+  for (int k = 0; k < RG; ++k) p_next[k] = t0 + AHEAD < t1 ? pos_at(t0 + AHEAD, k) : 0;
+
+  for (int t = t0; t < t1; ++t) {
+    const int issued_after = min(AHEAD - 1, t1 - 1 - t);
+    if (issued_after >= 2) wait_vmcnt<(2 * NINS < 64 ? 2 * NINS : 0)>();
+    else if (issued_after == 1) wait_vmcnt<(NINS < 64 ? NINS : 0)>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (t + AHEAD < t1) {
+      gather_tile<NW>(a, ri.kbase, p_next, smem + (size_t)((t + AHEAD - t0) % kNumBuf) * kTileBytes);
+      if (t + AHEAD + 1 < t1) {
+#pragma unroll
+        for (int k = 0; k < RG; ++k) p_next[k] = pos_at(t + AHEAD + 1, k);
+      }
+    }
+    if (t > t0) finish(t - 1);
+    const uint32_t vmask = tile_mask(t);
+    if (vmask == 0) continue;
+    const DSA_LDS uint8_t* lb = (const DSA_LDS uint8_t*)smem + (size_t)((t - t0) % kNumBuf) * kTileBytes;
+    f32x4 sacc[2][NT];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const DSA_LDS uint8_t* kb[2] = {lb + koff[0], lb + koff[1]};
+    auto load_k = [&](int c, bf16x8 (&kf)[2]) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) kf[mt] = *(const DSA_LDS bf16x8*)(kb[c & 1] + 4096 * (c >> 1) + 2048 * mt);
+    };
+    bf16x8 kring[kQkAhead][2];
+#pragma unroll
+    for (int i = 0; i < kQkAhead; ++i) load_k(i, kring[i]);
+#pragma unroll
+    for (int c = 0; c < kQkSteps; ++c) {
+      const bf16x8 kc0 = kring[c % kQkAhead][0], kc1 = kring[c % kQkAhead][1];
+      if (c + kQkAhead < kQkSteps) load_k(c + kQkAhead, kring[c % kQkAhead]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        sacc[0][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc0, qf[nt][c], sacc[0][nt], 0, 0, 0);
+        sacc[1][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc1, qf[nt][c], sacc[1][nt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // probabilities of this lane's head(s), summed over the wave's heads:
+    // lane (g, li) holds keys 16 mt + 4 g + rr of head 16 nt + li
+    float ps[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        float v = 0.0f;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          v += lse2[nt] == -INFINITY ? 0.0f
+                                     : __builtin_amdgcn_exp2f(fmaf(sacc[mt][nt][rr], a.scale_log2, -lse2[nt]));
+        ps[mt][rr] = v;
+      }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) ps[mt][rr] += __shfl_xor(ps[mt][rr], m);
+    if (li == 0) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) psum[((t & 1) * NW + wave) * kTile + 16 * mt + 4 * g + rr] = ps[mt][rr];
+    }
+  }
+  __syncthreads();
+  if (t1 > t0) finish(t1 - 1);
+}
+
 // Combine key-split partials: o = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M).
 // One workgroup per (row, head); each thread owns 4 consecutive value columns.
 template <bool BF16>
@@ -430,6 +603,38 @@ __global__ __launch_bounds__(128) void merge_kernel(MlaArgs a, int d_v) {
     }
   }
   if (threadIdx.x == 0 && a.lse) a.lse[(int64_t)r * a.H + h] = norm[1];
+}
+
+// fp32 inputs, alignment target: one workgroup per row, the heads in turn;
+// each head's probabilities exp(z - lse_h) are added to the row's entries in
+// LDS, which are stored / H at the end.
+__global__ __launch_bounds__(256) void mla_target_f32_kernel(MlaArgs a, int d_qk, float scale, int m) {
+  extern __shared__ float fs[];  // [d_qk] query of one head, [m] head sum
+  const int32_t rl = blockIdx.x, r = a.row_begin + rl;
+  const RowInfo ri = locate_row(a.cu_q, a.cu_k, a.num_seqs, r);
+  float* qs = fs;
+  float* acc = fs + d_qk;
+  const float* kv = (const float*)a.kv;
+  const int32_t* sel = a.dense ? nullptr : a.idx + (int64_t)rl * a.k;
+  for (int e = threadIdx.x; e < m; e += blockDim.x) acc[e] = 0.0f;
+  for (int h = 0; h < a.H; ++h) {
+    __syncthreads();
+    const float* q = (const float*)a.q + ((int64_t)r * a.H + h) * d_qk;
+    for (int d = threadIdx.x; d < d_qk; d += blockDim.x) qs[d] = q[d];
+    __syncthreads();
+    const float lse = a.lse_in[(int64_t)r * a.H + h];
+    if (lse == -INFINITY) continue;
+    for (int e = threadIdx.x; e < m; e += blockDim.x) {
+      const int32_t p = a.dense ? (e <= ri.pos ? e : -1) : (e < a.k ? sel[e] : -1);
+      if (p < 0) continue;
+      const float* row = kv + (int64_t)(ri.kbase + p) * d_qk;
+      float dot = 0.0f;
+      for (int d = 0; d < d_qk; ++d) dot = fmaf(qs[d], row[d], dot);
+      acc[e] += expf(dot * scale - lse);
+    }
+  }
+  const float inv_h = 1.0f / (float)a.H;
+  for (int e = threadIdx.x; e < m; e += blockDim.x) a.p_out[(int64_t)rl * a.ld_p + e] = acc[e] * inv_h;
 }
 
 // fp32 inputs: plain two-pass softmax per (row, head) on the VALU.
@@ -490,6 +695,22 @@ __global__ __launch_bounds__(256) void mla_f32_kernel(MlaArgs a, int d_qk, int d
 }
 
 template <int HPW, int NW, bool DENSE>
+hipError_t launch_target(const MlaArgs& a, int rows, hipStream_t s) {
+  const size_t lds = (size_t)kNumBuf * kTileBytes + kMaxSel * sizeof(int32_t) + (kMaxSel / kTile) * sizeof(uint32_t) +
+                     2 * NW * kTile * sizeof(float);
+  static bool attr_set = false;  // benign race: idempotent attribute call
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)mla_target_kernel<HPW, NW, DENSE>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((mla_target_kernel<HPW, NW, DENSE>), dim3((unsigned)rows, (unsigned)a.splits), dim3(NW * 64),
+                     lds, s, a);
+  return hipGetLastError();
+}
+
+template <int HPW, int NW, bool DENSE>
 hipError_t launch_bf16(const MlaArgs& a, int rows, hipStream_t s) {
   const size_t lds = (size_t)kNumBuf * kTileBytes + kMaxSel * sizeof(int32_t) + (kMaxSel / kTile) * sizeof(uint32_t);
   static bool attr_set = false;  // benign race: idempotent attribute call
@@ -539,6 +760,27 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t s) {
   a.ws_lse = L.ws_lse;
   a.dense = L.dense ? 1 : 0;
   a.dense_short = L.dense_short ? 1 : 0;
+  a.lse_in = L.lse_in;
+  a.p_out = L.p_out;
+  a.ld_p = L.ld_p;
+  if (L.target) {
+    if (!L.bf16) {
+      // entries written per row: the candidates' span, whole tiles of the walk
+      const int m = L.dense ? L.b.max_ctx : L.k;
+      const size_t lds = (size_t)(L.d_qk + m) * sizeof(float);
+      hipLaunchKernelGGL(mla_target_f32_kernel, dim3((unsigned)rows), dim3(256), lds, s, a, L.d_qk, L.scale, m);
+      return hipGetLastError();
+    }
+    switch (L.H * 2 + (L.dense ? 1 : 0)) {
+      case 64: return launch_target<32, 1, false>(a, rows, s);
+      case 128: return launch_target<32, 2, false>(a, rows, s);
+      case 256: return launch_target<32, 4, false>(a, rows, s);
+      case 65: return launch_target<32, 1, true>(a, rows, s);
+      case 129: return launch_target<32, 2, true>(a, rows, s);
+      case 257: return launch_target<32, 4, true>(a, rows, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (!L.bf16) {
     const size_t lds = (size_t)(L.d_qk + L.k + 8) * sizeof(float);
     hipLaunchKernelGGL(mla_f32_kernel, dim3((unsigned)rows, (unsigned)L.H), dim3(256), lds, s, a, L.d_qk, L.d_v,

@@ -58,6 +58,8 @@ _SIGS = {
                             ctypes.c_int),
     "dsa_dense_mla_attn_workspace_size": ([_BP, ctypes.c_int, _i32, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
     "dsa_dense_mla_attn": ([_BP, _p, _p, ctypes.c_int, _i32, _i32, _i32, _f32, _p, _p, _p, _sz, _p], ctypes.c_int),
+    "dsa_attn_target": ([_BP, _p, _p, ctypes.c_int, _p, _i32, _i32, _i32, _f32, _p, _p, _i64, _p], ctypes.c_int),
+    "dsa_indexer_kl": ([_BP, _p, _i64, _p, _i32, _p, _i64, _p, _p, _p], ctypes.c_int),
     "dsa_cache_append": ([_i64, _p, _i64, _p, ctypes.c_int, _i32, _p, _p, _p, ctypes.c_int, _i32, _p, _p],
                          ctypes.c_int),
     "dsa_forward_workspace_size": ([_FP, ctypes.POINTER(_sz)], ctypes.c_int),
@@ -183,6 +185,19 @@ def forward_params(batch: DsaBatch, q_idx, k_idx, w, q, kv, k: int, d_v: int, so
     p.lse = None if lse is None else lse.data_ptr()
     p.out_idx = None if out_idx is None else out_idx.data_ptr()
     return p
+
+
+def dsa_attn_target(batch: DsaBatch, q, kv, softmax_scale: float, lse, p, idx=None, stream=None):
+    """Alignment target p [total_q, ld_p] (dense when idx is None)."""
+    _check(_lib.dsa_attn_target(ctypes.byref(batch), _ptr(q), _ptr(kv), _dtype_code(q), _ptr(idx),
+                                0 if idx is None else idx.shape[1], q.shape[1], q.shape[2], float(softmax_scale),
+                                _ptr(lse), _ptr(p), p.stride(0), _stream(stream)), "dsa_attn_target")
+
+
+def dsa_indexer_kl(batch: DsaBatch, scores, p, loss=None, dI=None, idx=None, stream=None):
+    _check(_lib.dsa_indexer_kl(ctypes.byref(batch), _ptr(scores), scores.stride(0), _ptr(idx),
+                               0 if idx is None else idx.shape[1], _ptr(p), p.stride(0), _ptr(loss), _ptr(dI),
+                               _stream(stream)), "dsa_indexer_kl")
 
 
 def dsa_cache_append(k_new=None, k_cache=None, k_scale=None, kv_new=None, kv_cache=None, dst_rows=None,

@@ -1,0 +1,180 @@
+"""Indexer alignment loss (HIP) against the CPU oracle: the target
+distribution (dsa_attn_target), KL(p || softmax(I)) and its gradient
+(dsa_indexer_kl)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dsa_check import announce, host, row_norm_err, rows_of
+from sparse_attention_03_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+# target: the exponent z - lse carries fp32 rounding of the score sum and of
+# the given lse (|z|, |lse| up to ~20: a few 1e-6 absolute), which is the
+# probability's relative error; measured about 2e-6, the bar is 10x that
+TOL_TARGET = 2e-5
+TOL_TARGET_F32 = 1e-5
+# KL: fp32 terms and tree sums over up to 8K entries.  dI = (sum p) q - p with
+# q = exp(I - lse): the fp32 lse (|lse| up to ~25 here) is off by up to
+# |lse| 2^-23 ~ 3e-6, a relative error of q; dI values are at most 1
+TOL_KL_LOSS = 1e-5
+TOL_KL_GRAD = 1e-5
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    from sparse_attention_03_amd import dsa as d
+    return d
+
+
+def _lse_dense(dsa, p):
+    _, lse = dsa.dense_mla_attn(p)
+    return lse
+
+
+def _target(dsa, p, lse, idx=None, ld=None):
+    from sparse_attention_03_amd import libdsa as L
+    m = p.max_ctx if idx is None else idx.shape[1]
+    ld = (m + 31) // 32 * 32 if ld is None else ld
+    out = torch.full((p.total_q, ld), float("nan"), dtype=torch.float32, device=DEV)
+    L.dsa_attn_target(L.batch_of(p), p.q, p.kv, p.scale, lse, out, idx=idx)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("H", [32, 64, 128])
+def test_dense_target(dsa, H):
+    announce("target dense", H)
+    p = gen.make_problem("t", [700, 300, 1200, 65], [700, 3, 1, 65], H_I=16, H=H, k=64, device=DEV, seed=80)
+    lse = _lse_dense(dsa, p)
+    got = _target(dsa, p, lse)
+    _, _, q = rows_of(p, None)
+    ref = oracle.attn_target(p.cu_q_host, p.cu_k_host, q, host(p.kv), p.scale, ld=got.shape[1])
+    pos = p.positions()
+    valid = np.arange(got.shape[1])[None, :] <= pos[:, None]
+    err = row_norm_err(got, ref, valid)
+    print("row-normalised error", err)
+    assert err <= TOL_TARGET
+    tail = (np.arange(got.shape[1])[None, :] > pos[:, None]) & \
+        (np.arange(got.shape[1])[None, :] < ((pos[:, None] + 1 + 31) // 32 * 32))
+    assert np.all(got[tail] == 0.0)          # the rest of the last tile: written as 0
+    np.testing.assert_allclose(np.where(valid, got, 0).sum(1), 1.0, atol=1e-4)
+
+
+def _subset_idx(seed, p, k):
+    rng = np.random.default_rng(seed)
+    pos = p.positions()
+    idx = np.full((p.total_q, k), -1, np.int32)
+    for i, ps in enumerate(pos):
+        n = ps + 1
+        sel = np.arange(n) if n <= k else np.sort(rng.choice(n, k, replace=False))
+        idx[i, :len(sel)] = sel
+    return idx
+
+
+@pytest.mark.parametrize("H,k", [(128, 256), (64, 2048), (32, 100)])
+def test_selected_set_target(dsa, H, k):
+    announce("target selected", H, k)
+    p = gen.make_problem("t", [3000, 150, 2500], [40, 1, 2], H_I=16, H=H, k=k, device=DEV, seed=81)
+    idx_h = _subset_idx(82, p, k)
+    idx = torch.from_numpy(idx_h).to(DEV)
+    _, lse = dsa.sparse_mla_attn(p, idx)
+    got = _target(dsa, p, lse, idx=idx)
+    _, _, q = rows_of(p, None)
+    ref = oracle.attn_target(p.cu_q_host, p.cu_k_host, q, host(p.kv), p.scale, idx=idx_h)
+    valid = idx_h >= 0
+    err = row_norm_err(got[:, :k], ref, valid)
+    print("row-normalised error", err)
+    assert err <= TOL_TARGET
+    assert np.all(got[:, :k][~valid] == 0.0)
+    np.testing.assert_allclose(got[:, :k].sum(1), 1.0, atol=1e-4)
+
+
+def test_selected_set_target_with_key_splits(dsa):
+    """Few rows: the walk is split over keys (every split writes its own tiles)."""
+    announce("target selected, splits")
+    p = gen.make_problem("t", [20000, 9000], [1, 1], H_I=16, H=128, k=2048, device=DEV, seed=83)
+    idx_h = _subset_idx(84, p, 2048)
+    idx = torch.from_numpy(idx_h).to(DEV)
+    _, lse = dsa.sparse_mla_attn(p, idx)
+    got = _target(dsa, p, lse, idx=idx)
+    _, _, q = rows_of(p, None)
+    ref = oracle.attn_target(p.cu_q_host, p.cu_k_host, q, host(p.kv), p.scale, idx=idx_h)
+    assert row_norm_err(got, ref, idx_h >= 0) <= TOL_TARGET
+
+
+def test_tiny_fp32_target(dsa):
+    announce("target fp32")
+    p = gen.make_config("tiny_fp32", device=DEV)
+    _, lse = dsa.dense_mla_attn(p)
+    got = _target(dsa, p, lse)
+    _, _, q = rows_of(p, None)
+    ref = oracle.attn_target(p.cu_q_host, p.cu_k_host, q, host(p.kv), p.scale, ld=got.shape[1])
+    valid = np.arange(got.shape[1])[None, :] <= p.positions()[:, None]
+    assert row_norm_err(got, ref, valid) <= TOL_TARGET_F32
+    idx_h = _subset_idx(85, p, 32)
+    idx = torch.from_numpy(idx_h).to(DEV)
+    _, lse = dsa.sparse_mla_attn(p, idx)
+    got = _target(dsa, p, lse, idx=idx)
+    ref = oracle.attn_target(p.cu_q_host, p.cu_k_host, q, host(p.kv), p.scale, idx=idx_h)
+    assert row_norm_err(got[:, :32], ref, idx_h >= 0) <= TOL_TARGET_F32
+
+
+def _kl_inputs(seed, p, m, idx_h=None):
+    """Synthetic index scores (by position) and targets (by entry)."""
+    rng = np.random.default_rng(seed)
+    ld = (p.max_ctx + 63) // 64 * 64
+    scores = (rng.standard_normal((p.total_q, ld)) * 4).astype(np.float32)
+    tgt = (rng.random((p.total_q, m)) ** 4).astype(np.float32)
+    tgt[:, 1::7] = 0.0
+    pos = p.positions()
+    for i, ps in enumerate(pos):
+        valid = (np.arange(m) <= ps) if idx_h is None else (idx_h[i] >= 0)
+        tgt[i, ~valid] = 0.0
+        tgt[i] /= max(tgt[i].sum(), 1e-30)
+    return scores, tgt
+
+
+def _kl_call(p, scores, tgt, idx=None):
+    from sparse_attention_03_amd import libdsa as L
+    s_d = torch.from_numpy(scores).to(DEV)
+    p_d = torch.from_numpy(tgt).to(DEV)
+    loss = torch.full((p.total_q,), float("nan"), dtype=torch.float32, device=DEV)
+    dI = torch.full(tgt.shape, float("nan"), dtype=torch.float32, device=DEV)
+    L.dsa_indexer_kl(L.batch_of(p), s_d, p_d, loss, dI, idx=idx)
+    torch.cuda.synchronize()
+    return loss.cpu().numpy(), dI.cpu().numpy()
+
+
+def test_kl_dense(dsa):
+    announce("kl dense")
+    p = gen.make_problem("kl", [5000, 300, 8000], [5000, 2, 1], H_I=16, H=32, k=64, device=DEV, seed=86)
+    m = (p.max_ctx + 63) // 64 * 64
+    scores, tgt = _kl_inputs(87, p, m)
+    loss, dI = _kl_call(p, scores, tgt)
+    pos = p.positions()
+    ref_loss, ref_dI = oracle.indexer_kl(scores[:, :m], tgt, pos + 1)
+    rel = np.abs(loss - ref_loss) / np.maximum(np.abs(ref_loss), 1.0)
+    print("loss rel error", rel.max())
+    assert rel.max() <= TOL_KL_LOSS
+    valid = np.arange(m)[None, :] <= pos[:, None]
+    assert np.max(np.abs(np.where(valid, dI - ref_dI, 0.0))) <= TOL_KL_GRAD
+    assert np.all(np.isnan(dI[~valid]))       # entries past the causal bound are not written
+
+
+def test_kl_selected_set(dsa):
+    announce("kl selected")
+    p = gen.make_problem("kl", [3000, 100, 2600], [300, 1, 2], H_I=16, H=32, k=512, device=DEV, seed=88)
+    k = 512
+    idx_h = _subset_idx(89, p, k)
+    scores, tgt = _kl_inputs(90, p, k, idx_h)
+    loss, dI = _kl_call(p, scores, tgt, idx=torch.from_numpy(idx_h).to(DEV))
+    gathered = np.take_along_axis(scores, np.maximum(idx_h, 0), axis=1)
+    cnt = (idx_h >= 0).sum(1)
+    ref_loss, ref_dI = oracle.indexer_kl(gathered, tgt, cnt)
+    rel = np.abs(loss - ref_loss) / np.maximum(np.abs(ref_loss), 1.0)
+    assert rel.max() <= TOL_KL_LOSS
+    assert np.max(np.abs(dI - ref_dI)) <= TOL_KL_GRAD     # non-candidate entries: 0 on both sides

@@ -242,6 +242,34 @@ dsa_status dsa_indexer_kl(const dsa_batch* batch, const float* scores, int64_t l
                           int32_t k, const float* p, int64_t ld_p, float* loss, float* dI, dsa_stream_t stream);
 
 /*
+ * Backward of the index score to the indexer's inputs: what the alignment
+ * loss trains.  [P1] training "Step 2": the indexer's input is detached from
+ * the computational graph, so its gradient ends at q_I, w and k_I (the
+ * projections that make them are outside this library).  For an upstream
+ * gradient g over each row's candidates (as dsa_attn_target: dense, entry
+ * e = position e; else entry e = position idx[r, e] when >= 0), with
+ * x = q_idx[r, j, :] . k[s, :] and k the (scaled) key:
+ *   dw[r, j]        += sum_e g[r, e] act(x)
+ *   dq_idx[r, j, :] += sum_e g[r, e] w[r, j] act'(x) k[s_e, :]
+ *   dk_idx[s, :]    += sum over rows and heads of g w act'(x) q_idx[r, j, :]
+ * act' of ReLU is 1 for x > 0 and 0 otherwise (0 at x = 0); of GELU
+ * Phi(x) + x phi(x).  dk is by key row of the batch (kbase + s); with scales it
+ * is the gradient with respect to the scaled key.
+ *   q_idx, k_idx, k_idx_scale, w, H_I, d_I, act as dsa_indexer_scores (FP8 only)
+ *   g       [total_q, ld_g] fp32, ld_g >= max_ctx (dense) or k
+ *   dq_idx  [total_q, H_I, d_I] fp32, dw [total_q, H_I] fp32, dk_idx [total_k, d_I]
+ *           fp32: ACCUMULATED with float atomics (zero them first; the order
+ *           of the additions, and so the last bits, may vary between runs)
+ * Arithmetic: x by FP8 MFMA (exact products, fp32 sums); g w act'(x) rounded
+ * to bf16 for the two bf16 MFMA products (k and q_idx are exact in bf16); fp32
+ * accumulation.  No workspace.
+ */
+dsa_status dsa_indexer_backward(const dsa_batch* batch, const void* q_idx, const void* k_idx, dsa_dtype idx_dtype,
+                                const uint8_t* k_idx_scale, const float* w, int32_t H_I, int32_t d_I, dsa_act act,
+                                const int32_t* idx, int32_t k, const float* g, int64_t ld_g,
+                                float* dq_idx, float* dw, float* dk_idx, dsa_stream_t stream);
+
+/*
  * New tokens into the caches.  [P1] "Lightning indexer": the indexer runs in
  * FP8, so the indexer key of every token is stored as E4M3 codes;
  * "在MLA下實例化DSA": one latent row per token serves all query heads.  For

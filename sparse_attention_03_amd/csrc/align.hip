@@ -118,7 +118,304 @@ __global__ __launch_bounds__(kKlThreads) void indexer_kl_kernel(KlArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Backward of the index score to the indexer's inputs (the indexer is what
+// the alignment loss trains; its input is detached from the rest, training
+// "Step 2").  For an upstream gradient g over a row's candidates, with
+// x = q_I[t,j] . k[s] (k scaled per token if scales are given):
+//   dw[t,j] += g act(x),  dq_I[t,j,:] += g w[t,j] act'(x) k[s,:],
+//   dk_I[s,:] += g w[t,j] act'(x) q_I[t,j,:].
+// One workgroup per (query row, key split), one wave per 16 indexer heads;
+// the row's candidates go in chunks of 32 keys through a double-buffered LDS
+// slab (key row kk: 16-byte chunk c at chunk c ^ ((kk >> 1) & 7)).  Per chunk
+// and wave:
+//   * x^T = K Q^T and x = Q K^T, two FP8 MFMAs each from the same fragments
+//     (the per-token key scale in the MFMA's scale operand): lane (g, li)
+//     holds keys 4g + r of head li, and heads 4g + r of key li;
+//   * dq[head][dim] += G^T-as-A (head li, keys 4g..4g+3: exactly the x^T
+//     lane layout) x K (keys 4g..4g+3 at dim li: four LDS bytes), bf16
+//     16x16x16 MFMAs with fp32 accumulators kept for the whole row;
+//   * dk^T[dim][key] = Q^T (dim li, heads 4g..4g+3, held in VGPRs) x G (the
+//     x lane layout), added over the waves with LDS float atomics, then
+//     scatter-added to dk in HBM (global float atomics) once per chunk.
+// G = g w act'(x) is rounded to bf16 for the two products (K and Q are E4M3
+// values, exact in bf16).  dq, dw and dk are accumulated with float atomics:
+// zero them first; the order of additions, and so the last bits, can vary.
+
+constexpr int kBwChunk = 32;
+
+struct IbArgs {
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t num_seqs, row_begin, row_end;
+  const uint8_t* q_idx;
+  const uint8_t* k_idx;
+  const uint8_t* k_scale;
+  const float* w;
+  int32_t H_I;
+  const int32_t* idx;
+  int32_t k;
+  const float* g;
+  int64_t ld_g;
+  float* dq;
+  float* dw;
+  float* dk;
+  int32_t chunks_per_split;
+};
+
+typedef __attribute__((ext_vector_type(4))) short bf16x4_t;
+
+__device__ __forceinline__ short bf16_bits(float f) {
+  __bf16 b = (__bf16)f;  // round to nearest even
+  return __builtin_bit_cast(short, b);
+}
+
+template <int ACT>
+__device__ __forceinline__ void act_and_slope(float x, float& a, float& da) {
+  if constexpr (ACT == 0) {
+    a = fmaxf(x, 0.0f);
+    da = x > 0.0f ? 1.0f : 0.0f;
+  } else {
+    const float cdf = 0.5f * (1.0f + erff(x * 0.70710678118654752f));
+    a = x * cdf;
+    da = cdf + x * 0.39894228040143268f * expf(-0.5f * x * x);
+  }
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+}
+
+template <int ACT>
+__global__ __launch_bounds__(256) void indexer_bwd_kernel(IbArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t slab[2][kBwChunk * 128];
+  __shared__ float dk_acc[kBwChunk * 128];
+  __shared__ int32_t kpos_s[2][kBwChunk];
+  __shared__ float g_s[2][kBwChunk];
+  __shared__ int32_t ksc_s[2][kBwChunk];
+  const int nthreads = blockDim.x;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, li = lane & 15;
+  const int32_t rl = blockIdx.x, r = a.row_begin + rl;
+  const RowInfo ri = locate_row(a.cu_q, a.cu_k, a.num_seqs, r);
+  const bool dense = a.idx == nullptr;
+  const int32_t m = dense ? ri.pos + 1 : a.k;
+  const int nchunks = (m + kBwChunk - 1) / kBwChunk;
+  const int c0 = blockIdx.y * a.chunks_per_split;
+  const int c1 = min(nchunks, c0 + a.chunks_per_split);
+  if (c0 >= c1) return;  // uniform over the workgroup
+  const int h0 = 16 * wave;
+  const uint8_t* qrow = a.q_idx + (int64_t)r * a.H_I * 128;
+  // FP8 fragments of the wave's heads (head h0 + li, dims 32g .. 32g + 31)
+  i32x8 qf;
+  {
+    const i32x4* p = (const i32x4*)(qrow + (h0 + li) * 128 + 32 * g);
+    const i32x4 lo = p[0], hi = p[1];
+    qf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  // Q^T as the A operand of dk^T (dim 16 dt + li, heads h0 + 4g .. + 3), bf16
+  bf16x4_t qT[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    short v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = bf16_bits(e4m3_to_f32(qrow[(h0 + 4 * g + j) * 128 + 16 * dt + li]));
+    qT[dt] = bf16x4_t{v[0], v[1], v[2], v[3]};
+  }
+  const float* wrow = a.w + (int64_t)r * a.H_I;
+  const float w_li = wrow[h0 + li];
+  float w_g[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w_g[j] = wrow[h0 + 4 * g + j];
+  const float* grow = a.g + (int64_t)rl * a.ld_g;
+  const int32_t* irow = dense ? nullptr : a.idx + (int64_t)rl * a.k;
+  const uint8_t* kbase = a.k_idx + (int64_t)ri.kbase * 128;
+
+  // staging of one chunk: 256 pieces of 16 bytes (key kk = piece / 8, chunk
+  // piece % 8), up to four per thread; the chunk's positions, g and scales
+  i32x4 stage[4];
+  int32_t st_pos = -1;
+  float st_g = 0.0f;
+  int32_t st_sc = 127;
+  auto entry_pos = [&](int32_t e) -> int32_t {
+    if (e >= m) return -1;
+    if (dense) return e;
+    const int32_t s = irow[e];
+    return s >= 0 && s <= ri.pos ? s : -1;
+  };
+  auto fetch = [&](int c) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int piece = tid + u * nthreads;
+      if (piece < kBwChunk * 8) {
+        const int kk = piece >> 3, ch = piece & 7;
+        const int32_t s = entry_pos(kBwChunk * c + kk);
+        stage[u] = *(const i32x4*)(kbase + (int64_t)(s < 0 ? 0 : s) * 128 + 16 * ch);
+      }
+    }
+    if (tid < kBwChunk) {
+      const int32_t e = kBwChunk * c + tid;
+      st_pos = entry_pos(e);
+      st_g = st_pos >= 0 ? grow[e] : 0.0f;
+      st_sc = (st_pos >= 0 && a.k_scale) ? (int32_t)a.k_scale[ri.kbase + st_pos] : 127;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int piece = tid + u * nthreads;
+      if (piece < kBwChunk * 8) {
+        const int kk = piece >> 3, ch = piece & 7;
+        *(DSA_LDS i32x4*)((DSA_LDS uint8_t*)slab[buf] + kk * 128 + 16 * (ch ^ ((kk >> 1) & 7))) = stage[u];
+      }
+    }
+    if (tid < kBwChunk) {
+      kpos_s[buf][tid] = st_pos;
+      g_s[buf][tid] = st_g;
+      ksc_s[buf][tid] = st_sc;
+    }
+  };
+  for (int e = tid; e < kBwChunk * 128; e += nthreads) dk_acc[e] = 0.0f;
+  fetch(c0);
+  store(0);
+  __syncthreads();
+
+  f32x4 dq_acc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) dq_acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dw_acc = 0.0f;
+
+  for (int c = c0; c < c1; ++c) {
+    const int buf = (c - c0) & 1;
+    if (c + 1 < c1) fetch(c + 1);  // in flight during this chunk
+    const DSA_LDS uint8_t* sb = (const DSA_LDS uint8_t*)slab[buf];
+    // key fragments (key 16 kt + li, dims 32g .. 32g + 31) and their scales
+    i32x8 kf[2];
+    int ksc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int kk = 16 * kt + li;
+      const int sw = (kk >> 1) & 7;
+      const i32x4 lo = *(const DSA_LDS i32x4*)(sb + kk * 128 + 16 * ((2 * g) ^ sw));
+      const i32x4 hi = *(const DSA_LDS i32x4*)(sb + kk * 128 + 16 * ((2 * g + 1) ^ sw));
+      kf[kt] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      ksc[kt] = ksc_s[buf][kk];
+    }
+    bf16x4_t gA[2], gB[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      // x^T: keys 16 kt + 4g + rr of head h0 + li
+      const f32x4 xt = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf[kt], qf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                                        0, ksc[kt], 0, 127);
+      // x: heads h0 + 4g + rr of key 16 kt + li
+      const f32x4 xx = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf, kf[kt], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                                        0, 127, 0, ksc[kt]);
+      short va[4], vb[4];
+      const float gl = g_s[buf][16 * kt + li];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float gk = g_s[buf][16 * kt + 4 * g + rr];
+        float av, dv;
+        act_and_slope<ACT>(xt[rr], av, dv);
+        dw_acc = fmaf(gk, av, dw_acc);
+        va[rr] = bf16_bits(gk * w_li * dv);
+        act_and_slope<ACT>(xx[rr], av, dv);
+        vb[rr] = bf16_bits(gl * w_g[rr] * dv);
+      }
+      gA[kt] = bf16x4_t{va[0], va[1], va[2], va[3]};
+      gB[kt] = bf16x4_t{vb[0], vb[1], vb[2], vb[3]};
+    }
+    // dq[head 4g + rr][dim 16 dt + li] += sum over keys of G^T x K
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      float kscale[4];
+      int kk4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kk4[j] = 16 * kt + 4 * g + j;
+        kscale[j] = __builtin_ldexpf(1.0f, ksc_s[buf][kk4[j]] - 127);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        short v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kk = kk4[j];
+          const uint32_t byte = sb[kk * 128 + 16 * (dt ^ ((kk >> 1) & 7)) + li];
+          v[j] = bf16_bits(e4m3_to_f32(byte) * kscale[j]);
+        }
+        dq_acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(gA[kt], bf16x4_t{v[0], v[1], v[2], v[3]}, dq_acc[dt],
+                                                                0, 0, 0);
+      }
+    }
+    // dk^T[dim 16 dt + 4g + rr][key 16 kt + li] for this wave's heads, summed over the waves in LDS
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qT[dt], gB[kt], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          atomicAdd(&dk_acc[(16 * kt + li) * 128 + 16 * dt + 4 * g + rr], d[rr]);
+      }
+    __syncthreads();  // every wave's dk part added, every wave done with slab[buf]
+    if (c + 1 < c1) store(buf ^ 1);
+    // scatter-add the chunk's dk rows, then clear the accumulator
+    for (int e = tid; e < kBwChunk * 128; e += nthreads) {
+      const int kk = e >> 7;
+      const int32_t s = kpos_s[buf][kk];
+      const float v = dk_acc[e];
+      if (s >= 0 && v != 0.0f) atomicAdd(a.dk + (int64_t)(ri.kbase + s) * 128 + (e & 127), v);
+      dk_acc[e] = 0.0f;
+    }
+    __syncthreads();
+  }
+  // dw: sum over the lane groups; dq: this split's share
+  dw_acc += __shfl_xor(dw_acc, 16);
+  dw_acc += __shfl_xor(dw_acc, 32);
+  if (g == 0) atomicAdd(a.dw + (int64_t)r * a.H_I + h0 + li, dw_acc);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      atomicAdd(a.dq + ((int64_t)r * a.H_I + h0 + 4 * g + rr) * 128 + 16 * dt + li, dq_acc[dt][rr]);
+}
+
 }  // namespace
+
+hipError_t launch_indexer_bwd(const IndexerBwdLaunch& L, hipStream_t s) {
+  const int32_t rows = L.b.row_end - L.b.row_begin;
+  if (rows <= 0) return hipSuccess;
+  IbArgs a;
+  a.cu_q = L.b.cu_q;
+  a.cu_k = L.b.cu_k;
+  a.num_seqs = L.b.num_seqs;
+  a.row_begin = L.b.row_begin;
+  a.row_end = L.b.row_end;
+  a.q_idx = (const uint8_t*)L.q_idx;
+  a.k_idx = (const uint8_t*)L.k_idx;
+  a.k_scale = L.k_scale;
+  a.w = L.w;
+  a.H_I = L.H_I;
+  a.idx = L.idx;
+  a.k = L.k;
+  a.g = L.g;
+  a.ld_g = L.ld_g;
+  a.dq = L.dq;
+  a.dw = L.dw;
+  a.dk = L.dk;
+  const int m = L.idx ? L.k : L.b.max_ctx;
+  const int nchunks = (m + kBwChunk - 1) / kBwChunk;
+  int splits = 1;
+  while (splits < nchunks && (int64_t)rows * splits < 2LL * L.num_cus) splits <<= 1;
+  if (splits > nchunks) splits = nchunks;
+  a.chunks_per_split = (nchunks + splits - 1) / splits;
+  const dim3 grid((unsigned)rows, (unsigned)splits), block((unsigned)(64 * (L.H_I / 16)));
+  if (L.act == 0) hipLaunchKernelGGL((indexer_bwd_kernel<0>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((indexer_bwd_kernel<1>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_indexer_kl(const KlLaunch& L, hipStream_t s) {
   const int32_t rows = L.b.row_end - L.b.row_begin;

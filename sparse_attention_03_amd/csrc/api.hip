@@ -336,6 +336,29 @@ dsa_status dsa_indexer_kl(const dsa_batch* batch, const float* scores, int64_t l
   return e == hipSuccess ? DSA_OK : hip_fail(e, "indexer kl launch");
 }
 
+dsa_status dsa_indexer_backward(const dsa_batch* batch, const void* q_idx, const void* k_idx, dsa_dtype idx_dtype,
+                                const uint8_t* k_idx_scale, const float* w, int32_t H_I, int32_t d_I, dsa_act act,
+                                const int32_t* idx, int32_t k, const float* g, int64_t ld_g, float* dq_idx,
+                                float* dw, float* dk_idx, dsa_stream_t stream) {
+  g_err[0] = 0;
+  if (dsa_status s = check_batch(batch)) return s;
+  if (dsa_status s = check_indexer(batch, q_idx, k_idx, idx_dtype, w, H_I, d_I, act)) return s;
+  if (idx_dtype != DSA_FP8_E4M3) return fail(DSA_ERR_UNSUPPORTED, "indexer backward needs FP8 inputs");
+  if (!g || !dq_idx || !dw || !dk_idx) return fail(DSA_ERR_INVALID_ARG, "g / dq_idx / dw / dk_idx is NULL");
+  if (!aligned16(g) || !aligned16(dq_idx) || !aligned16(dw) || !aligned16(dk_idx))
+    return fail(DSA_ERR_INVALID_ARG, "g and the gradients must be 16-byte aligned");
+  if (idx && (k < 1 || !aligned16(idx))) return fail(DSA_ERR_INVALID_ARG, "idx misaligned or k < 1");
+  const int64_t m = idx ? k : batch->max_ctx;
+  if (ld_g < m) return fail(DSA_ERR_INVALID_ARG, "ld_g = %lld < %lld", (long long)ld_g, (long long)m);
+  if (batch->total_q == 0) return DSA_OK;
+  int cus = 0;
+  if (dsa_status s = device_cus(&cus)) return s;
+  dsa::IndexerBwdLaunch L{view(batch, 0, batch->total_q), q_idx, k_idx, k_idx_scale, w, H_I, (int32_t)act, idx, k,
+                          g, ld_g, dq_idx, dw, dk_idx, cus};
+  hipError_t e = dsa::launch_indexer_bwd(L, (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "indexer backward launch");
+}
+
 dsa_status dsa_cache_append(int64_t n, const int32_t* dst_rows, int64_t cache_rows, const void* k_new,
                             dsa_dtype k_dtype, int32_t d_I, uint8_t* k_cache, uint8_t* k_scale, const void* kv_new,
                             dsa_dtype kv_dtype, int32_t d_qk, void* kv_cache, dsa_stream_t stream) {

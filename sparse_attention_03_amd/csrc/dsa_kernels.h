@@ -96,7 +96,27 @@ struct KlLaunch {
   float* dI;               // [rows, ld_p] by entry, or null
 };
 
+// Backward of the FP8 index score to q_I, w and k_I (accumulated with atomics).
+struct IndexerBwdLaunch {
+  BatchView b;
+  const void* q_idx;       // [total_q, H_I, 128] e4m3
+  const void* k_idx;       // [total_k, 128] e4m3
+  const uint8_t* k_scale;  // [total_k] or null
+  const float* w;          // [total_q, H_I]
+  int32_t H_I;
+  int32_t act;
+  const int32_t* idx;      // [rows, k] or null (dense)
+  int32_t k;
+  const float* g;          // [rows, ld_g] by entry
+  int64_t ld_g;
+  float* dq;               // [total_q, H_I, 128]
+  float* dw;               // [total_q, H_I]
+  float* dk;               // [total_k, 128]
+  int32_t num_cus;
+};
+
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s);
+hipError_t launch_indexer_bwd(const IndexerBwdLaunch& a, hipStream_t s);
 hipError_t launch_indexer_kl(const KlLaunch& a, hipStream_t s);
 hipError_t launch_cache_append(const AppendLaunch& a, hipStream_t s);
 

@@ -60,6 +60,8 @@ _SIGS = {
     "dsa_dense_mla_attn": ([_BP, _p, _p, ctypes.c_int, _i32, _i32, _i32, _f32, _p, _p, _p, _sz, _p], ctypes.c_int),
     "dsa_attn_target": ([_BP, _p, _p, ctypes.c_int, _p, _i32, _i32, _i32, _f32, _p, _p, _i64, _p], ctypes.c_int),
     "dsa_indexer_kl": ([_BP, _p, _i64, _p, _i32, _p, _i64, _p, _p, _p], ctypes.c_int),
+    "dsa_indexer_backward": ([_BP, _p, _p, ctypes.c_int, _p, _p, _i32, _i32, ctypes.c_int, _p, _i32, _p, _i64,
+                              _p, _p, _p, _p], ctypes.c_int),
     "dsa_cache_append": ([_i64, _p, _i64, _p, ctypes.c_int, _i32, _p, _p, _p, ctypes.c_int, _i32, _p, _p],
                          ctypes.c_int),
     "dsa_forward_workspace_size": ([_FP, ctypes.POINTER(_sz)], ctypes.c_int),
@@ -198,6 +200,15 @@ def dsa_indexer_kl(batch: DsaBatch, scores, p, loss=None, dI=None, idx=None, str
     _check(_lib.dsa_indexer_kl(ctypes.byref(batch), _ptr(scores), scores.stride(0), _ptr(idx),
                                0 if idx is None else idx.shape[1], _ptr(p), p.stride(0), _ptr(loss), _ptr(dI),
                                _stream(stream)), "dsa_indexer_kl")
+
+
+def dsa_indexer_backward(batch: DsaBatch, q_idx, k_idx, w, g, dq_idx, dw, dk_idx, act=DSA_ACT_RELU, idx=None,
+                         k_idx_scale=None, stream=None):
+    """Adds the index score's gradients for the upstream g into dq_idx, dw, dk_idx."""
+    _check(_lib.dsa_indexer_backward(ctypes.byref(batch), _ptr(q_idx), _ptr(k_idx), _dtype_code(q_idx),
+                                     _ptr(k_idx_scale), _ptr(w), q_idx.shape[1], q_idx.shape[2], act, _ptr(idx),
+                                     0 if idx is None else idx.shape[1], _ptr(g), g.stride(0), _ptr(dq_idx), _ptr(dw),
+                                     _ptr(dk_idx), _stream(stream)), "dsa_indexer_backward")
 
 
 def dsa_cache_append(k_new=None, k_cache=None, k_scale=None, kv_new=None, kv_cache=None, dst_rows=None,

@@ -178,3 +178,120 @@ def test_kl_selected_set(dsa):
     rel = np.abs(loss - ref_loss) / np.maximum(np.abs(ref_loss), 1.0)
     assert rel.max() <= TOL_KL_LOSS
     assert np.max(np.abs(dI - ref_dI)) <= TOL_KL_GRAD     # non-candidate entries: 0 on both sides
+
+
+# ------------------------------------------------------- indexer backward
+
+# dq and dk: g w act'(x) is rounded to bf16 (relative 2^-9) for the two
+# products, whose fp32 sums then carry about that relative error against the
+# terms' magnitudes; the bar is the bf16 attention bar.  dw is fp32 throughout.
+TOL_BWD_BF16 = 1e-2
+TOL_BWD_DW = 1e-5
+
+
+def _bwd_call(p, g_np, act=0, idx=None):
+    from sparse_attention_03_amd import libdsa as L
+    g_d = torch.from_numpy(g_np).to(DEV)
+    dq = torch.zeros(p.q_idx.shape, dtype=torch.float32, device=DEV)
+    dw = torch.zeros(p.w.shape, dtype=torch.float32, device=DEV)
+    dk = torch.zeros(p.k_idx.shape, dtype=torch.float32, device=DEV)
+    L.dsa_indexer_backward(L.batch_of(p), p.q_idx, p.k_idx, p.w, g_d, dq, dw, dk, act=act, idx=idx,
+                           k_idx_scale=p.k_idx_scale)
+    torch.cuda.synchronize()
+    return dq.cpu().numpy(), dw.cpu().numpy(), dk.cpu().numpy()
+
+
+def _bwd_oracle(p, g_np, act=0, idx_h=None):
+    q_idx, w, _ = rows_of(p, None)
+    return oracle.indexer_backward(p.cu_q_host, p.cu_k_host, q_idx, host(p.k_idx), w, g_np.astype(np.float64),
+                                   act=act, idx=idx_h,
+                                   k_scale=None if p.k_idx_scale is None else host(p.k_idx_scale))
+
+
+def _upstream(seed, p, m, integer, idx_h=None):
+    rng = np.random.default_rng(seed)
+    g = rng.integers(-4, 5, (p.total_q, m)).astype(np.float32) if integer else \
+        rng.standard_normal((p.total_q, m)).astype(np.float32)
+    pos = p.positions()
+    for i, ps in enumerate(pos):
+        valid = (np.arange(m) <= ps) if idx_h is None else (idx_h[i] >= 0)
+        g[i, ~valid] = 0.0
+    return g
+
+
+@pytest.mark.parametrize("H_I", [16, 64])
+@pytest.mark.parametrize("mode", ["dense", "selected"])
+def test_indexer_backward_integer_exact(dsa, H_I, mode):
+    """Integer inputs and upstream: g w act'(x) is exact in bf16 and every sum
+    is exact in fp32 in any order, so all three gradients are bit-exact."""
+    announce("indexer backward integer", H_I, mode)
+    p = gen.make_problem("bw", [300, 77, 1000, 129], [300, 5, 3, 64], H_I=H_I, H=32, k=64, integer=True,
+                         device=DEV, seed=91)
+    idx_h = _subset_idx(92, p, 64) if mode == "selected" else None
+    m = (p.max_ctx + 63) // 64 * 64 if idx_h is None else 64
+    g = _upstream(93, p, m, True, idx_h)
+    idx = None if idx_h is None else torch.from_numpy(idx_h).to(DEV)
+    dq, dw, dk = _bwd_call(p, g, idx=idx)
+    rq, rw, rk = _bwd_oracle(p, g, idx_h=idx_h)
+    assert np.array_equal(dq, rq.astype(np.float32))
+    assert np.array_equal(dw, rw.astype(np.float32))
+    assert np.array_equal(dk, rk.astype(np.float32))
+
+
+def _drop_ambiguous_relu(p, g, idx_h):
+    """ReLU's slope steps at x = 0, so where x lies within the fp32 rounding of
+    the kernel's sum (|x| <= 2^-17 sum |q_d k_d|: 128 products, fp32) the two
+    sides may take different branches.  Such (row, key) pairs get g = 0, so
+    every decision that counts is the same on both sides."""
+    vals = np.array([oracle.e4m3_value(c) for c in range(256)])
+    q = vals[host(p.q_idx)]
+    k = vals[host(p.k_idx)]
+    pos, base = p.positions(), p.cu_k_host[:-1][np.searchsorted(p.cu_q_host, np.arange(p.total_q), "right") - 1]
+    dropped = 0
+    for i in range(p.total_q):
+        sel = np.arange(pos[i] + 1) if idx_h is None else idx_h[i][idx_h[i] >= 0]
+        ent = sel if idx_h is None else np.nonzero(idx_h[i] >= 0)[0]
+        kk = k[base[i] + sel]
+        x = q[i] @ kk.T
+        band = 2.0 ** -17 * (np.abs(q[i]) @ np.abs(kk).T)
+        amb = np.any(np.abs(x) <= band, axis=0)
+        g[i, ent[amb]] = 0.0
+        dropped += int(amb.sum())
+    print("ambiguous (row, key) pairs dropped:", dropped)
+    return g
+
+
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("mode", ["dense", "selected"])
+def test_indexer_backward_random(dsa, act, mode):
+    announce("indexer backward random", act, mode)
+    p = gen.make_problem("bw", [2000, 300, 700], [400, 2, 1], H_I=64, H=32, k=256, device=DEV, seed=94)
+    idx_h = _subset_idx(95, p, 256) if mode == "selected" else None
+    m = (p.max_ctx + 63) // 64 * 64 if idx_h is None else 256
+    g = _upstream(96, p, m, False, idx_h)
+    if act == 0:
+        g = _drop_ambiguous_relu(p, g, idx_h)
+    idx = None if idx_h is None else torch.from_numpy(idx_h).to(DEV)
+    dq, dw, dk = _bwd_call(p, g, act=act, idx=idx)
+    rq, rw, rk = _bwd_oracle(p, g, act=act, idx_h=idx_h)
+    e_q = row_norm_err(dq, rq)
+    e_w = row_norm_err(dw, rw)
+    used = np.abs(rk).max(1) > 0
+    e_k = row_norm_err(dk[used], rk[used])
+    print(f"row-normalised errors: dq {e_q:.2e} dw {e_w:.2e} dk {e_k:.2e}")
+    assert e_q <= TOL_BWD_BF16 and e_k <= TOL_BWD_BF16 and e_w <= TOL_BWD_DW
+    assert np.all(dk[~used] == 0.0)
+
+
+def test_indexer_backward_scaled_keys(dsa):
+    announce("indexer backward scaled keys")
+    p = gen.make_problem("bw", [900, 40], [200, 1], H_I=32, H=32, k=128, integer=True, device=DEV, seed=97)
+    rng = np.random.default_rng(98)
+    p.k_idx_scale = torch.from_numpy(rng.integers(124, 131, p.total_k).astype(np.uint8)).to(DEV)
+    m = (p.max_ctx + 63) // 64 * 64
+    g = _upstream(99, p, m, True)
+    dq, dw, dk = _bwd_call(p, g)
+    rq, rw, rk = _bwd_oracle(p, g)
+    assert np.array_equal(dq, rq.astype(np.float32))
+    assert np.array_equal(dw, rw.astype(np.float32))
+    assert np.array_equal(dk, rk.astype(np.float32))

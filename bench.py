@@ -289,6 +289,80 @@ def append_bench(steps=10, warmup=2):
     return res
 
 
+def align_bench(steps=5, warmup=1):
+    """The indexer-alignment training kernels on one sequence of L tokens (all
+    rows as queries, the prefill distributions): the sparse stage (target over
+    the k = 2048 selected entries, KL, indexer backward) for L = 8192 and for a
+    4096-row chunk of the 131072-token prefill, and the dense warm-up stage
+    (target over every candidate, KL, backward) for L = 8192."""
+    import torch
+    from sparse_attention_03_amd import dsa, inputs as gen, libdsa as L
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    res = {}
+    for name, cfg, rows_from in (("prefill_8k", "prefill_8k", 0), ("prefill_128k_chunk", "prefill_128k", 131072 - 4096)):
+        p = gen.make_config(cfg, device="cuda")
+        if rows_from:
+            # the last 4096 query rows of the sequence (every row has 2048 selected entries)
+            n = p.total_q
+            keep = slice(rows_from, n)
+            p.q_idx, p.w, p.q = p.q_idx[keep].contiguous(), p.w[keep].contiguous(), p.q[keep].contiguous()
+            p.cu_q = torch.tensor([0, n - rows_from], dtype=torch.int32, device="cuda")
+            p.cu_q_host = np.array([0, n - rows_from], dtype=np.int32)
+        b = L.batch_of(p)
+        f = dsa.Forward(p)
+        out, lse, idx = f()
+        scores = dsa.indexer_scores(p, fill=0.0)
+        T, k, H_I = p.total_q, p.k, p.H_I
+        tgt = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        loss = torch.empty((T,), dtype=torch.float32, device="cuda")
+        dI = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        dq = torch.zeros(p.q_idx.shape, dtype=torch.float32, device="cuda")
+        dw = torch.zeros(p.w.shape, dtype=torch.float32, device="cuda")
+        dk = torch.zeros(p.k_idx.shape, dtype=torch.float32, device="cuda")
+        t_tgt = timed(lambda: L.dsa_attn_target(b, p.q, p.kv, p.scale, lse, tgt, idx=idx))
+        t_kl = timed(lambda: L.dsa_indexer_kl(b, scores, tgt, loss, dI, idx=idx))
+        t_bw = timed(lambda: L.dsa_indexer_backward(b, p.q_idx, p.k_idx, p.w, dI, dq, dw, dk, idx=idx))
+        pairs = T * k
+        r = {"rows": T, "k": k,
+             "target_ms": t_tgt, "target_TFLOPs": pairs * p.H * 576 * 2 / t_tgt / 1e9,
+             "kl_ms": t_kl, "kl_GBs": pairs * (4 + 4 + 4 + 4) / t_kl / 1e6,
+             "backward_ms": t_bw, "backward_TFLOPs": pairs * H_I * 128 * 2 * 4 / t_bw / 1e9}
+        res[f"sparse_{name}"] = r
+        log("sparse", name, json.dumps(r))
+        if not rows_from:
+            # dense warm-up: every candidate
+            ld = dsa.score_ld(p.max_ctx)
+            _, lse_d = dsa.dense_mla_attn(p)
+            tgt_d = torch.empty((T, ld), dtype=torch.float32, device="cuda")
+            dI_d = torch.empty((T, ld), dtype=torch.float32, device="cuda")
+            t_tgt = timed(lambda: L.dsa_attn_target(b, p.q, p.kv, p.scale, lse_d, tgt_d))
+            t_kl = timed(lambda: L.dsa_indexer_kl(b, scores, tgt_d, loss, dI_d))
+            t_bw = timed(lambda: L.dsa_indexer_backward(b, p.q_idx, p.k_idx, p.w, dI_d, dq, dw, dk))
+            pairs = int((p.positions() + 1).sum())
+            r = {"rows": T, "pairs": pairs,
+                 "target_ms": t_tgt, "target_TFLOPs": pairs * p.H * 576 * 2 / t_tgt / 1e9,
+                 "kl_ms": t_kl, "kl_GBs": pairs * (4 + 4 + 4 + 4) / t_kl / 1e6,
+                 "backward_ms": t_bw, "backward_TFLOPs": pairs * H_I * 128 * 2 * 4 / t_bw / 1e9}
+            res[f"dense_{name}"] = r
+            log("dense", name, json.dumps(r))
+            del tgt_d, dI_d
+        del p, f, out, lse, idx, scores, tgt, dI, dq, dw, dk
+        torch.cuda.empty_cache()
+    return res
+
+
 def _short(name):
     m = re.search(r"dsa::\(anonymous namespace\)::(\w+)", name)
     if m:
@@ -377,6 +451,8 @@ def main():
     ap.add_argument("--crossover", metavar="L", type=int, nargs="+",
                     help="masked mode (dense attention) against the sparse path on one prefill sequence of each "
                          "length L, and exit")
+    ap.add_argument("--align", action="store_true",
+                    help="time the indexer-alignment kernels (target, KL, indexer backward), then exit")
     ap.add_argument("--append", action="store_true",
                     help="time dsa_cache_append (prefill and decode) and the indexer with key scales, then exit")
     ap.add_argument("--summarize", metavar="DIR", nargs="+", help="summarise rocprofv3 CSV output in DIR... and exit")
@@ -396,6 +472,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.crossover:
         print(json.dumps({"crossover": crossover(args.crossover, steps=args.steps, warmup=args.warmup)}), flush=True)
+        return
+    if args.align:
+        print(json.dumps({"align": align_bench(steps=args.steps, warmup=args.warmup)}), flush=True)
         return
     if args.append:
         print(json.dumps({"append": append_bench(steps=args.steps, warmup=args.warmup)}), flush=True)

@@ -135,14 +135,18 @@ __global__ __launch_bounds__(kKlThreads) void indexer_kl_kernel(KlArgs a) {
 //   * dq[head][dim] += G^T-as-A (head li, keys 4g..4g+3: exactly the x^T
 //     lane layout) x K (keys 4g..4g+3 at dim li: four LDS bytes), bf16
 //     16x16x16 MFMAs with fp32 accumulators kept for the whole row;
-//   * dk^T[dim][key] = Q^T (dim li, heads 4g..4g+3, held in VGPRs) x G (the
-//     x lane layout), added over the waves with LDS float atomics, then
-//     scatter-added to dk in HBM (global float atomics) once per chunk.
+//   * dk[key][dim] = G-as-A (key li, heads 4g..4g+3: the x lane layout) x Q
+//     (heads 4g..4g+3 at dim li, held in VGPRs); each wave stores its part
+//     into its own LDS region (rows of 132 floats: the four lane groups land
+//     on disjoint banks), and once per chunk the waves' parts are added in a
+//     fixed order and scatter-added to dk in HBM (global float atomics).
+//     (Adding the parts with LDS float atomics instead cost 5x the kernel.)
 // G = g w act'(x) is rounded to bf16 for the two products (K and Q are E4M3
 // values, exact in bf16).  dq, dw and dk are accumulated with float atomics:
 // zero them first; the order of additions, and so the last bits, can vary.
 
 constexpr int kBwChunk = 32;
+constexpr int kBwStride = 132;  // floats per key row of a wave's dk part
 
 struct IbArgs {
   const int32_t* cu_q;
@@ -189,7 +193,7 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
 template <int ACT>
 __global__ __launch_bounds__(256) void indexer_bwd_kernel(IbArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t slab[2][kBwChunk * 128];
-  __shared__ float dk_acc[kBwChunk * 128];
+  __shared__ float dk_part[4][kBwChunk * kBwStride];
   __shared__ int32_t kpos_s[2][kBwChunk];
   __shared__ float g_s[2][kBwChunk];
   __shared__ int32_t ksc_s[2][kBwChunk];
@@ -214,7 +218,7 @@ __global__ __launch_bounds__(256) void indexer_bwd_kernel(IbArgs a) {
     const i32x4 lo = p[0], hi = p[1];
     qf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
-  // Q^T as the A operand of dk^T (dim 16 dt + li, heads h0 + 4g .. + 3), bf16
+  // Q as the B operand of dk (heads h0 + 4g .. + 3 at dim 16 dt + li), bf16
   bf16x4_t qT[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
@@ -276,7 +280,6 @@ __global__ __launch_bounds__(256) void indexer_bwd_kernel(IbArgs a) {
       ksc_s[buf][tid] = st_sc;
     }
   };
-  for (int e = tid; e < kBwChunk * 128; e += nthreads) dk_acc[e] = 0.0f;
   fetch(c0);
   store(0);
   __syncthreads();
@@ -349,25 +352,26 @@ __global__ __launch_bounds__(256) void indexer_bwd_kernel(IbArgs a) {
                                                                 0, 0, 0);
       }
     }
-    // dk^T[dim 16 dt + 4g + rr][key 16 kt + li] for this wave's heads, summed over the waves in LDS
+    // dk[key 16 kt + 4g + rr][dim 16 dt + li] for this wave's heads, into its LDS part
+    float* part = dk_part[wave];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qT[dt], gB[kt], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(gB[kt], qT[dt], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          atomicAdd(&dk_acc[(16 * kt + li) * 128 + 16 * dt + 4 * g + rr], d[rr]);
+        for (int rr = 0; rr < 4; ++rr) part[(16 * kt + 4 * g + rr) * kBwStride + 16 * dt + li] = d[rr];
       }
-    __syncthreads();  // every wave's dk part added, every wave done with slab[buf]
+    __syncthreads();  // every wave's dk part written, every wave done with slab[buf]
     if (c + 1 < c1) store(buf ^ 1);
-    // scatter-add the chunk's dk rows, then clear the accumulator
+    // the waves' parts added in order, scatter-added to the chunk's key rows
+    const int nwaves = nthreads >> 6;
     for (int e = tid; e < kBwChunk * 128; e += nthreads) {
       const int kk = e >> 7;
       const int32_t s = kpos_s[buf][kk];
-      const float v = dk_acc[e];
+      float v = 0.0f;
+      for (int w = 0; w < nwaves; ++w) v += dk_part[w][kk * kBwStride + (e & 127)];
       if (s >= 0 && v != 0.0f) atomicAdd(a.dk + (int64_t)(ri.kbase + s) * 128 + (e & 127), v);
-      dk_acc[e] = 0.0f;
     }
     __syncthreads();
   }

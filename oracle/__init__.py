@@ -37,6 +37,8 @@ def lib():
         L.dsa_oracle_sparse_mla.argtypes = [i32, p, p, i32, p, p, p, i32, p, i32, i32, i32, i32, dbl, p, p]
         L.dsa_oracle_dense_mla.argtypes = [i32, p, p, i32, p, p, p, i32, i32, i32, i32, dbl, p, p]
         L.dsa_oracle_quantize_keys.argtypes = [p, i32, i64, i32, i32, p, p]
+        L.dsa_oracle_sparse_mla_backward.argtypes = [i32, p, p, i32, p, p, p, i32, p, i32, i32, i32, i32, dbl,
+                                                     p, p, p]
         L.dsa_oracle_attn_target.argtypes = [i32, p, p, i32, p, p, p, i32, p, i32, i32, i32, dbl, p]
         L.dsa_oracle_indexer_kl.argtypes = [i32, i32, p, p, p, p, p]
         L.dsa_oracle_indexer_backward.argtypes = [i32, p, p, i32, p, p, p, i32, p, p, i32, i32, i32, p, i32, p,
@@ -45,7 +47,7 @@ def lib():
                                          p, p, i32, i32, i32, i32, dbl, i32, i64, p, p, p, p]
         for f in (L.dsa_oracle_indexer, L.dsa_oracle_topk, L.dsa_oracle_sparse_mla, L.dsa_oracle_dense_mla,
                   L.dsa_oracle_quantize_keys, L.dsa_oracle_forward, L.dsa_oracle_attn_target,
-                  L.dsa_oracle_indexer_kl, L.dsa_oracle_indexer_backward):
+                  L.dsa_oracle_indexer_kl, L.dsa_oracle_indexer_backward, L.dsa_oracle_sparse_mla_backward):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -139,6 +141,28 @@ def sparse_mla(cu_q, cu_k, q, kv, idx, d_v, scale, rows=None):
     if rc != 0:
         raise ValueError("oracle sparse_mla: invalid batch / rows / indices")
     return out, lse
+
+
+def sparse_mla_backward(cu_q, cu_k, q, kv, idx, d_v, scale, dout, rows=None):
+    """Gradients of the sparse MQA attention for the upstream dout [nrows, H, d_v]:
+    (dq [nrows, H, d_qk], dkv [total_k, d_qk]) float64, dkv summed over rows."""
+    cu_q, cu_k = _c(cu_q, np.int32), _c(cu_k, np.int32)
+    rows = _rows(rows, cu_q)
+    q, kv = np.ascontiguousarray(q), np.ascontiguousarray(kv)
+    dt = _dtype_code(q)
+    assert _dtype_code(kv) == dt
+    nrows, H, d_qk = q.shape
+    idx = _c(idx, np.int32)
+    dout = _c(dout, np.float64)
+    assert dout.shape == (nrows, H, d_v)
+    dq = np.zeros((nrows, H, d_qk), dtype=np.float64)
+    dkv = np.zeros(kv.shape, dtype=np.float64)
+    rc = lib().dsa_oracle_sparse_mla_backward(len(cu_q) - 1, _ptr(cu_q), _ptr(cu_k), nrows, _ptr(rows), _ptr(q),
+                                              _ptr(kv), dt, _ptr(idx), idx.shape[1], H, d_qk, d_v, float(scale),
+                                              _ptr(dout), _ptr(dq), _ptr(dkv))
+    if rc != 0:
+        raise ValueError("oracle sparse_mla_backward: invalid batch / rows / indices")
+    return dq, dkv
 
 
 def dense_mla(cu_q, cu_k, q, kv, d_v, scale, rows=None):

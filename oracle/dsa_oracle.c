@@ -450,6 +450,89 @@ int dsa_oracle_indexer_backward(int nseq, const int32_t* cu_q, const int32_t* cu
 }
 
 /* ------------------------------------------------------------------ */
+/* Backward of the sparse MQA attention.  [P2] 【稀疏训练阶段】 / [P5]: the
+ * sparse training stage updates every parameter through the sparse attention,
+ * so its gradient flows to the query and, by scatter-add, to the latent rows
+ * that were selected.  For row i, head h, selected positions S (entries of
+ * idx >= 0), z_s = scale q_h . kv_s, P = softmax(z), out_h = sum_s P_s v_s
+ * (v_s = kv_s[0:d_v]) and the upstream gradient dout_h:
+ *   dP_s = dout_h . v_s,  D_h = dout_h . out_h = sum_s P_s dP_s,
+ *   dz_s = P_s (dP_s - D_h),
+ *   dq_h   = scale sum_s dz_s kv_s
+ *   dkv_s += scale dz_s q_h   (all d_qk columns)  +  P_s dout_h   (first d_v)
+ * dkv is accumulated over rows and heads (the caller zeroes it). */
+/* ------------------------------------------------------------------ */
+int dsa_oracle_sparse_mla_backward(int nseq, const int32_t* cu_q, const int32_t* cu_k,
+                                   int nrows, const int32_t* rows,
+                                   const void* q, const void* kv, int dtype,
+                                   const int32_t* idx, int k, int H, int d_qk, int d_v, double scale,
+                                   const double* dout, double* dq, double* dkv) {
+    double table[256];
+    for (int c = 0; c < 256; ++c) table[c] = dsa_oracle_e4m3_value(c);
+    double* z = (double*)malloc((size_t)(k > 0 ? k : 1) * sizeof(double));
+    double* dp = (double*)malloc((size_t)(k > 0 ? k : 1) * sizeof(double));
+    double* o = (double*)malloc((size_t)(d_v > 0 ? d_v : 1) * sizeof(double));
+    int rc = 0;
+    for (int i = 0; i < nrows && rc == 0; ++i) {
+        int64_t pos, kbase;
+        if (locate_row(nseq, cu_q, cu_k, rows[i], &pos, &kbase) != 0) { rc = -1; break; }
+        const int32_t* sel = idx + (int64_t)i * k;
+        for (int h = 0; h < H; ++h) {
+            const int64_t qo = ((int64_t)i * H + h) * d_qk;
+            double* dqh = dq + qo;
+            for (int d = 0; d < d_qk; ++d) dqh[d] = 0.0;
+            double m = -INFINITY;
+            int nvalid = 0;
+            for (int e = 0; e < k; ++e) {
+                if (sel[e] < 0) continue;
+                if (sel[e] > pos) { rc = -1; break; }
+                double dot = 0.0;
+                for (int d = 0; d < d_qk; ++d)
+                    dot += load_elem(q, dtype, qo + d, table) * load_elem(kv, dtype, (kbase + sel[e]) * d_qk + d, table);
+                z[e] = scale * dot;
+                if (z[e] > m) m = z[e];
+                ++nvalid;
+            }
+            if (rc != 0 || nvalid == 0) continue;
+            double l = 0.0;
+            for (int e = 0; e < k; ++e)
+                if (sel[e] >= 0) l += exp(z[e] - m);
+            /* probabilities, the output and dP */
+            const double* dO = dout + ((int64_t)i * H + h) * d_v;
+            for (int d = 0; d < d_v; ++d) o[d] = 0.0;
+            for (int e = 0; e < k; ++e) {
+                if (sel[e] < 0) continue;
+                z[e] = exp(z[e] - m) / l;  /* now P */
+                double acc = 0.0;
+                for (int d = 0; d < d_v; ++d) {
+                    const double v = load_elem(kv, dtype, (kbase + sel[e]) * d_qk + d, table);
+                    o[d] += z[e] * v;
+                    acc += dO[d] * v;
+                }
+                dp[e] = acc;
+            }
+            double D = 0.0;
+            for (int d = 0; d < d_v; ++d) D += dO[d] * o[d];
+            for (int e = 0; e < k; ++e) {
+                if (sel[e] < 0) continue;
+                const double dz = z[e] * (dp[e] - D);
+                double* row = dkv + (kbase + sel[e]) * d_qk;
+                for (int d = 0; d < d_qk; ++d) {
+                    const double c = load_elem(kv, dtype, (kbase + sel[e]) * d_qk + d, table);
+                    dqh[d] += scale * dz * c;
+                    row[d] += scale * dz * load_elem(q, dtype, qo + d, table);
+                }
+                for (int d = 0; d < d_v; ++d) row[d] += z[e] * dO[d];
+            }
+        }
+    }
+    free(z);
+    free(dp);
+    free(o);
+    return rc;
+}
+
+/* ------------------------------------------------------------------ */
 /* Dense causal MQA: attention of every query row over all its candidates
  * [0, pos], no selection.  [P2] 【推理成本评估】 describes this "masked mode"
  * for short prefill, where DSA is emulated by a mask over the dense

@@ -654,6 +654,72 @@ def test_indexer_backward_with_key_scales():
         np.testing.assert_allclose(a_, b_, rtol=1e-13, atol=1e-300)
 
 
+# ------------------------------------------------- sparse attention backward
+
+def _torch_attn_grads(cu_q, cu_k, q, kv, idx, d_v, scale, dout):
+    """Gradients of sum(dout * out) through torch's autograd, the sparse MQA
+    attention built from torch ops in float64 (gather, softmax, matmul)."""
+    pos, base = _positions(cu_q, cu_k)
+    qt = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    kt = torch.tensor(kv, dtype=torch.float64, requires_grad=True)
+    total = torch.zeros((), dtype=torch.float64)
+    for i in range(len(pos)):
+        sel = idx[i][idx[i] >= 0]
+        if len(sel) == 0:
+            continue
+        c = kt[torch.from_numpy(base[i] + sel)]
+        pr = torch.softmax(scale * qt[i] @ c.T, dim=-1)
+        out = pr @ c[:, :d_v]
+        total = total + (torch.from_numpy(dout[i]) * out).sum()
+    total.backward()
+    return qt.grad.numpy(), kt.grad.numpy()
+
+
+def test_sparse_attention_backward_matches_torch_autograd():
+    rng = np.random.default_rng(72)
+    cu_q, cu_k = _ragged([40, 26, 9], [40, 3, 1])
+    pos, _ = _positions(cu_q, cu_k)
+    H, d_qk, d_v, k = 3, 24, 16, 10
+    q = rng.standard_normal((len(pos), H, d_qk)).astype(np.float32)
+    kv = rng.standard_normal((int(cu_k[-1]), d_qk)).astype(np.float32)
+    idx = np.full((len(pos), k), -1, np.int32)
+    for i in range(len(pos)):
+        n = pos[i] + 1
+        sel = np.sort(rng.choice(n, min(n, k), replace=False))
+        idx[i, :len(sel)] = sel
+    idx[5, :] = -1                                  # an empty selection: no gradient
+    dout = rng.standard_normal((len(pos), H, d_v))
+    dq, dkv = oracle.sparse_mla_backward(cu_q, cu_k, q, kv, idx, d_v, 0.3, dout)
+    rq, rk = _torch_attn_grads(cu_q, cu_k, q, kv, idx, d_v, 0.3, dout)
+    np.testing.assert_allclose(dq, rq, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dkv, rk, rtol=1e-10, atol=1e-12)
+    assert np.all(dq[5] == 0.0)
+    # rows nobody selected get no gradient
+    chosen = np.zeros(len(kv), bool)
+    for i in range(len(pos)):
+        chosen[_positions(cu_q, cu_k)[1][i] + idx[i][idx[i] >= 0]] = True
+    assert np.all(dkv[~chosen] == 0.0)
+
+
+def test_sparse_attention_backward_closed_forms():
+    """One selected entry: P = 1, so dq = 0 and that row's gradient is dout on
+    the value columns only; a zero upstream gives zero gradients."""
+    rng = np.random.default_rng(73)
+    cu_q, cu_k = _ragged([5], [5])
+    q = rng.standard_normal((5, 2, 6)).astype(np.float32)
+    kv = rng.standard_normal((5, 6)).astype(np.float32)
+    idx = np.array([[0, -1], [1, -1], [0, -1], [3, -1], [2, -1]], np.int32)
+    dout = rng.standard_normal((5, 2, 4))
+    dq, dkv = oracle.sparse_mla_backward(cu_q, cu_k, q, kv, idx, 4, 0.5, dout)
+    assert np.max(np.abs(dq)) < 1e-15
+    want = np.zeros((5, 6))
+    for i in range(5):
+        want[idx[i, 0], :4] += dout[i].sum(0)
+    np.testing.assert_allclose(dkv, want, atol=1e-14)
+    z = oracle.sparse_mla_backward(cu_q, cu_k, q, kv, idx, 4, 0.5, np.zeros_like(dout))
+    assert np.all(z[0] == 0.0) and np.all(z[1] == 0.0)
+
+
 # ---------------------------------------------------------------- end to end
 
 def test_forward_composes_the_steps_and_is_causal():

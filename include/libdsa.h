@@ -198,6 +198,38 @@ dsa_status dsa_dense_mla_attn(const dsa_batch* batch, const void* q, const void*
                               void* out, float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
 
 /*
+ * Backward of the sparse MLA attention.  [P2] 【稀疏训练阶段】 / [P5]: the
+ * sparse training stage optimises every parameter through the sparse
+ * attention, so the gradient reaches the query and, by scatter-add, the
+ * selected latent rows.  With z_s = softmax_scale q[r,h,:] . kv[s,:], P the
+ * softmax over the entries of idx[r] >= 0, out = P V (V = first d_v columns)
+ * and the upstream dout:
+ *   dP_s = dout[r,h,:] . V_s,  D = dout[r,h,:] . out[r,h,:],
+ *   dS_s = softmax_scale P_s (dP_s - D),
+ *   dq[r,h,:]   += sum_s dS_s kv[kbase + s, :]
+ *   dkv[kbase + s, :] += sum_h dS_s q[r,h,:]  (all d_qk columns)
+ *                      + sum_h P_s dout[r,h,:] (first d_v columns)
+ *   q, kv, idx, k, H, d_qk, d_v, softmax_scale as dsa_sparse_mla_attn (BF16 only)
+ *   lse  [total_q, H] fp32: the forward's log-sum-exp (P is recomputed against
+ *        it; D = sum_s P_s dP_s is formed in fp32 over the row's entries)
+ *   dout [total_q, H, d_v] bf16, 16-B aligned
+ *   dq   [total_q, H, d_qk] fp32 and dkv [total_k, d_qk] fp32, 16-B aligned:
+ *        ACCUMULATED (zero them first); dkv by float atomics, so the order of
+ *        its additions (its last bits) may vary between runs
+ * Arithmetic: bf16 MFMAs with fp32 accumulation; P and dS are kept in the
+ * workspace as bf16, dS for dq as a hi + lo pair of bf16 (dq sums terms that
+ * cancel).
+ * Workspace: dsa_sparse_mla_backward_workspace_size bytes (4 x rows x H x k
+ * rounded up to 32, bf16), 16-B aligned.
+ */
+dsa_status dsa_sparse_mla_backward_workspace_size(const dsa_batch* batch, int32_t H, int32_t k,
+                                                  size_t* bytes /* host */);
+dsa_status dsa_sparse_mla_backward(const dsa_batch* batch, const void* q, const void* kv, dsa_dtype dtype,
+                                   const int32_t* idx, int32_t k, int32_t H, int32_t d_qk, int32_t d_v,
+                                   float softmax_scale, const float* lse, const void* dout,
+                                   float* dq, float* dkv, void* ws, size_t ws_bytes, dsa_stream_t stream);
+
+/*
  * Indexer-alignment target.  [P1] training "Step 1" (dense warm-up) and
  * "Step 2" (sparse training), [P2] 【密集预热阶段】 / 【稀疏训练阶段】: for each
  * query row the main attention's probabilities of every head are summed over

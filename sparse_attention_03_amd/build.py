@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "libdsa.so")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip", "align.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip", "align.hip", "mla_backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

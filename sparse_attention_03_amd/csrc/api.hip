@@ -288,6 +288,37 @@ dsa_status dsa_dense_mla_attn(const dsa_batch* batch, const void* q, const void*
   return e == hipSuccess ? DSA_OK : hip_fail(e, "dense attention launch");
 }
 
+dsa_status dsa_sparse_mla_backward_workspace_size(const dsa_batch* batch, int32_t H, int32_t k, size_t* bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is NULL");
+  if (dsa_status s = check_batch(batch)) return s;
+  if (dsa_status s = check_k(k)) return s;
+  if (H != 32 && H != 64 && H != 128) return fail(DSA_ERR_UNSUPPORTED, "backward needs H in {32, 64, 128}");
+  *bytes = dsa::mla_backward_workspace_bytes(batch->total_q, H, k);
+  return DSA_OK;
+}
+
+dsa_status dsa_sparse_mla_backward(const dsa_batch* batch, const void* q, const void* kv, dsa_dtype dtype,
+                                   const int32_t* idx, int32_t k, int32_t H, int32_t d_qk, int32_t d_v,
+                                   float softmax_scale, const float* lse, const void* dout, float* dq, float* dkv,
+                                   void* ws, size_t ws_bytes, dsa_stream_t stream) {
+  g_err[0] = 0;
+  if (dsa_status s = check_batch(batch)) return s;
+  if (dsa_status s = check_attention(q, kv, dtype, idx, k, H, d_qk, d_v, softmax_scale, dq, lse)) return s;
+  if (dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "attention backward needs BF16");
+  if (!lse || !dout || !dq || !dkv) return fail(DSA_ERR_INVALID_ARG, "lse / dout / dq / dkv is NULL");
+  if (!aligned16(dout) || !aligned16(dkv)) return fail(DSA_ERR_INVALID_ARG, "dout and dkv must be 16-byte aligned");
+  if (batch->total_q == 0) return DSA_OK;
+  const size_t need = dsa::mla_backward_workspace_bytes(batch->total_q, H, k);
+  if (!ws || ws_bytes < need || !aligned16(ws))
+    return fail(DSA_ERR_WORKSPACE, "attention backward workspace: need %zu bytes (got %zu)", need, ws_bytes);
+  int cus = 0;
+  if (dsa_status s = device_cus(&cus)) return s;
+  dsa::MlaBwdLaunch L{view(batch, 0, batch->total_q), q, kv, idx, k, H, softmax_scale, lse, dout, dq, dkv, ws, cus};
+  hipError_t e = dsa::launch_mla_backward(L, (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "attention backward launch");
+}
+
 dsa_status dsa_attn_target(const dsa_batch* batch, const void* q, const void* kv, dsa_dtype dtype,
                            const int32_t* idx, int32_t k, int32_t H, int32_t d_qk, float softmax_scale,
                            const float* lse, float* p, int64_t ld_p, dsa_stream_t stream) {

@@ -115,6 +115,24 @@ struct IndexerBwdLaunch {
   int32_t num_cus;
 };
 
+// Backward of the bf16 sparse MQA attention (dq and dkv accumulated).
+struct MlaBwdLaunch {
+  BatchView b;
+  const void* q;           // [total_q, H, 576] bf16
+  const void* kv;          // [total_k, 576] bf16
+  const int32_t* idx;      // [rows, k]
+  int32_t k, H;
+  float scale;
+  const float* lse;        // [total_q, H]
+  const void* dout;        // [total_q, H, 512] bf16
+  float* dq;               // [total_q, H, 576]
+  float* dkv;              // [total_k, 576]
+  void* ws;                // mla_backward_workspace_bytes(rows, H, k)
+  int32_t num_cus;
+};
+size_t mla_backward_workspace_bytes(int rows, int H, int k);
+hipError_t launch_mla_backward(const MlaBwdLaunch& a, hipStream_t s);
+
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s);
 hipError_t launch_indexer_bwd(const IndexerBwdLaunch& a, hipStream_t s);
 hipError_t launch_indexer_kl(const KlLaunch& a, hipStream_t s);

@@ -30,23 +30,12 @@
 //     reads of the row-major tile.
 #include "dsa_common.h"
 #include "dsa_kernels.h"
+#include "mla_tile.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kDqk = 576;
-constexpr int kDv = 512;
-constexpr int kRowBytes = kDqk * 2;        // 1152
-constexpr int kChunksPerRow = kRowBytes / 16;  // 72
-constexpr int kTile = 32;                  // selected entries per tile
-constexpr int kTileBytes = kTile * kRowBytes;  // 36864
-constexpr int kNumBuf = 4;                 // LDS tile buffers (147456 bytes)
-constexpr int kMaxSel = 2048;              // selected entries staged in LDS per row
-constexpr int kQkAhead = 3;                // K fragment steps read ahead of their MFMAs
-constexpr int kPvAhead = 8;                // V^T fragments read ahead of their MFMAs
-constexpr int kQkSteps = kDqk / 32;        // 18
-constexpr int kDvTiles = kDv / 16;         // 32
-constexpr float kSumLimit = 0x1p90f;       // per-lane row sums beyond this trigger the recompute
+using namespace mla;
 
 struct MlaArgs {
   const int32_t* cu_q;
@@ -68,62 +57,6 @@ struct MlaArgs {
   float* p_out;         // target: [rows, ld_p]
   int64_t ld_p;
 };
-
-// Tile layout in LDS: line blocks.  The tile (32 rows x 72 chunks of 16 bytes)
-// is 36 blocks of 1 KB; block 4 s + rg holds segment s (chunks 8 s .. 8 s + 7,
-// one 128-byte line of each latent row) of tile rows 8 rg .. 8 rg + 7.  Rows 2k
-// and 2k + 1 of a block share its 256-byte bank row k, and chunk 8 s + x of row
-// r sits in 16-byte slot 8 (r & 1) + (x ^ tile_swz(r)) of it.  Properties:
-//   * every 8 lanes of a copy instruction read one whole 128-byte line of one
-//     latent row (a row's chunks permuted inside the line), so the gather
-//     touches each line of a tile once;
-//   * a lane copies from one latent row for the whole tile (one address per
-//     lane and row group, immediate offsets after);
-//   * a transposed V read (8 rows x 2 chunks per 32 lanes) covers each bank
-//     once;
-//   * the 16 rows of one chunk in a K fragment read sit in 16 different
-//     slots, but lane groups 0 and 1 (2 and 3) read different chunks of the
-//     same rows, which the LDS serves in two passes.  Line-sized gathers are
-//     worth far more than that pass.
-constexpr int kSegments = kChunksPerRow / 8;  // 9 lines per latent row
-__device__ __forceinline__ int tile_swz(int r) { return 2 * ((r >> 1) & 3) + ((r >> 3) & 1); }
-__device__ __forceinline__ int tile_off(int r, int ch) {
-  return ((ch >> 3) * 4 + (r >> 3)) * 1024 + ((r & 7) >> 1) * 256 + (8 * (r & 1) + ((ch & 7) ^ tile_swz(r))) * 16;
-}
-
-__device__ __forceinline__ uint16_t to_bf16_bits(float f) {
-  __bf16 b = (__bf16)f;  // round to nearest even
-  return __builtin_bit_cast(uint16_t, b);
-}
-
-// Issue the HBM -> LDS copy of tile t (the latent rows of selected entries
-// 32 t .. 32 t + 31): 36 lane-contiguous 1-KB copy instructions, one per block.
-// Wave w copies the row groups rg = w, w + NW, ... (all nine segments of each);
-// lane l copies tile row 8 rg + l / 8.  Invalid entries (-1) copy row 0 of the
-// sequence, always in bounds, and are masked later.
-template <int NW>
-constexpr int row_groups_per_wave() { return 4 / NW; }
-
-// Tile row copied by this lane for its k-th row group.
-__device__ __forceinline__ int gather_row(int wave, int NW, int k, int lane) { return 8 * (wave + NW * k) + (lane >> 3); }
-
-// p[k]: selected position of this lane's tile row for row group k.
-template <int NW>
-__device__ __forceinline__ void gather_tile(const MlaArgs& a, int32_t kbase, const int32_t (&p)[4 / NW],
-                                            uint8_t* buf) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-#pragma unroll
-  for (int k = 0; k < row_groups_per_wave<NW>(); ++k) {
-    const int rg = wave + NW * k;
-    const int x = (lane & 7) ^ tile_swz(8 * rg + (lane >> 3));  // chunk of the line this lane copies
-    const int32_t pk = p[k] < 0 ? 0 : p[k];
-    const uint8_t* src = a.kv + ((int64_t)(kbase + pk) * kChunksPerRow + x) * 16;
-#pragma unroll
-    for (int sg = 0; sg < kSegments; ++sg)
-      __builtin_amdgcn_global_load_lds((const void*)(src + 128 * sg),
-                                       (DSA_LDS void*)((DSA_LDS uint8_t*)buf + 1024 * (4 * sg + rg)), 16, 0, 0);
-  }
-}
 
 // DENSE: every candidate [0, pos] in position order (the masked mode of short
 // prefill), tile t holding positions 32 t .. 32 t + 31, instead of the row's
@@ -231,7 +164,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
         int32_t pj[RG];
 #pragma unroll
         for (int k = 0; k < RG; ++k) pj[k] = pos_at(t0 + j, k);
-        gather_tile<NW>(a, ri.kbase, pj, smem + (size_t)j * kTileBytes);
+        gather_tile<NW>(a.kv, ri.kbase, pj, smem + (size_t)j * kTileBytes);
       }
     // positions for the next gather, read a tile ahead so their LDS latency hides
     int32_t p_next[RG];
@@ -249,7 +182,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
       else wait_vmcnt<0>();
       lds_barrier();
       if (t + AHEAD < t1) {
-        gather_tile<NW>(a, ri.kbase, p_next, smem + (size_t)((t + AHEAD - t0) % kNumBuf) * kTileBytes);
+        gather_tile<NW>(a.kv, ri.kbase, p_next, smem + (size_t)((t + AHEAD - t0) % kNumBuf) * kTileBytes);
         if (t + AHEAD + 1 < t1) {
 #pragma unroll
           for (int k = 0; k < RG; ++k) p_next[k] = pos_at(t + AHEAD + 1, k);
@@ -487,7 +420,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_target_kernel(MlaArgs a) {
       int32_t pj[RG];
 #pragma unroll
       for (int k = 0; k < RG; ++k) pj[k] = pos_at(t0 + j, k);
-      gather_tile<NW>(a, ri.kbase, pj, smem + (size_t)j * kTileBytes);
+      gather_tile<NW>(a.kv, ri.kbase, pj, smem + (size_t)j * kTileBytes);
     }
   int32_t p_next[RG];
 #pragma unroll
@@ -500,7 +433,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_target_kernel(MlaArgs a) {
     else wait_vmcnt<0>();
     lds_barrier();
     if (t + AHEAD < t1) {
-      gather_tile<NW>(a, ri.kbase, p_next, smem + (size_t)((t + AHEAD - t0) % kNumBuf) * kTileBytes);
+      gather_tile<NW>(a.kv, ri.kbase, p_next, smem + (size_t)((t + AHEAD - t0) % kNumBuf) * kTileBytes);
       if (t + AHEAD + 1 < t1) {
 #pragma unroll
         for (int k = 0; k < RG; ++k) p_next[k] = pos_at(t + AHEAD + 1, k);

@@ -58,6 +58,9 @@ _SIGS = {
                             ctypes.c_int),
     "dsa_dense_mla_attn_workspace_size": ([_BP, ctypes.c_int, _i32, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
     "dsa_dense_mla_attn": ([_BP, _p, _p, ctypes.c_int, _i32, _i32, _i32, _f32, _p, _p, _p, _sz, _p], ctypes.c_int),
+    "dsa_sparse_mla_backward_workspace_size": ([_BP, _i32, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
+    "dsa_sparse_mla_backward": ([_BP, _p, _p, ctypes.c_int, _p, _i32, _i32, _i32, _i32, _f32, _p, _p, _p, _p, _p,
+                                 _sz, _p], ctypes.c_int),
     "dsa_attn_target": ([_BP, _p, _p, ctypes.c_int, _p, _i32, _i32, _i32, _f32, _p, _p, _i64, _p], ctypes.c_int),
     "dsa_indexer_kl": ([_BP, _p, _i64, _p, _i32, _p, _i64, _p, _p, _p], ctypes.c_int),
     "dsa_indexer_backward": ([_BP, _p, _p, ctypes.c_int, _p, _p, _i32, _i32, ctypes.c_int, _p, _i32, _p, _i64,
@@ -187,6 +190,22 @@ def forward_params(batch: DsaBatch, q_idx, k_idx, w, q, kv, k: int, d_v: int, so
     p.lse = None if lse is None else lse.data_ptr()
     p.out_idx = None if out_idx is None else out_idx.data_ptr()
     return p
+
+
+def dsa_sparse_mla_backward_workspace_size(batch: DsaBatch, H: int, k: int) -> int:
+    n = _sz(0)
+    _check(_lib.dsa_sparse_mla_backward_workspace_size(ctypes.byref(batch), H, k, ctypes.byref(n)),
+           "dsa_sparse_mla_backward_workspace_size")
+    return n.value
+
+
+def dsa_sparse_mla_backward(batch: DsaBatch, q, kv, idx, d_v: int, softmax_scale: float, lse, dout, dq, dkv, ws,
+                            stream=None):
+    """Adds the sparse attention's gradients for dout into dq [total_q, H, d_qk] and dkv [total_k, d_qk]."""
+    _check(_lib.dsa_sparse_mla_backward(ctypes.byref(batch), _ptr(q), _ptr(kv), _dtype_code(q), _ptr(idx),
+                                        idx.shape[1], q.shape[1], q.shape[2], d_v, float(softmax_scale),
+                                        _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dkv), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)), "dsa_sparse_mla_backward")
 
 
 def dsa_attn_target(batch: DsaBatch, q, kv, softmax_scale: float, lse, p, idx=None, stream=None):

@@ -363,6 +363,53 @@ def align_bench(steps=5, warmup=1):
     return res
 
 
+def attn_backward_bench(steps=3, warmup=1):
+    """dsa_sparse_mla_backward on one sequence, all rows as queries, k = 2048,
+    H = 128 (the prefill distributions, selections from dsa_forward, a random
+    upstream gradient): L = 8192, and the last 4096 rows of the 131072-token
+    prefill."""
+    import torch
+    from sparse_attention_03_amd import dsa, inputs as gen, libdsa as L
+
+    res = {}
+    for name, cfg, rows_from in (("prefill_8k", "prefill_8k", 0), ("prefill_128k_chunk", "prefill_128k", 131072 - 4096)):
+        p = gen.make_config(cfg, device="cuda")
+        if rows_from:
+            n = p.total_q
+            keep = slice(rows_from, n)
+            p.q_idx, p.w, p.q = p.q_idx[keep].contiguous(), p.w[keep].contiguous(), p.q[keep].contiguous()
+            p.cu_q = torch.tensor([0, n - rows_from], dtype=torch.int32, device="cuda")
+            p.cu_q_host = np.array([0, n - rows_from], dtype=np.int32)
+        b = L.batch_of(p)
+        _, lse, idx = dsa.Forward(p)()
+        g = torch.Generator(device="cuda")
+        g.manual_seed(1)
+        dout = torch.randn((p.total_q, p.H, p.d_v), generator=g, device="cuda", dtype=torch.bfloat16)
+        dq = torch.zeros((p.total_q, p.H, p.d_qk), dtype=torch.float32, device="cuda")
+        dkv = torch.zeros((p.total_k, p.d_qk), dtype=torch.float32, device="cuda")
+        ws = torch.empty(L.dsa_sparse_mla_backward_workspace_size(b, p.H, p.k), dtype=torch.uint8, device="cuda")
+        call = lambda: L.dsa_sparse_mla_backward(b, p.q, p.kv, idx, p.d_v, p.scale, lse, dout, dq, dkv, ws)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        # algorithmic: scores 576, dP 512, dq 576, dkv 576 + 512 multiply-adds per (row, entry, head)
+        flop = p.total_q * p.k * p.H * 2 * (576 + 512 + 576 + 576 + 512)
+        r = {"rows": p.total_q, "k": p.k, "H": p.H, "ms": ms, "TFLOPs": flop / ms / 1e9,
+             "frac_bf16": flop / ms / 1e9 / 2500.0}
+        res[name] = r
+        log("attention backward", name, json.dumps(r))
+        del p, lse, idx, dout, dq, dkv, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def _short(name):
     m = re.search(r"dsa::\(anonymous namespace\)::(\w+)", name)
     if m:
@@ -451,6 +498,8 @@ def main():
     ap.add_argument("--crossover", metavar="L", type=int, nargs="+",
                     help="masked mode (dense attention) against the sparse path on one prefill sequence of each "
                          "length L, and exit")
+    ap.add_argument("--attn-backward", action="store_true",
+                    help="time the sparse attention backward, then exit")
     ap.add_argument("--align", action="store_true",
                     help="time the indexer-alignment kernels (target, KL, indexer backward), then exit")
     ap.add_argument("--append", action="store_true",
@@ -472,6 +521,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.crossover:
         print(json.dumps({"crossover": crossover(args.crossover, steps=args.steps, warmup=args.warmup)}), flush=True)
+        return
+    if args.attn_backward:
+        print(json.dumps({"attn_backward": attn_backward_bench(steps=args.steps, warmup=args.warmup)}), flush=True)
         return
     if args.align:
         print(json.dumps({"align": align_bench(steps=args.steps, warmup=args.warmup)}), flush=True)

@@ -274,6 +274,21 @@ __device__ __forceinline__ void bwd_dq_half(const BwdArgs& a) {
   for (int dt = 0; dt < kQkTiles; ++dt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // dS^T fragments (the forward's probability layout): head 16 nt + li, MFMA
+  // K index 8g + e <-> entry 4g + e (e < 4), 16 + 4g + e - 4 otherwise; hi and
+  // lo parts, loaded a tile ahead
+  auto load_ds = [&](int t, bf16x8 (&hi)[NT], bf16x8 (&lo)[NT]) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int64_t o = ((int64_t)rl * a.H + head0 + 16 * nt + li) * a.k32 + kTile * t + 4 * g;
+      const uint2 a0 = *(const uint2*)(a.ds_he + o), a1 = *(const uint2*)(a.ds_he + o + 16);
+      const uint2 b0 = *(const uint2*)(a.ds_he_lo + o), b1 = *(const uint2*)(a.ds_he_lo + o + 16);
+      hi[nt] = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
+      lo[nt] = __builtin_bit_cast(bf16x8, make_uint4(b0.x, b0.y, b1.x, b1.y));
+    }
+  };
+  bf16x8 dsf_n[NT], dsl_n[NT];
+  if (t0 < t1) load_ds(t0, dsf_n, dsl_n);
 
 #pragma unroll
   for (int j = 0; j < AHEAD; ++j)
@@ -301,18 +316,14 @@ __device__ __forceinline__ void bwd_dq_half(const BwdArgs& a) {
       }
     }
     const uint32_t vmask = (uint32_t)__builtin_amdgcn_readlane((int)tmask_lane, t);
-    if (vmask == 0) continue;
-    // dS^T fragments (the forward's probability layout): head 16 nt + li, MFMA
-    // K index 8g + e <-> entry 4g + e (e < 4), 16 + 4g + e - 4 otherwise
     bf16x8 dsf[NT], dsl[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int64_t o = ((int64_t)rl * a.H + head0 + 16 * nt + li) * a.k32 + kTile * t + 4 * g;
-      const uint2 a0 = *(const uint2*)(a.ds_he + o), a1 = *(const uint2*)(a.ds_he + o + 16);
-      const uint2 b0 = *(const uint2*)(a.ds_he_lo + o), b1 = *(const uint2*)(a.ds_he_lo + o + 16);
-      dsf[nt] = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
-      dsl[nt] = __builtin_bit_cast(bf16x8, make_uint4(b0.x, b0.y, b1.x, b1.y));
+      dsf[nt] = dsf_n[nt];
+      dsl[nt] = dsl_n[nt];
     }
+    if (t + 1 < t1) load_ds(t + 1, dsf_n, dsl_n);  // in flight during this tile
+    if (vmask == 0) continue;
     const DSA_LDS uint8_t* lb = (const DSA_LDS uint8_t*)smem + (size_t)((t - t0) % kNumBuf) * kTileBytes;
     const DSA_LDS uint8_t* vb[4] = {lb + voff[0], lb + voff[1], lb + voff[2], lb + voff[3]};
     auto load_c = [&](int dt) -> bf16x8 {
@@ -361,14 +372,25 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bwd_dq_kernel(BwdArgs a) {
 }
 
 // dkv: three workgroups of four waves per (row, split); wave w of workgroup z
-// owns the latent columns 48 (4 z + w) .. + 47 (3 tiles of 16).  Per 32-entry tile,
-// dc[entry][col] = sum over heads of dS^T[entry][h] Q[h][col] (+ P^T[entry][h]
-// dout[h][col] for value columns), heads in steps of 32 as the MFMA's K.
+// owns the latent columns 48 (4 z + w) .. + 47 (3 tiles of 16).  Per 32-entry
+// tile, dc[entry][col] = sum over heads of dS^T[entry][h] Q[h][col] (+ P^T[entry][h]
+// dout[h][col] for value columns), heads in steps of 32 as the MFMA's K.  The
+// tile's dS and P rows (32 entries x H heads each, contiguous in the workspace)
+// are staged in LDS once per workgroup, double-buffered: entry e's 16-byte
+// chunk c at chunk c ^ (e mod chunks per row), so that the 16 entries of one
+// fragment read sit in distinct bank slots.
 constexpr int kDkvTiles = 3;
 
 template <int KS>
 __global__ __launch_bounds__(256, 1) void mla_bwd_dkv_kernel(BwdArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int H = 32 * KS;
+  constexpr int CPR = H / 8;                    // 16-byte chunks per entry row
+  constexpr int PIECES = 2 * kTile * CPR;       // dS and P rows of one tile
+  constexpr int PPT = (PIECES + 255) / 256;     // pieces per thread
+  __shared__ __attribute__((aligned(16))) uint8_t stage_lds[2][2][kTile * H * 2];
+  __shared__ int32_t pos_lds[2][kTile];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, li = lane & 15;
   const int32_t rl = blockIdx.x, r = a.row_begin + rl;
   const int sp = blockIdx.y;
@@ -376,7 +398,7 @@ __global__ __launch_bounds__(256, 1) void mla_bwd_dkv_kernel(BwdArgs a) {
   const int ntiles = (a.k + kTile - 1) / kTile;
   const int t0 = sp * a.tiles_per_split;
   const int t1 = min(ntiles, t0 + a.tiles_per_split);
-  if (t0 >= t1) return;
+  if (t0 >= t1) return;  // uniform over the workgroup
   const int col0 = 16 * kDkvTiles * (4 * (int)blockIdx.z + wave);
   // B fragments: heads 32 ks + 8g .. + 7 at column col0 + 16 j + li
   bf16x8 qb[kDkvTiles][KS], ob[kDkvTiles][KS];
@@ -400,23 +422,52 @@ __global__ __launch_bounds__(256, 1) void mla_bwd_dkv_kernel(BwdArgs a) {
   }
   const bool has_v = col0 < kDv;
   const int32_t* idx_row = a.idx + (int64_t)rl * a.k;
+  // staging of tile t: piece = array (dS, P) x entry x chunk
+  i32x4 st[PPT];
+  int32_t st_pos = -1;
+  auto fetch = [&](int t) {
+    if (tid < kTile) st_pos = kTile * t + tid < a.k ? idx_row[kTile * t + tid] : -1;
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int piece = tid + 256 * u;
+      if (piece < PIECES) {
+        const int arr = piece / (kTile * CPR), rem = piece % (kTile * CPR);
+        const uint16_t* src = (arr == 0 ? a.ds_eh : a.p_eh) + ((int64_t)rl * a.k32 + kTile * t) * H + 8 * rem;
+        st[u] = *(const i32x4*)src;
+      }
+    }
+  };
+  auto store = [&](int buf) {
+    if (tid < kTile) pos_lds[buf][tid] = st_pos;
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int piece = tid + 256 * u;
+      if (piece < PIECES) {
+        const int arr = piece / (kTile * CPR), rem = piece % (kTile * CPR);
+        const int e = rem / CPR, c = rem % CPR;
+        *(DSA_LDS i32x4*)((DSA_LDS uint8_t*)stage_lds[buf][arr] + (e * CPR + (c ^ (e & (CPR - 1)))) * 16) = st[u];
+      }
+    }
+  };
+  fetch(t0);
+  store(0);
+  __syncthreads();
   for (int t = t0; t < t1; ++t) {
+    const int buf = (t - t0) & 1;
+    if (t + 1 < t1) fetch(t + 1);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int32_t e_a = kTile * t + 16 * kt + li;  // A row of this lane
+      const int e = 16 * kt + li;  // A row of this lane within the tile
       bf16x8 dsa[KS], pa[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int64_t o = ((int64_t)rl * a.k32 + e_a) * a.H + 32 * ks + 8 * g;
-        dsa[ks] = *(const bf16x8*)(a.ds_eh + o);
-        pa[ks] = *(const bf16x8*)(a.p_eh + o);
+        const int off = (e * CPR + ((4 * ks + g) ^ (e & (CPR - 1)))) * 16;
+        dsa[ks] = *(const DSA_LDS bf16x8*)((const DSA_LDS uint8_t*)stage_lds[buf][0] + off);
+        pa[ks] = *(const DSA_LDS bf16x8*)((const DSA_LDS uint8_t*)stage_lds[buf][1] + off);
       }
       int32_t spos[4];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int32_t e = kTile * t + 16 * kt + 4 * g + rr;
-        spos[rr] = e < a.k ? idx_row[e] : -1;
-      }
+      for (int rr = 0; rr < 4; ++rr) spos[rr] = pos_lds[buf][16 * kt + 4 * g + rr];
 #pragma unroll
       for (int j = 0; j < kDkvTiles; ++j) {
         f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -431,6 +482,9 @@ __global__ __launch_bounds__(256, 1) void mla_bwd_dkv_kernel(BwdArgs a) {
           if (spos[rr] >= 0) atomicAdd(a.dkv + (int64_t)(ri.kbase + spos[rr]) * kDqk + col0 + 16 * j + li, d[rr]);
       }
     }
+    __syncthreads();  // every wave done with stage_lds[buf ^ 1]'s last use and this tile
+    if (t + 1 < t1) store(buf ^ 1);
+    __syncthreads();
   }
 }
 

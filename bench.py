@@ -34,14 +34,17 @@ sys.path.insert(0, ROOT)
 PEAK = {"fp8": 5.0e15, "bf16": 2.5e15}   # MI355X dense MFMA, FLOP/s
 HBM_PEAK = 8.0e12                         # bytes/s
 CSRC = os.path.join(ROOT, "sparse_attention_03_amd", "csrc")
-KERNEL_SOURCE = {"attention": "sparse_mla.hip", "indexer": "indexer.hip", "topk": "topk.hip"}
+KERNEL_SOURCE = {"attention": ("sparse_mla.hip", "mla_tile.h"), "indexer": ("indexer.hip",), "topk": ("topk.hip",)}
 KERNEL_SYMBOL = {"attention": "mla_bf16_kernel", "indexer": "indexer_fp8_kernel", "topk": "topk_kernel"}
 COPY_BYTES = 1 << 30                      # the calibration copy moves this many bytes each way
 
 
 def source_sha(step):
-    with open(os.path.join(CSRC, KERNEL_SOURCE[step]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCE[step]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic(step):

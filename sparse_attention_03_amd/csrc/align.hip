@@ -190,200 +190,274 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
   return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
 }
 
-template <int ACT>
+// NR query rows per workgroup.  Over a selected set (NR = 1) every row has
+// keys of its own.  In the dense warm-up (NR = 4, 2 with GELU) the rows of one sequence
+// share their keys: one slab serves all of them and their dk contributions are
+// summed in the MFMA accumulators before the scatter, so it issues a quarter of
+// the atomics (which bound the kernel: about one fp32 atomic per L2 channel
+// and clock).  Rows of different sequences are taken one at a time.
+template <int ACT, int NR>
 __global__ __launch_bounds__(256) void indexer_bwd_kernel(IbArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t slab[2][kBwChunk * 128];
   __shared__ float dk_part[4][kBwChunk * kBwStride];
   __shared__ int32_t kpos_s[2][kBwChunk];
-  __shared__ float g_s[2][kBwChunk];
+  __shared__ float g_s[2][NR][kBwChunk];
   __shared__ int32_t ksc_s[2][kBwChunk];
   const int nthreads = blockDim.x;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, li = lane & 15;
-  const int32_t rl = blockIdx.x, r = a.row_begin + rl;
-  const RowInfo ri = locate_row(a.cu_q, a.cu_k, a.num_seqs, r);
   const bool dense = a.idx == nullptr;
-  const int32_t m = dense ? ri.pos + 1 : a.k;
-  const int nchunks = (m + kBwChunk - 1) / kBwChunk;
-  const int c0 = blockIdx.y * a.chunks_per_split;
-  const int c1 = min(nchunks, c0 + a.chunks_per_split);
-  if (c0 >= c1) return;  // uniform over the workgroup
   const int h0 = 16 * wave;
-  const uint8_t* qrow = a.q_idx + (int64_t)r * a.H_I * 128;
-  // FP8 fragments of the wave's heads (head h0 + li, dims 32g .. 32g + 31)
-  i32x8 qf;
-  {
+  // the workgroup's rows (row i of the list is global row rb + i)
+  const int32_t rb = a.row_begin + (int32_t)blockIdx.x * NR;
+  int32_t pos[NR], kb[NR];
+  bool live[NR];
+  bool same = true;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    live[i] = rb + i < a.row_end;
+    pos[i] = -1;
+    kb[i] = 0;
+    if (live[i]) {
+      const RowInfo ri = locate_row(a.cu_q, a.cu_k, a.num_seqs, rb + i);
+      pos[i] = ri.pos;
+      kb[i] = ri.kbase;
+      same = same && kb[i] == kb[0];
+    }
+  }
+  // per-row fragments and weights (live rows; the others stay zero)
+  i32x8 qf[NR];
+  bf16x4_t qT[NR][8];
+  float w_li[NR], w_g[NR][4];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    qf[i] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    w_li[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w_g[i][j] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) qT[i][dt] = bf16x4_t{0, 0, 0, 0};
+    if (!live[i]) continue;
+    const uint8_t* qrow = a.q_idx + (int64_t)(rb + i) * a.H_I * 128;
     const i32x4* p = (const i32x4*)(qrow + (h0 + li) * 128 + 32 * g);
     const i32x4 lo = p[0], hi = p[1];
-    qf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    qf[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      short v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = bf16_bits(e4m3_to_f32(qrow[(h0 + 4 * g + j) * 128 + 16 * dt + li]));
+      qT[i][dt] = bf16x4_t{v[0], v[1], v[2], v[3]};
+    }
+    const float* wrow = a.w + (int64_t)(rb + i) * a.H_I;
+    w_li[i] = wrow[h0 + li];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w_g[i][j] = wrow[h0 + 4 * g + j];
   }
-  // Q as the B operand of dk (heads h0 + 4g .. + 3 at dim 16 dt + li), bf16
-  bf16x4_t qT[8];
+  f32x4 dq_acc[NR][8];
+  float dw_acc[NR];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    short v[4];
+  for (int i = 0; i < NR; ++i) {
+    dw_acc[i] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = bf16_bits(e4m3_to_f32(qrow[(h0 + 4 * g + j) * 128 + 16 * dt + li]));
-    qT[dt] = bf16x4_t{v[0], v[1], v[2], v[3]};
+    for (int dt = 0; dt < 8; ++dt) dq_acc[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const float* wrow = a.w + (int64_t)r * a.H_I;
-  const float w_li = wrow[h0 + li];
-  float w_g[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) w_g[j] = wrow[h0 + 4 * g + j];
-  const float* grow = a.g + (int64_t)rl * a.ld_g;
-  const int32_t* irow = dense ? nullptr : a.idx + (int64_t)rl * a.k;
-  const uint8_t* kbase = a.k_idx + (int64_t)ri.kbase * 128;
 
-  // staging of one chunk: 256 pieces of 16 bytes (key kk = piece / 8, chunk
-  // piece % 8), up to four per thread; the chunk's positions, g and scales
-  i32x4 stage[4];
-  int32_t st_pos = -1;
-  float st_g = 0.0f;
-  int32_t st_sc = 127;
-  auto entry_pos = [&](int32_t e) -> int32_t {
-    if (e >= m) return -1;
-    if (dense) return e;
-    const int32_t s = irow[e];
-    return s >= 0 && s <= ri.pos ? s : -1;
-  };
-  auto fetch = [&](int c) {
+  // One pass over the chunks of the rows in `act` (a bit per row, all of one
+  // sequence: base key row kbase), entries [0, mmax).
+  auto run = [&](uint32_t act, int32_t kbase, int32_t mmax) {
+    const int nchunks = (mmax + kBwChunk - 1) / kBwChunk;
+    const int c0 = blockIdx.y * a.chunks_per_split;
+    const int c1 = min(nchunks, c0 + a.chunks_per_split);
+    if (c0 >= c1) return;  // uniform over the workgroup
+    const uint8_t* kbytes = a.k_idx + (int64_t)kbase * 128;
+    // position of entry e for row i (dense: e; selected: idx), -1 if no candidate
+    auto entry_pos = [&](int i, int32_t e) -> int32_t {
+      if (!((act >> i) & 1u)) return -1;
+      if (dense) return e <= pos[i] ? e : -1;
+      if (e >= a.k) return -1;
+      const int32_t s = a.idx[(int64_t)(rb + i - a.row_begin) * a.k + e];
+      return s >= 0 && s <= pos[i] ? s : -1;
+    };
+    // staging of one chunk: 256 pieces of 16 bytes (key kk = piece / 8, chunk
+    // piece % 8), up to four per thread; positions, g of each row, scales
+    i32x4 stage[4];
+    int32_t st_pos = -1, st_sc = 127;
+    float st_g[NR];
+    auto fetch = [&](int c) {
+      // the chunk's key rows: dense, one position list for all rows; selected,
+      // the single row's
+      const int irow = dense ? 0 : __builtin_ctz(act);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int piece = tid + u * nthreads;
-      if (piece < kBwChunk * 8) {
-        const int kk = piece >> 3, ch = piece & 7;
-        const int32_t s = entry_pos(kBwChunk * c + kk);
-        stage[u] = *(const i32x4*)(kbase + (int64_t)(s < 0 ? 0 : s) * 128 + 16 * ch);
+      for (int u = 0; u < 4; ++u) {
+        const int piece = tid + u * nthreads;
+        if (piece < kBwChunk * 8) {
+          const int kk = piece >> 3, ch = piece & 7;
+          const int32_t e = kBwChunk * c + kk;
+          const int32_t s = dense ? (e < mmax ? e : -1) : entry_pos(irow, e);
+          stage[u] = *(const i32x4*)(kbytes + (int64_t)(s < 0 ? 0 : s) * 128 + 16 * ch);
+        }
       }
-    }
-    if (tid < kBwChunk) {
-      const int32_t e = kBwChunk * c + tid;
-      st_pos = entry_pos(e);
-      st_g = st_pos >= 0 ? grow[e] : 0.0f;
-      st_sc = (st_pos >= 0 && a.k_scale) ? (int32_t)a.k_scale[ri.kbase + st_pos] : 127;
-    }
-  };
-  auto store = [&](int buf) {
+      if (tid < kBwChunk) {
+        const int32_t e = kBwChunk * c + tid;
+        st_pos = dense ? (e < mmax ? e : -1) : entry_pos(irow, e);
+        st_sc = (st_pos >= 0 && a.k_scale) ? (int32_t)a.k_scale[kbase + st_pos] : 127;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int piece = tid + u * nthreads;
-      if (piece < kBwChunk * 8) {
-        const int kk = piece >> 3, ch = piece & 7;
-        *(DSA_LDS i32x4*)((DSA_LDS uint8_t*)slab[buf] + kk * 128 + 16 * (ch ^ ((kk >> 1) & 7))) = stage[u];
+        for (int i = 0; i < NR; ++i)
+          st_g[i] = entry_pos(i, e) >= 0 ? a.g[(int64_t)(rb + i - a.row_begin) * a.ld_g + e] : 0.0f;
       }
-    }
-    if (tid < kBwChunk) {
-      kpos_s[buf][tid] = st_pos;
-      g_s[buf][tid] = st_g;
-      ksc_s[buf][tid] = st_sc;
-    }
-  };
-  fetch(c0);
-  store(0);
-  __syncthreads();
-
-  f32x4 dq_acc[8];
+    };
+    auto store = [&](int buf) {
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) dq_acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float dw_acc = 0.0f;
-
-  for (int c = c0; c < c1; ++c) {
-    const int buf = (c - c0) & 1;
-    if (c + 1 < c1) fetch(c + 1);  // in flight during this chunk
-    const DSA_LDS uint8_t* sb = (const DSA_LDS uint8_t*)slab[buf];
-    // key fragments (key 16 kt + li, dims 32g .. 32g + 31) and their scales
-    i32x8 kf[2];
-    int ksc[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int kk = 16 * kt + li;
-      const int sw = (kk >> 1) & 7;
-      const i32x4 lo = *(const DSA_LDS i32x4*)(sb + kk * 128 + 16 * ((2 * g) ^ sw));
-      const i32x4 hi = *(const DSA_LDS i32x4*)(sb + kk * 128 + 16 * ((2 * g + 1) ^ sw));
-      kf[kt] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      ksc[kt] = ksc_s[buf][kk];
-    }
-    bf16x4_t gA[2], gB[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      // x^T: keys 16 kt + 4g + rr of head h0 + li
-      const f32x4 xt = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf[kt], qf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
-                                                                        0, ksc[kt], 0, 127);
-      // x: heads h0 + 4g + rr of key 16 kt + li
-      const f32x4 xx = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf, kf[kt], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
-                                                                        0, 127, 0, ksc[kt]);
-      short va[4], vb[4];
-      const float gl = g_s[buf][16 * kt + li];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float gk = g_s[buf][16 * kt + 4 * g + rr];
-        float av, dv;
-        act_and_slope<ACT>(xt[rr], av, dv);
-        dw_acc = fmaf(gk, av, dw_acc);
-        va[rr] = bf16_bits(gk * w_li * dv);
-        act_and_slope<ACT>(xx[rr], av, dv);
-        vb[rr] = bf16_bits(gl * w_g[rr] * dv);
+      for (int u = 0; u < 4; ++u) {
+        const int piece = tid + u * nthreads;
+        if (piece < kBwChunk * 8) {
+          const int kk = piece >> 3, ch = piece & 7;
+          *(DSA_LDS i32x4*)((DSA_LDS uint8_t*)slab[buf] + kk * 128 + 16 * (ch ^ ((kk >> 1) & 7))) = stage[u];
+        }
       }
-      gA[kt] = bf16x4_t{va[0], va[1], va[2], va[3]};
-      gB[kt] = bf16x4_t{vb[0], vb[1], vb[2], vb[3]};
-    }
-    // dq[head 4g + rr][dim 16 dt + li] += sum over keys of G^T x K
+      if (tid < kBwChunk) {
+        kpos_s[buf][tid] = st_pos;
+        ksc_s[buf][tid] = st_sc;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      float kscale[4];
-      int kk4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kk4[j] = 16 * kt + 4 * g + j;
-        kscale[j] = __builtin_ldexpf(1.0f, ksc_s[buf][kk4[j]] - 127);
+        for (int i = 0; i < NR; ++i) g_s[buf][i][tid] = st_g[i];
       }
+    };
+    __syncthreads();  // the buffers are free
+    fetch(c0);
+    store(0);
+    __syncthreads();
+    for (int c = c0; c < c1; ++c) {
+      const int buf = (c - c0) & 1;
+      if (c + 1 < c1) fetch(c + 1);  // in flight during this chunk
+      const DSA_LDS uint8_t* sb = (const DSA_LDS uint8_t*)slab[buf];
+      // key fragments (key 16 kt + li, dims 32g .. 32g + 31) and their scales
+      i32x8 kf[2];
+      int ksc[2];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        short v[4];
+      for (int kt = 0; kt < 2; ++kt) {
+        const int kk = 16 * kt + li;
+        const int sw = (kk >> 1) & 7;
+        const i32x4 lo = *(const DSA_LDS i32x4*)(sb + kk * 128 + 16 * ((2 * g) ^ sw));
+        const i32x4 hi = *(const DSA_LDS i32x4*)(sb + kk * 128 + 16 * ((2 * g + 1) ^ sw));
+        kf[kt] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        ksc[kt] = ksc_s[buf][kk];
+      }
+      // G of every row: x^T (keys 16 kt + 4g + rr of head h0 + li) gives G^T,
+      // the A operand of dq; x (heads h0 + 4g + rr of key 16 kt + li) gives G,
+      // the A operand of dk
+      bf16x4_t gA[NR][2], gB[NR][2];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          gA[i][kt] = bf16x4_t{0, 0, 0, 0};
+          gB[i][kt] = bf16x4_t{0, 0, 0, 0};
+        }
+        if (!((act >> i) & 1u)) continue;  // uniform
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const f32x4 xt = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf[kt], qf[i], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                            0, 0, 0, ksc[kt], 0, 127);
+          const f32x4 xx = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[i], kf[kt], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                            0, 0, 0, 127, 0, ksc[kt]);
+          short va[4], vb[4];
+          const float gl = g_s[buf][i][16 * kt + li];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const float gk = g_s[buf][i][16 * kt + 4 * g + rr];
+            float av, dv;
+            act_and_slope<ACT>(xt[rr], av, dv);
+            dw_acc[i] = fmaf(gk, av, dw_acc[i]);
+            va[rr] = bf16_bits(gk * w_li[i] * dv);
+            act_and_slope<ACT>(xx[rr], av, dv);
+            vb[rr] = bf16_bits(gl * w_g[i][rr] * dv);
+          }
+          gA[i][kt] = bf16x4_t{va[0], va[1], va[2], va[3]};
+          gB[i][kt] = bf16x4_t{vb[0], vb[1], vb[2], vb[3]};
+        }
+      }
+      // per (key tile, column tile): K's column (keys 16 kt + 4g .. + 3 at dim
+      // 16 dt + li) converted once, then every row's dq product and its dk
+      // product, the latter summed over the rows:
+      // dk[key 16 kt + 4g + rr][dim 16 dt + li] into this wave's LDS part
+      float* part = dk_part[wave];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        float kscale[4];
+        int kk4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int kk = kk4[j];
-          const uint32_t byte = sb[kk * 128 + 16 * (dt ^ ((kk >> 1) & 7)) + li];
-          v[j] = bf16_bits(e4m3_to_f32(byte) * kscale[j]);
+          kk4[j] = 16 * kt + 4 * g + j;
+          kscale[j] = __builtin_ldexpf(1.0f, ksc_s[buf][kk4[j]] - 127);
         }
-        dq_acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(gA[kt], bf16x4_t{v[0], v[1], v[2], v[3]}, dq_acc[dt],
-                                                                0, 0, 0);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          short v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int kk = kk4[j];
+            const uint32_t byte = sb[kk * 128 + 16 * (dt ^ ((kk >> 1) & 7)) + li];
+            v[j] = bf16_bits(e4m3_to_f32(byte) * kscale[j]);
+          }
+          const bf16x4_t kB = bf16x4_t{v[0], v[1], v[2], v[3]};
+          f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < NR; ++i) {
+            if (!((act >> i) & 1u)) continue;  // uniform
+            dq_acc[i][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(gA[i][kt], kB, dq_acc[i][dt], 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(gB[i][kt], qT[i][dt], d, 0, 0, 0);
+          }
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) part[(16 * kt + 4 * g + rr) * kBwStride + 16 * dt + li] = d[rr];
+        }
       }
-    }
-    // dk[key 16 kt + 4g + rr][dim 16 dt + li] for this wave's heads, into its LDS part
-    float* part = dk_part[wave];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(gB[kt], qT[dt], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) part[(16 * kt + 4 * g + rr) * kBwStride + 16 * dt + li] = d[rr];
+      __syncthreads();  // every wave's dk part written, every wave done with slab[buf]
+      if (c + 1 < c1) store(buf ^ 1);
+      // the waves' parts added in order, scatter-added to the chunk's key rows
+      const int nwaves = nthreads >> 6;
+      for (int e = tid; e < kBwChunk * 128; e += nthreads) {
+        const int kk = e >> 7;
+        const int32_t s = kpos_s[buf][kk];
+        float v = 0.0f;
+        for (int w = 0; w < nwaves; ++w) v += dk_part[w][kk * kBwStride + (e & 127)];
+        if (s >= 0 && v != 0.0f) atomicAdd(a.dk + (int64_t)(kbase + s) * 128 + (e & 127), v);
       }
-    __syncthreads();  // every wave's dk part written, every wave done with slab[buf]
-    if (c + 1 < c1) store(buf ^ 1);
-    // the waves' parts added in order, scatter-added to the chunk's key rows
-    const int nwaves = nthreads >> 6;
-    for (int e = tid; e < kBwChunk * 128; e += nthreads) {
-      const int kk = e >> 7;
-      const int32_t s = kpos_s[buf][kk];
-      float v = 0.0f;
-      for (int w = 0; w < nwaves; ++w) v += dk_part[w][kk * kBwStride + (e & 127)];
-      if (s >= 0 && v != 0.0f) atomicAdd(a.dk + (int64_t)(ri.kbase + s) * 128 + (e & 127), v);
+      __syncthreads();
     }
-    __syncthreads();
+  };
+
+  if (dense && same) {
+    uint32_t act = 0;
+    int32_t pmax = -1;
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      if (live[i]) {
+        act |= 1u << i;
+        pmax = max(pmax, pos[i]);
+      }
+    run(act, kb[0], pmax + 1);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      if (live[i]) run(1u << i, kb[i], dense ? pos[i] + 1 : a.k);
   }
   // dw: sum over the lane groups; dq: this split's share
-  dw_acc += __shfl_xor(dw_acc, 16);
-  dw_acc += __shfl_xor(dw_acc, 32);
-  if (g == 0) atomicAdd(a.dw + (int64_t)r * a.H_I + h0 + li, dw_acc);
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
+  for (int i = 0; i < NR; ++i) {
+    if (!live[i]) continue;
+    const int32_t r = rb + i;
+    float d = dw_acc[i];
+    d += __shfl_xor(d, 16);
+    d += __shfl_xor(d, 32);
+    if (g == 0) atomicAdd(a.dw + (int64_t)r * a.H_I + h0 + li, d);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      atomicAdd(a.dq + ((int64_t)r * a.H_I + h0 + 4 * g + rr) * 128 + 16 * dt + li, dq_acc[dt][rr]);
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        atomicAdd(a.dq + ((int64_t)r * a.H_I + h0 + 4 * g + rr) * 128 + 16 * dt + li, dq_acc[i][dt][rr]);
+  }
 }
 
 }  // namespace
@@ -410,14 +484,24 @@ hipError_t launch_indexer_bwd(const IndexerBwdLaunch& L, hipStream_t s) {
   a.dw = L.dw;
   a.dk = L.dk;
   const int m = L.idx ? L.k : L.b.max_ctx;
+  // rows per workgroup: 4 in the dense warm-up (2 with GELU, whose epilogue
+  // needs the registers), 1 over selected sets
+  const int nr = L.idx ? 1 : (L.act == 0 ? 4 : 2);
+  const int64_t blocks = (rows + nr - 1) / nr;
   const int nchunks = (m + kBwChunk - 1) / kBwChunk;
   int splits = 1;
-  while (splits < nchunks && (int64_t)rows * splits < 2LL * L.num_cus) splits <<= 1;
+  while (splits < nchunks && blocks * splits < 2LL * L.num_cus) splits <<= 1;
   if (splits > nchunks) splits = nchunks;
   a.chunks_per_split = (nchunks + splits - 1) / splits;
-  const dim3 grid((unsigned)rows, (unsigned)splits), block((unsigned)(64 * (L.H_I / 16)));
-  if (L.act == 0) hipLaunchKernelGGL((indexer_bwd_kernel<0>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((indexer_bwd_kernel<1>), grid, block, 0, s, a);
+  const dim3 grid((unsigned)blocks, (unsigned)splits), block((unsigned)(64 * (L.H_I / 16)));
+  if (nr == 1) {
+    if (L.act == 0) hipLaunchKernelGGL((indexer_bwd_kernel<0, 1>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((indexer_bwd_kernel<1, 1>), grid, block, 0, s, a);
+  } else if (L.act == 0) {
+    hipLaunchKernelGGL((indexer_bwd_kernel<0, 4>), grid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((indexer_bwd_kernel<1, 2>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

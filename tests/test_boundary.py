@@ -167,6 +167,56 @@ def test_cache_append_validation(L):
     assert call(kn=None, vn=None) == L.DSA_OK
 
 
+def test_alignment_and_backward_validation(L):
+    b = _batch(L)
+    # dsa_attn_target(batch, q, kv, dtype, idx, k, H, d_qk, scale, lse, p, ld_p, stream)
+    t = L._lib.dsa_attn_target
+    assert t(ctypes.byref(b), 0x10000, 0x20000, 1, None, 0, 128, 576, 0.1, None, 0x40000, 32, None) \
+        == L.DSA_ERR_INVALID_ARG                                          # lse NULL
+    assert t(ctypes.byref(b), 0x10000, 0x20000, 1, None, 0, 128, 576, 0.1, 0x30000, 0x40000, 4, None) \
+        == L.DSA_ERR_INVALID_ARG                                          # ld_p below whole tiles of max_ctx
+    assert t(ctypes.byref(b), 0x10000, 0x20000, 1, 0x50000, 100, 128, 576, 0.1, 0x30000, 0x40000, 100, None) \
+        == L.DSA_ERR_INVALID_ARG                                          # ld_p below k rounded up to 32
+    assert t(ctypes.byref(b), 0x10000, 0x20000, 1, None, 0, 96, 576, 0.1, 0x30000, 0x40000, 32, None) \
+        == L.DSA_ERR_UNSUPPORTED                                          # H
+    # dsa_indexer_kl(batch, scores, ld_s, idx, k, p, ld_p, loss, dI, stream)
+    k = L._lib.dsa_indexer_kl
+    assert k(ctypes.byref(b), 0x10000, 64, None, 0, 0, 64, None, None, None) == L.DSA_ERR_INVALID_ARG   # p NULL
+    assert k(ctypes.byref(b), 0x10000, 64, None, 0, 0x20008, 64, None, None, None) == L.DSA_ERR_INVALID_ARG
+    assert k(ctypes.byref(b), 0x10000, 64, None, 0, 0x20000, 4, None, None, None) == L.DSA_ERR_INVALID_ARG
+    assert k(ctypes.byref(b), 0x10000, 64, 0x30000, 0, 0x20000, 64, None, None, None) == L.DSA_ERR_INVALID_ARG
+    assert k(ctypes.byref(b), 0x10000, 2, None, 0, 0x20000, 64, None, None, None) == L.DSA_ERR_INVALID_ARG
+    # dsa_indexer_backward(batch, q_idx, k_idx, dtype, k_scale, w, H_I, d_I, act, idx, k, g, ld_g, dq, dw, dk, stream)
+    bw = L._lib.dsa_indexer_backward
+
+    def ib(dt=2, g=0x40000, ld=64, dq=0x50000, idx=None, kk=0, H_I=64):
+        return bw(ctypes.byref(b), 0x10000, 0x20000, dt, None, 0x30000, H_I, 128 if dt == 2 else 32, 0, idx, kk,
+                  g, ld, dq, 0x60000, 0x70000, None)
+    assert ib(dt=0, H_I=8) == L.DSA_ERR_UNSUPPORTED                  # FP8 only
+    assert ib(g=0) == L.DSA_ERR_INVALID_ARG
+    assert ib(dq=0x50004) == L.DSA_ERR_INVALID_ARG                   # misaligned gradient
+    assert ib(ld=4) == L.DSA_ERR_INVALID_ARG                         # ld_g < max_ctx
+    assert ib(idx=0x80000, kk=0) == L.DSA_ERR_INVALID_ARG            # k < 1 with idx
+    # dsa_sparse_mla_backward(batch, q, kv, dtype, idx, k, H, d_qk, d_v, scale, lse, dout, dq, dkv, ws, ws_bytes, s)
+    ab = L._lib.dsa_sparse_mla_backward
+
+    def mb(dt=1, lse=0x30000, dout=0x40000, dkv=0x60000, ws=0x70000, wsb=1 << 30, H=128):
+        return ab(ctypes.byref(b), 0x10000, 0x20000, dt, 0x80000, 64, H, 576 if dt == 1 else 64, 512 if dt == 1 else 64,
+                  0.1, lse, dout, 0x50000, dkv, ws, wsb, None)
+    assert mb(dt=0) == L.DSA_ERR_UNSUPPORTED                         # BF16 only
+    assert mb(lse=None) == L.DSA_ERR_INVALID_ARG
+    assert mb(dout=0x40004) == L.DSA_ERR_INVALID_ARG
+    assert mb(dkv=None) == L.DSA_ERR_INVALID_ARG
+    assert mb(ws=None) == L.DSA_ERR_WORKSPACE
+    assert mb(wsb=16) == L.DSA_ERR_WORKSPACE
+    assert mb(H=96) == L.DSA_ERR_UNSUPPORTED
+    n = ctypes.c_size_t(0)
+    assert L._lib.dsa_sparse_mla_backward_workspace_size(ctypes.byref(b), 128, 64, ctypes.byref(n)) == L.DSA_OK
+    assert n.value == 4 * ((8 * 128 * 64 * 2 + 255) // 256 * 256)
+    assert L._lib.dsa_sparse_mla_backward_workspace_size(ctypes.byref(b), 100, 64, ctypes.byref(n)) \
+        == L.DSA_ERR_UNSUPPORTED
+
+
 def test_forward_validation(L):
     import torch
     b = _batch(L)

@@ -269,7 +269,7 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
   };
 
   // One 64-key slab with the keys in kf and their scales in ks.
-  auto slab = [&](int32_t s0, const i32x8 (&kf)[NST], const int (&ks)[NST]) {
+  auto slab = [&](int32_t s0, i32x8 (&kf)[NST], const int (&ks)[NST]) {
     float acc[NST][NR];
     f32x4 x[LAG + 1];
 #pragma unroll
@@ -286,6 +286,14 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
                                                                               0, SC ? ks[st] : 127);
         }
       }
+      // Order pins (empty volatile asm, kept in program order): MFMA j's result
+      // and the one whose epilogue runs now (MFMA j - LAG) pass through the
+      // first, the accumulators that epilogue wrote and the keys of MFMA j + 1
+      // through the second.  So the epilogue of MFMA j - LAG runs after MFMA j
+      // issues and before MFMA j + 1: left alone, the compiler runs each
+      // epilogue straight after its own MFMA, and the wave waits out every one.
+      if (j < NM) asm volatile("" : "+v"(x[j % (LAG + 1)]));
+      if (j >= LAG) asm volatile("" : "+v"(x[(j - LAG) % (LAG + 1)]));
       if (j >= LAG) {
         const int e = j - LAG;
         const int st = e / NPS, u = e % NPS;
@@ -305,12 +313,14 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
             }
           }
         }
-      }
-    }
+        if (LIN && u == 0) {
 #pragma unroll
-    for (int j = 0; j < NM; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, LIN ? 4 : 8, 0);   // then the epilogue VALU work
+          for (int i = 0; i < NR; ++i) asm volatile("" : "+v"(acc[st][i]));
+        } else {
+          asm volatile("" : "+v"(acc[st][(u - (LIN ? 1 : 0)) / NHT]));
+        }
+      }
+      if (j + 1 < NM) asm volatile("" : "+v"(kf[(j + 1) / NPS]));
     }
 #pragma unroll
     for (int i = 0; i < NR; ++i) {

@@ -41,7 +41,7 @@ typedef struct ihipStream_t* dsa_stream_t; /* a hipStream_t; NULL = default stre
 typedef enum {
   DSA_OK = 0,
   DSA_ERR_INVALID_ARG = 1,  /* null / misaligned pointer, inconsistent sizes */
-  DSA_ERR_UNSUPPORTED = 2,  /* a valid shape / dtype this build does not implement */
+  DSA_ERR_UNSUPPORTED = 2,  /* a valid shape / dtype the library does not implement */
   DSA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the size query */
   DSA_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
 } dsa_status;

@@ -8,7 +8,12 @@ import torch
 import oracle
 from sparse_attention_03_amd import inputs as gen
 
-# Tolerances of the acceptance bar (row-normalised max error).
+# Tolerances of the acceptance bar.  The error is row-normalised: per row,
+# max |gpu - ref| / max |ref|, and the worst row counts (score rows are per
+# query, attention rows per (query, head)).  FP8 indexer scores: 2e-2 against
+# the oracle on the same e4m3 bytes; bf16 attention: 1e-2; the fp32 tiny
+# workload: 1e-5 for both; FP8 selection recall against the oracle's scores:
+# 0.995 on rows with more than k candidates.
 TOL_SCORES_FP8 = 2e-2
 TOL_SCORES_F32 = 1e-5
 TOL_ATTN_BF16 = 1e-2

@@ -101,7 +101,11 @@ const char* dsa_version(void);
  * qt = sum_j w[r,j] q_idx[r,j,:] (the same function, since
  * ReLU(x) = (x + |x|) / 2); qt is carried as four E4M3 terms with power-of-two
  * scales per 32 elements, within about 2^-16 of each block's largest value.
- * Other batches (decode) apply the activation per head.
+ * Other batches (decode) apply the activation per head.  The two forms differ
+ * in the last bits of a score.  The form is chosen from the whole batch
+ * (batch->total_q >= 8 * num_seqs), and dsa_forward makes the same choice for
+ * every chunk it scores, so a row gets the same score from dsa_forward as
+ * from dsa_indexer_scores over the batch, whatever q_block is.
  * k_idx_scale [total_k] uint8 E8M0, or NULL: FP8 keys with a per-token
  *   power-of-two scale (as dsa_cache_append writes them); key s is then
  *   value(k_idx[s, :]) * 2^(k_idx_scale[s] - 127).  The MFMA applies the
@@ -161,7 +165,11 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scor
  *   lse  [total_q, H]        fp32 output, or NULL
  * Arithmetic (BF16): bf16 MFMA with fp32 accumulation, fp32 softmax
  * statistics, probabilities rounded to bf16 for the value product, output
- * rounded to nearest even.  Supported: BF16 with d_qk = 576, d_v = 512,
+ * rounded to nearest even.  Range: the scores z must be finite in fp32 and
+ * the value columns below 2^117 in magnitude (2048 of them summed with
+ * weights <= 1 stay finite in fp32); within that the output is finite, also
+ * when a late entry's score dominates the first ones (the row is then
+ * recomputed against its true maximum).  Supported: BF16 with d_qk = 576, d_v = 512,
  * H in {32, 64, 128}; F32 with d_qk <= 1024, d_v <= d_qk, H <= 128;
  * 1 <= k <= 2048.  The workspace (possibly 0 bytes) holds split partials.
  */

@@ -1,36 +1,49 @@
 """Builds libdsa.so (the HIP kernels and the C interface) for gfx950 with hipcc.
 
 The library is built in-tree, next to this file, so that it travels with the
-source tree.  Packed-FP32 instructions are disabled for the device code.
+source tree.  Each source compiles to its own object in parallel (the
+kernels of one file never call into another file's device code), then the
+objects are linked into the shared library.  Packed-FP32 instructions are
+disabled for the device code.
 """
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
+OBJ_DIR = os.path.join(LIB_DIR, "obj")
 LIB = os.path.join(LIB_DIR, "libdsa.so")
 SOURCES = ["api.hip", "indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip", "align.hip", "mla_backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-FLAGS = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",
+FLAGS = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wno-unused-command-line-argument"]
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    os.makedirs(LIB_DIR, exist_ok=True)
-    cmd = [HIPCC, *FLAGS, *extra_flags, *(os.path.join(CSRC, s) for s in SOURCES), "-o", LIB + ".tmp"]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed to build libdsa.so")
+        raise RuntimeError("hipcc failed: " + " ".join(cmd[-3:]))
     errs = [ln for ln in res.stderr.splitlines() if "error" in ln]
     if errs:
         sys.stderr.write("\n".join(errs) + "\n")
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    objs = [os.path.join(OBJ_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cmds = [[HIPCC, *FLAGS, *extra_flags, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    workers = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"], verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -526,6 +526,7 @@ dsa_status dsa_forward(const dsa_forward_params* p, void* ws, size_t ws_bytes, d
     dsa::IndexerLaunch IL{v, p->k, p->q_idx, p->k_idx, p->w, scores, f.ld, p->H_I, p->d_I, (int32_t)p->act,
                           p->idx_dtype == DSA_FP8_E4M3, cus, base + f.off_lin};
     IL.k_scale = p->k_idx_scale;
+    IL.batch_rows = b->total_q;  // every chunk scores its rows as the whole batch does
     hipError_t e = dsa::launch_indexer(IL, st);
     if (e != hipSuccess) return hip_fail(e, "forward indexer launch");
     dsa::TopkLaunch TL{v, scores, f.ld, p->k, idx, base + f.off_topk, cus};

@@ -32,7 +32,17 @@ struct IndexerLaunch {
   int32_t num_cus;
   void* ws;                // indexer_workspace_bytes(rows, fp8, act) bytes, or null when that is 0
   const uint8_t* k_scale = nullptr;  // [total_k] E8M0 per-key scales (FP8), or null
+  // FP8 kernel family: prefill-like batches (at least 8 query rows per
+  // sequence) share key slabs between rows and, with ReLU, take the
+  // linear-term form of the score; other batches stream keys per row.  The
+  // two differ in the last bits of a score, so the choice is made from the
+  // whole batch (its total rows), not from the rows of one launch: a chunk of
+  // a batch scores its rows as the batch does.
+  int32_t batch_rows = -1;  // total query rows of the batch; -1: this launch's rows
 };
+// True when a batch of `total_rows` query rows in `num_seqs` sequences takes
+// the prefill-like (shared key slab) FP8 indexer.
+inline bool indexer_prefill_like(int64_t total_rows, int num_seqs) { return total_rows >= 8LL * num_seqs; }
 
 struct TopkLaunch {
   BatchView b;

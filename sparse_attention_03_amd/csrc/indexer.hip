@@ -581,7 +581,7 @@ hipError_t launch_indexer(const IndexerLaunch& L, hipStream_t s) {
   if (L.fp8) {
     // prefill-like batches (sequences of many query rows): workgroups of eight
     // rows share their keys; otherwise every row streams its own
-    const bool shared = (int64_t)rows >= 8LL * L.b.num_seqs;
+    const bool shared = indexer_prefill_like(L.batch_rows >= 0 ? L.batch_rows : rows, L.b.num_seqs);
     if (!shared) {
       // one workgroup per CU (128 KB of LDS): key chunks that cover the CUs once
       const int64_t row_blocks = (rows + kStreamRows - 1) / kStreamRows;

@@ -286,16 +286,26 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
       }
     }
     if (pass == 0) {
-      // Probabilities grew past the fp32 / bf16 range only if some row sum did.
-      // Four lanes share a head's row, so with every per-lane sum below 2^90
-      // the row sum stays below 2^92 and every sum of p * v (|v| < 2^31, the
-      // bf16 values a latent holds in practice) below 2^123: finite in fp32.
-      // Every wave agrees on whether the row is recomputed (the buffers are
-      // shared).
+      // Against the first tile's max, a later score far above it scales its
+      // probability up.  The row is recomputed against the true max when a
+      // per-lane row sum reaches 2^90 (the four lanes of a head then keep its
+      // sum below 2^92, inside the fp32 / bf16 range) or when a sum of p * v
+      // left the fp32 range (large latents: x - x is NaN exactly for inf and
+      // NaN, so one sum of those flags every non-finite accumulator).  Every
+      // wave agrees on whether the row is recomputed (the buffers are shared).
+      float nf = 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < kDvTiles; ++dt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) nf += oacc[dt][nt][e] - oacc[dt][nt][e];
+      overflow = !(nf == 0.0f);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) overflow |= !(l_run[nt] < kSumLimit);
       if (!__syncthreads_or(overflow)) break;
-    }  // after the max-only pass m_fix holds the true max: the recompute cannot overflow
+    }  // after the max-only pass m_fix holds the true max: every p <= 1, so the
+       // recompute stays finite while 2048 max|v| does (|v| < 2^117)
   }
 
   // ---- epilogue
@@ -500,25 +510,40 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_target_kernel(MlaArgs a) {
 
 // Combine key-split partials: o = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M).
 // One workgroup per (row, head); each thread owns 4 consecutive value columns.
+// Up to kMaxSplits splits: the weights are formed by the whole workgroup
+// (strided over the splits, then a max and a sum across its two waves).
 template <bool BF16>
 __global__ __launch_bounds__(128) void merge_kernel(MlaArgs a, int d_v) {
-  __shared__ float wsh[64];
-  __shared__ float norm[2];
+  __shared__ float wsh[kMaxSplits];
+  __shared__ float red[2][2];
   const int32_t rl = blockIdx.x, r = a.row_begin + rl;
   const int h = blockIdx.y;
   const int S = a.splits;
+  const int tid = threadIdx.x, wv = tid >> 6;
   const int64_t slot0 = (int64_t)rl * S * a.H + h;  // split s: slot0 + s * H
-  if (threadIdx.x < 64) {
-    float ls = threadIdx.x < S ? a.ws_lse[slot0 + (int64_t)threadIdx.x * a.H] : -INFINITY;
-    const float M = wave_max(ls);
-    const float wgt = (M == -INFINITY || ls == -INFINITY) ? 0.0f : expf(ls - M);
-    if (threadIdx.x < S) wsh[threadIdx.x] = wgt;
-    const float den = wave_sum(wgt);
-    if (threadIdx.x == 0) { norm[0] = den > 0.0f ? 1.0f / den : 0.0f; norm[1] = den > 0.0f ? M + logf(den) : -INFINITY; }
+  float mloc = -INFINITY;
+  for (int s = tid; s < S; s += 128) {
+    const float ls = a.ws_lse[slot0 + (int64_t)s * a.H];
+    wsh[s] = ls;
+    mloc = fmaxf(mloc, ls);
   }
+  mloc = wave_max(mloc);
+  if ((tid & 63) == 0) red[0][wv] = mloc;
   __syncthreads();
-  const float inv = norm[0];
-  for (int d = 4 * threadIdx.x; d < d_v; d += 4 * blockDim.x) {
+  const float M = fmaxf(red[0][0], red[0][1]);
+  float dloc = 0.0f;
+  for (int s = tid; s < S; s += 128) {
+    const float ls = wsh[s];
+    const float wgt = (M == -INFINITY || ls == -INFINITY) ? 0.0f : expf(ls - M);
+    wsh[s] = wgt;
+    dloc += wgt;
+  }
+  dloc = wave_sum(dloc);
+  if ((tid & 63) == 0) red[1][wv] = dloc;
+  __syncthreads();
+  const float den = red[1][0] + red[1][1];
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  for (int d = 4 * tid; d < d_v; d += 4 * blockDim.x) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < S; ++s) {
       const float wgt = wsh[s];
@@ -535,7 +560,7 @@ __global__ __launch_bounds__(128) void merge_kernel(MlaArgs a, int d_v) {
       *(f32x4*)((float*)a.out + oi) = acc;
     }
   }
-  if (threadIdx.x == 0 && a.lse) a.lse[(int64_t)r * a.H + h] = norm[1];
+  if (tid == 0 && a.lse) a.lse[(int64_t)r * a.H + h] = den > 0.0f ? M + logf(den) : -INFINITY;
 }
 
 // fp32 inputs, alignment target: one workgroup per row, the heads in turn;
@@ -664,8 +689,9 @@ int attention_splits(int rows, int k, bool bf16, int num_cus) {
   if (!bf16 || rows <= 0) return 1;
   const int ntiles = (k + kTile - 1) / kTile;
   int splits = 1;
-  while (splits < ntiles && (int64_t)rows * splits < (int64_t)num_cus) splits <<= 1;
+  while (splits < ntiles && splits < kMaxSplits && (int64_t)rows * splits < (int64_t)num_cus) splits <<= 1;
   if (splits > ntiles) splits = ntiles;
+  if (splits > kMaxSplits) splits = kMaxSplits;
   return splits < 1 ? 1 : splits;
 }
 

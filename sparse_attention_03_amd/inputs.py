@@ -114,20 +114,26 @@ def _gen(device, seed):
     return g
 
 
-def _normal(shape, g, device, std, out_dtype, chunk_elems=1 << 28):
+def _normal(shape, g, device, std, out_dtype, chunk_elems=1 << 28, keep=None):
     """N(0, std^2) drawn in float32 and stored as out_dtype, in chunks to bound
-    the float32 temporary."""
+    the float32 temporary.  `keep`: a list that receives the float32 draws
+    before the storage cast (the same random stream either way)."""
     shape = tuple(int(s) for s in shape)
     n = math.prod(shape)
-    if out_dtype == torch.bfloat16 and std == 1.0:
+    if out_dtype == torch.bfloat16 and std == 1.0 and keep is None:
         return torch.randn(shape, generator=g, device=device, dtype=torch.bfloat16)
     out = torch.empty(n, dtype=out_dtype, device=device)
+    full = torch.empty(n, dtype=torch.float32, device=device) if keep is not None else None
     for s in range(0, n, chunk_elems):
         e = min(n, s + chunk_elems)
         x = torch.randn(e - s, generator=g, device=device, dtype=torch.float32)
         if std != 1.0:
             x.mul_(std)
         out[s:e] = x.to(out_dtype)
+        if full is not None:
+            full[s:e] = x
+    if keep is not None:
+        keep.append(full.view(shape))
     return out.view(shape)
 
 
@@ -138,9 +144,12 @@ def _integer_values(shape, g, device, lo, hi, out_dtype):
 
 def make_problem(name, seq_ctx, seq_q, *, H_I=64, d_I=128, H=128, d_qk=576, d_v=512, k=2048,
                  idx_dtype=E4M3, dtype=torch.bfloat16, w_scale=0.125, qk_std=None, kv_std=1.0,
-                 q_std=None, scale=None, device="cpu", seed=0, integer=False, q_block=0):
+                 q_std=None, scale=None, device="cpu", seed=0, integer=False, q_block=0,
+                 keep_unquantised=False):
     """General ragged problem: sequence b has seq_ctx[b] cached tokens (the
-    query rows included) and its last seq_q[b] tokens are the queries."""
+    query rows included) and its last seq_q[b] tokens are the queries.
+    keep_unquantised: also keep the float32 draws of q_idx and k_idx (before
+    their storage cast) in meta["q_idx_f32"] / meta["k_idx_f32"]."""
     seq_ctx = [int(c) for c in seq_ctx]
     seq_q = [int(x) for x in seq_q]
     assert len(seq_ctx) == len(seq_q) and all(0 < qq <= c for qq, c in zip(seq_q, seq_ctx))
@@ -162,16 +171,19 @@ def make_problem(name, seq_ctx, seq_q, *, H_I=64, d_I=128, H=128, d_qk=576, d_v=
         k_idx = _integer_values((K, d_I), g, device, -4, 4, idx_dtype)
         w = torch.randint(0, 9, (T, H_I), generator=g, device=device, dtype=torch.int32).to(torch.float32) * 0.25
     else:
-        q_idx = _normal((T, H_I, d_I), g, device, qk_std, idx_dtype)
-        k_idx = _normal((K, d_I), g, device, qk_std, idx_dtype)
+        kq, kk = ([], []) if keep_unquantised else (None, None)
+        q_idx = _normal((T, H_I, d_I), g, device, qk_std, idx_dtype, keep=kq)
+        k_idx = _normal((K, d_I), g, device, qk_std, idx_dtype, keep=kk)
         w = torch.rand((T, H_I), generator=g, device=device, dtype=torch.float32) * w_scale
     q = _normal((T, H, d_qk), g, device, q_std, dtype)
     kv = _normal((K, d_qk), g, device, kv_std, dtype)
+    meta = dict(seed=seed, integer=integer)
+    if keep_unquantised and not integer:
+        meta["q_idx_f32"], meta["k_idx_f32"] = kq[0], kk[0]
     return DSAInputs(name=name,
                      cu_q=torch.from_numpy(cu_q).to(device), cu_k=torch.from_numpy(cu_k).to(device),
                      cu_q_host=cu_q, cu_k_host=cu_k, q_idx=q_idx, k_idx=k_idx, w=w, q=q, kv=kv,
-                     k=k, d_v=d_v, scale=float(scale), q_block=q_block,
-                     meta=dict(seed=seed, integer=integer))
+                     k=k, d_v=d_v, scale=float(scale), q_block=q_block, meta=meta)
 
 
 def mixed_decode_lengths(seed=0, n_long=32, n_short=8, lo=4096, hi=131072, short=1024):

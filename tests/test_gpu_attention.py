@@ -89,6 +89,46 @@ def test_bf16_later_scores_far_above_the_first_tile(dsa):
         assert torch.allclose(out[r].float(), torch.full_like(out[r].float(), 4.0))
 
 
+def _large_latents(p, idx, hot_rows, v_log2=40, hot_score=848.0):
+    """Value columns scaled by 2^v_log2 (exact in bf16); queries read only
+    rope column 512, which is 0 in every latent row except the row at each hot
+    row's own position (hot_score there).  The hot entry's probability against
+    a reference max of 0 is about 2^88 (below the row-sum limit of the
+    recompute), and 2^88 times values of 2^40 overflows fp32."""
+    p.q.zero_()
+    p.q[:, :, 512] = 1.0
+    p.kv[:, 512:] = 0
+    p.kv[:, :512] *= 2.0 ** v_log2
+    pos = p.positions()
+    base = np.repeat(p.cu_k_host[:-1], np.diff(p.cu_q_host))
+    for r in hot_rows:
+        p.kv[int(base[r] + pos[r]), 512] = hot_score
+        idx[r, np.sum(idx[r] >= 0) - 1] = pos[r]   # the last valid entry (ascending order kept)
+    return idx
+
+
+def test_bf16_large_latents_late_dominant_entry(dsa):
+    """Latent values of 2^40 and an entry in a late tile whose probability is
+    about 2^88 against the first tile's max: the sums of p * v leave the fp32
+    range although the row sum does not.  The row is recomputed against its
+    true max and matches the oracle."""
+    announce("attention bf16 large latents, late dominant entry")
+    p = gen.make_problem("attn", [600], [600], H_I=16, H=128, k=256, device=DEV, seed=14)
+    idx = _large_latents(p, random_selection(p, 256, 14), [400, 599])
+    out, _ = _compare(dsa, p, idx, TOL_ATTN_BF16)
+    assert torch.isfinite(out.float()).all()
+
+
+def test_bf16_large_latents_with_key_splits(dsa):
+    """The same in decode rows split over keys (several tiles per split): the
+    split holding the dominant entry recomputes; the merge stays finite."""
+    announce("attention bf16 large latents, key splits")
+    p = gen.make_problem("attn", [3000] * 16, [1] * 16, H_I=16, H=128, k=2048, device=DEV, seed=15)
+    idx = _large_latents(p, random_selection(p, 2048, 15), list(range(0, 16, 3)))
+    out, _ = _compare(dsa, p, idx, TOL_ATTN_BF16)
+    assert torch.isfinite(out.float()).all()
+
+
 def test_bf16_only_selected_rows_matter(dsa):
     announce("attention bf16 non-selected rows")
     p = gen.make_problem("attn", [400, 300], [50, 300], H_I=16, H=64, k=128, device=DEV, seed=11)

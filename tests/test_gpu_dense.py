@@ -53,6 +53,16 @@ def test_dense_bf16_decode_rows_use_key_splits(dsa):
     _check(p, out, lse, list(range(p.total_q)), TOL_ATTN_BF16)
 
 
+@pytest.mark.parametrize("ctx", [4100, 9000, 70000])
+def test_dense_bf16_one_row_many_key_splits(dsa, ctx):
+    """One long row: it is split over keys into 128 or 256 parts (more than a
+    wave's worth), all of which the merge must weigh."""
+    announce("dense attention bf16 one row, many splits", ctx)
+    p = gen.make_problem("dense", [ctx], [1], H_I=16, H=128, k=2048, device=DEV, seed=ctx)
+    out, lse = dsa.dense_mla_attn(p)
+    _check(p, out, lse, [0], TOL_ATTN_BF16)
+
+
 def test_dense_equals_sparse_over_every_candidate(dsa):
     """With as many rows as compute units neither call splits rows, and the
     dense kernel walks the same tiles in the same order as the sparse kernel

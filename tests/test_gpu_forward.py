@@ -1,11 +1,12 @@
-"""dsa_forward (HIP) end to end: against the separate calls, against the CPU
-oracle on the standard workloads (sampled rows where the oracle is slow)."""
+"""dsa_forward (HIP) end to end: against the separate calls and against the CPU
+oracle on ragged batches (the five standard workloads are in
+test_gpu_configs.py)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from dsa_check import (MIN_RECALL, TOL_ATTN_BF16, TOL_ATTN_F32, announce, host, oracle_attention_on, recall,
+from dsa_check import (MIN_RECALL, TOL_ATTN_BF16, announce, host, oracle_attention_on, recall,
                        row_norm_err, rows_of)
 from sparse_attention_03_amd import inputs as gen
 
@@ -38,7 +39,7 @@ def _check_rows(p, out, idx, rows, tol, need_exact_idx=False, act=0):
     assert np.array_equal(g_idx[short], ref_idx[short])
     if need_exact_idx:
         assert np.array_equal(g_idx, ref_idx)
-    assert rec >= MIN_RECALL
+    assert rec >= MIN_RECALL and rec_min >= 0.99
     # attention on the selection the GPU made
     o_on, _ = oracle_attention_on(p, g_idx, rows=rows)
     err = row_norm_err(g_out, o_on)
@@ -61,6 +62,27 @@ def test_forward_equals_separate_calls(dsa):
     # chunking never changes the result
     out3, lse3, idx3 = dsa.forward(p, q_block=512)
     assert torch.equal(idx3, idx) and torch.equal(out3, out)
+
+
+@pytest.mark.parametrize("act", [0, 1])
+def test_forward_short_last_chunk_scores_as_the_batch(dsa, act):
+    """A prefill-like batch whose last chunk holds fewer than 8 rows per
+    sequence: the indexer keeps the batch's form for that chunk, so on random
+    inputs the selection equals the separate calls over the whole batch bit
+    for bit.  (The attention of such a short chunk is split over keys, while
+    the one call over the whole batch is not, so there the outputs agree to
+    rounding, not bit for bit.)"""
+    announce("forward short last chunk", act)
+    p = gen.make_problem("fwd", [3001, 2600], [3001, 1], H_I=64, H=128, k=512, device=DEV, seed=28 + act)
+    idx_ref = dsa.topk(p, dsa.indexer_scores(p, act=act))
+    out_ref, lse_ref = dsa.sparse_mla_attn(p, idx_ref)
+    for qb in (1000, 3000, 997):       # last chunks of 2, 2 and 10 rows
+        out, lse, idx = dsa.forward(p, act=act, q_block=qb)
+        assert torch.equal(idx, idx_ref), qb
+        assert row_norm_err(out.float().cpu().numpy(), out_ref.float().cpu().numpy()) <= TOL_ATTN_BF16, qb
+        assert float((lse - lse_ref).abs().max()) <= 1e-3, qb
+        n_full = (p.total_q // qb) * qb  # rows of whole chunks: the same split as the one call
+        assert torch.equal(out[:n_full], out_ref[:n_full]), qb
 
 
 def test_forward_short_rows_masked_mode_with_key_splits(dsa):
@@ -105,39 +127,3 @@ def test_forward_random_inputs(dsa, act):
     out, _, idx = dsa.forward(p, act=act)
     rows = np.array([0, 1023, 1024, 1025, 2222, 3999, 4000, 4001], np.int32)
     _check_rows(p, out, idx, rows, TOL_ATTN_BF16, act=act)
-
-
-def test_tiny_fp32_config(dsa):
-    announce("forward tiny_fp32")
-    p = gen.make_config("tiny_fp32", device=DEV)
-    out, _, idx = dsa.forward(p)
-    _check_rows(p, out, idx, np.arange(p.total_q, dtype=np.int32), TOL_ATTN_F32)
-
-
-def test_prefill_8k_config(dsa):
-    announce("forward prefill_8k")
-    p = gen.make_config("prefill_8k", device=DEV)
-    out, _, idx = dsa.forward(p)
-    _check_rows(p, out, idx, [0, 1, 2046, 2047, 2048, 2049, 4100, 6000, 8191], TOL_ATTN_BF16)
-
-
-def test_decode_64x32k_config(dsa):
-    announce("forward decode_64x32k")
-    p = gen.make_config("decode_64x32k", device=DEV)
-    out, _, idx = dsa.forward(p)
-    _check_rows(p, out, idx, [0, 31, 63], TOL_ATTN_BF16)
-
-
-def test_decode_mixed_config(dsa):
-    announce("forward decode_mixed")
-    p = gen.make_config("decode_mixed", device=DEV)
-    out, _, idx = dsa.forward(p)
-    _check_rows(p, out, idx, [0, 5, 31, 32, 39], TOL_ATTN_BF16)
-
-
-def test_prefill_128k_config(dsa):
-    announce("forward prefill_128k (bench launch configuration)")
-    p = gen.make_config("prefill_128k", device=DEV)
-    out, _, idx = dsa.forward(p)
-    torch.cuda.synchronize()
-    _check_rows(p, out, idx, [0, 2047, 2048, 65535, 131071], TOL_ATTN_BF16)

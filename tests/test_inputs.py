@@ -50,3 +50,17 @@ def test_tiny_config():
     p = gen.make_config("tiny_fp32")
     assert p.q_idx.dtype == torch.float32 and p.q.shape == (256, 8, 80) and p.k == 32 and p.d_v == 64
     assert abs(p.scale - 1 / math.sqrt(80)) < 1e-12
+
+
+def test_unquantised_draws_are_the_same_stream():
+    """keep_unquantised changes nothing in the stored inputs, and the kept
+    float32 draws cast to E4M3 are exactly the stored codes."""
+    a = gen.make_problem("x", [70, 20], [70, 1], H_I=16, H=8, seed=4)
+    b = gen.make_problem("x", [70, 20], [70, 1], H_I=16, H=8, seed=4, keep_unquantised=True)
+    for n in ("q_idx", "k_idx", "w", "q", "kv"):
+        assert np.array_equal(gen.storage_numpy(getattr(a, n)), gen.storage_numpy(getattr(b, n)))
+    assert "q_idx_f32" not in a.meta
+    for n in ("q_idx", "k_idx"):
+        f = b.meta[n + "_f32"]
+        assert f.dtype == torch.float32 and f.shape == getattr(b, n).shape
+        assert np.array_equal(gen.storage_numpy(f.to(gen.E4M3)), gen.storage_numpy(getattr(b, n)))

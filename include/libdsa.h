@@ -368,6 +368,24 @@ typedef struct {
 dsa_status dsa_forward_workspace_size(const dsa_forward_params* p, size_t* bytes /* host */);
 dsa_status dsa_forward(const dsa_forward_params* p, void* ws, size_t ws_bytes, dsa_stream_t stream);
 
+/*
+ * dsa_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc.  The
+ * workspace is the library's own static device array of 128 MiB (134217728
+ * bytes), which each device the library runs on holds until the process
+ * ends; the caller still passes every input and output.  The call allocates
+ * nothing and enqueues exactly the kernels dsa_forward enqueues, so the
+ * results are identical.  A batch whose dsa_forward_workspace_size exceeds
+ * 128 MiB gives DSA_ERR_WORKSPACE with nothing enqueued (decode steps of tens
+ * of sequences fit; long prefills need dsa_forward with their own workspace).
+ * Nothing in the array needs to start at zero: a call writes every byte it
+ * reads.  Every call on one device shares that device's array, so calls that
+ * overlap on one device (other streams, other threads) race: serialise them.
+ * The first call on a device takes the array's device address (HIP error:
+ * DSA_ERR_HIP).
+ */
+dsa_status dsa_forward_noalloc(const dsa_forward_params* p, dsa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

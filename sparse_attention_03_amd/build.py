@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 OBJ_DIR = os.path.join(LIB_DIR, "obj")
 LIB = os.path.join(LIB_DIR, "libdsa.so")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip", "align.hip", "mla_backward.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "sparse_mla.hip", "cache_append.hip", "align.hip", "mla_backward.hip",
+           "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

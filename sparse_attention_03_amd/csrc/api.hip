@@ -127,6 +127,17 @@ size_t attention_ws_bytes(int32_t rows, int splits, int32_t H, int32_t d_v) {
 
 }  // namespace
 
+namespace dsa {
+// The error reporting of the C interface for the library's other sources.
+dsa_status report_error(dsa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+}  // namespace dsa
+
 extern "C" {
 
 const char* dsa_status_string(dsa_status s) {

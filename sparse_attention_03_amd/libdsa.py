@@ -69,6 +69,7 @@ _SIGS = {
                          ctypes.c_int),
     "dsa_forward_workspace_size": ([_FP, ctypes.POINTER(_sz)], ctypes.c_int),
     "dsa_forward": ([_FP, _p, _sz, _p], ctypes.c_int),
+    "dsa_forward_noalloc": ([_FP, _p], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -256,6 +257,11 @@ def dsa_forward_workspace_size(params: DsaForwardParams) -> int:
 def dsa_forward(params: DsaForwardParams, ws, stream=None):
     _check(_lib.dsa_forward(ctypes.byref(params), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                             _stream(stream)), "dsa_forward")
+
+
+def dsa_forward_noalloc(params: DsaForwardParams, stream=None):
+    """dsa_forward on the library's static scratch (no workspace argument)."""
+    _check(_lib.dsa_forward_noalloc(ctypes.byref(params), _stream(stream)), "dsa_forward_noalloc")
 
 
 def version() -> str:

@@ -10,7 +10,12 @@ FP8 + causal top-k 2048 + sparse MLA attention over 128 heads, processed in
                    step, against the MI355X dense MFMA peak of its dtype
   cpu_baseline     the CPU oracle on a bounded sample of the same workload,
                    extrapolated with the per-row cost model
-  decode           the 64 x 32K decode batch: microseconds per token
+  decode           the 64 x 32K decode batch: microseconds per token (cold:
+                   caches flushed before each step; warm beside it)
+  decode_mixed     the mixed-length decode batch, the same way
+  prefill_8k       tokens/s of the 8192-token prefill
+  length_sweep     prefill of L = 8K .. 128K tokens: step and per-kernel
+                   times, log-log slopes against L
 
 Per-kernel times come from a second, instrumented pass that issues the same
 per-chunk launches through the individual C entry points with HIP events
@@ -159,21 +164,100 @@ def cpu_baseline(p, work, n_rows=640, seed=0):
                       f"extrapolated to all rows with the per-row MAC cost model ({full:.0f} s per step)"}
 
 
-def decode_us_per_token(steps=20, warmup=3):
+DECODE_WORKLOADS = {
+    "decode_64x32k": "64 sequences x 32768 cached tokens, 1 query each, k=2048",
+    "decode_mixed": "32 sequences of U{4096..131072} cached tokens (seed 0) + 8 of 1024 (n <= k), 1 query each, k=2048",
+}
+
+
+def decode_us_per_token(name="decode_64x32k", steps=20, warmup=3):
+    """One decode step = dsa_forward over the batch (one new query per
+    sequence).  Cold: before each timed step a 1 GiB buffer is written, which
+    evicts the L2s and the 256-MB MALL, so the step reads its caches from HBM;
+    the step alone is bracketed by HIP events on the launch stream (median).
+    Warm: `steps` back-to-back steps between two events."""
     import torch
     from sparse_attention_03_amd import dsa, inputs as gen
-    p = gen.make_config("decode_64x32k", device="cuda")
+    p = gen.make_config(name, device="cuda")
     f = dsa.Forward(p)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    ev = lambda: torch.cuda.Event(enable_timing=True)
     for _ in range(warmup):
         f()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    cold = []
+    for i in range(steps):
+        flush.fill_(float(i))
+        e0, e1 = ev(), ev()
+        e0.record()
+        f()
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1) * 1e3)
+    e0, e1 = ev(), ev()
+    e0.record()
     for _ in range(steps):
         f()
+    e1.record()
     torch.cuda.synchronize()
-    step_s = (time.perf_counter() - t0) / steps
-    return {"workload": "decode_64x32k: 64 sequences x 32768 cached tokens, 1 query each, k=2048",
-            "us_per_token": step_s * 1e6 / p.total_q, "us_per_step": step_s * 1e6}
+    warm = e0.elapsed_time(e1) * 1e3 / steps
+    cold_us = float(np.median(cold))
+    del f, flush
+    torch.cuda.empty_cache()
+    return {"workload": f"{name}: {DECODE_WORKLOADS[name]}", "tokens_per_step": p.total_q,
+            "us_per_token": cold_us / p.total_q, "us_per_step": cold_us, "timing": "cold (L2 and MALL flushed), median",
+            "warm_us_per_token": warm / p.total_q, "warm_us_per_step": warm}
+
+
+def prefill_tokens_s(p, steps=5, warmup=1):
+    """dsa_forward over a whole prefill: tokens/s and ms per step (HIP events)."""
+    import torch
+    from sparse_attention_03_amd import dsa
+    f = dsa.Forward(p, with_idx=False, with_lse=False)
+    for _ in range(warmup):
+        f()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del f
+    return ms
+
+
+def length_sweep(lengths, main=None):
+    """Prefill of one sequence of L tokens (the prefill_8k distributions,
+    4096-row chunks) for each L: ms per step of the whole dsa_forward and of
+    each step's kernels, and log-log slopes of time against L.  The pages say
+    the indexer stays quadratic in L while the attention becomes linear (each
+    query attends to k = 2048 entries); the slopes test that.  `main`: the
+    already measured 131072-token figures (reused, not measured again)."""
+    import torch
+    from sparse_attention_03_amd import inputs as gen
+    rows = []
+    for L in lengths:
+        if main is not None and L == main["seq_len"]:
+            rows.append(main)
+            continue
+        p = gen.make_problem("sweep", [L], [L], device="cuda", seed=0, q_block=4096)
+        ms = prefill_tokens_s(p)
+        kt = kernel_times(p)
+        row = {"seq_len": L, "step_ms": ms, "tokens_s": L / ms * 1e3,
+               "indexer_ms": kt["indexer"], "topk_ms": kt["topk"], "attention_ms": kt["attention"]}
+        log("sweep", json.dumps(row))
+        rows.append(row)
+        del p
+        torch.cuda.empty_cache()
+    lx = np.log([r["seq_len"] for r in rows])
+    slopes = {k: float(np.polyfit(lx, np.log([r[k] for r in rows]), 1)[0])
+              for k in ("step_ms", "indexer_ms", "topk_ms", "attention_ms")}
+    # the last doubling alone (the asymptotic slope of the attention is reached late: rows with n <= k cost less)
+    last = {k: float(np.log(rows[-1][k] / rows[-2][k]) / np.log(rows[-1]["seq_len"] / rows[-2]["seq_len"]))
+            for k in ("step_ms", "indexer_ms", "topk_ms", "attention_ms")} if len(rows) > 1 else {}
+    return {"rows": rows, "loglog_slope_fit": slopes, "loglog_slope_last_doubling": last}
 
 
 def crossover(lengths, steps=3, warmup=1):
@@ -495,6 +579,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip prefill_8k and the prefill length sweep")
     ap.add_argument("--decode-only", action="store_true", help="time only the 64 x 32K decode batch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy 3 times (counter calibration under rocprofv3)")
@@ -535,7 +620,8 @@ def main():
         print(json.dumps({"append": append_bench(steps=args.steps, warmup=args.warmup)}), flush=True)
         return
     if args.decode_only:
-        print(json.dumps({"decode": decode_us_per_token(steps=args.steps, warmup=args.warmup)}), flush=True)
+        print(json.dumps({name: decode_us_per_token(name, steps=args.steps, warmup=args.warmup)
+                          for name in DECODE_WORKLOADS}), flush=True)
         return
     if args.copy_calibration:
         # an elementwise kernel (not hipMemcpy, which the counters do not see)
@@ -601,12 +687,32 @@ def main():
                               "flop_per_launch": fl[dom][0] / launches}
         result["kernels"] = rows
         log(json.dumps(rows))
-    if not args.no_decode:
-        log("decode_64x32k")
-        result["decode"] = decode_us_per_token()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on sampled rows)")
         result["cpu_baseline"] = cpu_baseline(p, work)
+    main_row = None
+    if "kernels" in result:
+        main_row = {"seq_len": p.total_q, "step_ms": ms_step, "tokens_s": tokens_s,
+                    "indexer_ms": result["kernels"]["indexer"]["ms_per_step"],
+                    "topk_ms": result["kernels"]["topk"]["ms_per_step"],
+                    "attention_ms": result["kernels"]["attention"]["ms_per_step"]}
+    del f, p
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        for name in DECODE_WORKLOADS:
+            log(name)
+            result["decode" if name == "decode_64x32k" else name] = decode_us_per_token(name)
+    if not args.no_sweep:
+        log("prefill_8k")
+        p8 = gen.make_config("prefill_8k", device="cuda")
+        ms8 = prefill_tokens_s(p8, steps=10, warmup=2)
+        result["prefill_8k"] = {"workload": "prefill_8k: 1 sequence, L=8192, k=2048, H=128 (q_block 4096)",
+                                "tokens_s": p8.total_q / ms8 * 1e3, "ms_per_step": ms8}
+        del p8
+        torch.cuda.empty_cache()
+        if main_row is not None:
+            log("length sweep")
+            result["length_sweep"] = length_sweep([8192, 16384, 32768, 65536, 131072], main=main_row)
     print(json.dumps(result), flush=True)
 
 

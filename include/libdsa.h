@@ -38,7 +38,16 @@ extern "C" {
 
 typedef struct ihipStream_t* dsa_stream_t; /* a hipStream_t; NULL = default stream */
 
-typedef enum {
+/* The enums are int-sized in C and C++ alike.  In C++ they have a fixed int
+ * underlying type, so a value a C caller passes outside the listed ones is
+ * still a value of the type, which the library then rejects. */
+#ifdef __cplusplus
+#define DSA_ENUM_BASE : int
+#else
+#define DSA_ENUM_BASE
+#endif
+
+typedef enum DSA_ENUM_BASE {
   DSA_OK = 0,
   DSA_ERR_INVALID_ARG = 1,  /* null / misaligned pointer, inconsistent sizes */
   DSA_ERR_UNSUPPORTED = 2,  /* a valid shape / dtype the library does not implement */
@@ -46,13 +55,13 @@ typedef enum {
   DSA_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
 } dsa_status;
 
-typedef enum {
+typedef enum DSA_ENUM_BASE {
   DSA_F32 = 0,
   DSA_BF16 = 1,
   DSA_FP8_E4M3 = 2          /* OCP E4M3FN: bias 7, max 448, no infinities */
 } dsa_dtype;
 
-typedef enum {
+typedef enum DSA_ENUM_BASE {
   DSA_ACT_RELU = 0,         /* [P1] "Lightning indexer / Step 1": ReLU, chosen for throughput */
   DSA_ACT_GELU = 1          /* [P2] 【闪电索引器】 names GELU: x * Phi(x), erf form */
 } dsa_act;

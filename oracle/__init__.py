@@ -18,7 +18,8 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 ACT_RELU, ACT_GELU = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# DSA_ORACLE_LIB: another build of the oracle (e.g. the sanitized build)
+_LIB_PATH = os.environ.get("DSA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 

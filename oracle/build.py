@@ -11,15 +11,23 @@ SRC = os.path.join(HERE, "dsa_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(verbose: bool = False) -> str:
+# AddressSanitizer / UndefinedBehaviorSanitizer build for the CPU tests (load
+# it with DSA_ORACLE_LIB and preload gcc's libasan).
+SANITIZED_LIB = os.path.join(HERE, "liboracle_sanitized.so")
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    out = SANITIZED_LIB if sanitize else LIB
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
     cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
-           "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm"]
+           "-Wall", "-Wextra", *(san if sanitize else []), "-o", out + ".tmp", SRC, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv))

@@ -37,17 +37,33 @@ def _run(cmd, verbose):
         sys.stderr.write("\n".join(errs) + "\n")
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    objs = [os.path.join(OBJ_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    cmds = [[HIPCC, *FLAGS, *extra_flags, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+# Host code (argument checks, workspace plans, launches) instrumented with
+# AddressSanitizer and UndefinedBehaviorSanitizer; the device code is built as
+# usual.  For CPU-side tests only: load it with LIBDSA_PATH and preload clang's
+# ASan runtime (the command is in the library's design notes).
+SANITIZED_LIB = os.path.join(LIB_DIR, "libdsa_sanitized.so")
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                  "-Xarch_host", "-g"]
+
+
+def build(verbose: bool = False, extra_flags=(), sanitize: bool = False) -> str:
+    obj_dir = os.path.join(LIB_DIR, "obj_sanitized" if sanitize else "obj")
+    out = SANITIZED_LIB if sanitize else LIB
+    flags = [*FLAGS, *(SANITIZE_FLAGS if sanitize else ()), *extra_flags]
+    os.makedirs(obj_dir, exist_ok=True)
+    objs = [os.path.join(obj_dir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cmds = [[HIPCC, *flags, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
     workers = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with ThreadPoolExecutor(max_workers=workers) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"], verbose)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out + ".tmp"]
+    if sanitize:
+        link[3:3] = ["-fsanitize=address", "-fsanitize=undefined", "-shared-libsan"]
+    _run(link, verbose)
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv))

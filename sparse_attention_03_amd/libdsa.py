@@ -13,7 +13,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "lib", "libdsa.so")
+# LIBDSA_PATH: another build of the library (e.g. the sanitized host build)
+LIB_PATH = os.environ.get("LIBDSA_PATH") or os.path.join(_HERE, "lib", "libdsa.so")
 
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2

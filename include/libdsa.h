@@ -122,7 +122,9 @@ const char* dsa_version(void);
  * Workspace: dsa_indexer_workspace_size bytes (528 per query row for FP8 with
  * ReLU, else 0), 16-B aligned; ws may be NULL when that is 0; a smaller
  * workspace gives DSA_ERR_WORKSPACE.  The size needs no device.
- * Supported: FP8 with d_I = 128, H_I in {16, 32, 48, 64} and max_ctx <= 2^24;
+ * Supported: FP8 with d_I = 128, H_I a multiple of 4 up to 64 (heads are
+ * taken 16 at a time; past H_I the query and weight are zero) and
+ * max_ctx <= 2^24;
  * F32 with d_I <= 256, H_I <= 64 and H_I * d_I <= 8192.
  */
 dsa_status dsa_indexer_workspace_size(const dsa_batch* batch, dsa_dtype idx_dtype, int32_t H_I, int32_t d_I,
@@ -175,11 +177,13 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scor
  * Arithmetic (BF16): bf16 MFMA with fp32 accumulation, fp32 softmax
  * statistics, probabilities rounded to bf16 for the value product, output
  * rounded to nearest even.  Range: the scores z must be finite in fp32 and
- * the value columns below 2^117 in magnitude (2048 of them summed with
- * weights <= 1 stay finite in fp32); within that the output is finite, also
- * when a late entry's score dominates the first ones (the row is then
- * recomputed against its true maximum).  Supported: BF16 with d_qk = 576, d_v = 512,
- * H in {32, 64, 128}; F32 with d_qk <= 1024, d_v <= d_qk, H <= 128;
+ * the value columns below 2^66 in magnitude; within that the output is
+ * finite, also when a late entry's score dominates the first ones (a row
+ * whose probabilities, taken against its first tile's maximum, grow past
+ * 2^60 is recomputed against its true maximum).  Supported: BF16 with d_qk = 576, d_v = 512,
+ * H a multiple of 8 up to 128 (the kernel runs waves of 32 heads; heads
+ * past H in the last wave are computed on a copy and not stored);
+ * F32 with d_qk <= 1024, d_v <= d_qk, H <= 128;
  * 1 <= k <= 2048.  The workspace (possibly 0 bytes) holds split partials.
  */
 dsa_status dsa_sparse_mla_attn_workspace_size(const dsa_batch* batch, dsa_dtype dtype, int32_t H,
@@ -226,7 +230,8 @@ dsa_status dsa_dense_mla_attn(const dsa_batch* batch, const void* q, const void*
  *   dq[r,h,:]   += sum_s dS_s kv[kbase + s, :]
  *   dkv[kbase + s, :] += sum_h dS_s q[r,h,:]  (all d_qk columns)
  *                      + sum_h P_s dout[r,h,:] (first d_v columns)
- *   q, kv, idx, k, H, d_qk, d_v, softmax_scale as dsa_sparse_mla_attn (BF16 only)
+ *   q, kv, idx, k, H, d_qk, d_v, softmax_scale as dsa_sparse_mla_attn (BF16 only,
+ *        H in {32, 64, 128})
  *   lse  [total_q, H] fp32: the forward's log-sum-exp (P is recomputed against
  *        it; D = sum_s P_s dP_s is formed in fp32 over the row's entries)
  *   dout [total_q, H, d_v] bf16, 16-B aligned
@@ -258,7 +263,7 @@ dsa_status dsa_sparse_mla_backward(const dsa_batch* batch, const void* q, const 
  * (sum_e p[r, e] = 1 up to rounding).  Candidates: idx == NULL, every
  * position s_e = e <= pos_r (dense warm-up); else s_e = idx[r, e] for the
  * entries >= 0 (the selected set of the sparse stage).
- *   q, kv   as dsa_sparse_mla_attn (BF16: d_qk = 576, H in {32, 64, 128};
+ *   q, kv   as dsa_sparse_mla_attn (BF16: d_qk = 576, H a multiple of 8 up to 128;
  *           F32: d_qk <= 1024, H <= 128)
  *   idx     [total_q, k] int32 or NULL; k as dsa_sparse_mla_attn (ignored when NULL)
  *   lse     [total_q, H] fp32 (natural log); a head with lse = -inf adds nothing

@@ -239,21 +239,27 @@ __global__ __launch_bounds__(256) void indexer_bwd_kernel(IbArgs a) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) qT[i][dt] = bf16x4_t{0, 0, 0, 0};
     if (!live[i]) continue;
+    // heads past H_I (H_I a multiple of 4, not of 16) keep a zero query and
+    // weight: they add nothing and store nothing
     const uint8_t* qrow = a.q_idx + (int64_t)(rb + i) * a.H_I * 128;
-    const i32x4* p = (const i32x4*)(qrow + (h0 + li) * 128 + 32 * g);
-    const i32x4 lo = p[0], hi = p[1];
-    qf[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      short v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = bf16_bits(e4m3_to_f32(qrow[(h0 + 4 * g + j) * 128 + 16 * dt + li]));
-      qT[i][dt] = bf16x4_t{v[0], v[1], v[2], v[3]};
-    }
     const float* wrow = a.w + (int64_t)(rb + i) * a.H_I;
-    w_li[i] = wrow[h0 + li];
+    if (h0 + li < a.H_I) {
+      const i32x4* p = (const i32x4*)(qrow + (h0 + li) * 128 + 32 * g);
+      const i32x4 lo = p[0], hi = p[1];
+      qf[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      w_li[i] = wrow[h0 + li];
+    }
+    if (h0 + 4 * g < a.H_I) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w_g[i][j] = wrow[h0 + 4 * g + j];
+      for (int dt = 0; dt < 8; ++dt) {
+        short v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = bf16_bits(e4m3_to_f32(qrow[(h0 + 4 * g + j) * 128 + 16 * dt + li]));
+        qT[i][dt] = bf16x4_t{v[0], v[1], v[2], v[3]};
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w_g[i][j] = wrow[h0 + 4 * g + j];
+    }
   }
   f32x4 dq_acc[NR][8];
   float dw_acc[NR];
@@ -451,12 +457,14 @@ __global__ __launch_bounds__(256) void indexer_bwd_kernel(IbArgs a) {
     float d = dw_acc[i];
     d += __shfl_xor(d, 16);
     d += __shfl_xor(d, 32);
-    if (g == 0) atomicAdd(a.dw + (int64_t)r * a.H_I + h0 + li, d);
+    if (g == 0 && h0 + li < a.H_I) atomicAdd(a.dw + (int64_t)r * a.H_I + h0 + li, d);
+    if (h0 + 4 * g < a.H_I) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+      for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        atomicAdd(a.dq + ((int64_t)r * a.H_I + h0 + 4 * g + rr) * 128 + 16 * dt + li, dq_acc[i][dt][rr]);
+        for (int rr = 0; rr < 4; ++rr)
+          atomicAdd(a.dq + ((int64_t)r * a.H_I + h0 + 4 * g + rr) * 128 + 16 * dt + li, dq_acc[i][dt][rr]);
+    }
   }
 }
 
@@ -493,7 +501,7 @@ hipError_t launch_indexer_bwd(const IndexerBwdLaunch& L, hipStream_t s) {
   while (splits < nchunks && blocks * splits < 2LL * L.num_cus) splits <<= 1;
   if (splits > nchunks) splits = nchunks;
   a.chunks_per_split = (nchunks + splits - 1) / splits;
-  const dim3 grid((unsigned)blocks, (unsigned)splits), block((unsigned)(64 * (L.H_I / 16)));
+  const dim3 grid((unsigned)blocks, (unsigned)splits), block((unsigned)(64 * ((L.H_I + 15) / 16)));
   if (nr == 1) {
     if (L.act == 0) hipLaunchKernelGGL((indexer_bwd_kernel<0, 1>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((indexer_bwd_kernel<1, 1>), grid, block, 0, s, a);

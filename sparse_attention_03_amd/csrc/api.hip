@@ -74,7 +74,7 @@ dsa_status check_indexer(const dsa_batch* b, const void* q_idx, const void* k_id
   if (H_I < 1 || d_I < 1) return fail(DSA_ERR_INVALID_ARG, "H_I = %d, d_I = %d", H_I, d_I);
   if (dt == DSA_FP8_E4M3) {
     if (d_I != 128) return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer needs d_I = 128 (got %d)", d_I);
-    if (H_I % 16 != 0 || H_I > 64) return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer needs H_I in {16,32,48,64} (got %d)", H_I);
+    if (H_I % 4 != 0 || H_I > 64) return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer needs H_I a multiple of 4, <= 64 (got %d)", H_I);
     if (b->max_ctx > (1 << 24)) return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer needs max_ctx <= 2^24 (got %d)", b->max_ctx);
   } else if (dt == DSA_F32) {
     if (d_I > 256 || H_I > 64 || H_I * d_I > 8192)
@@ -110,7 +110,7 @@ dsa_status check_attention(const void* q, const void* kv, dsa_dtype dt, const in
   if (H < 1 || d_qk < 1 || d_v < 1 || d_v > d_qk) return fail(DSA_ERR_INVALID_ARG, "bad H / d_qk / d_v");
   if (dt == DSA_BF16) {
     if (d_qk != 576 || d_v != 512) return fail(DSA_ERR_UNSUPPORTED, "BF16 attention needs d_qk = 576, d_v = 512");
-    if (H != 32 && H != 64 && H != 128) return fail(DSA_ERR_UNSUPPORTED, "BF16 attention needs H in {32, 64, 128}");
+    if (H % 8 != 0 || H > 128) return fail(DSA_ERR_UNSUPPORTED, "BF16 attention needs H a multiple of 8, <= 128");
   } else if (dt == DSA_F32) {
     if (d_qk > 1024 || H > 128) return fail(DSA_ERR_UNSUPPORTED, "F32 attention needs d_qk <= 1024, H <= 128");
   } else {
@@ -317,6 +317,7 @@ dsa_status dsa_sparse_mla_backward(const dsa_batch* batch, const void* q, const 
   if (dsa_status s = check_batch(batch)) return s;
   if (dsa_status s = check_attention(q, kv, dtype, idx, k, H, d_qk, d_v, softmax_scale, dq, lse)) return s;
   if (dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "attention backward needs BF16");
+  if (H != 32 && H != 64 && H != 128) return fail(DSA_ERR_UNSUPPORTED, "attention backward needs H in {32, 64, 128}");
   if (!lse || !dout || !dq || !dkv) return fail(DSA_ERR_INVALID_ARG, "lse / dout / dq / dkv is NULL");
   if (!aligned16(dout) || !aligned16(dkv)) return fail(DSA_ERR_INVALID_ARG, "dout and dkv must be 16-byte aligned");
   if (batch->total_q == 0) return DSA_OK;

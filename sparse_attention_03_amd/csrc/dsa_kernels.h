@@ -162,5 +162,7 @@ bool topk_may_segment(int max_ctx, int k);
 
 // Number of key-splits the attention uses for `rows` query rows.
 int attention_splits(int rows, int k, bool bf16, int num_cus);
+// Waves (of 32 heads each) of the bf16 attention workgroup for H heads.
+int attention_waves(int H);
 
 }  // namespace dsa

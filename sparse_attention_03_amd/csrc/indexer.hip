@@ -98,9 +98,9 @@ __global__ __launch_bounds__(256) void indexer_lin_kernel(IdxArgs a) {
   const uint8_t* qrow = a.q_idx + (int64_t)r * a.H_I * 128 + 2 * lane;
   const float* wr = a.w + (int64_t)r * a.H_I;
   float q0 = 0.0f, q1 = 0.0f;
-  for (int h = 0; h < a.H_I; h += 16) {
+  for (int h = 0; h < a.H_I; h += 4) {  // H_I is a multiple of 4
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < 4; ++u) {
       const uint32_t two = *(const uint16_t*)(qrow + (h + u) * 128);
       const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)two, false);
       const float wh = wr[h + u];
@@ -175,10 +175,16 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
     const uint8_t* qrow = a.q_idx + (int64_t)rows[i] * a.H_I * 128;
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
-      const i32x4* p = (const i32x4*)(qrow + (16 * ht + li) * 128 + 32 * g);
-      i32x4 lo = p[0], hi = p[1];
-      qf[i][ht] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      const f32x4 wq = *(const f32x4*)(a.w + (int64_t)rows[i] * a.H_I + 16 * ht + 4 * g);
+      // heads past H_I (H_I a multiple of 4, not of 16) have a zero query and
+      // a zero weight: x = 0 and they add nothing
+      qf[i][ht] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (16 * ht + li < a.H_I) {
+        const i32x4* p = (const i32x4*)(qrow + (16 * ht + li) * 128 + 32 * g);
+        i32x4 lo = p[0], hi = p[1];
+        qf[i][ht] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      f32x4 wq = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (16 * ht + 4 * g < a.H_I) wq = *(const f32x4*)(a.w + (int64_t)rows[i] * a.H_I + 16 * ht + 4 * g);
       wv[i][ht][0] = wq[0]; wv[i][ht][1] = wq[1]; wv[i][ht][2] = wq[2]; wv[i][ht][3] = wq[3];
     }
   }
@@ -589,7 +595,7 @@ hipError_t launch_indexer(const IndexerLaunch& L, hipStream_t s) {
       while (chunk > 256 && row_blocks * ((L.b.max_ctx + chunk - 1) / chunk) < L.num_cus) chunk >>= 1;
       a.key_chunk = chunk;
       dim3 grid((unsigned)row_blocks, (unsigned)((L.b.max_ctx + chunk - 1) / chunk));
-      switch (L.H_I / 16) {
+      switch ((L.H_I + 15) / 16) {
         case 1: return launch_stream<1>(a, L.act, grid, s);
         case 2: return launch_stream<2>(a, L.act, grid, s);
         case 3: return launch_stream<3>(a, L.act, grid, s);
@@ -609,7 +615,7 @@ hipError_t launch_indexer(const IndexerLaunch& L, hipStream_t s) {
     while (chunk > 256 && row_blocks * ((L.b.max_ctx + chunk - 1) / chunk) < 4LL * L.num_cus) chunk >>= 1;
     a.key_chunk = chunk;
     dim3 grid((unsigned)row_blocks, (unsigned)((L.b.max_ctx + chunk - 1) / chunk));
-    switch (L.H_I / 16) {
+    switch ((L.H_I + 15) / 16) {
       case 1: return launch_fp8<1>(a, L.act, grid, s);
       case 2: return launch_fp8<2>(a, L.act, grid, s);
       case 3: return launch_fp8<3>(a, L.act, grid, s);

@@ -21,7 +21,7 @@ constexpr int kPvAhead = 8;                // V^T fragments read ahead of their 
 constexpr int kQkSteps = kDqk / 32;        // 18
 constexpr int kDvTiles = kDv / 16;         // 32
 constexpr int kMaxSplits = 256;            // key splits of one row (the merge's weight buffer)
-constexpr float kSumLimit = 0x1p90f;       // per-lane row sums beyond this trigger the recompute
+constexpr float kSumLimit = 0x1p60f;       // per-lane row sums beyond this trigger the recompute
 
 // Tile layout in LDS: line blocks.  The tile (32 rows x 72 chunks of 16 bytes)
 // is 36 blocks of 1 KB; block 4 s + rg holds segment s (chunks 8 s .. 8 s + 7,

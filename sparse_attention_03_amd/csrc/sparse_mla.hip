@@ -63,7 +63,12 @@ struct MlaArgs {
 // selected entries.  With a.dense_short, rows with n <= k (which select every
 // candidate) take the same dense walk; their tiles and tile order equal those
 // of the index walk over idx = 0 .. pos, so the result is the same.
-template <int HPW, int NW, bool DENSE>
+// GHOST: H is not NW * 32; the heads past H compute on a copy of head H - 1
+// and store nothing, and the recompute also triggers on a non-finite sum of
+// the value accumulators.  (The H = 32, 64, 128 instances keep the plain code:
+// at this register pressure the compiler's output changed with the shape of
+// the code, and only the combinations in these two instances were validated.)
+template <int HPW, int NW, bool DENSE, bool GHOST>
 __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   constexpr int NT = HPW / 16;
   static_assert(4 % NW == 0, "a wave copies whole row groups");
@@ -108,7 +113,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   const int head0 = wave * HPW;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const uint16_t* qrow = a.q + ((int64_t)r * a.H + head0 + 16 * nt + li) * kDqk + 8 * g;
+    const int hq = GHOST ? min(head0 + 16 * nt + li, a.H - 1) : head0 + 16 * nt + li;
+    const uint16_t* qrow = a.q + ((int64_t)r * a.H + hq) * kDqk + 8 * g;
 #pragma unroll
     for (int c = 0; c < kQkSteps; ++c) qf[nt][c] = *(const bf16x8*)(qrow + 32 * c);
   }
@@ -288,19 +294,25 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
     if (pass == 0) {
       // Against the first tile's max, a later score far above it scales its
       // probability up.  The row is recomputed against the true max when a
-      // per-lane row sum reaches 2^90 (the four lanes of a head then keep its
-      // sum below 2^92, inside the fp32 / bf16 range) or when a sum of p * v
-      // left the fp32 range (large latents: x - x is NaN exactly for inf and
-      // NaN, so one sum of those flags every non-finite accumulator).  Every
-      // wave agrees on whether the row is recomputed (the buffers are shared).
-      float nf = 0.0f;
+      // per-lane row sum reaches 2^60: below that the four lanes of a head keep
+      // its row sum below 2^62, so every p is below 2^62 and every sum of p * v
+      // stays finite in fp32 while the latent values are below 2^66 in
+      // magnitude.  (Scores differ from the first tile's max by far less than
+      // the 40 nats it takes to reach the limit.)  Every wave agrees on whether
+      // the row is recomputed (the buffers are shared).
+      if constexpr (GHOST) {
+        // also on a non-finite accumulator: one running sum of the lane's
+        // accumulators is non-finite when any of them is (x - x is NaN
+        // exactly for inf and NaN; an overflow of the sum only costs a recompute)
+        float sum = 0.0f;
 #pragma unroll
-      for (int dt = 0; dt < kDvTiles; ++dt)
+        for (int dt = 0; dt < kDvTiles; ++dt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+          for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) nf += oacc[dt][nt][e] - oacc[dt][nt][e];
-      overflow = !(nf == 0.0f);
+            for (int e = 0; e < 4; ++e) sum += oacc[dt][nt][e];
+        overflow = !(sum - sum == 0.0f);
+      }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) overflow |= !(l_run[nt] < kSumLimit);
       if (!__syncthreads_or(overflow)) break;
@@ -318,6 +330,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
     const bool empty = !(l > 0.0f);
     const float inv = empty ? 0.0f : 1.0f / l;
     const float lse_v = empty ? -INFINITY : (m_fix[nt] + log2f(l)) * 0.69314718055994531f;
+    if (GHOST && h >= a.H) continue;  // a head past H: nothing to store
     if (a.splits == 1) {
       uint16_t* orow = a.out + ((int64_t)r * a.H + h) * kDv + 4 * g;
 #pragma unroll
@@ -389,10 +402,11 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_target_kernel(MlaArgs a) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int h = head0 + 16 * nt + li;
-    const uint16_t* qrow = a.q + ((int64_t)r * a.H + h) * kDqk + 8 * g;
+    const int hq = min(h, a.H - 1);  // heads past H copy head H - 1 and add nothing
+    const uint16_t* qrow = a.q + ((int64_t)r * a.H + hq) * kDqk + 8 * g;
 #pragma unroll
     for (int c = 0; c < kQkSteps; ++c) qf[nt][c] = *(const bf16x8*)(qrow + 32 * c);
-    lse2[nt] = a.lse_in[(int64_t)r * a.H + h] * 1.4426950408889634f;  // -inf: the head adds nothing
+    lse2[nt] = h < a.H ? a.lse_in[(int64_t)r * a.H + h] * 1.4426950408889634f : -INFINITY;  // -inf: adds nothing
   }
   __syncthreads();
   const uint32_t tmask_lane = !dense && lane < kMaxSel / kTile ? tmask[lane] : 0u;
@@ -668,22 +682,31 @@ hipError_t launch_target(const MlaArgs& a, int rows, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int HPW, int NW, bool DENSE>
-hipError_t launch_bf16(const MlaArgs& a, int rows, hipStream_t s) {
+template <int HPW, int NW, bool DENSE, bool GHOST>
+hipError_t launch_bf16_g(const MlaArgs& a, int rows, hipStream_t s) {
   const size_t lds = (size_t)kNumBuf * kTileBytes + kMaxSel * sizeof(int32_t) + (kMaxSel / kTile) * sizeof(uint32_t);
   static bool attr_set = false;  // benign race: idempotent attribute call
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)mla_bf16_kernel<HPW, NW, DENSE>,
+    hipError_t e = hipFuncSetAttribute((const void*)mla_bf16_kernel<HPW, NW, DENSE, GHOST>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((mla_bf16_kernel<HPW, NW, DENSE>), dim3((unsigned)rows, (unsigned)a.splits), dim3(NW * 64), lds,
-                     s, a);
+  hipLaunchKernelGGL((mla_bf16_kernel<HPW, NW, DENSE, GHOST>), dim3((unsigned)rows, (unsigned)a.splits),
+                     dim3(NW * 64), lds, s, a);
   return hipGetLastError();
 }
 
+template <int HPW, int NW, bool DENSE>
+hipError_t launch_bf16(const MlaArgs& a, int rows, hipStream_t s) {
+  return a.H == NW * HPW ? launch_bf16_g<HPW, NW, DENSE, false>(a, rows, s)
+                         : launch_bf16_g<HPW, NW, DENSE, true>(a, rows, s);
+}
+
 }  // namespace
+
+// Waves of 32 heads per workgroup for H heads (heads past H are masked).
+int attention_waves(int H) { return H <= 32 ? 1 : H <= 64 ? 2 : 4; }
 
 int attention_splits(int rows, int k, bool bf16, int num_cus) {
   if (!bf16 || rows <= 0) return 1;
@@ -730,13 +753,13 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t s) {
       hipLaunchKernelGGL(mla_target_f32_kernel, dim3((unsigned)rows), dim3(256), lds, s, a, L.d_qk, L.scale, m);
       return hipGetLastError();
     }
-    switch (L.H * 2 + (L.dense ? 1 : 0)) {
-      case 64: return launch_target<32, 1, false>(a, rows, s);
-      case 128: return launch_target<32, 2, false>(a, rows, s);
-      case 256: return launch_target<32, 4, false>(a, rows, s);
-      case 65: return launch_target<32, 1, true>(a, rows, s);
-      case 129: return launch_target<32, 2, true>(a, rows, s);
-      case 257: return launch_target<32, 4, true>(a, rows, s);
+    switch (attention_waves(L.H) * 2 + (L.dense ? 1 : 0)) {
+      case 2: return launch_target<32, 1, false>(a, rows, s);
+      case 4: return launch_target<32, 2, false>(a, rows, s);
+      case 8: return launch_target<32, 4, false>(a, rows, s);
+      case 3: return launch_target<32, 1, true>(a, rows, s);
+      case 5: return launch_target<32, 2, true>(a, rows, s);
+      case 9: return launch_target<32, 4, true>(a, rows, s);
       default: return hipErrorInvalidValue;
     }
   }
@@ -747,13 +770,13 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t s) {
     return hipGetLastError();
   }
   hipError_t e;
-  switch (L.H * 2 + (L.dense ? 1 : 0)) {
-    case 64: e = launch_bf16<32, 1, false>(a, rows, s); break;
-    case 128: e = launch_bf16<32, 2, false>(a, rows, s); break;
-    case 256: e = launch_bf16<32, 4, false>(a, rows, s); break;
-    case 65: e = launch_bf16<32, 1, true>(a, rows, s); break;
-    case 129: e = launch_bf16<32, 2, true>(a, rows, s); break;
-    case 257: e = launch_bf16<32, 4, true>(a, rows, s); break;
+  switch (attention_waves(L.H) * 2 + (L.dense ? 1 : 0)) {
+    case 2: e = launch_bf16<32, 1, false>(a, rows, s); break;
+    case 4: e = launch_bf16<32, 2, false>(a, rows, s); break;
+    case 8: e = launch_bf16<32, 4, false>(a, rows, s); break;
+    case 3: e = launch_bf16<32, 1, true>(a, rows, s); break;
+    case 5: e = launch_bf16<32, 2, true>(a, rows, s); break;
+    case 9: e = launch_bf16<32, 4, true>(a, rows, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || a.splits == 1) return e;

@@ -85,7 +85,8 @@ def test_indexer_validation(L):
     assert b"NULL" in L._lib.dsa_last_error()
     assert _call_indexer(L, b, q=0x10004) == L.DSA_ERR_INVALID_ARG        # misaligned
     assert _call_indexer(L, b, d_I=64) == L.DSA_ERR_UNSUPPORTED           # fp8 needs d_I 128
-    assert _call_indexer(L, b, H_I=20) == L.DSA_ERR_UNSUPPORTED
+    assert _call_indexer(L, b, H_I=18) == L.DSA_ERR_UNSUPPORTED           # fp8: H_I a multiple of 4
+    assert _call_indexer(L, b, H_I=68) == L.DSA_ERR_UNSUPPORTED           # ... up to 64
     assert _call_indexer(L, b, dt=1) == L.DSA_ERR_UNSUPPORTED             # bf16 indexer
     assert _call_indexer(L, b, act=7) == L.DSA_ERR_INVALID_ARG
     assert _call_indexer(L, b, ld=4) == L.DSA_ERR_INVALID_ARG             # ld < max_ctx
@@ -110,7 +111,7 @@ def test_indexer_validation(L):
     assert n.value == 0
     assert L._lib.dsa_indexer_workspace_size(ctypes.byref(b), 0, 8, 32, 0, ctypes.byref(n)) == L.DSA_OK
     assert n.value == 0
-    assert L._lib.dsa_indexer_workspace_size(ctypes.byref(b), 2, 20, 128, 0, ctypes.byref(n)) == L.DSA_ERR_UNSUPPORTED
+    assert L._lib.dsa_indexer_workspace_size(ctypes.byref(b), 2, 18, 128, 0, ctypes.byref(n)) == L.DSA_ERR_UNSUPPORTED
 
 
 def test_topk_validation(L):
@@ -134,7 +135,8 @@ def test_attention_validation(L):
     assert call(q=0) == L.DSA_ERR_INVALID_ARG
     assert call(out=0x40008) == L.DSA_ERR_INVALID_ARG
     assert call(dqk=512) == L.DSA_ERR_UNSUPPORTED
-    assert call(H=96) == L.DSA_ERR_UNSUPPORTED
+    assert call(H=100) == L.DSA_ERR_UNSUPPORTED    # bf16 heads: multiples of 8 up to 128
+    assert call(H=136) == L.DSA_ERR_UNSUPPORTED
     assert call(dt=2) == L.DSA_ERR_UNSUPPORTED
     assert call(k=3000) == L.DSA_ERR_UNSUPPORTED
     assert call(dv=600) == L.DSA_ERR_INVALID_ARG
@@ -177,7 +179,7 @@ def test_alignment_and_backward_validation(L):
         == L.DSA_ERR_INVALID_ARG                                          # ld_p below whole tiles of max_ctx
     assert t(ctypes.byref(b), 0x10000, 0x20000, 1, 0x50000, 100, 128, 576, 0.1, 0x30000, 0x40000, 100, None) \
         == L.DSA_ERR_INVALID_ARG                                          # ld_p below k rounded up to 32
-    assert t(ctypes.byref(b), 0x10000, 0x20000, 1, None, 0, 96, 576, 0.1, 0x30000, 0x40000, 32, None) \
+    assert t(ctypes.byref(b), 0x10000, 0x20000, 1, None, 0, 100, 576, 0.1, 0x30000, 0x40000, 32, None) \
         == L.DSA_ERR_UNSUPPORTED                                          # H
     # dsa_indexer_kl(batch, scores, ld_s, idx, k, p, ld_p, loss, dI, stream)
     k = L._lib.dsa_indexer_kl

@@ -45,7 +45,7 @@ def _target(dsa, p, lse, idx=None, ld=None):
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("H", [32, 64, 128])
+@pytest.mark.parametrize("H", [24, 32, 64, 128])
 def test_dense_target(dsa, H):
     announce("target dense", H)
     p = gen.make_problem("t", [700, 300, 1200, 65], [700, 3, 1, 65], H_I=16, H=H, k=64, device=DEV, seed=80)
@@ -219,7 +219,7 @@ def _upstream(seed, p, m, integer, idx_h=None):
     return g
 
 
-@pytest.mark.parametrize("H_I", [16, 64])
+@pytest.mark.parametrize("H_I", [16, 20, 64])
 @pytest.mark.parametrize("mode", ["dense", "selected"])
 def test_indexer_backward_integer_exact(dsa, H_I, mode):
     """Integer inputs and upstream: g w act'(x) is exact in bf16 and every sum

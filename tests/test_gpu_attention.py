@@ -47,7 +47,7 @@ def _compare(dsa, p, idx_np, tol):
     return out, lse
 
 
-@pytest.mark.parametrize("H", [32, 64, 128])
+@pytest.mark.parametrize("H", [8, 16, 24, 32, 40, 64, 96, 120, 128])
 def test_bf16_prefill_rows(dsa, H):
     announce("attention bf16 prefill", H)
     p = gen.make_problem("attn", [700], [700], H_I=16, H=H, k=256, device=DEV, seed=H)

@@ -127,3 +127,15 @@ def test_forward_random_inputs(dsa, act):
     out, _, idx = dsa.forward(p, act=act)
     rows = np.array([0, 1023, 1024, 1025, 2222, 3999, 4000, 4001], np.int32)
     _check_rows(p, out, idx, rows, TOL_ATTN_BF16, act=act)
+
+
+def test_forward_head_counts_not_multiples_of_32_or_16(dsa):
+    """16 query heads and 12 indexer heads (a sharded model's share, say):
+    exact selections on integer inputs and attention within the bf16 bar."""
+    announce("forward H=16, H_I=12")
+    p = gen.make_problem("fwd", [1500, 900], [1500, 2], H_I=12, H=16, k=256, integer=True, device=DEV, seed=29)
+    out, _, idx = dsa.forward(p)
+    idx2 = dsa.topk(p, dsa.indexer_scores(p))
+    assert torch.equal(idx, idx2)
+    rows = np.array([0, 255, 256, 900, 1499, 1500, 1501], np.int32)
+    _check_rows(p, out, idx, rows, TOL_ATTN_BF16, need_exact_idx=True)

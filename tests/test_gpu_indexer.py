@@ -29,7 +29,7 @@ def _ragged(H_I, integer, seed, dtype=gen.E4M3):
                             idx_dtype=dtype, integer=integer, device=DEV, seed=seed)
 
 
-@pytest.mark.parametrize("H_I", [16, 32, 48, 64])
+@pytest.mark.parametrize("H_I", [4, 16, 20, 32, 48, 52, 64])
 def test_fp8_integer_inputs_bit_exact(dsa, H_I):
     announce("indexer fp8 integer", H_I)
     p = _ragged(H_I, True, 1)
@@ -41,7 +41,21 @@ def test_fp8_integer_inputs_bit_exact(dsa, H_I):
     assert np.all(np.isnan(got[~mask]))   # nothing written beyond the causal bound
 
 
-@pytest.mark.parametrize("H_I", [16, 64])
+@pytest.mark.parametrize("H_I", [4, 64])
+def test_fp8_integer_inputs_bit_exact_decode_rows(dsa, H_I):
+    """Fewer than 8 query rows per sequence: the streaming kernel, including
+    indexer head counts that are not a multiple of 16."""
+    announce("indexer fp8 integer decode", H_I)
+    p = gen.make_problem("ragged", [300, 77, 1000, 129], [1, 1, 2, 1], H_I=H_I, H=32, k=64, integer=True,
+                         device=DEV, seed=3)
+    got = dsa.indexer_scores(p).cpu().numpy()
+    ld = got.shape[1]
+    ref = _oracle_scores(p, ld=ld)
+    mask = causal_mask(p, None, ld)
+    assert np.array_equal(got[mask], ref[mask].astype(np.float32))
+
+
+@pytest.mark.parametrize("H_I", [16, 20, 64])
 @pytest.mark.parametrize("act", [0, 1])
 def test_fp8_random_inputs(dsa, H_I, act):
     announce("indexer fp8 random", H_I, act)

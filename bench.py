@@ -506,11 +506,18 @@ def _short(name):
     return re.split(r"[<(]", name, maxsplit=1)[0][-40:]
 
 
-def summarize(dirs, command):
+def _is_copy(path):
+    """A counter file from `--copy-calibration`: its name or its folder's starts with copy."""
+    return any(os.path.basename(p).startswith(("copy", "prof_copy")) for p in (path, os.path.dirname(path)))
+
+
+def summarize(dirs, command, traffic_json=True):
     """Print a text summary of rocprofv3 output in `dirs` (kernel stats and, if
-    present, FETCH_SIZE / WRITE_SIZE counter collections, where the files named
-    copy_* come from `--copy-calibration`); for counter runs also write
-    profiles/traffic_<step>.json for the kernels of the path."""
+    present, counter collections, where files or folders named copy* or
+    prof_copy* come from `--copy-calibration`); for FETCH_SIZE / WRITE_SIZE runs
+    also write
+    profiles/traffic_<step>.json for the kernels of the path (unless
+    traffic_json is false: decode runs share kernel names with the prefill)."""
     out = []
     if command:
         out.append(f"command: {command}")
@@ -538,15 +545,47 @@ def summarize(dirs, command):
             for (k, gx, gy), v in shapes.items():
                 out.append(f"  {k:44s} {f'{gx}x{gy}':>14s} {len(v):6d} {sum(v) / len(v):10.2f} {min(v):10.2f}")
     counters = {}
+    other = {}     # (kernel instance, counter) -> [(value, ns)] for counters other than FETCH/WRITE
     for f in files("*counter_collection.csv"):
-        calib = os.path.basename(f).startswith("copy")
+        if _is_copy(f):
+            continue
+        for r in csv.DictReader(open(f)):
+            c = r["Counter_Name"]
+            if c in ("FETCH_SIZE", "WRITE_SIZE") or "dsa::" not in r["Kernel_Name"]:
+                continue
+            m = re.search(r"(\w+)(<[^()]*>)?\(", r["Kernel_Name"].replace("(anonymous namespace)::", ""))
+            key = m.group(1) + (m.group(2) or "") if m else _short(r["Kernel_Name"])
+            other.setdefault((key, c), []).append(
+                (float(r["Counter_Value"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    if other:
+        # GRBM_GUI_ACTIVE is summed over the 8 XCDs: the clock is GUI_ACTIVE / 8 / kernel time, and the
+        # MFMA pipes' busy share is SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GUI_ACTIVE / 8)
+        names = sorted({c for _, c in other})
+        out.append("counters per dispatch (mean), with the clock and the MFMA busy share where both are present:")
+        out.append(f"  {'kernel':40s} {'n':>4s} " + " ".join(f"{c[:24]:>24s}" for c in names)
+                   + f" {'GHz':>6s} {'MFMA busy':>9s}")
+        for k in sorted({k for k, _ in other}):
+            vals = {c: other.get((k, c), []) for c in names}
+            mean = {c: (sum(v for v, _ in x) / len(x) if x else float("nan")) for c, x in vals.items()}
+            n = max(len(x) for x in vals.values())
+            ghz = busy = float("nan")
+            gui = vals.get("GRBM_GUI_ACTIVE")
+            if gui:
+                ns = sum(t for _, t in gui) / len(gui)
+                ghz = mean["GRBM_GUI_ACTIVE"] / 8 / ns if ns > 0 else float("nan")
+                if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and mean["GRBM_GUI_ACTIVE"] > 0:
+                    busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * mean["GRBM_GUI_ACTIVE"] / 8)
+            out.append(f"  {k[:40]:40s} {n:4d} " + " ".join(f"{mean[c]:24.4g}" for c in names)
+                       + f" {ghz:6.2f} {busy:9.3f}")
+    for f in files("*counter_collection.csv"):
+        calib = _is_copy(f)
         for r in csv.DictReader(open(f)):
             name = r["Kernel_Name"]
             if calib and "MulFunctor" not in name:
                 continue
             key = "copy" if calib else _short(name)
             counters.setdefault((key, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
-    if counters:
+    if any(c in ("FETCH_SIZE", "WRITE_SIZE") for _, c in counters):
         fac = {}
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             vals = counters.get(("copy", c), [])
@@ -563,6 +602,8 @@ def summarize(dirs, command):
             ff, wf = fac.get("FETCH_SIZE", 1.0), fac.get("WRITE_SIZE", 1.0)
             per_launch = fk * 1024 * ff + wk * 1024 * wf
             out.append(f"  {sym:28s} FETCH {fk:12.1f} KiB  WRITE {wk:12.1f} KiB  -> {per_launch / 1e9:8.3f} GB per launch")
+            if not traffic_json:
+                continue
             with open(os.path.join(ROOT, "profiles", f"traffic_{step}.json"), "w") as f:
                 json.dump({"kernel": sym, "source_sha": source_sha(step), "bytes_per_launch": per_launch,
                            "fetch_kib_per_launch": fk, "write_kib_per_launch": wk, "fetch_factor": ff,
@@ -594,9 +635,11 @@ def main():
                     help="time dsa_cache_append (prefill and decode) and the indexer with key scales, then exit")
     ap.add_argument("--summarize", metavar="DIR", nargs="+", help="summarise rocprofv3 CSV output in DIR... and exit")
     ap.add_argument("--summary-command", default="", help="the command that produced DIR (recorded)")
+    ap.add_argument("--no-traffic-json", action="store_true",
+                    help="with --summarize: do not write profiles/traffic_<step>.json (for decode runs)")
     args = ap.parse_args()
     if args.summarize:
-        summarize(args.summarize, args.summary_command)
+        summarize(args.summarize, args.summary_command, traffic_json=not args.no_traffic_json)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",

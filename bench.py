@@ -170,12 +170,51 @@ DECODE_WORKLOADS = {
 }
 
 
+def decode_kernel_us(p, reps=5, flush=None):
+    """Microseconds per decode step in each step's kernels, through the
+    separate entry points (the attention's time includes its split merge),
+    mean of `reps` steps; with `flush` (a 1 GiB device buffer) it is written
+    and read before each step, so every step starts with cold L2s and MALL
+    (holding clean lines)."""
+    import torch
+    from sparse_attention_03_amd import dsa, libdsa as L
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    b = L.batch_of(p)
+    scores = torch.empty((p.total_q, dsa.score_ld(p.max_ctx)), dtype=torch.float32, device=p.q.device)
+    ws = torch.empty(max(L.dsa_indexer_workspace_size(b, p.q_idx), 16), dtype=torch.uint8, device=p.q.device)
+    idx = torch.empty((p.total_q, p.k), dtype=torch.int32, device=p.q.device)
+    tws = torch.empty(max(L.dsa_topk_workspace_size(b, p.k), 16), dtype=torch.uint8, device=p.q.device)
+    tot = {"indexer": 0.0, "topk": 0.0, "attention": 0.0}
+    for i in range(reps + 1):
+        if flush is not None:
+            flush.fill_(float(i))
+            flush.sum()
+        e = [ev() for _ in range(4)]
+        e[0].record()
+        L.dsa_indexer_scores(b, p.q_idx, p.k_idx, p.w, scores, ws=ws)
+        e[1].record()
+        L.dsa_topk(b, scores, p.k, idx, ws=tws)
+        e[2].record()
+        dsa.sparse_mla_attn(p, idx)
+        e[3].record()
+        torch.cuda.synchronize()
+        if i == 0:
+            continue  # first pass: allocations
+        for j, name in enumerate(tot):
+            tot[name] += e[j].elapsed_time(e[j + 1]) * 1e3 / reps
+    return tot
+
+
 def decode_us_per_token(name="decode_64x32k", steps=20, warmup=3):
     """One decode step = dsa_forward over the batch (one new query per
-    sequence).  Cold: before each timed step a 1 GiB buffer is written, which
-    evicts the L2s and the 256-MB MALL, so the step reads its caches from HBM;
+    sequence).  Cold: before each timed step a 1 GiB buffer is written and
+    then read, which evicts the L2s and the 256-MB MALL and leaves them
+    holding clean lines of that buffer, so the step reads its caches from HBM;
     the step alone is bracketed by HIP events on the launch stream (median).
-    Warm: `steps` back-to-back steps between two events."""
+    After a write alone the caches hold 256 MB of the buffer's dirty lines,
+    and the step also pays for writing them back: reported as well
+    (cold_after_write_*).  Warm: `steps` back-to-back steps between two
+    events."""
     import torch
     from sparse_attention_03_amd import dsa, inputs as gen
     p = gen.make_config(name, device="cuda")
@@ -185,15 +224,17 @@ def decode_us_per_token(name="decode_64x32k", steps=20, warmup=3):
     for _ in range(warmup):
         f()
     torch.cuda.synchronize()
-    cold = []
-    for i in range(steps):
+    cold, dirty = [], []
+    for i in range(2 * steps):
         flush.fill_(float(i))
+        if i % 2 == 0:
+            flush.sum()
         e0, e1 = ev(), ev()
         e0.record()
         f()
         e1.record()
         torch.cuda.synchronize()
-        cold.append(e0.elapsed_time(e1) * 1e3)
+        (cold if i % 2 == 0 else dirty).append(e0.elapsed_time(e1) * 1e3)
     e0, e1 = ev(), ev()
     e0.record()
     for _ in range(steps):
@@ -202,11 +243,19 @@ def decode_us_per_token(name="decode_64x32k", steps=20, warmup=3):
     torch.cuda.synchronize()
     warm = e0.elapsed_time(e1) * 1e3 / steps
     cold_us = float(np.median(cold))
-    del f, flush
+    dirty_us = float(np.median(dirty))
+    del f
+    # the same kernels through the separate entry points, cold and warm (attention includes the split merge)
+    kc = decode_kernel_us(p, flush=flush)
+    kw = decode_kernel_us(p)
+    del flush
     torch.cuda.empty_cache()
     return {"workload": f"{name}: {DECODE_WORKLOADS[name]}", "tokens_per_step": p.total_q,
-            "us_per_token": cold_us / p.total_q, "us_per_step": cold_us, "timing": "cold (L2 and MALL flushed), median",
-            "warm_us_per_token": warm / p.total_q, "warm_us_per_step": warm}
+            "us_per_token": cold_us / p.total_q, "us_per_step": cold_us,
+            "timing": "cold (L2 and MALL flushed by a 1 GiB write and read), median",
+            "cold_after_write_us_per_token": dirty_us / p.total_q, "cold_after_write_us_per_step": dirty_us,
+            "warm_us_per_token": warm / p.total_q, "warm_us_per_step": warm,
+            "cold_kernel_us": kc, "warm_kernel_us": kw}
 
 
 def prefill_tokens_s(p, steps=5, warmup=1):
@@ -609,6 +658,27 @@ def summarize(dirs, command, traffic_json=True):
                            "fetch_kib_per_launch": fk, "write_kib_per_launch": wk, "fetch_factor": ff,
                            "write_factor": wf, "dispatches": len(fetch), "command": command}, f, indent=1)
         out.append(f"  copy calibration factors: {json.dumps(fac)} (bytes moved / counter bytes, 1 GiB copy)")
+        # the same per template instance and launch size (workgroups), calibrated
+        per = {}
+        for f in files("*counter_collection.csv"):
+            if _is_copy(f):
+                continue
+            for r in csv.DictReader(open(f)):
+                c = r["Counter_Name"]
+                if c not in ("FETCH_SIZE", "WRITE_SIZE") or "dsa::" not in r["Kernel_Name"]:
+                    continue
+                m = re.search(r"(\w+)(<[^()]*>)?\(", r["Kernel_Name"].replace("(anonymous namespace)::", ""))
+                key = (m.group(1) + (m.group(2) or "") if m else _short(r["Kernel_Name"]),
+                       int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])))
+                per.setdefault(key, {}).setdefault(c, []).append(float(r["Counter_Value"]))
+        if per:
+            out.append("  per instance and launch size (MB per dispatch, calibrated):")
+            out.append(f"    {'kernel':44s} {'workgroups':>10s} {'n':>4s} {'read MB':>10s} {'write MB':>10s}")
+            for (k, wg), d in sorted(per.items()):
+                rd = sum(d.get("FETCH_SIZE", [0])) / max(1, len(d.get("FETCH_SIZE", []))) * 1024 * fac.get("FETCH_SIZE", 1.0)
+                wr = sum(d.get("WRITE_SIZE", [0])) / max(1, len(d.get("WRITE_SIZE", []))) * 1024 * fac.get("WRITE_SIZE", 1.0)
+                n = max(len(v) for v in d.values())
+                out.append(f"    {k[:44]:44s} {wg:10d} {n:4d} {rd / 1e6:10.2f} {wr / 1e6:10.2f}")
     print("\n".join(out))
 
 

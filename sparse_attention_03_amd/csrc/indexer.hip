@@ -238,28 +238,40 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
     for (int st = 0; st < NST; ++st) ks[st] = SC ? (int)src[4 * (li + 16 * st)] : 127;
   };
 
-  // LDS ring (SHARED), chunk-major: 16-byte chunk c of slab key row r sits at
-  // byte (64 c + r) * 16.  Copy instruction c of a slab fills chunk column c
-  // (lane i: key row i); a fragment read (lane group g: chunks 2g, 2g + 1 of
-  // rows 16 st + li) puts every lane group on the same bank slot for the same
-  // row, which is what ds_read_b128 needs to run without bank conflicts.
+  // LDS rings: a 64-key slab is eight 1-KB blocks of eight whole key rows.
+  // Block b holds rows 8 b .. 8 b + 7; 16-byte chunk c of its row 8 b + q sits
+  // in slot 8 q + (c ^ q ^ (b & 1)).  Copy instruction b of a slab fills block
+  // b, every eight lanes one whole 128-byte key row (lane l: row 8 b + l / 8,
+  // the chunk its slot l holds), so each instruction touches eight lines.  A
+  // fragment read (lane group g: chunks 2 g, 2 g + 1 of rows 16 st + li) has
+  // the 16 rows of a lane group on 16 different bank slots: within a block the
+  // slots of one chunk are c ^ q, offset by 8 for odd q, and block 2 st + 1
+  // flips the low bit, which moves each row to the other parity's free slots.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint8_t* kglob = a.k_idx + (int64_t)kbase * 128;
+  const int crow = lane >> 3;                       // copy lane: row within its block
+  auto copy_src = [&](int32_t s0, int b) {
+    const int c = (lane & 7) ^ crow ^ (b & 1);
+    return kglob + (int64_t)min(s0 + 8 * b + crow, kend - 1) * 128 + 16 * c;  // rows past kend: a valid key
+  };
   auto copy_slab = [&](int32_t s0, int slot) {
     copy_scales(s0, sarea + slot * 4 * kScaleArea);
     DSA_LDS uint8_t* dst = ring + slot * kSlabBytes;
-    const uint8_t* src = kglob + (int64_t)min(s0 + lane, kend - 1) * 128;
-    __builtin_amdgcn_global_load_lds((const void*)(src + 16 * wave), (DSA_LDS void*)(dst + 1024 * wave), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(src + 16 * (wave + 4)), (DSA_LDS void*)(dst + 1024 * (wave + 4)),
+    __builtin_amdgcn_global_load_lds((const void*)copy_src(s0, wave), (DSA_LDS void*)(dst + 1024 * wave), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)copy_src(s0, wave + 4), (DSA_LDS void*)(dst + 1024 * (wave + 4)),
                                      16, 0, 0);
   };
-  const int ro = 2 * g * 1024 + li * 16;
+  // this lane's chunks 2 g (lo) and 2 g + 1 (hi) of row li of sub-tile 0:
+  // block li / 8, row q = li % 8; the two slots differ in their low bit
+  const int rq = li & 7, rb = li >> 3;
+  const int lo_slot = 8 * rq + ((2 * g) ^ rq ^ rb);
+  const int ro = rb * 1024 + 16 * lo_slot, rh = rb * 1024 + 16 * (lo_slot ^ 1);
   auto read_keys = [&](int slot, i32x8 (&kf)[NST]) {
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
-      const DSA_LDS uint8_t* base = ring + slot * kSlabBytes + st * 256 + ro;
-      const i32x4 lo = *(const DSA_LDS i32x4*)base;
-      const i32x4 hi = *(const DSA_LDS i32x4*)(base + 1024);
+      const DSA_LDS uint8_t* base = ring + slot * kSlabBytes + st * 2048;
+      const i32x4 lo = *(const DSA_LDS i32x4*)(base + ro);
+      const i32x4 hi = *(const DSA_LDS i32x4*)(base + rh);
       kf[st] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   };
@@ -361,7 +373,7 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
     }
   } else if constexpr (KEYS == kKeysPrivate) {
     // ring: this wave's kPrivSlots slabs.  Slab n sits in slot n % kPrivSlots;
-    // its 8 copies (chunk column c: lane i copies key row i) are issued
+    // its 8 copies (copy b: block b, eight whole key rows) are issued
     // kPrivSlots - 1 slabs ahead.  Ahead of slab n's wait, this wave issued the
     // copies of slabs n + 1 .. n + kPrivSlots - 2 and the score stores of the
     // (at most kPrivSlots - 1) slabs before n, all counted by vmcnt.
@@ -369,11 +381,10 @@ __device__ __forceinline__ void fp8_rows(const IdxArgs& a, const int32_t (&rows)
     constexpr int C = SC ? 9 : 8;  // copies per slab
     auto copy_own = [&](int32_t s0, int slot) {
       copy_scales(s0, sarea + slot * kScaleArea);
-      const uint8_t* src = kglob + (int64_t)min(s0 + lane, kend - 1) * 128;  // rows past kend: a valid key
       DSA_LDS uint8_t* dst = ring + slot * kSlabBytes;
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        __builtin_amdgcn_global_load_lds((const void*)(src + 16 * c), (DSA_LDS void*)(dst + 1024 * c), 16, 0, 0);
+      for (int b = 0; b < 8; ++b)
+        __builtin_amdgcn_global_load_lds((const void*)copy_src(s0, b), (DSA_LDS void*)(dst + 1024 * b), 16, 0, 0);
     };
 #pragma unroll
     for (int j = 0; j < P - 1; ++j) copy_own(kstart + 64 * j, j);

@@ -234,16 +234,21 @@ __device__ int stream_select(TopkShared& sh, const Src& src, int32_t count, int 
   bool have_tau = have_tau0;
   uint32_t tau = tau0;
   int parity = 0;
-  typename Src::Fetch f0, f1, f2, f3;
-  src.fetch(0, f0);
-  src.fetch(kChunk, f1);
-  src.fetch(2 * kChunk, f2);
-  for (int32_t c0 = 0; c0 < count; c0 += kChunk) {
-    src.fetch(c0 + 3 * kChunk, f3);
+  // a ring of four chunks' loads, unrolled so that every slot is a fixed set
+  // of registers (a rotation by register copies would make each chunk wait
+  // for the newest loads).  Whole groups of four chunks run without any exit
+  // between them, so the compiler's wait before a chunk's keys covers that
+  // chunk's loads only; the last partial group runs after them.
+  typename Src::Fetch f[4];
+  src.fetch(0, f[0]);
+  src.fetch(kChunk, f[1]);
+  src.fetch(2 * kChunk, f[2]);
+  auto step = [&](int32_t c0, int u) __attribute__((always_inline)) {
+    src.fetch(c0 + 3 * kChunk, f[(u + 3) & 3]);
     uint32_t key[kPer];
     int32_t pos[kPer];
     bool ok[kPer];
-    src.decode(f0, c0 + tid * kPer, key, pos, ok);
+    src.decode(f[u], c0 + tid * kPer, key, pos, ok);
     int c = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) c += ok[j] && (!have_tau || key[j] > tau);
@@ -265,9 +270,16 @@ __device__ int stream_select(TopkShared& sh, const Src& src, int32_t count, int 
     }
     cnt += total;
     adm += total;
-    f0 = f1;
-    f1 = f2;
-    f2 = f3;
+  };
+  int32_t c00 = 0;
+  for (; c00 + 4 * kChunk <= count; c00 += 4 * kChunk) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) step(c00 + u * kChunk, u);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {  // count - c00 < 4 chunks: at most four, the last one partial
+    if (c00 + u * kChunk >= count) break;
+    step(c00 + u * kChunk, u);
   }
   __syncthreads();
   if (admitted) *admitted = adm;

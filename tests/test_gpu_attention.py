@@ -129,6 +129,18 @@ def test_bf16_large_latents_with_key_splits(dsa):
     assert torch.isfinite(out.float()).all()
 
 
+def test_bf16_latents_near_the_range_limit(dsa):
+    """Values up to about 2^65 (the stated range is below 2^66) and a late
+    entry whose probability against the first tile's max is about 2^59, just
+    under the recompute trigger: the row is not redone, and the sums of p * v
+    (about 2^124) stay finite and match the oracle."""
+    announce("attention bf16 latents near the range limit")
+    p = gen.make_problem("attn", [600], [600], H_I=16, H=128, k=256, device=DEV, seed=16)
+    idx = _large_latents(p, random_selection(p, 256, 16), [400, 599], v_log2=63, hot_score=566.0)
+    out, _ = _compare(dsa, p, idx, TOL_ATTN_BF16)
+    assert torch.isfinite(out.float()).all()
+
+
 def test_bf16_only_selected_rows_matter(dsa):
     announce("attention bf16 non-selected rows")
     p = gen.make_problem("attn", [400, 300], [50, 300], H_I=16, H=64, k=128, device=DEV, seed=11)

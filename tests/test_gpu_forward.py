@@ -139,3 +139,42 @@ def test_forward_head_counts_not_multiples_of_32_or_16(dsa):
     assert torch.equal(idx, idx2)
     rows = np.array([0, 255, 256, 900, 1499, 1500, 1501], np.int32)
     _check_rows(p, out, idx, rows, TOL_ATTN_BF16, need_exact_idx=True)
+
+
+@pytest.mark.parametrize("act", [0, 1])
+def test_forward_long_rows_random(dsa, act):
+    """One long sequence (rows of up to 12000 candidates, 24 times k) in the
+    default chunks and in chunks of 3000 rows: the selection equals the
+    separate calls bit for bit."""
+    announce("forward long rows, random", act)
+    p = gen.make_problem("fwd", [12000], [12000], H_I=64, H=32, k=512, device=DEV, seed=40 + act)
+    idx_ref = dsa.topk(p, dsa.indexer_scores(p, act=act))
+    for qb in (0, 3000):
+        _, _, idx = dsa.forward(p, act=act, q_block=qb)
+        assert torch.equal(idx, idx_ref), qb
+
+
+def test_forward_long_rows_ties(dsa):
+    """Integer inputs: long rows whose scores hold many exact ties, so the
+    k-th place is a tie that goes to the lower positions; the selection equals
+    the separate calls and the oracle."""
+    announce("forward long rows, ties")
+    p = gen.make_problem("fwd", [9000, 7000], [9000, 300], H_I=64, H=32, k=384, integer=True, device=DEV, seed=42)
+    out, _, idx = dsa.forward(p)
+    idx_ref = dsa.topk(p, dsa.indexer_scores(p))
+    assert torch.equal(idx, idx_ref)
+    rows = np.array([3071, 3072, 3073, 5000, 8999, 9000, 9150, 9299], np.int32)
+    _check_rows(p, out, idx, rows, TOL_ATTN_BF16, need_exact_idx=True)
+
+
+def test_forward_nan_keys(dsa):
+    """Keys holding the E4M3 NaN code give NaN scores, which rank below every
+    number: rows select exactly what the separate calls select."""
+    announce("forward NaN keys")
+    p = gen.make_problem("fwd", [10000], [10000], H_I=64, H=32, k=512, device=DEV, seed=43)
+    kb = p.k_idx.view(torch.uint8)
+    kb[::37, 5] = 0x7F            # NaN in one element of every 37th key
+    kb[4096:4104, :] = 0x7F       # eight NaN keys in a row
+    idx_ref = dsa.topk(p, dsa.indexer_scores(p))
+    _, _, idx = dsa.forward(p)
+    assert torch.equal(idx, idx_ref)

@@ -120,11 +120,14 @@ const char* dsa_version(void);
  *   value(k_idx[s, :]) * 2^(k_idx_scale[s] - 127).  The MFMA applies the
  *   scale to each key's dot products, so the products stay exact.  FP8 only.
  * Workspace: dsa_indexer_workspace_size bytes (528 per query row for FP8 with
- * ReLU, else 0), 16-B aligned; ws may be NULL when that is 0; a smaller
- * workspace gives DSA_ERR_WORKSPACE.  The size needs no device.
- * Supported: FP8 with d_I = 128, H_I a multiple of 4 up to 64 (heads are
- * taken 16 at a time; past H_I the query and weight are zero) and
- * max_ctx <= 2^24;
+ * ReLU; for FP8 with d_I < 128 also 128 * H_I per query row and 128 per key
+ * row, where q_idx and k_idx are widened to 128-byte rows with zero bytes,
+ * which add nothing to the dot products; else 0), 16-B aligned; ws may be
+ * NULL when that is 0; a smaller workspace gives DSA_ERR_WORKSPACE.  The size
+ * needs no device.
+ * Supported: FP8 with d_I a multiple of 16 up to 128 (one MFMA covers 128),
+ * H_I a multiple of 4 up to 64 (heads are taken 16 at a time; past H_I the
+ * query and weight are zero) and max_ctx <= 2^24;
  * F32 with d_I <= 256, H_I <= 64 and H_I * d_I <= 8192.
  */
 dsa_status dsa_indexer_workspace_size(const dsa_batch* batch, dsa_dtype idx_dtype, int32_t H_I, int32_t d_I,
@@ -309,7 +312,8 @@ dsa_status dsa_indexer_kl(const dsa_batch* batch, const float* scores, int64_t l
  * act' of ReLU is 1 for x > 0 and 0 otherwise (0 at x = 0); of GELU
  * Phi(x) + x phi(x).  dk is by key row of the batch (kbase + s); with scales it
  * is the gradient with respect to the scaled key.
- *   q_idx, k_idx, k_idx_scale, w, H_I, d_I, act as dsa_indexer_scores (FP8 only)
+ *   q_idx, k_idx, k_idx_scale, w, H_I, act as dsa_indexer_scores (FP8 only,
+ *           d_I = 128 only)
  *   g       [total_q, ld_g] fp32, ld_g >= max_ctx (dense) or k
  *   dq_idx  [total_q, H_I, d_I] fp32, dw [total_q, H_I] fp32, dk_idx [total_k, d_I]
  *           fp32: ACCUMULATED with float atomics (zero them first; the order

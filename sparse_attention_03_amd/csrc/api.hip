@@ -73,7 +73,8 @@ dsa_status check_indexer(const dsa_batch* b, const void* q_idx, const void* k_id
   if (act != DSA_ACT_RELU && act != DSA_ACT_GELU) return fail(DSA_ERR_INVALID_ARG, "unknown activation %d", (int)act);
   if (H_I < 1 || d_I < 1) return fail(DSA_ERR_INVALID_ARG, "H_I = %d, d_I = %d", H_I, d_I);
   if (dt == DSA_FP8_E4M3) {
-    if (d_I != 128) return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer needs d_I = 128 (got %d)", d_I);
+    if (d_I % 16 != 0 || d_I > 128)
+      return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer needs d_I a multiple of 16, <= 128 (got %d)", d_I);
     if (H_I % 4 != 0 || H_I > 64) return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer needs H_I a multiple of 4, <= 64 (got %d)", H_I);
     if (b->max_ctx > (1 << 24)) return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer needs max_ctx <= 2^24 (got %d)", b->max_ctx);
   } else if (dt == DSA_F32) {
@@ -83,6 +84,15 @@ dsa_status check_indexer(const dsa_batch* b, const void* q_idx, const void* k_id
     return fail(DSA_ERR_UNSUPPORTED, "indexer dtype must be FP8_E4M3 or F32");
   }
   return DSA_OK;
+}
+
+// FP8 indexer inputs with d_I < 128 are widened to 128-byte rows (zero-filled)
+// in the workspace: q_I rows of `q_rows` query rows, then the k_I rows.
+size_t fp8_pad_q_bytes(int64_t q_rows, int32_t H_I, int32_t d_I, bool fp8) {
+  return fp8 && d_I < 128 ? round_up((size_t)q_rows * (size_t)H_I * 128, 256) : 0;
+}
+size_t fp8_pad_k_bytes(int64_t k_rows, int32_t d_I, bool fp8) {
+  return fp8 && d_I < 128 ? round_up((size_t)k_rows * 128, 256) : 0;
 }
 
 dsa_status check_scores(const dsa_batch* b, const void* scores, int64_t ld) {
@@ -162,7 +172,9 @@ dsa_status dsa_indexer_workspace_size(const dsa_batch* batch, dsa_dtype idx_dtyp
   if (dsa_status s = check_batch(batch)) return s;
   static const uint8_t kDummy[16] __attribute__((aligned(16))) = {};
   if (dsa_status s = check_indexer(batch, kDummy, kDummy, idx_dtype, (const float*)kDummy, H_I, d_I, act)) return s;
-  *bytes = dsa::indexer_workspace_bytes(batch->total_q, idx_dtype == DSA_FP8_E4M3, (int)act);
+  const bool fp8 = idx_dtype == DSA_FP8_E4M3;
+  *bytes = round_up(dsa::indexer_workspace_bytes(batch->total_q, fp8, (int)act), 256) +
+           fp8_pad_q_bytes(batch->total_q, H_I, d_I, fp8) + fp8_pad_k_bytes(batch->total_k, d_I, fp8);
   return DSA_OK;
 }
 
@@ -174,16 +186,30 @@ dsa_status dsa_indexer_scores(const dsa_batch* batch, const void* q_idx, const v
   if (dsa_status s = check_indexer(batch, q_idx, k_idx, idx_dtype, w, H_I, d_I, act)) return s;
   if (k_idx_scale && idx_dtype != DSA_FP8_E4M3) return fail(DSA_ERR_INVALID_ARG, "k_idx_scale needs FP8 keys");
   if (dsa_status s = check_scores(batch, scores, ld_scores)) return s;
-  const size_t need = dsa::indexer_workspace_bytes(batch->total_q, idx_dtype == DSA_FP8_E4M3, (int)act);
+  const bool fp8 = idx_dtype == DSA_FP8_E4M3;
+  const size_t lin = dsa::indexer_workspace_bytes(batch->total_q, fp8, (int)act);
+  const size_t pad_q = fp8_pad_q_bytes(batch->total_q, H_I, d_I, fp8);
+  const size_t need = round_up(lin, 256) + pad_q + fp8_pad_k_bytes(batch->total_k, d_I, fp8);
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
     return fail(DSA_ERR_WORKSPACE, "indexer workspace: need %zu bytes (got %zu)", need, ws_bytes);
   if (batch->total_q == 0) return DSA_OK;
   int cus = 0;
   if (dsa_status s = device_cus(&cus)) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (pad_q) {  // FP8 with d_I < 128: the kernels read 128-byte rows, zero-filled past d_I
+    char* pq = (char*)ws + round_up(lin, 256);
+    char* pk = pq + pad_q;
+    hipError_t e = dsa::launch_pad_rows(q_idx, pq, (int64_t)batch->total_q * H_I, d_I, cus, st);
+    if (e == hipSuccess) e = dsa::launch_pad_rows(k_idx, pk, batch->total_k, d_I, cus, st);
+    if (e != hipSuccess) return hip_fail(e, "indexer input widening");
+    q_idx = pq;
+    k_idx = pk;
+    d_I = 128;
+  }
   dsa::IndexerLaunch L{view(batch, 0, batch->total_q), 0, q_idx, k_idx, w, scores, ld_scores, H_I, d_I, (int32_t)act,
-                       idx_dtype == DSA_FP8_E4M3, cus, need > 0 ? ws : nullptr};
+                       fp8, cus, lin > 0 ? ws : nullptr};
   L.k_scale = k_idx_scale;
-  hipError_t e = dsa::launch_indexer(L, (hipStream_t)stream);
+  hipError_t e = dsa::launch_indexer(L, st);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "indexer launch");
 }
 
@@ -387,6 +413,7 @@ dsa_status dsa_indexer_backward(const dsa_batch* batch, const void* q_idx, const
   if (dsa_status s = check_batch(batch)) return s;
   if (dsa_status s = check_indexer(batch, q_idx, k_idx, idx_dtype, w, H_I, d_I, act)) return s;
   if (idx_dtype != DSA_FP8_E4M3) return fail(DSA_ERR_UNSUPPORTED, "indexer backward needs FP8 inputs");
+  if (d_I != 128) return fail(DSA_ERR_UNSUPPORTED, "indexer backward needs d_I = 128 (got %d)", d_I);
   if (!g || !dq_idx || !dw || !dk_idx) return fail(DSA_ERR_INVALID_ARG, "g / dq_idx / dw / dk_idx is NULL");
   if (!aligned16(g) || !aligned16(dq_idx) || !aligned16(dw) || !aligned16(dk_idx))
     return fail(DSA_ERR_INVALID_ARG, "g and the gradients must be 16-byte aligned");
@@ -451,7 +478,8 @@ namespace {
 struct ForwardPlan {
   int32_t qb;       // rows per chunk
   int64_t ld;       // score row stride
-  size_t off_scores, off_idx, off_topk, off_attn, off_lin, total;
+  size_t off_scores, off_idx, off_topk, off_attn, off_lin, off_pad_q, off_pad_k, total;
+  bool pad;         // FP8 with d_I < 128: q_I (per chunk) and k_I widened to 128-byte rows
   int max_splits;
 };
 
@@ -495,7 +523,13 @@ dsa_status plan_forward(const dsa_forward_params* p, int cus, ForwardPlan* f) {
   off += round_up(a_full > a_last ? a_full : a_last, 256);
   f->max_splits = s_full > s_last ? s_full : s_last;
   f->off_lin = off;
-  off += dsa::indexer_workspace_bytes(f->qb, p->idx_dtype == DSA_FP8_E4M3, (int)p->act);
+  const bool fp8 = p->idx_dtype == DSA_FP8_E4M3;
+  off += round_up(dsa::indexer_workspace_bytes(f->qb, fp8, (int)p->act), 256);
+  f->pad = fp8 && p->d_I < 128;
+  f->off_pad_q = off;
+  off += fp8_pad_q_bytes(f->qb, p->H_I, p->d_I, fp8);
+  f->off_pad_k = off;
+  off += fp8_pad_k_bytes(b->total_k, p->d_I, fp8);
   f->total = off;
   return DSA_OK;
 }
@@ -530,12 +564,30 @@ dsa_status dsa_forward(const dsa_forward_params* p, void* ws, size_t ws_bytes, d
   hipStream_t st = (hipStream_t)stream;
   char* base = (char*)ws;
   float* scores = (float*)(base + f.off_scores);
+  const void* k_idx = p->k_idx;
+  int32_t d_I = p->d_I;
+  if (f.pad) {  // FP8 with d_I < 128: the kernels read 128-byte rows, zero-filled past d_I
+    hipError_t e = dsa::launch_pad_rows(p->k_idx, base + f.off_pad_k, b->total_k, p->d_I, cus, st);
+    if (e != hipSuccess) return hip_fail(e, "forward key widening");
+    k_idx = base + f.off_pad_k;
+    d_I = 128;
+  }
   for (int32_t r0 = 0; r0 < b->total_q; r0 += f.qb) {
     const int32_t r1 = r0 + f.qb < b->total_q ? r0 + f.qb : b->total_q;
     const dsa::BatchView v = view(b, r0, r1);
     int32_t* idx = p->out_idx ? p->out_idx + (int64_t)r0 * p->k : (int32_t*)(base + f.off_idx);
+    const void* q_idx = p->q_idx;
+    if (f.pad) {
+      // the chunk's query rows widened; the indexer addresses q_I by global row,
+      // so it gets the buffer's address less r0 rows
+      const size_t row_bytes = (size_t)p->H_I * 128;
+      hipError_t e = dsa::launch_pad_rows((const char*)p->q_idx + (size_t)r0 * p->H_I * p->d_I, base + f.off_pad_q,
+                                          (int64_t)(r1 - r0) * p->H_I, p->d_I, cus, st);
+      if (e != hipSuccess) return hip_fail(e, "forward query widening");
+      q_idx = (const void*)((uintptr_t)(base + f.off_pad_q) - (uintptr_t)r0 * row_bytes);
+    }
     // rows with pos + 1 <= k select every candidate: their scores are never read
-    dsa::IndexerLaunch IL{v, p->k, p->q_idx, p->k_idx, p->w, scores, f.ld, p->H_I, p->d_I, (int32_t)p->act,
+    dsa::IndexerLaunch IL{v, p->k, q_idx, k_idx, p->w, scores, f.ld, p->H_I, d_I, (int32_t)p->act,
                           p->idx_dtype == DSA_FP8_E4M3, cus, base + f.off_lin};
     IL.k_scale = p->k_idx_scale;
     IL.batch_rows = b->total_q;  // every chunk scores its rows as the whole batch does

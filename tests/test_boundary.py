@@ -84,7 +84,8 @@ def test_indexer_validation(L):
     assert _call_indexer(L, b, q=0) == L.DSA_ERR_INVALID_ARG
     assert b"NULL" in L._lib.dsa_last_error()
     assert _call_indexer(L, b, q=0x10004) == L.DSA_ERR_INVALID_ARG        # misaligned
-    assert _call_indexer(L, b, d_I=64) == L.DSA_ERR_UNSUPPORTED           # fp8 needs d_I 128
+    assert _call_indexer(L, b, d_I=136) == L.DSA_ERR_UNSUPPORTED          # fp8: d_I up to 128 ...
+    assert _call_indexer(L, b, d_I=24) == L.DSA_ERR_UNSUPPORTED           # ... a multiple of 16
     assert _call_indexer(L, b, H_I=18) == L.DSA_ERR_UNSUPPORTED           # fp8: H_I a multiple of 4
     assert _call_indexer(L, b, H_I=68) == L.DSA_ERR_UNSUPPORTED           # ... up to 64
     assert _call_indexer(L, b, dt=1) == L.DSA_ERR_UNSUPPORTED             # bf16 indexer
@@ -195,6 +196,8 @@ def test_alignment_and_backward_validation(L):
         return bw(ctypes.byref(b), 0x10000, 0x20000, dt, None, 0x30000, H_I, 128 if dt == 2 else 32, 0, idx, kk,
                   g, ld, dq, 0x60000, 0x70000, None)
     assert ib(dt=0, H_I=8) == L.DSA_ERR_UNSUPPORTED                  # FP8 only
+    assert bw(ctypes.byref(b), 0x10000, 0x20000, 2, None, 0x30000, 64, 64, 0, None, 0, 0x40000, 64, 0x50000,
+              0x60000, 0x70000, None) == L.DSA_ERR_UNSUPPORTED       # d_I = 128 only
     assert ib(g=0) == L.DSA_ERR_INVALID_ARG
     assert ib(dq=0x50004) == L.DSA_ERR_INVALID_ARG                   # misaligned gradient
     assert ib(ld=4) == L.DSA_ERR_INVALID_ARG                         # ld_g < max_ctx

@@ -178,3 +178,17 @@ def test_forward_nan_keys(dsa):
     idx_ref = dsa.topk(p, dsa.indexer_scores(p))
     _, _, idx = dsa.forward(p)
     assert torch.equal(idx, idx_ref)
+
+
+def test_forward_narrow_indexer_keys(dsa):
+    """d_I = 64 (FP8): the forward widens the keys once and each chunk's
+    queries, and selects what the separate calls select; integer inputs,
+    exact against the oracle."""
+    announce("forward d_I = 64")
+    p = gen.make_problem("fwd", [2500, 1200], [2500, 3], H_I=32, d_I=64, H=32, k=256, integer=True, device=DEV,
+                         seed=44)
+    for qb in (0, 700):
+        out, _, idx = dsa.forward(p, q_block=qb)
+        assert torch.equal(idx, dsa.topk(p, dsa.indexer_scores(p))), qb
+    rows = np.array([0, 255, 256, 1999, 2499, 2500, 2502], np.int32)
+    _check_rows(p, out, idx, rows, TOL_ATTN_BF16, need_exact_idx=True)

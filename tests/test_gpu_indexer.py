@@ -70,6 +70,27 @@ def test_fp8_random_inputs(dsa, H_I, act):
     assert err <= 1e-4   # exact fp8 products, MFMA fp32 accumulation: far inside the bar
 
 
+@pytest.mark.parametrize("d_I", [16, 32, 64, 112])
+@pytest.mark.parametrize("rows", ["prefill", "decode"])
+def test_fp8_narrow_keys(dsa, d_I, rows):
+    """FP8 with d_I < 128: the inputs are widened to 128-byte rows with zero
+    bytes in the workspace, so the scores are those of the d_I-wide dot
+    products: bit-exact on integer inputs (ReLU) for the shared-ring and the
+    streaming kernels, within 1e-4 on random inputs (GELU)."""
+    announce("indexer fp8 narrow keys", d_I, rows)
+    q = [300, 5, 3, 64] if rows == "prefill" else [1, 1, 2, 1]
+    p = gen.make_problem("ragged", [300, 77, 1000, 129], q, H_I=20, d_I=d_I, H=32, k=64, integer=True,
+                         device=DEV, seed=5)
+    got = dsa.indexer_scores(p).cpu().numpy()
+    ld = got.shape[1]
+    mask = causal_mask(p, None, ld)
+    assert np.array_equal(got[mask], _oracle_scores(p, ld=ld)[mask].astype(np.float32))
+    p = gen.make_problem("ragged", [300, 77, 1000, 129], q, H_I=20, d_I=d_I, H=32, k=64, device=DEV, seed=6)
+    got = dsa.indexer_scores(p, act=1).cpu().numpy()
+    err = row_norm_err(got, _oracle_scores(p, act=1, ld=ld), mask)
+    assert err <= 1e-4, err
+
+
 def test_fp8_every_code_decodes_like_the_format(dsa):
     """Keys carry every finite e4m3 code in one column; a one-hot query (+1 in
     the first sequence, -1 in the second) reads each code through the MFMA."""

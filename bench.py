@@ -335,7 +335,7 @@ def crossover(lengths, steps=3, warmup=1):
         f = dsa.Forward(p, with_idx=False, with_lse=False)
         b = L.batch_of(p)
         out = torch.empty((p.total_q, p.H, p.d_v), dtype=p.q.dtype, device="cuda")
-        nws = L.dsa_dense_mla_attn_workspace_size(b, L._dtype_code(p.q), p.H, p.d_v)
+        nws = L.dsa_dense_mla_attn_workspace_size(b, L._dtype_code(p.q), p.H, p.d_qk, p.d_v)
         ws = torch.empty(max(nws, 256), dtype=torch.uint8, device="cuda")
         sparse_ms = timed(f)
         dense_ms = timed(lambda: L.dsa_dense_mla_attn(b, p.q, p.kv, p.d_v, p.scale, out, None, ws=ws))

@@ -183,14 +183,19 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scor
  * the value columns below 2^66 in magnitude; within that the output is
  * finite, also when a late entry's score dominates the first ones (a row
  * whose probabilities, taken against its first tile's maximum, grow past
- * 2^60 is recomputed against its true maximum).  Supported: BF16 with d_qk = 576, d_v = 512,
- * H a multiple of 8 up to 128 (the kernel runs waves of 32 heads; heads
- * past H in the last wave are computed on a copy and not stored);
+ * 2^60 is recomputed against its true maximum).  Supported: BF16 with d_qk and d_v
+ * multiples of 16, d_qk <= 576, d_v <= min(d_qk, 512) (the kernels are 576 /
+ * 512 wide; other widths run on copies in the workspace: q and kv rows widened
+ * with zeros, which add nothing to q . kv, and the output staged at 512
+ * columns, of which the first d_v are kept), H a multiple of 8 up to 128 (the
+ * kernel runs waves of 32 heads; heads past H in the last wave are computed on
+ * a copy and not stored);
  * F32 with d_qk <= 1024, d_v <= d_qk, H <= 128;
- * 1 <= k <= 2048.  The workspace (possibly 0 bytes) holds split partials.
+ * 1 <= k <= 2048.  The workspace (possibly 0 bytes) holds split partials and
+ * the widened copies.
  */
 dsa_status dsa_sparse_mla_attn_workspace_size(const dsa_batch* batch, dsa_dtype dtype, int32_t H,
-                                              int32_t k, int32_t d_v, size_t* bytes /* host */);
+                                              int32_t k, int32_t d_qk, int32_t d_v, size_t* bytes /* host */);
 dsa_status dsa_sparse_mla_attn(const dsa_batch* batch,
                                const void* q, const void* kv, dsa_dtype dtype,
                                const int32_t* idx, int32_t k,
@@ -213,9 +218,12 @@ dsa_status dsa_sparse_mla_attn(const dsa_batch* batch,
  * sequence's context length.
  * F32 additionally needs max_ctx + d_qk <= 16376.  Workspace:
  * dsa_dense_mla_attn_workspace_size bytes (split partials for batches with
- * fewer rows than compute units), 16-B aligned; ws may be NULL when that is 0.
+ * fewer rows than compute units, and the widened copies of BF16 shapes other
+ * than 576 / 512 as in dsa_sparse_mla_attn), 16-B aligned; ws may be NULL when
+ * that is 0.
  */
-dsa_status dsa_dense_mla_attn_workspace_size(const dsa_batch* batch, dsa_dtype dtype, int32_t H, int32_t d_v,
+dsa_status dsa_dense_mla_attn_workspace_size(const dsa_batch* batch, dsa_dtype dtype, int32_t H, int32_t d_qk,
+                                             int32_t d_v,
                                              size_t* bytes /* host */);
 dsa_status dsa_dense_mla_attn(const dsa_batch* batch, const void* q, const void* kv, dsa_dtype dtype,
                               int32_t H, int32_t d_qk, int32_t d_v, float softmax_scale,

@@ -119,7 +119,8 @@ dsa_status check_attention(const void* q, const void* kv, dsa_dtype dt, const in
   if (!(scale == scale)) return fail(DSA_ERR_INVALID_ARG, "softmax_scale is NaN");
   if (H < 1 || d_qk < 1 || d_v < 1 || d_v > d_qk) return fail(DSA_ERR_INVALID_ARG, "bad H / d_qk / d_v");
   if (dt == DSA_BF16) {
-    if (d_qk != 576 || d_v != 512) return fail(DSA_ERR_UNSUPPORTED, "BF16 attention needs d_qk = 576, d_v = 512");
+    if (d_qk % 16 != 0 || d_qk > 576 || d_v % 16 != 0 || d_v > 512)
+      return fail(DSA_ERR_UNSUPPORTED, "BF16 attention needs d_qk and d_v multiples of 16, d_qk <= 576, d_v <= 512");
     if (H % 8 != 0 || H > 128) return fail(DSA_ERR_UNSUPPORTED, "BF16 attention needs H a multiple of 8, <= 128");
   } else if (dt == DSA_F32) {
     if (d_qk > 1024 || H > 128) return fail(DSA_ERR_UNSUPPORTED, "F32 attention needs d_qk <= 1024, H <= 128");
@@ -127,6 +128,31 @@ dsa_status check_attention(const void* q, const void* kv, dsa_dtype dt, const in
     return fail(DSA_ERR_UNSUPPORTED, "attention dtype must be BF16 or F32");
   }
   return DSA_OK;
+}
+
+// BF16 shapes other than d_qk = 576, d_v = 512 run the 576 / 512 kernels on
+// widened copies in the workspace: q and kv rows widened to 576 columns with
+// zeros (which add nothing to q . kv), and the output staged at 512 value
+// columns, of which the first d_v are kept (the value is the first d_v columns
+// of kv either way).
+constexpr int64_t kQkW = 576, kVW = 512;  // the kernels' widths
+struct AttnWiden {
+  bool in;   // d_qk < 576: q and kv widened
+  bool out;  // d_v < 512: output staged
+  int32_t d_qk, d_v;  // the widths the kernels run
+};
+AttnWiden attn_widen(dsa_dtype dt, int32_t d_qk, int32_t d_v) {
+  const bool in = dt == DSA_BF16 && d_qk != kQkW, out = dt == DSA_BF16 && d_v != kVW;
+  return AttnWiden{in, out, in ? (int32_t)kQkW : d_qk, out ? (int32_t)kVW : d_v};
+}
+size_t widen_q_bytes(int64_t rows, int32_t H, const AttnWiden& w) {
+  return w.in ? round_up((size_t)rows * H * kQkW * 2, 256) : 0;
+}
+size_t widen_kv_bytes(int64_t total_k, const AttnWiden& w) {
+  return w.in ? round_up((size_t)total_k * kQkW * 2, 256) : 0;
+}
+size_t stage_out_bytes(int64_t rows, int32_t H, const AttnWiden& w) {
+  return w.out ? round_up((size_t)rows * H * kVW * 2, 256) : 0;
 }
 
 size_t attention_ws_bytes(int32_t rows, int splits, int32_t H, int32_t d_v) {
@@ -199,8 +225,8 @@ dsa_status dsa_indexer_scores(const dsa_batch* batch, const void* q_idx, const v
   if (pad_q) {  // FP8 with d_I < 128: the kernels read 128-byte rows, zero-filled past d_I
     char* pq = (char*)ws + round_up(lin, 256);
     char* pk = pq + pad_q;
-    hipError_t e = dsa::launch_pad_rows(q_idx, pq, (int64_t)batch->total_q * H_I, d_I, cus, st);
-    if (e == hipSuccess) e = dsa::launch_pad_rows(k_idx, pk, batch->total_k, d_I, cus, st);
+    hipError_t e = dsa::launch_copy_rows(q_idx, d_I, pq, 128, (int64_t)batch->total_q * H_I, d_I, cus, st);
+    if (e == hipSuccess) e = dsa::launch_copy_rows(k_idx, d_I, pk, 128, batch->total_k, d_I, cus, st);
     if (e != hipSuccess) return hip_fail(e, "indexer input widening");
     q_idx = pq;
     k_idx = pk;
@@ -247,16 +273,56 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld_scor
 }
 
 dsa_status dsa_sparse_mla_attn_workspace_size(const dsa_batch* batch, dsa_dtype dtype, int32_t H, int32_t k,
-                                              int32_t d_v, size_t* bytes) {
+                                              int32_t d_qk, int32_t d_v, size_t* bytes) {
   g_err[0] = 0;
   if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is NULL");
   if (dsa_status s = check_batch(batch)) return s;
   if (dsa_status s = check_k(k)) return s;
-  if (H < 1 || d_v < 1) return fail(DSA_ERR_INVALID_ARG, "bad H / d_v");
+  if (H < 1 || d_qk < 1 || d_v < 1) return fail(DSA_ERR_INVALID_ARG, "bad H / d_qk / d_v");
   int cus = 0;
   if (dsa_status s = device_cus(&cus)) return s;
+  const AttnWiden w = attn_widen(dtype, d_qk, d_v);
   const int splits = dsa::attention_splits(batch->total_q, k, dtype == DSA_BF16, cus);
-  *bytes = attention_ws_bytes(batch->total_q, splits, H, d_v);
+  *bytes = round_up(attention_ws_bytes(batch->total_q, splits, H, w.d_v), 256) +
+           widen_q_bytes(batch->total_q, H, w) + widen_kv_bytes(batch->total_k, w) +
+           stage_out_bytes(batch->total_q, H, w);
+  return DSA_OK;
+}
+
+// One attention launch over the whole batch (sparse or dense), with the
+// widening of other BF16 shapes around it.
+dsa_status run_attention(const dsa_batch* batch, dsa::AttnLaunch L, int32_t d_qk, int32_t d_v, dsa_dtype dtype,
+                         void* ws, size_t ws_bytes, int cus, hipStream_t st, const char* what) {
+  const int32_t rows = batch->total_q, H = L.H;
+  const AttnWiden w = attn_widen(dtype, d_qk, d_v);
+  const size_t part = round_up(attention_ws_bytes(rows, L.splits, H, w.d_v), 256);
+  const size_t wq = widen_q_bytes(rows, H, w), wkv = widen_kv_bytes(batch->total_k, w);
+  const size_t need = part + wq + wkv + stage_out_bytes(rows, H, w);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
+    return fail(DSA_ERR_WORKSPACE, "%s workspace: need %zu bytes (got %zu)", what, need, ws_bytes);
+  char* base = (char*)ws;
+  if (L.splits > 1) {
+    L.ws_o = (float*)base;
+    L.ws_lse = (float*)(base + round_up((size_t)rows * L.splits * H * w.d_v * sizeof(float), 256));
+  }
+  if (w.in) {
+    hipError_t e = dsa::launch_copy_rows(L.q, 2 * d_qk, base + part, 2 * kQkW, (int64_t)rows * H, 2 * d_qk, cus, st);
+    if (e == hipSuccess)
+      e = dsa::launch_copy_rows(L.kv, 2 * d_qk, base + part + wq, 2 * kQkW, batch->total_k, 2 * d_qk, cus, st);
+    if (e != hipSuccess) return hip_fail(e, "attention input widening");
+    L.q = base + part;
+    L.kv = base + part + wq;
+  }
+  void* out = L.out;
+  if (w.out) L.out = base + part + wq + wkv;
+  L.d_qk = w.d_qk;
+  L.d_v = w.d_v;
+  hipError_t e = dsa::launch_attention(L, st);
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (w.out) {
+    e = dsa::launch_copy_rows(L.out, 2 * kVW, out, 2 * d_v, (int64_t)rows * H, 2 * d_v, cus, st);
+    if (e != hipSuccess) return hip_fail(e, "attention output narrowing");
+  }
   return DSA_OK;
 }
 
@@ -271,29 +337,24 @@ dsa_status dsa_sparse_mla_attn(const dsa_batch* batch, const void* q, const void
   int cus = 0;
   if (dsa_status s = device_cus(&cus)) return s;
   const int splits = dsa::attention_splits(batch->total_q, k, dtype == DSA_BF16, cus);
-  const size_t need = attention_ws_bytes(batch->total_q, splits, H, d_v);
-  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
-    return fail(DSA_ERR_WORKSPACE, "attention workspace: need %zu bytes (got %zu)", need, ws_bytes);
   dsa::AttnLaunch L{view(batch, 0, batch->total_q), q, kv, idx, k, H, d_qk, d_v, softmax_scale, out, lse,
                     dtype == DSA_BF16, splits, nullptr, nullptr};
-  if (splits > 1) {
-    L.ws_o = (float*)ws;
-    L.ws_lse = (float*)((char*)ws + round_up((size_t)batch->total_q * splits * H * d_v * sizeof(float), 256));
-  }
-  hipError_t e = dsa::launch_attention(L, (hipStream_t)stream);
-  return e == hipSuccess ? DSA_OK : hip_fail(e, "attention launch");
+  return run_attention(batch, L, d_qk, d_v, dtype, ws, ws_bytes, cus, (hipStream_t)stream, "attention");
 }
 
-dsa_status dsa_dense_mla_attn_workspace_size(const dsa_batch* batch, dsa_dtype dtype, int32_t H, int32_t d_v,
-                                             size_t* bytes) {
+dsa_status dsa_dense_mla_attn_workspace_size(const dsa_batch* batch, dsa_dtype dtype, int32_t H, int32_t d_qk,
+                                             int32_t d_v, size_t* bytes) {
   g_err[0] = 0;
   if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is NULL");
   if (dsa_status s = check_batch(batch)) return s;
-  if (H < 1 || d_v < 1) return fail(DSA_ERR_INVALID_ARG, "bad H / d_v");
+  if (H < 1 || d_qk < 1 || d_v < 1) return fail(DSA_ERR_INVALID_ARG, "bad H / d_qk / d_v");
   int cus = 0;
   if (dsa_status s = device_cus(&cus)) return s;
+  const AttnWiden w = attn_widen(dtype, d_qk, d_v);
   const int splits = dsa::attention_splits(batch->total_q, batch->max_ctx, dtype == DSA_BF16, cus);
-  *bytes = attention_ws_bytes(batch->total_q, splits, H, d_v);
+  *bytes = round_up(attention_ws_bytes(batch->total_q, splits, H, w.d_v), 256) +
+           widen_q_bytes(batch->total_q, H, w) + widen_kv_bytes(batch->total_k, w) +
+           stage_out_bytes(batch->total_q, H, w);
   return DSA_OK;
 }
 
@@ -311,18 +372,10 @@ dsa_status dsa_dense_mla_attn(const dsa_batch* batch, const void* q, const void*
   int cus = 0;
   if (dsa_status s = device_cus(&cus)) return s;
   const int splits = dsa::attention_splits(batch->total_q, batch->max_ctx, dtype == DSA_BF16, cus);
-  const size_t need = attention_ws_bytes(batch->total_q, splits, H, d_v);
-  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
-    return fail(DSA_ERR_WORKSPACE, "attention workspace: need %zu bytes (got %zu)", need, ws_bytes);
   dsa::AttnLaunch L{view(batch, 0, batch->total_q), q, kv, nullptr, batch->max_ctx, H, d_qk, d_v, softmax_scale,
                     out, lse, dtype == DSA_BF16, splits, nullptr, nullptr};
   L.dense = true;
-  if (splits > 1) {
-    L.ws_o = (float*)ws;
-    L.ws_lse = (float*)((char*)ws + round_up((size_t)batch->total_q * splits * H * d_v * sizeof(float), 256));
-  }
-  hipError_t e = dsa::launch_attention(L, (hipStream_t)stream);
-  return e == hipSuccess ? DSA_OK : hip_fail(e, "dense attention launch");
+  return run_attention(batch, L, d_qk, d_v, dtype, ws, ws_bytes, cus, (hipStream_t)stream, "dense attention");
 }
 
 dsa_status dsa_sparse_mla_backward_workspace_size(const dsa_batch* batch, int32_t H, int32_t k, size_t* bytes) {
@@ -343,6 +396,7 @@ dsa_status dsa_sparse_mla_backward(const dsa_batch* batch, const void* q, const 
   if (dsa_status s = check_batch(batch)) return s;
   if (dsa_status s = check_attention(q, kv, dtype, idx, k, H, d_qk, d_v, softmax_scale, dq, lse)) return s;
   if (dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "attention backward needs BF16");
+  if (d_qk != 576 || d_v != 512) return fail(DSA_ERR_UNSUPPORTED, "attention backward needs d_qk = 576, d_v = 512");
   if (H != 32 && H != 64 && H != 128) return fail(DSA_ERR_UNSUPPORTED, "attention backward needs H in {32, 64, 128}");
   if (!lse || !dout || !dq || !dkv) return fail(DSA_ERR_INVALID_ARG, "lse / dout / dq / dkv is NULL");
   if (!aligned16(dout) || !aligned16(dkv)) return fail(DSA_ERR_INVALID_ARG, "dout and dkv must be 16-byte aligned");
@@ -370,6 +424,7 @@ dsa_status dsa_attn_target(const dsa_batch* batch, const void* q, const void* kv
                                      p, lse))
     return s;
   if (!lse || !p) return fail(DSA_ERR_INVALID_ARG, "lse / p is NULL");
+  if (dtype == DSA_BF16 && d_qk != 576) return fail(DSA_ERR_UNSUPPORTED, "BF16 target needs d_qk = 576");
   const int64_t m = dense ? batch->max_ctx : k;
   if (ld_p < (m + 31) / 32 * 32 || ld_p % 4 != 0)
     return fail(DSA_ERR_INVALID_ARG, "ld_p = %lld must be >= %lld (whole 32-entry tiles) and a multiple of 4",
@@ -478,8 +533,9 @@ namespace {
 struct ForwardPlan {
   int32_t qb;       // rows per chunk
   int64_t ld;       // score row stride
-  size_t off_scores, off_idx, off_topk, off_attn, off_lin, off_pad_q, off_pad_k, total;
+  size_t off_scores, off_idx, off_topk, off_attn, off_lin, off_pad_q, off_pad_k, off_wq, off_wkv, off_stage, total;
   bool pad;         // FP8 with d_I < 128: q_I (per chunk) and k_I widened to 128-byte rows
+  AttnWiden w;      // BF16 attention shapes other than 576 / 512: q (per chunk), kv, output staging
   int max_splits;
 };
 
@@ -518,8 +574,9 @@ dsa_status plan_forward(const dsa_forward_params* p, int cus, ForwardPlan* f) {
   const int32_t last = b->total_q % f->qb;
   const int s_full = dsa::attention_splits(f->qb, p->k, p->dtype == DSA_BF16, cus);
   const int s_last = last ? dsa::attention_splits(last, p->k, p->dtype == DSA_BF16, cus) : 1;
-  const size_t a_full = attention_ws_bytes(f->qb, s_full, p->H, p->d_v);
-  const size_t a_last = last ? attention_ws_bytes(last, s_last, p->H, p->d_v) : 0;
+  f->w = attn_widen(p->dtype, p->d_qk, p->d_v);
+  const size_t a_full = attention_ws_bytes(f->qb, s_full, p->H, f->w.d_v);
+  const size_t a_last = last ? attention_ws_bytes(last, s_last, p->H, f->w.d_v) : 0;
   off += round_up(a_full > a_last ? a_full : a_last, 256);
   f->max_splits = s_full > s_last ? s_full : s_last;
   f->off_lin = off;
@@ -530,6 +587,12 @@ dsa_status plan_forward(const dsa_forward_params* p, int cus, ForwardPlan* f) {
   off += fp8_pad_q_bytes(f->qb, p->H_I, p->d_I, fp8);
   f->off_pad_k = off;
   off += fp8_pad_k_bytes(b->total_k, p->d_I, fp8);
+  f->off_wq = off;
+  off += widen_q_bytes(f->qb, p->H, f->w);
+  f->off_wkv = off;
+  off += widen_kv_bytes(b->total_k, f->w);
+  f->off_stage = off;
+  off += stage_out_bytes(f->qb, p->H, f->w);
   f->total = off;
   return DSA_OK;
 }
@@ -566,8 +629,14 @@ dsa_status dsa_forward(const dsa_forward_params* p, void* ws, size_t ws_bytes, d
   float* scores = (float*)(base + f.off_scores);
   const void* k_idx = p->k_idx;
   int32_t d_I = p->d_I;
+  const void* kv = p->kv;
+  if (f.w.in) {  // BF16 with d_qk < 576: latent rows widened to 576 columns, zero-filled
+    hipError_t e = dsa::launch_copy_rows(p->kv, 2 * p->d_qk, base + f.off_wkv, 2 * kQkW, b->total_k, 2 * p->d_qk, cus, st);
+    if (e != hipSuccess) return hip_fail(e, "forward latent widening");
+    kv = base + f.off_wkv;
+  }
   if (f.pad) {  // FP8 with d_I < 128: the kernels read 128-byte rows, zero-filled past d_I
-    hipError_t e = dsa::launch_pad_rows(p->k_idx, base + f.off_pad_k, b->total_k, p->d_I, cus, st);
+    hipError_t e = dsa::launch_copy_rows(p->k_idx, p->d_I, base + f.off_pad_k, 128, b->total_k, p->d_I, cus, st);
     if (e != hipSuccess) return hip_fail(e, "forward key widening");
     k_idx = base + f.off_pad_k;
     d_I = 128;
@@ -581,8 +650,8 @@ dsa_status dsa_forward(const dsa_forward_params* p, void* ws, size_t ws_bytes, d
       // the chunk's query rows widened; the indexer addresses q_I by global row,
       // so it gets the buffer's address less r0 rows
       const size_t row_bytes = (size_t)p->H_I * 128;
-      hipError_t e = dsa::launch_pad_rows((const char*)p->q_idx + (size_t)r0 * p->H_I * p->d_I, base + f.off_pad_q,
-                                          (int64_t)(r1 - r0) * p->H_I, p->d_I, cus, st);
+      hipError_t e = dsa::launch_copy_rows((const char*)p->q_idx + (size_t)r0 * p->H_I * p->d_I, p->d_I,
+                                           base + f.off_pad_q, 128, (int64_t)(r1 - r0) * p->H_I, p->d_I, cus, st);
       if (e != hipSuccess) return hip_fail(e, "forward query widening");
       q_idx = (const void*)((uintptr_t)(base + f.off_pad_q) - (uintptr_t)r0 * row_bytes);
     }
@@ -597,16 +666,33 @@ dsa_status dsa_forward(const dsa_forward_params* p, void* ws, size_t ws_bytes, d
     e = dsa::launch_topk(TL, st);
     if (e != hipSuccess) return hip_fail(e, "forward topk launch");
     const int splits = dsa::attention_splits(r1 - r0, p->k, p->dtype == DSA_BF16, cus);
-    dsa::AttnLaunch AL{v, p->q, p->kv, idx, p->k, p->H, p->d_qk, p->d_v, p->softmax_scale, p->out, p->lse,
+    // q and out are addressed by global row: widened / staged copies of this
+    // chunk's rows are passed as their buffer's address less r0 rows
+    const void* q = p->q;
+    void* out = p->out;
+    if (f.w.in) {
+      const size_t row = (size_t)p->H * kQkW * 2;
+      e = dsa::launch_copy_rows((const char*)p->q + (size_t)r0 * p->H * p->d_qk * 2, 2 * p->d_qk, base + f.off_wq,
+                                2 * kQkW, (int64_t)(r1 - r0) * p->H, 2 * p->d_qk, cus, st);
+      if (e != hipSuccess) return hip_fail(e, "forward query widening");
+      q = (const void*)((uintptr_t)(base + f.off_wq) - (uintptr_t)r0 * row);
+    }
+    if (f.w.out) out = (void*)((uintptr_t)(base + f.off_stage) - (uintptr_t)r0 * ((size_t)p->H * kVW * 2));
+    dsa::AttnLaunch AL{v, q, kv, idx, p->k, p->H, f.w.d_qk, f.w.d_v, p->softmax_scale, out, p->lse,
                        p->dtype == DSA_BF16, splits, nullptr, nullptr};
     AL.dense_short = true;  // rows with pos + 1 <= k: the masked mode, same result as their idx = 0 .. pos
     if (splits > 1) {
       AL.ws_o = (float*)(base + f.off_attn);
       AL.ws_lse = (float*)(base + f.off_attn +
-                           round_up((size_t)(r1 - r0) * splits * p->H * p->d_v * sizeof(float), 256));
+                           round_up((size_t)(r1 - r0) * splits * p->H * f.w.d_v * sizeof(float), 256));
     }
     e = dsa::launch_attention(AL, st);
     if (e != hipSuccess) return hip_fail(e, "forward attention launch");
+    if (f.w.out) {
+      e = dsa::launch_copy_rows(base + f.off_stage, 2 * kVW, (char*)p->out + (size_t)r0 * p->H * p->d_v * 2,
+                                2 * p->d_v, (int64_t)(r1 - r0) * p->H, 2 * p->d_v, cus, st);
+      if (e != hipSuccess) return hip_fail(e, "forward output narrowing");
+    }
   }
   return DSA_OK;
 }

@@ -14,6 +14,8 @@
 // Both parts stream HBM once (no LDS, one or two 16-byte loads per lane), so
 // they share one launch: workgroups [0, key_blocks) quantise keys, the rest
 // copy latent rows.
+#include <algorithm>
+
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
@@ -153,6 +155,34 @@ hipError_t launch_lpr(const AppendArgs& a, bool bf16, bool scaled, unsigned grid
 }
 
 }  // namespace
+
+namespace {
+// dst row r (out_stride bytes) = the first copy_bytes of src row r (in_stride
+// bytes), zero-filled up to out_stride; every size a multiple of 16.  One
+// thread per 16-byte chunk of the output, grid-stride.
+__global__ __launch_bounds__(256) void copy_rows_kernel(const uint8_t* __restrict__ src, int64_t in_stride,
+                                                       uint8_t* __restrict__ dst, int64_t out_stride, int64_t rows,
+                                                       int64_t copy_bytes) {
+  const int64_t per_row = out_stride / 16, total = rows * per_row;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / per_row, c = e - r * per_row;
+    i32x4 v = i32x4{0, 0, 0, 0};
+    if (16 * c < copy_bytes) v = *(const i32x4*)(src + r * in_stride + 16 * c);
+    *(i32x4*)(dst + r * out_stride + 16 * c) = v;
+  }
+}
+}  // namespace
+
+hipError_t launch_copy_rows(const void* src, int64_t in_stride, void* dst, int64_t out_stride, int64_t rows,
+                            int64_t copy_bytes, int num_cus, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if ((in_stride | out_stride | copy_bytes) % 16 != 0 || copy_bytes > in_stride) return hipErrorInvalidValue;
+  const int64_t total = rows * (out_stride / 16);
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8LL * num_cus);
+  hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint8_t*)src, in_stride,
+                     (uint8_t*)dst, out_stride, rows, copy_bytes);
+  return hipGetLastError();
+}
 
 hipError_t launch_cache_append(const AppendLaunch& L, hipStream_t s) {
   if (L.n <= 0) return hipSuccess;

@@ -151,9 +151,12 @@ hipError_t launch_cache_append(const AppendLaunch& a, hipStream_t s);
 // Workspace of the indexer for `rows` query rows (the FP8 ReLU path keeps the
 // linear-term fragments of every row there).
 size_t indexer_workspace_bytes(int rows, bool fp8, int act);
-// rows of in_bytes (< 128, a multiple of 16) bytes copied into rows of 128
-// bytes, zero-filled past in_bytes (FP8 indexer inputs with d_I < 128)
-hipError_t launch_pad_rows(const void* src, void* dst, int64_t rows, int in_bytes, int num_cus, hipStream_t s);
+// Row reshaping (sizes in bytes, multiples of 16): dst row r of out_stride
+// bytes gets the first copy_bytes (<= in_stride) of src row r, zero-filled up
+// to out_stride.  Widens narrow FP8 indexer rows and attention rows, and keeps
+// the first d_v columns of a staged attention output.
+hipError_t launch_copy_rows(const void* src, int64_t in_stride, void* dst, int64_t out_stride, int64_t rows,
+                            int64_t copy_bytes, int num_cus, hipStream_t s);
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
 

@@ -29,8 +29,6 @@
 // one contiguous 256-byte store per row.  Key loads and score stores are
 // buffer instructions whose range check replaces per-lane clamps: keys past
 // the chunk read as zero, scores past the causal bound are dropped.
-#include <algorithm>
-
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
@@ -571,29 +569,7 @@ hipError_t launch_stream(const IdxArgs& a, int act, dim3 grid, hipStream_t s) {
   return act == 0 ? launch_stream_act<NHT, 0, false>(a, grid, s) : launch_stream_act<NHT, 1, false>(a, grid, s);
 }
 
-// FP8 rows of fewer than 128 bytes (d_I < 128) widened to 128 with zero bytes,
-// so the 128-wide kernels run unchanged (a zero byte is E4M3 +0 and its
-// products add nothing).  One thread per 16-byte chunk of the output.
-__global__ __launch_bounds__(256) void pad_rows_kernel(const i32x4* __restrict__ src, i32x4* __restrict__ dst,
-                                                      int64_t rows, int in_chunks) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < rows * 8; e += stride) {
-    const int64_t r = e >> 3;
-    const int c = (int)(e & 7);
-    dst[e] = c < in_chunks ? src[r * in_chunks + c] : i32x4{0, 0, 0, 0};
-  }
-}
-
 }  // namespace
-
-hipError_t launch_pad_rows(const void* src, void* dst, int64_t rows, int in_bytes, int num_cus, hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  const int64_t chunks = rows * 8;
-  const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 8LL * num_cus);
-  hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const i32x4*)src, (i32x4*)dst, rows,
-                     in_bytes / 16);
-  return hipGetLastError();
-}
 
 size_t indexer_workspace_bytes(int rows, bool fp8, int act) {
   if (!fp8 || act != 0 || rows <= 0) return 0;

@@ -41,7 +41,7 @@ def sparse_mla_attn(p, idx, with_lse=True):
     dev = p.q.device
     out = torch.empty((p.total_q, p.H, p.d_v), dtype=p.q.dtype, device=dev)
     lse = torch.empty((p.total_q, p.H), dtype=torch.float32, device=dev) if with_lse else None
-    n = L.dsa_sparse_mla_attn_workspace_size(b, L._dtype_code(p.q), p.H, idx.shape[1], p.d_v)
+    n = L.dsa_sparse_mla_attn_workspace_size(b, L._dtype_code(p.q), p.H, idx.shape[1], p.d_qk, p.d_v)
     L.dsa_sparse_mla_attn(b, p.q, p.kv, idx, p.d_v, p.scale, out, lse, ws=_ws(n, dev) if n else None)
     return out, lse
 
@@ -52,7 +52,7 @@ def dense_mla_attn(p, with_lse=True):
     dev = p.q.device
     out = torch.empty((p.total_q, p.H, p.d_v), dtype=p.q.dtype, device=dev)
     lse = torch.empty((p.total_q, p.H), dtype=torch.float32, device=dev) if with_lse else None
-    n = L.dsa_dense_mla_attn_workspace_size(b, L._dtype_code(p.q), p.H, p.d_v)
+    n = L.dsa_dense_mla_attn_workspace_size(b, L._dtype_code(p.q), p.H, p.d_qk, p.d_v)
     L.dsa_dense_mla_attn(b, p.q, p.kv, p.d_v, p.scale, out, lse, ws=_ws(n, dev) if n else None)
     return out, lse
 

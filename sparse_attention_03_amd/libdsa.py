@@ -54,10 +54,11 @@ _SIGS = {
                            ctypes.c_int),
     "dsa_topk_workspace_size": ([_BP, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
     "dsa_topk": ([_BP, _p, _i64, _i32, _p, _p, _sz, _p], ctypes.c_int),
-    "dsa_sparse_mla_attn_workspace_size": ([_BP, ctypes.c_int, _i32, _i32, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
+    "dsa_sparse_mla_attn_workspace_size": ([_BP, ctypes.c_int, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)],
+                                           ctypes.c_int),
     "dsa_sparse_mla_attn": ([_BP, _p, _p, ctypes.c_int, _p, _i32, _i32, _i32, _i32, _f32, _p, _p, _p, _sz, _p],
                             ctypes.c_int),
-    "dsa_dense_mla_attn_workspace_size": ([_BP, ctypes.c_int, _i32, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
+    "dsa_dense_mla_attn_workspace_size": ([_BP, ctypes.c_int, _i32, _i32, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
     "dsa_dense_mla_attn": ([_BP, _p, _p, ctypes.c_int, _i32, _i32, _i32, _f32, _p, _p, _p, _sz, _p], ctypes.c_int),
     "dsa_sparse_mla_backward_workspace_size": ([_BP, _i32, _i32, ctypes.POINTER(_sz)], ctypes.c_int),
     "dsa_sparse_mla_backward": ([_BP, _p, _p, ctypes.c_int, _p, _i32, _i32, _i32, _i32, _f32, _p, _p, _p, _p, _p,
@@ -149,9 +150,9 @@ def dsa_topk(batch: DsaBatch, scores, k: int, idx, ws=None, stream=None):
                          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)), "dsa_topk")
 
 
-def dsa_sparse_mla_attn_workspace_size(batch: DsaBatch, dtype: int, H: int, k: int, d_v: int) -> int:
+def dsa_sparse_mla_attn_workspace_size(batch: DsaBatch, dtype: int, H: int, k: int, d_qk: int, d_v: int) -> int:
     n = _sz(0)
-    _check(_lib.dsa_sparse_mla_attn_workspace_size(ctypes.byref(batch), dtype, H, k, d_v, ctypes.byref(n)),
+    _check(_lib.dsa_sparse_mla_attn_workspace_size(ctypes.byref(batch), dtype, H, k, d_qk, d_v, ctypes.byref(n)),
            "dsa_sparse_mla_attn_workspace_size")
     return n.value
 
@@ -164,9 +165,9 @@ def dsa_sparse_mla_attn(batch: DsaBatch, q, kv, idx, d_v: int, softmax_scale: fl
            "dsa_sparse_mla_attn")
 
 
-def dsa_dense_mla_attn_workspace_size(batch: DsaBatch, dtype: int, H: int, d_v: int) -> int:
+def dsa_dense_mla_attn_workspace_size(batch: DsaBatch, dtype: int, H: int, d_qk: int, d_v: int) -> int:
     n = _sz(0)
-    _check(_lib.dsa_dense_mla_attn_workspace_size(ctypes.byref(batch), dtype, H, d_v, ctypes.byref(n)),
+    _check(_lib.dsa_dense_mla_attn_workspace_size(ctypes.byref(batch), dtype, H, d_qk, d_v, ctypes.byref(n)),
            "dsa_dense_mla_attn_workspace_size")
     return n.value
 

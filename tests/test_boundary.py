@@ -135,7 +135,11 @@ def test_attention_validation(L):
 
     assert call(q=0) == L.DSA_ERR_INVALID_ARG
     assert call(out=0x40008) == L.DSA_ERR_INVALID_ARG
-    assert call(dqk=512) == L.DSA_ERR_UNSUPPORTED
+    assert call(dqk=600) == L.DSA_ERR_UNSUPPORTED    # bf16: d_qk up to 576 ...
+    assert call(dqk=568, dv=64) == L.DSA_ERR_UNSUPPORTED  # ... a multiple of 16
+    assert call(dqk=576, dv=520) == L.DSA_ERR_UNSUPPORTED  # d_v up to 512
+    # narrower bf16 shapes pass validation (here they stop at the missing device)
+    assert call(dqk=512, dv=128) not in (L.DSA_ERR_UNSUPPORTED, L.DSA_ERR_INVALID_ARG)
     assert call(H=100) == L.DSA_ERR_UNSUPPORTED    # bf16 heads: multiples of 8 up to 128
     assert call(H=136) == L.DSA_ERR_UNSUPPORTED
     assert call(dt=2) == L.DSA_ERR_UNSUPPORTED
@@ -182,6 +186,8 @@ def test_alignment_and_backward_validation(L):
         == L.DSA_ERR_INVALID_ARG                                          # ld_p below k rounded up to 32
     assert t(ctypes.byref(b), 0x10000, 0x20000, 1, None, 0, 100, 576, 0.1, 0x30000, 0x40000, 32, None) \
         == L.DSA_ERR_UNSUPPORTED                                          # H
+    assert t(ctypes.byref(b), 0x10000, 0x20000, 1, None, 0, 128, 512, 0.1, 0x30000, 0x40000, 32, None) \
+        == L.DSA_ERR_UNSUPPORTED                                          # bf16 target: d_qk = 576 only
     # dsa_indexer_kl(batch, scores, ld_s, idx, k, p, ld_p, loss, dI, stream)
     k = L._lib.dsa_indexer_kl
     assert k(ctypes.byref(b), 0x10000, 64, None, 0, 0, 64, None, None, None) == L.DSA_ERR_INVALID_ARG   # p NULL
@@ -215,6 +221,8 @@ def test_alignment_and_backward_validation(L):
     assert mb(ws=None) == L.DSA_ERR_WORKSPACE
     assert mb(wsb=16) == L.DSA_ERR_WORKSPACE
     assert mb(H=96) == L.DSA_ERR_UNSUPPORTED
+    assert ab(ctypes.byref(b), 0x10000, 0x20000, 1, 0x80000, 64, 128, 512, 256, 0.1, 0x30000, 0x40000, 0x50000,
+              0x60000, 0x70000, 1 << 30, None) == L.DSA_ERR_UNSUPPORTED   # backward: 576 / 512 only
     n = ctypes.c_size_t(0)
     assert L._lib.dsa_sparse_mla_backward_workspace_size(ctypes.byref(b), 128, 64, ctypes.byref(n)) == L.DSA_OK
     assert n.value == 4 * ((8 * 128 * 64 * 2 + 255) // 256 * 256)

@@ -54,6 +54,19 @@ def test_bf16_prefill_rows(dsa, H):
     _compare(dsa, p, random_selection(p, 256, H), TOL_ATTN_BF16)
 
 
+@pytest.mark.parametrize("d_qk,d_v", [(64, 64), (192, 128), (512, 512), (560, 512), (576, 256)])
+def test_bf16_narrow_widths(dsa, d_qk, d_v):
+    """BF16 shapes other than 576 / 512 run the 576 / 512 kernels on widened
+    copies (q and kv zero-filled to 576 columns, the output staged at 512 and
+    its first d_v kept): prefill rows and split decode rows against the oracle."""
+    announce("attention bf16 widths", d_qk, d_v)
+    p = gen.make_problem("attn", [700], [700], H_I=16, H=32, d_qk=d_qk, d_v=d_v, k=256, device=DEV, seed=d_qk + d_v)
+    _compare(dsa, p, random_selection(p, 256, 1), TOL_ATTN_BF16)
+    p = gen.make_problem("attn", [5000, 3000, 2100], [1] * 3, H_I=16, H=64, d_qk=d_qk, d_v=d_v, k=2048, device=DEV,
+                         seed=d_qk + d_v + 1)
+    _compare(dsa, p, random_selection(p, 2048, 2), TOL_ATTN_BF16)
+
+
 def test_bf16_decode_rows_use_key_splits(dsa):
     announce("attention bf16 decode split")
     p = gen.make_problem("attn", [5000, 3000, 2100, 2048, 700, 4500], [1] * 6, H_I=16, H=128, k=2048, device=DEV,

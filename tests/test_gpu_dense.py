@@ -63,6 +63,15 @@ def test_dense_bf16_one_row_many_key_splits(dsa, ctx):
     _check(p, out, lse, [0], TOL_ATTN_BF16)
 
 
+@pytest.mark.parametrize("d_qk,d_v", [(128, 64), (576, 128)])
+def test_dense_bf16_narrow_widths(dsa, d_qk, d_v):
+    """The masked mode with BF16 widths other than 576 / 512 (widened copies)."""
+    announce("dense attention bf16 widths", d_qk, d_v)
+    p = gen.make_problem("dense", [700, 1], [700, 1], H_I=16, H=32, d_qk=d_qk, d_v=d_v, k=2048, device=DEV, seed=3)
+    out, lse = dsa.dense_mla_attn(p)
+    _check(p, out, lse, [0, 1, 31, 32, 300, 699, 700], TOL_ATTN_BF16)
+
+
 def test_dense_equals_sparse_over_every_candidate(dsa):
     """With as many rows as compute units neither call splits rows, and the
     dense kernel walks the same tiles in the same order as the sparse kernel

@@ -192,3 +192,20 @@ def test_forward_narrow_indexer_keys(dsa):
         assert torch.equal(idx, dsa.topk(p, dsa.indexer_scores(p))), qb
     rows = np.array([0, 255, 256, 1999, 2499, 2500, 2502], np.int32)
     _check_rows(p, out, idx, rows, TOL_ATTN_BF16, need_exact_idx=True)
+
+
+def test_forward_narrow_attention_widths(dsa):
+    """d_qk = 192, d_v = 128 (BF16): the forward widens the latent once and
+    each chunk's queries, stages the output and keeps its first d_v columns;
+    equal to the separate calls, with and without key splits."""
+    announce("forward attention widths")
+    p = gen.make_problem("fwd", [3000, 2600], [3000, 1], H_I=64, H=64, d_qk=192, d_v=128, k=512, device=DEV,
+                         seed=45)
+    out, lse, idx = dsa.forward(p)
+    idx2 = dsa.topk(p, dsa.indexer_scores(p))
+    assert torch.equal(idx, idx2)
+    out2, lse2 = dsa.sparse_mla_attn(p, idx2)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    out3, lse3, idx3 = dsa.forward(p, q_block=1000)
+    assert torch.equal(idx3, idx)
+    assert row_norm_err(out3.float().cpu().numpy(), out.float().cpu().numpy()) <= TOL_ATTN_BF16

@@ -165,17 +165,18 @@ def _oracle_scores(p, act=0, ld=None):
 
 
 @pytest.mark.parametrize("shape", ["prefill", "decode"])
-@pytest.mark.parametrize("H_I", [16, 64])
-def test_scaled_keys_integer_inputs_bit_exact(dsa, shape, H_I):
+@pytest.mark.parametrize("H_I,d_I", [(16, 128), (64, 128), (20, 64)])
+def test_scaled_keys_integer_inputs_bit_exact(dsa, shape, H_I, d_I):
     """Integer-valued codes and power-of-two scales: every product and partial
     sum is exact, so the scores equal the oracle's bit for bit (workgroups of
-    one sequence, workgroups spanning two, and the decode streaming kernel)."""
-    announce("indexer scaled keys integer", shape, H_I)
+    one sequence, workgroups spanning two, and the decode streaming kernel;
+    d_I = 64 keys are widened with their scales unchanged)."""
+    announce("indexer scaled keys integer", shape, H_I, d_I)
     if shape == "prefill":
-        p = gen.make_problem("s", [300, 77, 1000, 129], [300, 5, 3, 64], H_I=H_I, H=32, k=64, integer=True,
+        p = gen.make_problem("s", [300, 77, 1000, 129], [300, 5, 3, 64], H_I=H_I, d_I=d_I, H=32, k=64, integer=True,
                              device=DEV, seed=46)
     else:
-        p = gen.make_problem("s", [2000, 3000, 700, 5000], [1, 1, 2, 1], H_I=H_I, H=32, k=64, integer=True,
+        p = gen.make_problem("s", [2000, 3000, 700, 5000], [1, 1, 2, 1], H_I=H_I, d_I=d_I, H=32, k=64, integer=True,
                              device=DEV, seed=47)
     _with_scales(p, 48)
     got = dsa.indexer_scores(p).cpu().numpy()

@@ -12,6 +12,7 @@ typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
 constexpr int kWave = 64;
 
@@ -23,6 +24,25 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+
+// One HBM -> LDS copy instruction (global_load_lds_dwordx4): lane l's 16 bytes
+// at src land at dst + 16 l; dst is wave-uniform.  Written out rather than
+// through the compiler builtin because the compiler, which cannot tell LDS
+// reads without type-based alias information (the transposing reads among
+// them) apart from the copies, would wait for every copy in flight before each
+// such read and so undo the prefetch.  The copy's completion is the caller's
+// to track, with counted vmcnt waits and a barrier before the data is read.
+// M0 carries the LDS base (one wait state separates its write from the copy);
+// the kernels that use this keep nothing else in M0, which the compiler
+// reserves and warns about naming as clobbered.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const void* src, DSA_LDS void* dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(src)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // Workgroup rendezvous for the tile loop that does not drain vector memory:
 // this wave's LDS operations complete (lgkmcnt 0), then every wave meets.

@@ -245,10 +245,21 @@ template <int HPW, int NW, int Z>
 __device__ __forceinline__ void bwd_dq_half(const BwdArgs& a) {
   constexpr int NT = HPW / 16;
   constexpr int RG = row_groups_per_wave<NW>();
-  constexpr int NINS = kSegments * RG;
-  constexpr int AHEAD = 2 * NINS < 64 ? 3 : 1;
   constexpr int kQkTiles = kDqk / 32;  // 18 column tiles of dq per half
   constexpr int DT0 = Z * kQkTiles;
+  // the latent lines this half reads: columns 288 Z .. 288 Z + 287 lie in
+  // lines 0 .. 4 (Z = 0) or 4 .. 8 (Z = 1), 5 of the 9
+  constexpr int SG0 = (16 * DT0) / 64, SG1 = (16 * (DT0 + kQkTiles) + 63) / 64;
+  // the tile's dS rows (hi and lo parts) travel with its latent lines, in the
+  // 16 blocks of the tile buffer this half leaves free (20 .. 35 or 0 .. 15):
+  // per wave and array, per head tile of 16 heads, 1 KB of [head][32 entries];
+  // the 16-byte chunk c of head h sits in slot (c + h / 4) % 4 of its row, so
+  // the fragment reads of 16 heads land on 16 different bank pairs
+  constexpr int DSOFF = SG0 == 0 ? 1024 * 4 * SG1 : 0;
+  static_assert(NW * 2 * NT * 1024 <= 1024 * (kTileBytes / 1024 - 4 * (SG1 - SG0)), "dS does not fit the free blocks");
+  constexpr int DSI = 2 * NT;                   // dS copies per tile and wave
+  constexpr int NINS = (SG1 - SG0) * RG + DSI;  // copies per tile and wave
+  constexpr int AHEAD = 2 * NINS < 64 ? 3 : 1;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   DSA_LDS int32_t* sel = (DSA_LDS int32_t*)((DSA_LDS uint8_t*)smem + kNumBuf * kTileBytes);
   DSA_LDS uint32_t* tmask = (DSA_LDS uint32_t*)(sel + kMaxSel);
@@ -276,19 +287,26 @@ __device__ __forceinline__ void bwd_dq_half(const BwdArgs& a) {
     for (int nt = 0; nt < NT; ++nt) acc[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // dS^T fragments (the forward's probability layout): head 16 nt + li, MFMA
   // K index 8g + e <-> entry 4g + e (e < 4), 16 + 4g + e - 4 otherwise; hi and
-  // lo parts, loaded a tile ahead
-  auto load_ds = [&](int t, bf16x8 (&hi)[NT], bf16x8 (&lo)[NT]) {
+  // lo parts.  copy_ds: this wave's rows of tile t into the buffer's dS area
+  // (lane l: head l / 4 of the head tile, the chunk its slot l holds)
+  auto copy_ds = [&](int t, uint8_t* buf) {
+    const int hh = lane >> 2, c = ((lane & 3) - (hh >> 2)) & 3;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int64_t o = ((int64_t)rl * a.H + head0 + 16 * nt + li) * a.k32 + kTile * t + 4 * g;
-      const uint2 a0 = *(const uint2*)(a.ds_he + o), a1 = *(const uint2*)(a.ds_he + o + 16);
-      const uint2 b0 = *(const uint2*)(a.ds_he_lo + o), b1 = *(const uint2*)(a.ds_he_lo + o + 16);
-      hi[nt] = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
-      lo[nt] = __builtin_bit_cast(bf16x8, make_uint4(b0.x, b0.y, b1.x, b1.y));
-    }
+    for (int arr = 0; arr < 2; ++arr)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint16_t* src = (arr == 0 ? a.ds_he : a.ds_he_lo) +
+                              ((int64_t)rl * a.H + head0 + 16 * nt + hh) * a.k32 + kTile * t + 8 * c;
+        copy16_to_lds(src, (DSA_LDS uint8_t*)buf + DSOFF + 1024 * ((wave * 2 + arr) * NT + nt));
+      }
   };
-  bf16x8 dsf_n[NT], dsl_n[NT];
-  if (t0 < t1) load_ds(t0, dsf_n, dsl_n);
+  const int dso0 = li * 64 + 16 * (((g >> 1) + (li >> 2)) & 3) + 8 * (g & 1);
+  const int dso1 = li * 64 + 16 * ((2 + (g >> 1) + (li >> 2)) & 3) + 8 * (g & 1);
+  auto read_ds = [&](const DSA_LDS uint8_t* lb, int arr, int nt) -> bf16x8 {
+    const DSA_LDS uint8_t* base = lb + DSOFF + 1024 * ((wave * 2 + arr) * NT + nt);
+    const u32x2 x0 = *(const DSA_LDS u32x2*)(base + dso0), x1 = *(const DSA_LDS u32x2*)(base + dso1);
+    return __builtin_bit_cast(bf16x8, i32x4{(int)x0.x, (int)x0.y, (int)x1.x, (int)x1.y});
+  };
 
 #pragma unroll
   for (int j = 0; j < AHEAD; ++j)
@@ -296,7 +314,8 @@ __device__ __forceinline__ void bwd_dq_half(const BwdArgs& a) {
       int32_t pj[RG];
 #pragma unroll
       for (int k = 0; k < RG; ++k) pj[k] = pos_at(t0 + j, k);
-      gather_tile<NW>(a.kv, ri.kbase, pj, smem + (size_t)j * kTileBytes);
+      gather_lines<NW, SG0, SG1>(a.kv, ri.kbase, pj, smem + (size_t)j * kTileBytes);
+      copy_ds(t0 + j, smem + (size_t)j * kTileBytes);
     }
   int32_t p_next[RG];
 #pragma unroll
@@ -309,23 +328,24 @@ __device__ __forceinline__ void bwd_dq_half(const BwdArgs& a) {
     else wait_vmcnt<0>();
     lds_barrier();
     if (t + AHEAD < t1) {
-      gather_tile<NW>(a.kv, ri.kbase, p_next, smem + (size_t)((t + AHEAD - t0) % kNumBuf) * kTileBytes);
+      uint8_t* nb = smem + (size_t)((t + AHEAD - t0) % kNumBuf) * kTileBytes;
+      gather_lines<NW, SG0, SG1>(a.kv, ri.kbase, p_next, nb);
+      copy_ds(t + AHEAD, nb);
       if (t + AHEAD + 1 < t1) {
 #pragma unroll
         for (int k = 0; k < RG; ++k) p_next[k] = pos_at(t + AHEAD + 1, k);
       }
     }
     const uint32_t vmask = (uint32_t)__builtin_amdgcn_readlane((int)tmask_lane, t);
-    bf16x8 dsf[NT], dsl[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      dsf[nt] = dsf_n[nt];
-      dsl[nt] = dsl_n[nt];
-    }
-    if (t + 1 < t1) load_ds(t + 1, dsf_n, dsl_n);  // in flight during this tile
     if (vmask == 0) continue;
     const DSA_LDS uint8_t* lb = (const DSA_LDS uint8_t*)smem + (size_t)((t - t0) % kNumBuf) * kTileBytes;
     const DSA_LDS uint8_t* vb[4] = {lb + voff[0], lb + voff[1], lb + voff[2], lb + voff[3]};
+    bf16x8 dsf[NT], dsl[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      dsf[nt] = read_ds(lb, 0, nt);
+      dsl[nt] = read_ds(lb, 1, nt);
+    }
     auto load_c = [&](int dt) -> bf16x8 {
       const DSA_LDS uint8_t* p = vb[dt & 3] + 4096 * (dt >> 2);
       const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS i16x4*)p);

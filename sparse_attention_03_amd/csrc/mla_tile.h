@@ -61,10 +61,12 @@ constexpr int row_groups_per_wave() { return 4 / NW; }
 // Tile row copied by this lane for its k-th row group.
 __device__ __forceinline__ int gather_row(int wave, int NW, int k, int lane) { return 8 * (wave + NW * k) + (lane >> 3); }
 
+// Lines [SG0, SG1) of each latent row of the tile (a kernel that reads only
+// some columns fetches only their lines; the layout is the whole tile's).
 // p[k]: selected position of this lane's tile row for row group k.
-template <int NW>
-__device__ __forceinline__ void gather_tile(const uint8_t* kv, int32_t kbase, const int32_t (&p)[4 / NW],
-                                            uint8_t* buf) {
+template <int NW, int SG0, int SG1>
+__device__ __forceinline__ void gather_lines(const uint8_t* kv, int32_t kbase, const int32_t (&p)[4 / NW],
+                                             uint8_t* buf) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 #pragma unroll
   for (int k = 0; k < row_groups_per_wave<NW>(); ++k) {
@@ -73,10 +75,16 @@ __device__ __forceinline__ void gather_tile(const uint8_t* kv, int32_t kbase, co
     const int32_t pk = p[k] < 0 ? 0 : p[k];
     const uint8_t* src = kv + ((int64_t)(kbase + pk) * kChunksPerRow + x) * 16;
 #pragma unroll
-    for (int sg = 0; sg < kSegments; ++sg)
-      __builtin_amdgcn_global_load_lds((const void*)(src + 128 * sg),
-                                       (DSA_LDS void*)((DSA_LDS uint8_t*)buf + 1024 * (4 * sg + rg)), 16, 0, 0);
+    for (int sg = SG0; sg < SG1; ++sg)
+      copy16_to_lds(src + 128 * sg, (DSA_LDS uint8_t*)buf + 1024 * (4 * sg + rg));
   }
+}
+
+// The whole tile: every line of every row.
+template <int NW>
+__device__ __forceinline__ void gather_tile(const uint8_t* kv, int32_t kbase, const int32_t (&p)[4 / NW],
+                                            uint8_t* buf) {
+  gather_lines<NW, 0, kSegments>(kv, kbase, p, buf);
 }
 
 }  // namespace mla

@@ -39,7 +39,8 @@ sys.path.insert(0, ROOT)
 PEAK = {"fp8": 5.0e15, "bf16": 2.5e15}   # MI355X dense MFMA, FLOP/s
 HBM_PEAK = 8.0e12                         # bytes/s
 CSRC = os.path.join(ROOT, "sparse_attention_03_amd", "csrc")
-KERNEL_SOURCE = {"attention": ("sparse_mla.hip", "mla_tile.h"), "indexer": ("indexer.hip",), "topk": ("topk.hip",)}
+KERNEL_SOURCE = {"attention": ("sparse_mla.hip", "mla_tile.h", "dsa_common.h"), "indexer": ("indexer.hip", "dsa_common.h"),
+                 "topk": ("topk.hip", "dsa_common.h")}
 KERNEL_SYMBOL = {"attention": "mla_bf16_kernel", "indexer": "indexer_fp8_kernel", "topk": "topk_kernel"}
 COPY_BYTES = 1 << 30                      # the calibration copy moves this many bytes each way
 

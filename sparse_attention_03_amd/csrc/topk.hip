@@ -37,6 +37,32 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The inverse of order_key on the keys it produces (NaN's key 0 gives a NaN,
+// -0's key gives +0: equal under every comparison made here).
+__device__ __forceinline__ uint32_t key_bits(uint32_t key) {
+  return (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
+}
+
+// The smallest float f with order_key(x) > tau  <=>  x >= f for every x
+// (NaN when no float qualifies).  The keys just above tau that no float takes
+// (1 .. 0x007ffffe below -inf's key, 0x7fffffff which -0 gives up to +0) are
+// skipped.  A float comparison is exact for the filter: NaN fails it, -0 and
+// +0 compare equal, denormals compare by value.
+__device__ __forceinline__ float admit_floor(uint32_t tau) {
+  if (tau >= 0xff800000u) return __uint_as_float(0x7fc00000u);  // nothing ranks above +inf
+  uint32_t k = tau + 1u;
+  if (k < 0x007fffffu) k = 0x007fffffu;
+  if (k == 0x7fffffffu) k = 0x80000000u;
+  return __uint_as_float(key_bits(k));
+}
+
+// The candidate buffer holds order keys, or (RAW) the scores' float bits,
+// which are turned into keys only when the buffer is cut.
+template <bool RAW>
+__device__ __forceinline__ uint32_t buf_key(uint32_t v) {
+  return RAW ? order_key(__uint_as_float(v)) : v;
+}
+
 struct TopkShared {
   uint32_t key[kCap];
   int32_t pos[kCap];
@@ -65,33 +91,13 @@ __device__ __forceinline__ int wave_excl_prefix_small(int v, int& wave_total) {
   return pre;
 }
 
-// Exclusive scan over the block (thread order) of a small count; every thread
-// gets the total.  One barrier: the wave totals alternate between two slots.
-template <int NBITS>
-__device__ __forceinline__ int block_excl_scan(int v, TopkShared& sh, int& parity, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int wt;
-  const int pre = wave_excl_prefix_small<NBITS>(v, wt);
-  if (lane == 0) sh.wave_sum[parity][wave] = wt;
-  __syncthreads();
-  int off = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kTkWaves; ++w) {
-    const int t = sh.wave_sum[parity][w];
-    off += (w < wave) ? t : 0;
-    tot += t;
-  }
-  parity ^= 1;
-  total = tot;
-  return off + pre;
-}
-
 // The k-th best key T of the first `cnt` (>= k) buffer entries, and in `need`
 // how many of the entries equal to T rank among the k best.  T is located by
 // histogram refinement over the buffer's own key range: each pass splits the
 // current interval [lo, hi] (known to hold T) into at most 256 equal
 // power-of-two bins, so clustered scores still spread over the bins; at most
 // four passes, none when every key is equal.
+template <bool RAW>
 __device__ uint32_t kth_key(TopkShared& sh, int cnt, int k, int& need) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // the thread's keys (entries tid + 256 j) stay in registers for every pass
@@ -102,7 +108,7 @@ __device__ uint32_t kth_key(TopkShared& sh, int cnt, int k, int& need) {
   for (int j = 0; j < kSegMax; ++j) {
     const int e = tid + kTkThreads * j;
     kv[j] = e < cnt;
-    kr[j] = kv[j] ? sh.key[e] : 0u;
+    kr[j] = kv[j] ? buf_key<RAW>(sh.key[e]) : 0u;
     if (kv[j]) {
       mn = min(mn, kr[j]);
       mx = max(mx, kr[j]);
@@ -165,11 +171,12 @@ __device__ uint32_t kth_key(TopkShared& sh, int cnt, int k, int& need) {
 // block, conflict-free LDS reads) into registers, ballots order the lanes and
 // one exchange of per-wave counts orders the waves; every read precedes the
 // barrier of that exchange, so the kept entries are written back in place.
+template <bool RAW>
 __device__ uint32_t cut_to_k(TopkShared& sh, int cnt, int k, int& parity) {
   (void)parity;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int need;
-  const uint32_t T = kth_key(sh, cnt, k, need);
+  const uint32_t T = kth_key<RAW>(sh, cnt, k, need);
   const int L = (cnt + 64 * kTkWaves - 1) / (64 * kTkWaves) * 64;  // <= 64 * kSegMax
   const int w0 = min(wave * L, cnt), w1 = min(w0 + L, cnt);
   uint32_t kk[kSegMax];
@@ -179,7 +186,7 @@ __device__ uint32_t cut_to_k(TopkShared& sh, int cnt, int k, int& parity) {
   for (int j = 0; j < kSegMax; ++j) {
     const int e = w0 + 64 * j + lane;
     const bool in = 64 * j < L && e < w1;
-    kk[j] = in ? sh.key[e] : 0u;
+    kk[j] = in ? buf_key<RAW>(sh.key[e]) : 0u;
     pp[j] = in ? sh.pos[e] : -1;  // buffered positions are >= 0: -1 marks an empty slot
     gt += __popcll(__ballot(in && kk[j] > T));
     eq += __popcll(__ballot(in && kk[j] == T));
@@ -208,7 +215,7 @@ __device__ uint32_t cut_to_k(TopkShared& sh, int cnt, int k, int& parity) {
     const uint64_t mk = __ballot(kept);
     const int o = keeprun + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
-    if (kept) { sh.key[o] = kk[j]; sh.pos[o] = pp[j]; }
+    if (kept) { sh.key[o] = RAW ? key_bits(kk[j]) : kk[j]; sh.pos[o] = pp[j]; }
     eqrun += __popcll(meq);
     keeprun += __popcll(mk);
   }
@@ -217,22 +224,54 @@ __device__ uint32_t cut_to_k(TopkShared& sh, int cnt, int k, int& parity) {
 }
 
 // ---------------------------------------------------------------------------
+// Offset of this wave's admitted elements in the block's (wave order), from
+// the admission masks of the wave's elements; every thread gets the block's
+// total.  One barrier: the wave totals alternate between two slots.
+__device__ __forceinline__ int block_base(const uint64_t (&m)[kPer], TopkShared& sh, int& parity, int& total) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int wt = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) wt += __popcll(m[j]);
+  if (lane == 0) sh.wave_sum[parity][wave] = wt;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    const int t = sh.wave_sum[parity][w];
+    off += (w < wave) ? t : 0;
+    tot += t;
+  }
+  parity ^= 1;
+  total = tot;
+  return off;
+}
+
+// ---------------------------------------------------------------------------
 // Streaming selection over a sequence of `count` elements given in ascending
 // position order.  Leaves the k best (or all, if fewer are valid) in
-// sh.key/sh.pos[0 .. returned count), in ascending position order.  Src
-// provides Fetch (the raw loads of one thread's kPer elements), fetch() and
-// decode(); three chunks of loads are kept in flight ahead of the one being
-// filtered, so the row streams at memory speed instead of load latency.
+// sh.key/sh.pos[0 .. returned count), in ascending position order (sh.key as
+// Src::kRaw says).  A chunk of 2048 elements gives wave w elements
+// 512 w .. 512 w + 511, lane l element 64 j + l of them for j < kPer, so the
+// admission test of element j is one compare whose lane mask is also the
+// lanes' order: element (j, l) lands at the wave's base plus the admitted
+// elements of j' < j plus those of lanes below l (mbcnt).  Src provides Fetch
+// (the raw loads of one thread's kPer elements), fetch(), admit() (the lane
+// masks of the elements that beat the threshold: every valid one before there
+// is one), value() and position(); three chunks of loads are kept in flight
+// ahead of the one being filtered, so the row streams at memory speed instead
+// of load latency.
 // ---------------------------------------------------------------------------
 // tau0 (have_tau0): start with the threshold tau0 -- only keys above it are
 // admitted; *admitted: how many entries were admitted in all.
 template <class Src>
 __device__ int stream_select(TopkShared& sh, const Src& src, int32_t count, int k, bool have_tau0 = false,
                              uint32_t tau0 = 0, int* admitted = nullptr) {
-  const int tid = threadIdx.x;
+  constexpr bool RAW = Src::kRaw;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int cnt = 0, adm = 0;
   bool have_tau = have_tau0;
   uint32_t tau = tau0;
+  float tfloor = admit_floor(tau0);
   int parity = 0;
   // a ring of four chunks' loads, unrolled so that every slot is a fixed set
   // of registers (a rotation by register copies would make each chunk wait
@@ -243,30 +282,32 @@ __device__ int stream_select(TopkShared& sh, const Src& src, int32_t count, int 
   src.fetch(0, f[0]);
   src.fetch(kChunk, f[1]);
   src.fetch(2 * kChunk, f[2]);
-  auto step = [&](int32_t c0, int u) __attribute__((always_inline)) {
+  // full: every element of the chunk lies before `count`
+  auto step = [&](int32_t c0, int u, bool full) __attribute__((always_inline)) {
     src.fetch(c0 + 3 * kChunk, f[(u + 3) & 3]);
-    uint32_t key[kPer];
-    int32_t pos[kPer];
-    bool ok[kPer];
-    src.decode(f[u], c0 + tid * kPer, key, pos, ok);
-    int c = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) c += ok[j] && (!have_tau || key[j] > tau);
+    const int32_t w0 = c0 + wave * (64 * kPer);  // the wave's first element
+    uint64_t m[kPer];
+    src.admit(f[u], w0, full, have_tau, tau, tfloor, m);
     int total;
-    int off = block_excl_scan<4>(c, sh, parity, total);
+    int base = block_base(m, sh, parity, total);
     if (cnt + total > kCap) {
-      tau = cut_to_k(sh, cnt, k, parity);
+      tau = cut_to_k<RAW>(sh, cnt, k, parity);
+      tfloor = admit_floor(tau);
       have_tau = true;
       cnt = k;
-      c = 0;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) c += ok[j] && key[j] > tau;
-      off = block_excl_scan<4>(c, sh, parity, total);
+      src.admit(f[u], w0, full, true, tau, tfloor, m);
+      base = block_base(m, sh, parity, total);
     }
-    off += cnt;
+    int o = cnt + base;  // uniform over the wave
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      if (ok[j] && (!have_tau || key[j] > tau)) { sh.key[off] = key[j]; sh.pos[off] = pos[j]; ++off; }
+      if (__builtin_amdgcn_inverse_ballot_w64(m[j])) {
+        const int e = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m[j] >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m[j], (uint32_t)o));
+        sh.key[e] = src.value(f[u], j);
+        sh.pos[e] = src.position(f[u], w0, j);
+      }
+      o += __popcll(m[j]);
     }
     cnt += total;
     adm += total;
@@ -274,17 +315,17 @@ __device__ int stream_select(TopkShared& sh, const Src& src, int32_t count, int 
   int32_t c00 = 0;
   for (; c00 + 4 * kChunk <= count; c00 += 4 * kChunk) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) step(c00 + u * kChunk, u);
+    for (int u = 0; u < 4; ++u) step(c00 + u * kChunk, u, true);
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {  // count - c00 < 4 chunks: at most four, the last one partial
     if (c00 + u * kChunk >= count) break;
-    step(c00 + u * kChunk, u);
+    step(c00 + u * kChunk, u, c00 + (u + 1) * kChunk <= count);
   }
   __syncthreads();
   if (admitted) *admitted = adm;
   if (cnt > k) {
-    cut_to_k(sh, cnt, k, parity);
+    cut_to_k<RAW>(sh, cnt, k, parity);
     cnt = k;
   }
   return cnt;
@@ -317,57 +358,71 @@ __device__ uint32_t sampled_threshold(TopkShared& sh, const float* row, int32_t 
   constexpr int m = kSampleBlocks * kSampleBlock;
   const int rank = (int)min((int64_t)m, 3LL * k * m / (2LL * n) + 8);
   int need;
-  return kth_key(sh, m, rank, need);
+  return kth_key<false>(sh, m, rank, need);
 }
 
-// Elements are the scores of one row at positions [lo, hi).
+// Elements are the scores of one row at positions [lo, hi).  The filter
+// compares floats against admit_floor(tau), which admits exactly the keys
+// above tau, so no key is formed for the elements it rejects; the buffer keeps
+// the admitted scores' bits.
 struct ScoreSrc {
-  struct Fetch { f32x4 a, b; };
+  static constexpr bool kRaw = true;
+  struct Fetch { float v[kPer]; };
   const float* row;
   int32_t lo, hi;
-  __device__ void fetch(int32_t c0, Fetch& f) const {
-    const int32_t p = lo + c0 + (int32_t)threadIdx.x * kPer;  // lo is a multiple of kPer
+  __device__ __forceinline__ void fetch(int32_t c0, Fetch& f) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int32_t p = lo + c0 + wave * (64 * kPer) + lane;
     // raw buffer loads over the row's first hi entries: entries past hi read
-    // as zero (and are masked in decode), and no load is conditional
+    // as zero (and are masked in admit), and no load is conditional
     const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)row, 0, (uint32_t)hi * 4, 0x00020000);
-    f.a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)p * 4, 0, 0));
-    f.b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)p * 4 + 16, 0, 0));
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      f.v[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(p + 64 * j) * 4, 0, 0));
   }
-  __device__ void decode(const Fetch& f, int32_t i0, uint32_t (&key)[kPer], int32_t (&pos)[kPer],
-                         bool (&ok)[kPer]) const {
+  __device__ __forceinline__ void admit(const Fetch& f, int32_t w0, bool full, bool have_tau, uint32_t,
+                                        float tfloor, uint64_t (&m)[kPer]) const {
+    const int lane = threadIdx.x & 63;
+    // the masks stay scalar: one compare per element, the rest is mask logic
+    // (without a threshold every lane's element is admitted, NaN included)
+    const uint64_t thr = have_tau ? ~0ull : 0ull, all = __ballot(true);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { key[j] = order_key(f.a[j]); key[4 + j] = order_key(f.b[j]); }
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) { pos[j] = lo + i0 + j; ok[j] = pos[j] < hi; }
+    for (int j = 0; j < kPer; ++j) {
+      uint64_t mj = (__ballot(f.v[j] >= tfloor) & thr) | (all & ~thr);
+      if (!full) mj &= __ballot(lo + w0 + 64 * j + lane < hi);
+      m[j] = mj;
+    }
+  }
+  __device__ __forceinline__ uint32_t value(const Fetch& f, int j) const { return __float_as_uint(f.v[j]); }
+  __device__ __forceinline__ int32_t position(const Fetch&, int32_t w0, int j) const {
+    return lo + w0 + 64 * j + (int)(threadIdx.x & 63);
   }
 };
 
 // Elements are (key, position) candidates; position -1 marks padding.
 struct CandSrc {
-  struct Fetch { i32x4 ka, kb, pa, pb; };
+  static constexpr bool kRaw = false;
+  struct Fetch { uint32_t k[kPer]; int32_t p[kPer]; };
   const uint32_t* key;
   const int32_t* pos;
   int32_t count;
-  __device__ void fetch(int32_t c0, Fetch& f) const {
-    const int32_t i = c0 + (int32_t)threadIdx.x * kPer;
-    f.ka = f.kb = i32x4{0, 0, 0, 0};
-    f.pa = f.pb = i32x4{-1, -1, -1, -1};
-    if (i < count) {  // count is a multiple of kPer
-      f.ka = *(const i32x4*)(key + i);
-      f.kb = *(const i32x4*)(key + i + 4);
-      f.pa = *(const i32x4*)(pos + i);
-      f.pb = *(const i32x4*)(pos + i + 4);
+  __device__ __forceinline__ void fetch(int32_t c0, Fetch& f) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int32_t i = c0 + wave * (64 * kPer) + lane;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const bool in = i + 64 * j < count;
+      f.k[j] = in ? key[i + 64 * j] : 0u;
+      f.p[j] = in ? pos[i + 64 * j] : -1;
     }
   }
-  __device__ void decode(const Fetch& f, int32_t, uint32_t (&k)[kPer], int32_t (&p)[kPer], bool (&ok)[kPer]) const {
+  __device__ __forceinline__ void admit(const Fetch& f, int32_t, bool, bool have_tau, uint32_t tau, float,
+                                        uint64_t (&m)[kPer]) const {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      k[j] = (uint32_t)f.ka[j]; k[4 + j] = (uint32_t)f.kb[j];
-      p[j] = f.pa[j]; p[4 + j] = f.pb[j];
-    }
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) ok[j] = p[j] >= 0;
+    for (int j = 0; j < kPer; ++j) m[j] = __ballot(f.p[j] >= 0 && (!have_tau || f.k[j] > tau));
   }
+  __device__ __forceinline__ uint32_t value(const Fetch& f, int j) const { return f.k[j]; }
+  __device__ __forceinline__ int32_t position(const Fetch& f, int32_t, int j) const { return f.p[j]; }
 };
 
 // One workgroup per row: the whole selection in one pass over the row.
@@ -424,7 +479,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_segment_kernel(const int32_t*
     cnt = stream_select(sh, src, hi - lo, k);
   }
   for (int e = threadIdx.x; e < k; e += kTkThreads) {
-    okey[e] = e < cnt ? sh.key[e] : 0u;
+    okey[e] = e < cnt ? buf_key<ScoreSrc::kRaw>(sh.key[e]) : 0u;
     opos[e] = e < cnt ? sh.pos[e] : -1;
   }
 }

@@ -110,6 +110,11 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bwd_ds_kernel(BwdArgs a) {
     for (int c = 0; c < kVSteps; ++c) dof[nt][c] = *(const bf16x8*)(drow + 32 * c);
     lse2[nt] = a.lse[(int64_t)r * a.H + h] * 1.4426950408889634f;
   }
+  // The query and dout loads complete here: the tile copies are issued outside
+  // the compiler's view, so a load it still thought in flight would make it
+  // wait on vmcnt inside the tile walks, and every such wait would also drain
+  // the copies issued ahead.
+  wait_vmcnt<0>();
   __syncthreads();
   const uint32_t tmask_lane = lane < kMaxSel / kTile ? tmask[lane] : 0u;
   auto pos_at = [&](int t, int k) -> int32_t { return sel[t * kTile + gather_row(wave, NW, k, lane)]; };

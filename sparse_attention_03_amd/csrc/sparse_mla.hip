@@ -118,6 +118,11 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
 #pragma unroll
     for (int c = 0; c < kQkSteps; ++c) qf[nt][c] = *(const bf16x8*)(qrow + 32 * c);
   }
+  // The query loads complete here: the tile copies are issued outside the
+  // compiler's view, so a query load it still thought in flight would make it
+  // wait on vmcnt inside the tile loop, and every such wait would also drain
+  // the copies issued ahead.
+  wait_vmcnt<0>();
   __syncthreads();  // sel[] and tmask[] visible
   const uint32_t tmask_lane = !dense && lane < kMaxSel / kTile ? tmask[lane] : 0u;  // tile t's mask: lane t
   // position copied by this lane for tile t, row group k (DENSE: invalid
@@ -408,6 +413,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_target_kernel(MlaArgs a) {
     for (int c = 0; c < kQkSteps; ++c) qf[nt][c] = *(const bf16x8*)(qrow + 32 * c);
     lse2[nt] = h < a.H ? a.lse_in[(int64_t)r * a.H + h] * 1.4426950408889634f : -INFINITY;  // -inf: adds nothing
   }
+  wait_vmcnt<0>();  // the query loads complete before the tile loop (see mla_bf16_kernel)
   __syncthreads();
   const uint32_t tmask_lane = !dense && lane < kMaxSel / kTile ? tmask[lane] : 0u;
   auto pos_at = [&](int t, int k) -> int32_t {

@@ -29,6 +29,9 @@ constexpr int kChunk = kTkThreads * kPer;  // 2048
 constexpr int kMaxK = 2048;
 constexpr int kCap = kMaxK + kChunk;       // 4096
 constexpr int kSegMax = kCap / kTkThreads; // 16
+constexpr int kHistBits = 8;               // bins per histogram pass: 256
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kBinsPerLane = kHistBins / 64;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -66,7 +69,7 @@ __device__ __forceinline__ uint32_t buf_key(uint32_t v) {
 struct TopkShared {
   uint32_t key[kCap];
   int32_t pos[kCap];
-  int hist[256];
+  int hist[kHistBins];
   int wave_sum[2][kTkWaves];   // double-buffered: one barrier per scan
   int fcnt[2][kTkWaves];       // per-wave counts of the cut's filter
   uint32_t red[2][kTkWaves];
@@ -94,11 +97,13 @@ __device__ __forceinline__ int wave_excl_prefix_small(int v, int& wave_total) {
 // The k-th best key T of the first `cnt` (>= k) buffer entries, and in `need`
 // how many of the entries equal to T rank among the k best.  T is located by
 // histogram refinement over the buffer's own key range: each pass splits the
-// current interval [lo, hi] (known to hold T) into at most 256 equal
+// current interval [lo, hi] (known to hold T) into at most kHistBins equal
 // power-of-two bins, so clustered scores still spread over the bins; at most
-// four passes, none when every key is equal.
+// four passes, none when every key is equal.  After max_passes passes the
+// lower end of the interval is returned instead: a key at most T, with `need`
+// then meaningless.
 template <bool RAW>
-__device__ uint32_t kth_key(TopkShared& sh, int cnt, int k, int& need) {
+__device__ uint32_t kth_key(TopkShared& sh, int cnt, int k, int& need, int max_passes = 4) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // the thread's keys (entries tid + 256 j) stay in registers for every pass
   uint32_t kr[kSegMax];
@@ -124,23 +129,24 @@ __device__ uint32_t kth_key(TopkShared& sh, int cnt, int k, int& need) {
 #pragma unroll
   for (int w = 1; w < kTkWaves; ++w) { lo = min(lo, sh.red[0][w]); hi = max(hi, sh.red[1][w]); }
   need = k;  // entries of [lo, hi] still to take, counted from the top
-  while (hi > lo) {
+  for (int pass = 0; hi > lo && pass < max_passes; ++pass) {
     const uint32_t span = hi - lo;
     const int bits = 32 - __clz(span);
-    const int shift = bits > 8 ? bits - 8 : 0;
-    const int nbins = (int)(span >> shift) + 1;  // <= 256
-    sh.hist[tid] = 0;
+    const int shift = bits > kHistBits ? bits - kHistBits : 0;
+    const int nbins = (int)(span >> shift) + 1;  // <= kHistBins
+#pragma unroll
+    for (int j = 0; j < kHistBins / kTkThreads; ++j) sh.hist[tid + kTkThreads * j] = 0;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kSegMax; ++j)
       if (kv[j] && kr[j] >= lo && kr[j] <= hi) atomicAdd(&sh.hist[(kr[j] - lo) >> shift], 1);
     __syncthreads();
     if (wave == 0) {
-      // lane l owns bins nbins-1-4l .. nbins-4-4l (descending key order)
-      int c[4], sum = 0;
+      // lane l owns bins nbins-1-B l .. nbins-B-B l (descending key order, B = kBinsPerLane)
+      int c[kBinsPerLane], sum = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int b = nbins - 1 - 4 * lane - j;
+      for (int j = 0; j < kBinsPerLane; ++j) {
+        const int b = nbins - 1 - kBinsPerLane * lane - j;
         c[j] = b >= 0 ? sh.hist[b] : 0;
         sum += c[j];
       }
@@ -149,8 +155,11 @@ __device__ uint32_t kth_key(TopkShared& sh, int cnt, int k, int& need) {
       if (excl < need && need <= incl) {
         int run = excl;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (run < need && need <= run + c[j]) { sh.digit = nbins - 1 - 4 * lane - j; sh.need = need - run; }
+        for (int j = 0; j < kBinsPerLane; ++j) {
+          if (run < need && need <= run + c[j]) {
+            sh.digit = nbins - 1 - kBinsPerLane * lane - j;
+            sh.need = need - run;
+          }
           run += c[j];
         }
       }
@@ -358,7 +367,9 @@ __device__ uint32_t sampled_threshold(TopkShared& sh, const float* row, int32_t 
   constexpr int m = kSampleBlocks * kSampleBlock;
   const int rank = (int)min((int64_t)m, 3LL * k * m / (2LL * n) + 8);
   int need;
-  return kth_key<false>(sh, m, rank, need);
+  // one pass: the lower end of the bin holding that rank, which only admits
+  // a few more entries
+  return kth_key<false>(sh, m, rank, need, 1);
 }
 
 // Elements are the scores of one row at positions [lo, hi).  The filter

@@ -270,11 +270,20 @@ __device__ __forceinline__ int block_base(const uint64_t (&m)[kPer], TopkShared&
 // ahead of the one being filtered, so the row streams at memory speed instead
 // of load latency.
 // ---------------------------------------------------------------------------
-// tau0 (have_tau0): start with the threshold tau0 -- only keys above it are
-// admitted; *admitted: how many entries were admitted in all.
+// f: the ring, its first three chunks already fetched (prime_ring), so that a
+// caller can overlap their latency with other work.  tau0 (have_tau0): start
+// with the threshold tau0 -- only keys above it are admitted; *admitted: how
+// many entries were admitted in all.
 template <class Src>
-__device__ int stream_select(TopkShared& sh, const Src& src, int32_t count, int k, bool have_tau0 = false,
-                             uint32_t tau0 = 0, int* admitted = nullptr) {
+__device__ __forceinline__ void prime_ring(const Src& src, typename Src::Fetch (&f)[4]) {
+  src.fetch(0, f[0]);
+  src.fetch(kChunk, f[1]);
+  src.fetch(2 * kChunk, f[2]);
+}
+
+template <class Src>
+__device__ int stream_select(TopkShared& sh, const Src& src, typename Src::Fetch (&f)[4], int32_t count, int k,
+                             bool have_tau0 = false, uint32_t tau0 = 0, int* admitted = nullptr) {
   constexpr bool RAW = Src::kRaw;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int cnt = 0, adm = 0;
@@ -287,10 +296,6 @@ __device__ int stream_select(TopkShared& sh, const Src& src, int32_t count, int 
   // for the newest loads).  Whole groups of four chunks run without any exit
   // between them, so the compiler's wait before a chunk's keys covers that
   // chunk's loads only; the last partial group runs after them.
-  typename Src::Fetch f[4];
-  src.fetch(0, f[0]);
-  src.fetch(kChunk, f[1]);
-  src.fetch(2 * kChunk, f[2]);
   // full: every element of the chunk lies before `count`
   auto step = [&](int32_t c0, int u, bool full) __attribute__((always_inline)) {
     src.fetch(c0 + 3 * kChunk, f[(u + 3) & 3]);
@@ -351,14 +356,17 @@ constexpr int kSampleBlock = 4 * kTkThreads;      // 1024 entries, one 16-byte l
 constexpr int kSampleMinRow = 16384;
 static_assert(kSampleBlocks * kSampleBlock <= kCap, "the sample is staged in the candidate buffer");
 
-__device__ uint32_t sampled_threshold(TopkShared& sh, const float* row, int32_t n, int k) {
+__device__ __forceinline__ void load_sample(const float* row, int32_t n, f32x4 (&v)[kSampleBlocks]) {
   const int tid = threadIdx.x;
-  f32x4 v[kSampleBlocks];
 #pragma unroll
   for (int b = 0; b < kSampleBlocks; ++b) {
     const int32_t start = (int32_t)((int64_t)b * (n - kSampleBlock) / (kSampleBlocks - 1)) & ~3;
     v[b] = *(const f32x4*)(row + start + 4 * tid);  // start + kSampleBlock <= n; rows are 16-byte aligned
   }
+}
+
+__device__ uint32_t sampled_threshold(TopkShared& sh, const f32x4 (&v)[kSampleBlocks], int32_t n, int k) {
+  const int tid = threadIdx.x;
 #pragma unroll
   for (int b = 0; b < kSampleBlocks; ++b)
     *(i32x4*)&sh.key[b * kSampleBlock + 4 * tid] = i32x4{(int)order_key(v[b][0]), (int)order_key(v[b][1]),
@@ -454,14 +462,24 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const int32_t* __restr
   const float* row = scores + (int64_t)blockIdx.x * ld;
   const ScoreSrc src{row, 0, n};
   int cnt = -1;
+  ScoreSrc::Fetch f[4];
   if (n >= kSampleMinRow) {
-    const uint32_t ts = sampled_threshold(sh, row, n, k);
+    // the sample's loads, then the stream's first chunks (in flight while the
+    // sample is ranked: waiting for the sample leaves them outstanding)
+    f32x4 v[kSampleBlocks];
+    load_sample(row, n, v);
+    __builtin_amdgcn_sched_barrier(0);  // keep the sample's loads older than the stream's
+    prime_ring(src, f);
+    const uint32_t ts = sampled_threshold(sh, v, n, k);
     int admitted;
-    const int c = stream_select(sh, src, n, k, ts > 0u, ts - 1u, &admitted);  // admits keys >= ts
+    const int c = stream_select(sh, src, f, n, k, ts > 0u, ts - 1u, &admitted);  // admits keys >= ts
     if (admitted >= k) cnt = c;
     __syncthreads();
   }
-  if (cnt < 0) cnt = stream_select(sh, src, n, k);
+  if (cnt < 0) {
+    prime_ring(src, f);
+    cnt = stream_select(sh, src, f, n, k);
+  }
   for (int e = tid; e < k; e += kTkThreads) out[e] = e < cnt ? sh.pos[e] : -1;
 }
 
@@ -487,7 +505,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_segment_kernel(const int32_t*
   int cnt = 0;
   if (lo < hi) {
     const ScoreSrc src{scores + (int64_t)rl * ld, lo, hi};
-    cnt = stream_select(sh, src, hi - lo, k);
+    ScoreSrc::Fetch f[4];
+    prime_ring(src, f);
+    cnt = stream_select(sh, src, f, hi - lo, k);
   }
   for (int e = threadIdx.x; e < k; e += kTkThreads) {
     okey[e] = e < cnt ? buf_key<ScoreSrc::kRaw>(sh.key[e]) : 0u;
@@ -513,7 +533,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(const int32_t* _
     return;
   }
   const CandSrc src{ckey + (int64_t)rl * nseg * kp, cpos + (int64_t)rl * nseg * kp, nseg * kp};
-  const int cnt = stream_select(sh, src, nseg * kp, k);
+  CandSrc::Fetch f[4];
+  prime_ring(src, f);
+  const int cnt = stream_select(sh, src, f, nseg * kp, k);
   for (int e = threadIdx.x; e < k; e += kTkThreads) out[e] = e < cnt ? sh.pos[e] : -1;
 }
 

@@ -184,3 +184,28 @@ def test_long_rows_sampled_threshold(dsa):
             s[r, start:start + rank // 4 + 1] = 100.0                  # the sample's top ranks: too high
     got, ref = _run(dsa, p, s, k)
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("k", [512, 2048])
+def test_special_values_on_the_threshold(dsa, k):
+    """Scores drawn from a few special floats (both infinities, the largest
+    finite and smallest normal magnitudes, denormals, both zeros, NaN) in
+    per-row mixtures, so that the k-th key and the running thresholds land on
+    them.  The prefill filter compares floats against the smallest float above
+    each threshold key; it must admit exactly the keys above it, on the short
+    rows' plain stream and on the long rows' sampled threshold alike."""
+    announce("topk special values", k)
+    p = _problem([20000, 6000, 40000], [8, 8, 8], k)
+    rng = np.random.default_rng(77 + k)
+    vals = np.array([-np.inf, -3.4e38, -1.0, -1e-45, -0.0, 0.0, 1e-45, 3e-45, 1.1754944e-38, 1.0, 3.4e38,
+                     np.inf, np.nan], dtype=np.float32)
+    s = np.empty((p.total_q, _ld(p)), np.float32)
+    for r in range(p.total_q):
+        w = rng.dirichlet(np.full(len(vals), 0.3))
+        s[r] = vals[rng.choice(len(vals), size=s.shape[1], p=w)]
+    # a few rows with fewer than k entries above -inf or above NaN
+    s[2] = np.where(rng.random(s.shape[1]) < 0.005, 1.0, -np.inf)
+    s[10] = np.where(rng.random(s.shape[1]) < 0.005, 0.0, np.nan)
+    s[17] = np.where(rng.random(s.shape[1]) < 0.5, 1e-45, -0.0)
+    got, ref = _run(dsa, p, s, k)
+    assert np.array_equal(got, ref)

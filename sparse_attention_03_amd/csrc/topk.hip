@@ -6,16 +6,17 @@
 // score descending, ties to the lower position, -0 == +0, NaN lowest.
 //
 // One workgroup per score row, one pass over the row (few long rows -- decode
-// batches -- split each row into segments first, see below).  Scores become
-// order-preserving 32-bit keys.  The row is streamed in 2048-element chunks;
-// candidates (key, position) that beat the running threshold are appended to
-// an LDS buffer in position order (block-wide exclusive scan, so the buffer
-// stays sorted by position).  When the buffer would overflow it is cut to
-// exactly k entries by a histogram refinement over the buffer's own key
-// range (LDS histograms, at most four passes) and a stable filter; the k-th key becomes the new threshold, and
+// batches -- split each row into segments first, see below).  The order is
+// that of order-preserving 32-bit keys.  The row is streamed in 2048-element
+// chunks; elements that beat the running threshold (one float comparison
+// against the smallest float above the threshold key) are appended to an LDS
+// buffer in position order, so the buffer stays sorted by position.  When the
+// buffer would overflow it is cut to exactly k entries by a histogram
+// refinement over the buffer's own key range (LDS histograms, at most four
+// passes) and a stable filter; the k-th key becomes the new threshold, and
 // later elements (larger positions) must beat it strictly.  The final cut
-// leaves the k winners already in ascending position order.  Integer work
-// only: the selection is exact.
+// leaves the k winners already in ascending position order.  Every decision
+// is exact: key comparisons, or float comparisons equivalent to them.
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 

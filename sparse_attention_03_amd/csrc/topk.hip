@@ -70,7 +70,7 @@ __device__ __forceinline__ uint32_t buf_key(uint32_t v) {
 struct TopkShared {
   uint32_t key[kCap];
   int32_t pos[kCap];
-  int hist[kHistBins];
+  int hist[3][kHistBins];       // one per histogram pass, in rotation
   int wave_sum[2][kTkWaves];   // double-buffered: one barrier per scan
   int fcnt[2][kTkWaves];       // per-wave counts of the cut's filter
   uint32_t red[2][kTkWaves];
@@ -95,6 +95,27 @@ __device__ __forceinline__ int wave_excl_prefix_small(int v, int& wave_total) {
   return pre;
 }
 
+// Wave-wide inclusive scan with op over lanes 0 .. 63 (every lane active):
+// shifts within each 16-lane row, then the row totals carried across rows by
+// broadcasts of lanes 15 and 31.  DPP moves, no LDS round trips.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t x, uint32_t ident, Op op) {
+  const int id = (int)ident;
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_dpp(x, 0xffffffffu, [](uint32_t a, uint32_t b) { return min(a, b); }), 63);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_dpp(x, 0u, [](uint32_t a, uint32_t b) { return max(a, b); }), 63);
+}
+
 // The k-th best key T of the first `cnt` (>= k) buffer entries, and in `need`
 // how many of the entries equal to T rank among the k best.  T is located by
 // histogram refinement over the buffer's own key range: each pass splits the
@@ -102,10 +123,13 @@ __device__ __forceinline__ int wave_excl_prefix_small(int v, int& wave_total) {
 // power-of-two bins, so clustered scores still spread over the bins; at most
 // four passes, none when every key is equal.  After max_passes passes the
 // lower end of the interval is returned instead: a key at most T, with `need`
-// then meaningless.
+// then meaningless.  One barrier per pass: the histograms rotate over three
+// buffers (a pass clears the next one, last read two passes before), and
+// every wave scans the histogram itself.
 template <bool RAW>
 __device__ uint32_t kth_key(TopkShared& sh, int cnt, int k, int& need, int max_passes = 4) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  static_assert(kHistBins == kTkThreads, "one histogram bin cleared per thread");
   // the thread's keys (entries tid + 256 j) stay in registers for every pass
   uint32_t kr[kSegMax];
   bool kv[kSegMax];
@@ -120,57 +144,59 @@ __device__ uint32_t kth_key(TopkShared& sh, int cnt, int k, int& need, int max_p
       mx = max(mx, kr[j]);
     }
   }
-  for (int o = 32; o >= 1; o >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
   if (lane == 0) { sh.red[0][wave] = mn; sh.red[1][wave] = mx; }
+  sh.hist[0][tid] = 0;
   __syncthreads();
   uint32_t lo = sh.red[0][0], hi = sh.red[1][0];
 #pragma unroll
   for (int w = 1; w < kTkWaves; ++w) { lo = min(lo, sh.red[0][w]); hi = max(hi, sh.red[1][w]); }
   need = k;  // entries of [lo, hi] still to take, counted from the top
+  int hb = 0;
   for (int pass = 0; hi > lo && pass < max_passes; ++pass) {
     const uint32_t span = hi - lo;
     const int bits = 32 - __clz(span);
     const int shift = bits > kHistBits ? bits - kHistBits : 0;
     const int nbins = (int)(span >> shift) + 1;  // <= kHistBins
-#pragma unroll
-    for (int j = 0; j < kHistBins / kTkThreads; ++j) sh.hist[tid + kTkThreads * j] = 0;
-    __syncthreads();
+    int* hist = sh.hist[hb];
 #pragma unroll
     for (int j = 0; j < kSegMax; ++j)
-      if (kv[j] && kr[j] >= lo && kr[j] <= hi) atomicAdd(&sh.hist[(kr[j] - lo) >> shift], 1);
+      if (kv[j] && kr[j] >= lo && kr[j] <= hi) atomicAdd(&hist[(kr[j] - lo) >> shift], 1);
+    hb = hb == 2 ? 0 : hb + 1;
+    sh.hist[hb][tid] = 0;
     __syncthreads();
-    if (wave == 0) {
-      // lane l owns bins nbins-1-B l .. nbins-B-B l (descending key order, B = kBinsPerLane)
-      int c[kBinsPerLane], sum = 0;
+    // lane l owns bins nbins-1-B l .. nbins-B-B l (descending key order, B = kBinsPerLane)
+    int c[kBinsPerLane], sum = 0;
+#pragma unroll
+    for (int j = 0; j < kBinsPerLane; ++j) {
+      const int b = nbins - 1 - kBinsPerLane * lane - j;
+      c[j] = b >= 0 ? hist[b] : 0;
+      sum += c[j];
+    }
+    const int incl = (int)wave_scan_dpp((uint32_t)sum, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+    const int excl = incl - sum;
+    const bool mine = excl < need && need <= incl;  // exactly one lane: T lies in [lo, hi]
+    int digit = 0, rest = 0;
+    if (mine) {
+      int run = excl;
 #pragma unroll
       for (int j = 0; j < kBinsPerLane; ++j) {
-        const int b = nbins - 1 - kBinsPerLane * lane - j;
-        c[j] = b >= 0 ? sh.hist[b] : 0;
-        sum += c[j];
-      }
-      const int incl = wave_inclusive_scan(sum);
-      const int excl = incl - sum;
-      if (excl < need && need <= incl) {
-        int run = excl;
-#pragma unroll
-        for (int j = 0; j < kBinsPerLane; ++j) {
-          if (run < need && need <= run + c[j]) {
-            sh.digit = nbins - 1 - kBinsPerLane * lane - j;
-            sh.need = need - run;
-          }
-          run += c[j];
+        if (run < need && need <= run + c[j]) {
+          digit = nbins - 1 - kBinsPerLane * lane - j;
+          rest = need - run;
         }
+        run += c[j];
       }
     }
-    __syncthreads();
-    const uint32_t blo = lo + ((uint32_t)sh.digit << shift);
+    const int owner = (int)__builtin_ctzll(__ballot(mine));
+    digit = __builtin_amdgcn_readlane(digit, owner);
+    rest = __builtin_amdgcn_readlane(rest, owner);
+    const uint32_t blo = lo + ((uint32_t)digit << shift);
     const uint32_t bhi = blo + ((1u << shift) - 1u);
     lo = blo;
     hi = min(hi, bhi);
-    need = sh.need;
+    need = rest;
   }
   return lo;
 }
@@ -274,7 +300,8 @@ __device__ __forceinline__ int block_base(const uint64_t (&m)[kPer], TopkShared&
 // f: the ring, its first three chunks already fetched (prime_ring), so that a
 // caller can overlap their latency with other work.  tau0 (have_tau0): start
 // with the threshold tau0 -- only keys above it are admitted; *admitted: how
-// many entries were admitted in all.
+// many entries were admitted in all.  Without final_cut the buffer is left
+// with up to kCap entries that hold the k best, cut only to make room.
 template <class Src>
 __device__ __forceinline__ void prime_ring(const Src& src, typename Src::Fetch (&f)[4]) {
   src.fetch(0, f[0]);
@@ -284,7 +311,8 @@ __device__ __forceinline__ void prime_ring(const Src& src, typename Src::Fetch (
 
 template <class Src>
 __device__ int stream_select(TopkShared& sh, const Src& src, typename Src::Fetch (&f)[4], int32_t count, int k,
-                             bool have_tau0 = false, uint32_t tau0 = 0, int* admitted = nullptr) {
+                             bool have_tau0 = false, uint32_t tau0 = 0, int* admitted = nullptr,
+                             bool final_cut = true) {
   constexpr bool RAW = Src::kRaw;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int cnt = 0, adm = 0;
@@ -339,7 +367,7 @@ __device__ int stream_select(TopkShared& sh, const Src& src, typename Src::Fetch
   }
   __syncthreads();
   if (admitted) *admitted = adm;
-  if (cnt > k) {
+  if (final_cut && cnt > k) {
     cut_to_k<RAW>(sh, cnt, k, parity);
     cnt = k;
   }
@@ -366,7 +394,10 @@ __device__ __forceinline__ void load_sample(const float* row, int32_t n, f32x4 (
   }
 }
 
-__device__ uint32_t sampled_threshold(TopkShared& sh, const f32x4 (&v)[kSampleBlocks], int32_t n, int k) {
+// passes: histogram passes of the ranking; after one, the lower end of the
+// bin holding that rank, which admits a few more entries.
+__device__ uint32_t sampled_threshold(TopkShared& sh, const f32x4 (&v)[kSampleBlocks], int32_t n, int k,
+                                      int passes) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int b = 0; b < kSampleBlocks; ++b)
@@ -376,9 +407,7 @@ __device__ uint32_t sampled_threshold(TopkShared& sh, const f32x4 (&v)[kSampleBl
   constexpr int m = kSampleBlocks * kSampleBlock;
   const int rank = (int)min((int64_t)m, 3LL * k * m / (2LL * n) + 8);
   int need;
-  // one pass: the lower end of the bin holding that rank, which only admits
-  // a few more entries
-  return kth_key<false>(sh, m, rank, need, 1);
+  return kth_key<false>(sh, m, rank, need, passes);
 }
 
 // Elements are the scores of one row at positions [lo, hi).  The filter
@@ -419,32 +448,6 @@ struct ScoreSrc {
   }
 };
 
-// Elements are (key, position) candidates; position -1 marks padding.
-struct CandSrc {
-  static constexpr bool kRaw = false;
-  struct Fetch { uint32_t k[kPer]; int32_t p[kPer]; };
-  const uint32_t* key;
-  const int32_t* pos;
-  int32_t count;
-  __device__ __forceinline__ void fetch(int32_t c0, Fetch& f) const {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int32_t i = c0 + wave * (64 * kPer) + lane;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const bool in = i + 64 * j < count;
-      f.k[j] = in ? key[i + 64 * j] : 0u;
-      f.p[j] = in ? pos[i + 64 * j] : -1;
-    }
-  }
-  __device__ __forceinline__ void admit(const Fetch& f, int32_t, bool, bool have_tau, uint32_t tau, float,
-                                        uint64_t (&m)[kPer]) const {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) m[j] = __ballot(f.p[j] >= 0 && (!have_tau || f.k[j] > tau));
-  }
-  __device__ __forceinline__ uint32_t value(const Fetch& f, int j) const { return f.k[j]; }
-  __device__ __forceinline__ int32_t position(const Fetch& f, int32_t, int j) const { return f.p[j]; }
-};
-
 // One workgroup per row: the whole selection in one pass over the row.
 __global__ __launch_bounds__(kTkThreads) void topk_kernel(const int32_t* __restrict__ cu_q,
                                                           const int32_t* __restrict__ cu_k, int32_t num_seqs,
@@ -471,7 +474,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const int32_t* __restr
     load_sample(row, n, v);
     __builtin_amdgcn_sched_barrier(0);  // keep the sample's loads older than the stream's
     prime_ring(src, f);
-    const uint32_t ts = sampled_threshold(sh, v, n, k);
+    const uint32_t ts = sampled_threshold(sh, v, n, k, 1);
     int admitted;
     const int c = stream_select(sh, src, f, n, k, ts > 0u, ts - 1u, &admitted);  // admits keys >= ts
     if (admitted >= k) cnt = c;
@@ -484,60 +487,144 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const int32_t* __restr
   for (int e = tid; e < k; e += kTkThreads) out[e] = e < cnt ? sh.pos[e] : -1;
 }
 
-// Few long rows: phase 1 selects the top k (>= the row's k_row) of each of
-// `nseg` segments of a row (the global winners are winners of their segment,
-// so nothing is lost), keeping (key, position) in position order, padded with
-// position -1.
+// Few long rows, phase 1: each row is cut into `nseg` segments of seg_len
+// entries, one workgroup each.  Every workgroup of a row derives the same
+// threshold from the row's sample (rows of kSegSampleMinRow entries or more;
+// shorter rows take none) and keeps the entries of its segment that reach it;
+// should they overflow the buffer, it is cut to the segment's k best, which
+// keeps every row winner of the segment.  Written per (row, segment), in a
+// slot of `cap` (= min(kCap, seg_len)) entries: the kept entries' keys and
+// positions in position order, and (count, admitted).
+constexpr int kSegSampleMinRow = kSampleBlocks * kSampleBlock;  // the sample's blocks tile such a row
+constexpr int kMaxSegs = 64;                                     // segments per row (one lane each in the merge)
+
 __global__ __launch_bounds__(kTkThreads) void topk_segment_kernel(const int32_t* __restrict__ cu_q,
                                                                   const int32_t* __restrict__ cu_k, int32_t num_seqs,
                                                                   int32_t row_begin, const float* __restrict__ scores,
-                                                                  int64_t ld, int32_t k_row, int32_t k,
-                                                                  int32_t seg_len,
-                                                                  uint32_t* __restrict__ ckey,
-                                                                  int32_t* __restrict__ cpos) {
+                                                                  int64_t ld, int32_t k, int32_t seg_len,
+                                                                  int32_t cap, uint32_t* __restrict__ ckey,
+                                                                  int32_t* __restrict__ cpos,
+                                                                  int32_t* __restrict__ cstat) {
   __shared__ TopkShared sh;
   const int32_t rl = blockIdx.x, seg = blockIdx.y, nseg = gridDim.y;
   const RowInfo ri = locate_row_wave(load_seq_table(cu_q, cu_k, num_seqs), cu_q, cu_k, row_begin + rl);
   const int32_t n = ri.pos + 1;
-  if (n <= k_row) return;  // the merge writes every candidate directly
+  if (n <= k) return;  // the merge writes every position directly
   const int32_t lo = seg * seg_len, hi = min(n, lo + seg_len);
-  uint32_t* okey = ckey + ((int64_t)rl * nseg + seg) * k;
-  int32_t* opos = cpos + ((int64_t)rl * nseg + seg) * k;
-  int cnt = 0;
+  const int64_t slot = (int64_t)rl * nseg + seg;
+  int cnt = 0, adm = 0;
   if (lo < hi) {
-    const ScoreSrc src{scores + (int64_t)rl * ld, lo, hi};
+    const float* row = scores + (int64_t)rl * ld;
+    const ScoreSrc src{row, lo, hi};
     ScoreSrc::Fetch f[4];
-    prime_ring(src, f);
-    cnt = stream_select(sh, src, f, hi - lo, k);
+    if (n >= kSegSampleMinRow) {
+      f32x4 v[kSampleBlocks];
+      load_sample(row, n, v);
+      __builtin_amdgcn_sched_barrier(0);  // keep the sample's loads older than the stream's
+      prime_ring(src, f);
+      // two passes: a tighter threshold keeps the row's lists within one buffer
+      const uint32_t ts = sampled_threshold(sh, v, n, k, 2);
+      cnt = stream_select(sh, src, f, hi - lo, k, ts > 0u, ts - 1u, &adm, false);  // admits keys >= ts
+    } else {
+      prime_ring(src, f);
+      cnt = stream_select(sh, src, f, hi - lo, k, false, 0u, &adm, false);
+    }
   }
-  for (int e = threadIdx.x; e < k; e += kTkThreads) {
-    okey[e] = e < cnt ? buf_key<ScoreSrc::kRaw>(sh.key[e]) : 0u;
-    opos[e] = e < cnt ? sh.pos[e] : -1;
+  uint32_t* okey = ckey + slot * cap;
+  int32_t* opos = cpos + slot * cap;
+  for (int e = threadIdx.x; e < cnt; e += kTkThreads) {
+    okey[e] = buf_key<ScoreSrc::kRaw>(sh.key[e]);
+    opos[e] = sh.pos[e];
+  }
+  if (threadIdx.x == 0) {
+    cstat[2 * slot] = cnt;
+    cstat[2 * slot + 1] = adm;
   }
 }
 
-// Phase 2: the same selection over the row's nseg * kp candidates (kp = k
-// rounded up to a multiple of 8, the padded length of each segment's list).
+// Phase 2, one workgroup per row.  The threshold was valid when at least k
+// entries of the row reached it: when no segment cut its list, the admitted
+// counts add up to exactly that number, and a segment that did cut alone held
+// more than k.  Then the row's k-th key is at least the threshold, every
+// winner is in its segment's list, and the lists, concatenated in segment
+// order (so in position order), are cut to the k best.  Otherwise, or when
+// the lists exceed one buffer, the row is streamed again without a threshold.
 __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(const int32_t* __restrict__ cu_q,
                                                                 const int32_t* __restrict__ cu_k, int32_t num_seqs,
-                                                                int32_t row_begin, int32_t nseg, int32_t k,
-                                                                int32_t kp, const uint32_t* __restrict__ ckey,
+                                                                int32_t row_begin, const float* __restrict__ scores,
+                                                                int64_t ld, int32_t nseg, int32_t k, int32_t cap,
+                                                                const uint32_t* __restrict__ ckey,
                                                                 const int32_t* __restrict__ cpos,
+                                                                const int32_t* __restrict__ cstat,
                                                                 int32_t* __restrict__ idx) {
   __shared__ TopkShared sh;
   const int32_t rl = blockIdx.x;
   const RowInfo ri = locate_row_wave(load_seq_table(cu_q, cu_k, num_seqs), cu_q, cu_k, row_begin + rl);
   const int32_t n = ri.pos + 1;
+  const int tid = threadIdx.x;
   int32_t* out = idx + (int64_t)rl * k;
   if (n <= k) {
-    for (int e = threadIdx.x; e < k; e += kTkThreads) out[e] = e < n ? e : -1;
+    for (int e = tid; e < k; e += kTkThreads) out[e] = e < n ? e : -1;
     return;
   }
-  const CandSrc src{ckey + (int64_t)rl * nseg * kp, cpos + (int64_t)rl * nseg * kp, nseg * kp};
-  CandSrc::Fetch f[4];
-  prime_ring(src, f);
-  const int cnt = stream_select(sh, src, f, nseg * kp, k);
-  for (int e = threadIdx.x; e < k; e += kTkThreads) out[e] = e < cnt ? sh.pos[e] : -1;
+  const int64_t s0 = (int64_t)rl * nseg;
+  // list offsets: exclusive prefix of the counts over the segments (lane s of
+  // wave 0), kept in sh.hist[0 .. nseg]
+  if (tid < 64) {
+    const int c = tid < nseg ? cstat[2 * (s0 + tid)] : 0;
+    const int a = tid < nseg ? cstat[2 * (s0 + tid) + 1] : 0;
+    const int incl = wave_inclusive_scan(c);
+    int adm = a;
+    for (int o = 32; o >= 1; o >>= 1) adm += __shfl_xor(adm, o);
+    if (tid < nseg) sh.hist[0][tid] = incl - c;
+    if (tid == 63) {
+      sh.hist[0][nseg] = incl;
+      sh.digit = incl;             // every list's entries
+      sh.need = adm >= k ? 1 : 0;  // the threshold was valid
+    }
+  }
+  __syncthreads();
+  const int total = sh.digit;
+  int cnt;
+  if (sh.need && total <= kCap) {
+    // where each buffer entry comes from (offset in the row's lists), written
+    // segment by segment into sh.pos: then one LDS read per entry locates it
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int sgi = wave; sgi < nseg; sgi += kTkWaves) {
+      const int b = sh.hist[0][sgi], c = sh.hist[0][sgi + 1] - b;
+      for (int o = lane; o < c; o += 64) sh.pos[b + o] = sgi * cap + o;
+    }
+    __syncthreads();
+    uint32_t kk[kSegMax];
+    int32_t pp[kSegMax];
+    const uint32_t* lkey = ckey + s0 * cap;
+    const int32_t* lpos = cpos + s0 * cap;
+#pragma unroll
+    for (int j = 0; j < kSegMax; ++j) {
+      const int e = tid + kTkThreads * j;
+      const int src = e < total ? sh.pos[e] : 0;  // every thread reads its own entries only
+      kk[j] = lkey[src];
+      pp[j] = lpos[src];
+    }
+#pragma unroll
+    for (int j = 0; j < kSegMax; ++j) {
+      const int e = tid + kTkThreads * j;
+      if (e < total) { sh.key[e] = kk[j]; sh.pos[e] = pp[j]; }
+    }
+    __syncthreads();
+    cnt = total;
+    if (cnt > k) {
+      int parity = 0;
+      cut_to_k<false>(sh, cnt, k, parity);
+      cnt = k;
+    }
+  } else {
+    const ScoreSrc src{scores + (int64_t)rl * ld, 0, n};
+    ScoreSrc::Fetch f[4];
+    prime_ring(src, f);
+    cnt = stream_select(sh, src, f, n, k);
+  }
+  for (int e = tid; e < k; e += kTkThreads) out[e] = e < cnt ? sh.pos[e] : -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -805,51 +892,43 @@ __global__ __launch_bounds__(kRxThreads) void topk_radix_kernel(const int32_t* _
 namespace {
 
 // How a batch is selected:
-//   kStream:     one 256-thread workgroup streams each row (many rows: the
-//                rows fill the machine, and each is read from HBM once);
-//   kRadix:      few rows of at most kRxCap entries: LDS radix select per row;
-//   kRadixSeg:   few longer rows: radix select per segment, then over the
-//                segments' winners;
-//   kStreamSeg:  few rows too long for the radix merge: streaming selection
-//                per segment, then over the segments' winners.
-enum TopkKind { kStream, kRadix, kRadixSeg, kStreamSeg };
+//   kStream:   one 256-thread workgroup streams each row (many rows: the rows
+//              fill the machine, and each is read from HBM once);
+//   kRadix:    few rows of at most kRxCap entries, too short to split: LDS
+//              radix select per row;
+//   kSegment:  few longer rows: sampled segments, then the merge of their
+//              lists (topk_segment_kernel, topk_merge_kernel).
+enum TopkKind { kStream, kRadix, kSegment };
 struct TopkPlan {
   TopkKind kind;
   int nseg;
   int32_t seg_len;
 };
 
+constexpr int kSegWgsPerCu = 2;  // segment workgroups per CU the split aims for
+
 TopkPlan topk_plan(int rows, int max_ctx, int k, int num_cus) {
   TopkPlan p{kStream, 1, 0};
   if (rows <= 0 || rows >= num_cus) return p;
-  // Radix select: enough (row, segment) workgroups to cover the machine, but
-  // segments of at least 4k entries (so that the segment pass discards most of
-  // them); a segment must fit the registers, and the winners of all segments
-  // of a row must fit one more radix pass.
-  const int kp = (k + kPer - 1) / kPer * kPer;
-  const int lo = (max_ctx + kRxCap - 1) / kRxCap;
-  const int hi = kRxCapPairs / kp;
-  int nseg = min((num_cus + rows - 1) / rows, max_ctx / (4 * k));
-  nseg = max(nseg, lo);
-  if (nseg <= 1) {
+  // one radix workgroup per row when the rows fit one and splitting would
+  // not add workgroups: the machine is covered or segments would be shorter
+  // than 4k entries
+  const int by_cus = (num_cus + rows - 1) / rows, by_len = max_ctx / (4 * k);
+  if (max_ctx <= kRxCap && min(by_cus, by_len) <= 1) {
     p.kind = kRadix;
     return p;
   }
-  if (nseg <= hi) {
-    p.kind = kRadixSeg;
-    p.nseg = nseg;
-    p.seg_len = ((max_ctx + nseg - 1) / nseg + 3) / 4 * 4;  // <= kRxCap
+  // segments of whole chunks, about kSegWgsPerCu workgroups per CU
+  int ns = (kSegWgsPerCu * num_cus + rows - 1) / rows;
+  ns = min(min(ns, kMaxSegs), max(1, max_ctx / kChunk));
+  if (ns <= 1 && max_ctx <= kRxCap) {
+    p.kind = kRadix;
     return p;
   }
-  // rows too long for the radix merge: streaming selection per segment
-  int ns = (2 * num_cus + rows - 1) / rows;
-  const int by_len = max_ctx / (4 * k);
-  if (ns > by_len) ns = by_len;
-  if (ns <= 1) return p;
-  p.kind = kStreamSeg;
-  p.nseg = ns;
   const int32_t len = (max_ctx + ns - 1) / ns;
   p.seg_len = (len + kChunk - 1) / kChunk * kChunk;
+  p.nseg = (max_ctx + p.seg_len - 1) / p.seg_len;  // no trailing empty segment
+  p.kind = kSegment;
   return p;
 }
 
@@ -880,11 +959,26 @@ hipError_t launch_radix(const TopkLaunch& L, dim3 grid, int32_t seg_len, int32_t
 
 bool topk_may_segment(int max_ctx, int k) { return k > 0 && (max_ctx > kRxCap || max_ctx / (4 * k) > 1); }
 
+namespace {
+// workspace of the segment plan: keys, positions, (count, admitted) per
+// (row, segment)
+struct SegWorkspace {
+  size_t off_pos, off_stat, bytes;
+};
+int seg_cap(const TopkPlan& p) { return min(kCap, (int)p.seg_len); }
+SegWorkspace seg_workspace(int rows, const TopkPlan& p) {
+  const size_t n = (size_t)rows * p.nseg * (size_t)seg_cap(p);
+  SegWorkspace w;
+  w.off_pos = (n * 4 + 255) / 256 * 256;
+  w.off_stat = 2 * w.off_pos;
+  w.bytes = w.off_stat + ((size_t)rows * p.nseg * 8 + 255) / 256 * 256;
+  return w;
+}
+}  // namespace
+
 size_t topk_workspace_bytes(int rows, int max_ctx, int k, int num_cus) {
   const TopkPlan p = topk_plan(rows, max_ctx, k, num_cus);
-  if (p.kind != kRadixSeg && p.kind != kStreamSeg) return 0;
-  const size_t n = (size_t)rows * p.nseg * (size_t)((k + kPer - 1) / kPer * kPer);
-  return 2 * ((n * 4 + 255) / 256 * 256);
+  return p.kind == kSegment ? seg_workspace(rows, p).bytes : 0;
 }
 
 hipError_t launch_topk(const TopkLaunch& L, hipStream_t s) {
@@ -899,23 +993,17 @@ hipError_t launch_topk(const TopkLaunch& L, hipStream_t s) {
   }
   if (p.kind == kRadix)
     return launch_radix<false, false>(L, dim3((unsigned)rows), kRxCap, 0, L.b.max_ctx, nullptr, nullptr, s);
-  // candidate lists are padded to a multiple of kPer so that loads stay aligned
-  const int kp = (L.k + kPer - 1) / kPer * kPer;
-  const size_t n = (size_t)rows * p.nseg * kp;
+  const SegWorkspace w = seg_workspace(rows, p);
+  const int cap = seg_cap(p);
   uint32_t* ckey = (uint32_t*)L.ws;
-  int32_t* cpos = (int32_t*)((char*)L.ws + (n * 4 + 255) / 256 * 256);
-  if (p.kind == kRadixSeg) {
-    hipError_t e = launch_radix<false, true>(L, dim3((unsigned)rows, (unsigned)p.nseg), p.seg_len, kp,
-                                             min(p.seg_len, L.b.max_ctx), ckey, cpos, s);
-    if (e != hipSuccess) return e;
-    return launch_radix<true, false>(L, dim3((unsigned)rows), 0, p.nseg * kp, p.nseg * kp, ckey, cpos, s);
-  }
+  int32_t* cpos = (int32_t*)((char*)L.ws + w.off_pos);
+  int32_t* cstat = (int32_t*)((char*)L.ws + w.off_stat);
   hipLaunchKernelGGL(topk_segment_kernel, dim3((unsigned)rows, (unsigned)p.nseg), dim3(kTkThreads), 0, s, L.b.cu_q,
-                     L.b.cu_k, L.b.num_seqs, L.b.row_begin, L.scores, L.ld, L.k, kp, p.seg_len, ckey, cpos);
+                     L.b.cu_k, L.b.num_seqs, L.b.row_begin, L.scores, L.ld, L.k, p.seg_len, cap, ckey, cpos, cstat);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)rows), dim3(kTkThreads), 0, s, L.b.cu_q, L.b.cu_k,
-                     L.b.num_seqs, L.b.row_begin, p.nseg, L.k, kp, ckey, cpos, L.idx);
+                     L.b.num_seqs, L.b.row_begin, L.scores, L.ld, p.nseg, L.k, cap, ckey, cpos, cstat, L.idx);
   return hipGetLastError();
 }
 

@@ -139,14 +139,37 @@ def test_radix_segments_and_winner_merge(dsa, k):
     assert np.array_equal(got, ref)
 
 
-def test_rows_beyond_the_radix_merge(dsa):
-    """Few rows too long for the radix merge take the streaming segment path."""
+def test_very_long_rows_many_segments(dsa):
+    """Few very long rows: many segments per row, ties at the cut."""
     announce("topk streaming segments")
     k = 2048
     p = _problem([340000, 5000], [1, 1], k)
     rng = np.random.default_rng(31)
     s = rng.standard_normal((p.total_q, _ld(p))).astype(np.float32)
     s[0, ::3] = 2.5                                                      # ties at the cut
+    got, ref = _run(dsa, p, s, k)
+    assert np.array_equal(got, ref)
+
+
+def test_segment_threshold_fallbacks(dsa):
+    """Few long rows are split into segments that share the row's sampled
+    threshold.  A row whose sample blocks hold a few outsized scores gets a
+    threshold that fewer than k entries reach, so the merge must select that
+    row again without it; a row of small integers puts so many ties on the
+    threshold that the segments' lists overflow the merge's buffer; a row of
+    exactly the sample's size is sampled whole, one entry shorter not at all."""
+    announce("topk segment fallbacks")
+    k = 2048
+    ctx = [60000, 131072, 20000, 4096, 5000, 4095]
+    p = _problem(ctx, [1] * len(ctx), k)
+    rng = np.random.default_rng(60)
+    s = (0.14 + 0.03 * rng.standard_normal((p.total_q, _ld(p)))).astype(np.float32)
+    n = ctx[0]
+    rank = min(4096, 3 * k * 4096 // (2 * n) + 8)
+    for b in range(4):
+        start = (b * (n - 1024) // 3) & ~3
+        s[0, start:start + rank // 4 + 1] = 100.0                      # the sample's top ranks: too high
+    s[1] = rng.integers(-2, 3, _ld(p)).astype(np.float32)
     got, ref = _run(dsa, p, s, k)
     assert np.array_equal(got, ref)
 

@@ -68,15 +68,14 @@ __device__ __forceinline__ uint32_t buf_key(uint32_t v) {
 }
 
 struct TopkShared {
-  uint32_t key[kCap];
-  int32_t pos[kCap];
-  int hist[3][kHistBins];       // one per histogram pass, in rotation
+  alignas(16) uint32_t key[kCap];
+  alignas(16) int32_t pos[kCap];
+  int hist[3][kHistBins];      // one per histogram pass, in rotation
   int wave_sum[2][kTkWaves];   // double-buffered: one barrier per scan
-  int fcnt[2][kTkWaves];       // per-wave counts of the cut's filter
+  int fcnt[2][kTkWaves];       // wave totals of the cut's two scans
   uint32_t red[2][kTkWaves];
-  int digit;
-  int need;
-  int parity;
+  int list_total;              // the merge: entries in the row's lists
+  int list_valid;              // the merge: the row's threshold was valid
 };
 
 // Exclusive prefix over the lanes of a small non-negative count (< 2^NBITS),
@@ -116,34 +115,66 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan_dpp(x, 0u, [](uint32_t a, uint32_t b) { return max(a, b); }), 63);
 }
 
-// The k-th best key T of the first `cnt` (>= k) buffer entries, and in `need`
-// how many of the entries equal to T rank among the k best.  T is located by
-// histogram refinement over the buffer's own key range: each pass splits the
-// current interval [lo, hi] (known to hold T) into at most kHistBins equal
-// power-of-two bins, so clustered scores still spread over the bins; at most
-// four passes, none when every key is equal.  After max_passes passes the
-// lower end of the interval is returned instead: a key at most T, with `need`
-// then meaningless.  One barrier per pass: the histograms rotate over three
-// buffers (a pass clears the next one, last read two passes before), and
-// every wave scans the histogram itself.
+// Entries in registers for a cut: thread t holds entries kSegMax t ..
+// kSegMax t + kSegMax - 1 of the buffer, so that the thread order is the
+// position order; valid are the first nv = cnt - kSegMax t of them.
+__device__ __forceinline__ int thread_valid(int cnt) {
+  return min(max(cnt - kSegMax * (int)threadIdx.x, 0), kSegMax);
+}
+
 template <bool RAW>
-__device__ uint32_t kth_key(TopkShared& sh, int cnt, int k, int& need, int max_passes = 4) {
+__device__ __forceinline__ void load_keys(const TopkShared& sh, uint32_t (&kr)[kSegMax]) {
+  const int e0 = kSegMax * threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < kSegMax / 4; ++i) {
+    const i32x4 kv = *(const i32x4*)&sh.key[e0 + 4 * i];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int kb = kv[c];
+      kr[4 * i + c] = buf_key<RAW>((uint32_t)kb);
+    }
+  }
+}
+
+// Exclusive prefix of v over the workgroup's threads, and in `total` its sum;
+// slot: kTkWaves ints of LDS (one barrier).
+__device__ __forceinline__ int block_excl_scan(int v, int* slot, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = (int)wave_scan_dpp((uint32_t)v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+  if (lane == 63) slot[wave] = incl;
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    const int t = slot[w];
+    pre += w < wave ? t : 0;
+    tot += t;
+  }
+  total = tot;
+  return pre + incl - v;
+}
+
+// The k-th best key T among the keys kr[0 .. nv) of every thread (at least k
+// in all), and in `need` how many of the entries equal to T rank among the k
+// best.  T is located by histogram refinement over the keys' own range: each
+// pass splits the current interval [lo, hi] (known to hold T) into at most
+// kHistBins equal power-of-two bins, so clustered scores still spread over the
+// bins; at most four passes, none when every key is equal.  After max_passes
+// passes the lower end of the interval is returned instead: a key at most T,
+// with `need` then meaningless.  One barrier per pass: the histograms rotate
+// over three buffers (a pass clears the next one, last read two passes
+// before), and every wave scans the histogram itself.
+__device__ uint32_t kth_key(TopkShared& sh, const uint32_t (&kr)[kSegMax], int nv, int k, int& need,
+                            int max_passes = 4) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   static_assert(kHistBins == kTkThreads, "one histogram bin cleared per thread");
-  // the thread's keys (entries tid + 256 j) stay in registers for every pass
-  uint32_t kr[kSegMax];
-  bool kv[kSegMax];
   uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
-  for (int j = 0; j < kSegMax; ++j) {
-    const int e = tid + kTkThreads * j;
-    kv[j] = e < cnt;
-    kr[j] = kv[j] ? buf_key<RAW>(sh.key[e]) : 0u;
-    if (kv[j]) {
+  for (int j = 0; j < kSegMax; ++j)
+    if (j < nv) {
       mn = min(mn, kr[j]);
       mx = max(mx, kr[j]);
     }
-  }
   mn = wave_min_u32(mn);
   mx = wave_max_u32(mx);
   if (lane == 0) { sh.red[0][wave] = mn; sh.red[1][wave] = mx; }
@@ -162,7 +193,7 @@ __device__ uint32_t kth_key(TopkShared& sh, int cnt, int k, int& need, int max_p
     int* hist = sh.hist[hb];
 #pragma unroll
     for (int j = 0; j < kSegMax; ++j)
-      if (kv[j] && kr[j] >= lo && kr[j] <= hi) atomicAdd(&hist[(kr[j] - lo) >> shift], 1);
+      if (j < nv && kr[j] >= lo && kr[j] <= hi) atomicAdd(&hist[(kr[j] - lo) >> shift], 1);
     hb = hb == 2 ? 0 : hb + 1;
     sh.hist[hb][tid] = 0;
     __syncthreads();
@@ -201,62 +232,67 @@ __device__ uint32_t kth_key(TopkShared& sh, int cnt, int k, int& need, int max_p
   return lo;
 }
 
-// Cut the first `cnt` (>= k) buffer entries to the k best, keeping position
-// order; returns the k-th best key (the smallest kept key).  The filter: wave
-// w takes a contiguous range of 64-entry blocks (lane l: entry l of each
-// block, conflict-free LDS reads) into registers, ballots order the lanes and
-// one exchange of per-wave counts orders the waves; every read precedes the
-// barrier of that exchange, so the kept entries are written back in place.
-template <bool RAW>
-__device__ uint32_t cut_to_k(TopkShared& sh, int cnt, int k, int& parity) {
-  (void)parity;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Cut `cnt` (> k) entries held as above (keys kr; their positions are
+// fetched by pos_of(pr) only once ranked, which keeps them out of the
+// registers the histogram passes hold) to the k best and write them to the
+// buffer's first k slots in position order (keys as RAW says); returns the
+// k-th best key.  The stable filter: one scan of the per-thread counts of
+// keys equal to T ranks the ties in position order (the earliest `need` are
+// kept), a second scan of the kept counts gives each thread its output
+// offset.  The buffer may be the entries' own source: every read of it
+// (pos_of's included) precedes the second scan's barrier, every write follows.
+template <bool RAW, class PosOf>
+__device__ uint32_t cut_entries(TopkShared& sh, const uint32_t (&kr)[kSegMax], int cnt, int k, PosOf pos_of) {
+  const int nv = thread_valid(cnt);
   int need;
-  const uint32_t T = kth_key<RAW>(sh, cnt, k, need);
-  const int L = (cnt + 64 * kTkWaves - 1) / (64 * kTkWaves) * 64;  // <= 64 * kSegMax
-  const int w0 = min(wave * L, cnt), w1 = min(w0 + L, cnt);
-  uint32_t kk[kSegMax];
-  int32_t pp[kSegMax];
-  int gt = 0, eq = 0;
+  const uint32_t T = kth_key(sh, kr, nv, k, need);
+  int eq = 0;
+#pragma unroll
+  for (int j = 0; j < kSegMax; ++j) eq += j < nv && kr[j] == T;
+  int eq_tot;
+  int rank = block_excl_scan(eq, sh.fcnt[0], eq_tot);
+  uint32_t kept = 0;
+  int keep = 0;
 #pragma unroll
   for (int j = 0; j < kSegMax; ++j) {
-    const int e = w0 + 64 * j + lane;
-    const bool in = 64 * j < L && e < w1;
-    kk[j] = in ? buf_key<RAW>(sh.key[e]) : 0u;
-    pp[j] = in ? sh.pos[e] : -1;  // buffered positions are >= 0: -1 marks an empty slot
-    gt += __popcll(__ballot(in && kk[j] > T));
-    eq += __popcll(__ballot(in && kk[j] == T));
+    const bool is_eq = j < nv && kr[j] == T;
+    const bool kp = (j < nv && kr[j] > T) || (is_eq && rank < need);
+    rank += is_eq;
+    kept |= (uint32_t)kp << j;
+    keep += kp;
   }
-  if (lane == 0) { sh.fcnt[0][wave] = eq; sh.fcnt[1][wave] = gt; }
-  __syncthreads();
-  int eqrun = 0, keeprun = 0;
-  {
-    int eq_pre = 0;
+  int32_t pr[kSegMax];
+  pos_of(pr);
+  int keep_tot;
+  int o = block_excl_scan(keep, sh.fcnt[1], keep_tot);
 #pragma unroll
-    for (int w = 0; w < kTkWaves; ++w) {
-      const int e_w = sh.fcnt[0][w], g_w = sh.fcnt[1][w];
-      const int keep_w = g_w + min(max(need - eq_pre, 0), e_w);
-      if (w < wave) { eqrun += e_w; keeprun += keep_w; }
-      eq_pre += e_w;
+  for (int j = 0; j < kSegMax; ++j)
+    if ((kept >> j) & 1u) {
+      sh.key[o] = RAW ? key_bits(kr[j]) : kr[j];
+      sh.pos[o] = pr[j];
+      ++o;
     }
-  }
-#pragma unroll
-  for (int j = 0; j < kSegMax; ++j) {
-    const bool in = pp[j] >= 0;
-    const bool is_eq = in && kk[j] == T;
-    const uint64_t meq = __ballot(is_eq);
-    const int rank = eqrun + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(meq >> 32),
-                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)meq, 0u));
-    const bool kept = (in && kk[j] > T) || (is_eq && rank < need);
-    const uint64_t mk = __ballot(kept);
-    const int o = keeprun + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
-                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
-    if (kept) { sh.key[o] = RAW ? key_bits(kk[j]) : kk[j]; sh.pos[o] = pp[j]; }
-    eqrun += __popcll(meq);
-    keeprun += __popcll(mk);
-  }
   __syncthreads();
   return T;
+}
+
+// Cut the first `cnt` (> k) buffer entries to the k best, keeping position
+// order; returns the k-th best key (the smallest kept key).
+template <bool RAW>
+__device__ uint32_t cut_to_k(TopkShared& sh, int cnt, int k) {
+  uint32_t kr[kSegMax];
+  load_keys<RAW>(sh, kr);
+  return cut_entries<RAW>(sh, kr, cnt, k, [&](int32_t (&pr)[kSegMax]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kSegMax / 4; ++i) {
+      const i32x4 pv = *(const i32x4*)&sh.pos[kSegMax * threadIdx.x + 4 * i];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int pb = pv[c];
+        pr[4 * i + c] = pb;
+      }
+    }
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -310,7 +346,7 @@ __device__ __forceinline__ void prime_ring(const Src& src, typename Src::Fetch (
 }
 
 template <class Src>
-__device__ int stream_select(TopkShared& sh, const Src& src, typename Src::Fetch (&f)[4], int32_t count, int k,
+__device__ __forceinline__ int stream_select(TopkShared& sh, const Src& src, typename Src::Fetch (&f)[4], int32_t count, int k,
                              bool have_tau0 = false, uint32_t tau0 = 0, int* admitted = nullptr,
                              bool final_cut = true) {
   constexpr bool RAW = Src::kRaw;
@@ -334,7 +370,7 @@ __device__ int stream_select(TopkShared& sh, const Src& src, typename Src::Fetch
     int total;
     int base = block_base(m, sh, parity, total);
     if (cnt + total > kCap) {
-      tau = cut_to_k<RAW>(sh, cnt, k, parity);
+      tau = cut_to_k<RAW>(sh, cnt, k);
       tfloor = admit_floor(tau);
       have_tau = true;
       cnt = k;
@@ -368,7 +404,7 @@ __device__ int stream_select(TopkShared& sh, const Src& src, typename Src::Fetch
   __syncthreads();
   if (admitted) *admitted = adm;
   if (final_cut && cnt > k) {
-    cut_to_k<RAW>(sh, cnt, k, parity);
+    cut_to_k<RAW>(sh, cnt, k);
     cnt = k;
   }
   return cnt;
@@ -383,7 +419,6 @@ __device__ int stream_select(TopkShared& sh, const Src& src, typename Src::Fetch
 constexpr int kSampleBlocks = 4;
 constexpr int kSampleBlock = 4 * kTkThreads;      // 1024 entries, one 16-byte load per thread
 constexpr int kSampleMinRow = 16384;
-static_assert(kSampleBlocks * kSampleBlock <= kCap, "the sample is staged in the candidate buffer");
 
 __device__ __forceinline__ void load_sample(const float* row, int32_t n, f32x4 (&v)[kSampleBlocks]) {
   const int tid = threadIdx.x;
@@ -396,18 +431,18 @@ __device__ __forceinline__ void load_sample(const float* row, int32_t n, f32x4 (
 
 // passes: histogram passes of the ranking; after one, the lower end of the
 // bin holding that rank, which admits a few more entries.
-__device__ uint32_t sampled_threshold(TopkShared& sh, const f32x4 (&v)[kSampleBlocks], int32_t n, int k,
+__device__ __forceinline__ uint32_t sampled_threshold(TopkShared& sh, const f32x4 (&v)[kSampleBlocks], int32_t n, int k,
                                       int passes) {
-  const int tid = threadIdx.x;
+  static_assert(4 * kSampleBlocks == kSegMax, "the sample's keys fill one thread's registers");
+  uint32_t kr[kSegMax];
 #pragma unroll
   for (int b = 0; b < kSampleBlocks; ++b)
-    *(i32x4*)&sh.key[b * kSampleBlock + 4 * tid] = i32x4{(int)order_key(v[b][0]), (int)order_key(v[b][1]),
-                                                         (int)order_key(v[b][2]), (int)order_key(v[b][3])};
-  __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kr[4 * b + c] = order_key(v[b][c]);
   constexpr int m = kSampleBlocks * kSampleBlock;
   const int rank = (int)min((int64_t)m, 3LL * k * m / (2LL * n) + 8);
   int need;
-  return kth_key<false>(sh, m, rank, need, passes);
+  return kth_key(sh, kr, kSegMax, rank, need, passes);
 }
 
 // Elements are the scores of one row at positions [lo, hi).  The filter
@@ -579,44 +614,51 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(const int32_t* _
     if (tid < nseg) sh.hist[0][tid] = incl - c;
     if (tid == 63) {
       sh.hist[0][nseg] = incl;
-      sh.digit = incl;             // every list's entries
-      sh.need = adm >= k ? 1 : 0;  // the threshold was valid
+      sh.list_total = incl;
+      sh.list_valid = adm >= k ? 1 : 0;
     }
   }
   __syncthreads();
-  const int total = sh.digit;
+  const int total = sh.list_total;
   int cnt;
-  if (sh.need && total <= kCap) {
+  if (sh.list_valid && total <= kCap) {
     // where each buffer entry comes from (offset in the row's lists), written
-    // segment by segment into sh.pos: then one LDS read per entry locates it
+    // segment by segment into sh.pos; each thread then reads the sources of
+    // its own entries (kSegMax t .. kSegMax t + kSegMax - 1) and loads them
     const int wave = tid >> 6, lane = tid & 63;
     for (int sgi = wave; sgi < nseg; sgi += kTkWaves) {
       const int b = sh.hist[0][sgi], c = sh.hist[0][sgi + 1] - b;
       for (int o = lane; o < c; o += 64) sh.pos[b + o] = sgi * cap + o;
     }
     __syncthreads();
-    uint32_t kk[kSegMax];
-    int32_t pp[kSegMax];
+    const int nv = thread_valid(total);
     const uint32_t* lkey = ckey + s0 * cap;
     const int32_t* lpos = cpos + s0 * cap;
+    uint32_t kr[kSegMax];
+    int32_t pr[kSegMax];
 #pragma unroll
-    for (int j = 0; j < kSegMax; ++j) {
-      const int e = tid + kTkThreads * j;
-      const int src = e < total ? sh.pos[e] : 0;  // every thread reads its own entries only
-      kk[j] = lkey[src];
-      pp[j] = lpos[src];
-    }
+    for (int i = 0; i < kSegMax / 4; ++i) {
+      const i32x4 sv = *(const i32x4*)&sh.pos[kSegMax * tid + 4 * i];
 #pragma unroll
-    for (int j = 0; j < kSegMax; ++j) {
-      const int e = tid + kTkThreads * j;
-      if (e < total) { sh.key[e] = kk[j]; sh.pos[e] = pp[j]; }
+      for (int c = 0; c < 4; ++c) {
+        const int sb = sv[c];
+        const int src = 4 * i + c < nv ? sb : 0;  // slots past the lists: any valid address
+        kr[4 * i + c] = lkey[src];
+        pr[4 * i + c] = lpos[src];
+      }
     }
-    __syncthreads();
-    cnt = total;
-    if (cnt > k) {
-      int parity = 0;
-      cut_to_k<false>(sh, cnt, k, parity);
+    if (total > k) {
+      cut_entries<false>(sh, kr, total, k, [&](int32_t (&p)[kSegMax]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kSegMax; ++j) p[j] = pr[j];
+      });
       cnt = k;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSegMax; ++j)
+        if (j < nv) sh.pos[kSegMax * tid + j] = pr[j];  // the thread's own slots
+      __syncthreads();
+      cnt = total;
     }
   } else {
     const ScoreSrc src{scores + (int64_t)rl * ld, 0, n};
@@ -628,112 +670,75 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(const int32_t* _
 }
 
 // ---------------------------------------------------------------------------
-// Few long rows (decode batches).  One 1024-thread workgroup per row, or per
-// segment of a row longer than kRxCap.  Each wave loads a contiguous range of
-// the row into registers (16-byte loads, lane l holding entries 4l .. 4l + 3
-// of every 256-entry block), so the row is read once and never staged in LDS.
-// The k-th key is found by histogram refinement (the range-adaptive 256-bin
-// passes of cut_to_k, LDS atomics fed from registers), and the winners are
-// written in ascending position order: ballots order the lanes of a wave, one
-// exchange of per-wave counts orders the waves.  Rows longer than kRxCap are
-// cut into segments whose winners, (key, position) padded with position -1,
-// go to a workspace; a second launch of the same kernel selects among them.
-// A winner of the row is a winner of its segment and the candidates keep
-// their keys, so the result is identical.
+// Few rows of at most kRxCap entries, too short to split: one 1024-thread
+// workgroup per row.  Each wave loads a contiguous range of the row into
+// registers (16-byte loads, lane l holding entries 4l .. 4l + 3 of every
+// 256-entry block), so the row is read once and never staged in LDS.  The
+// k-th key is found by histogram refinement (the range-adaptive 256-bin passes
+// of kth_key, LDS atomics fed from registers, one barrier per pass), and the
+// winners are written in ascending position order: ballots order the lanes of
+// a wave, one exchange of per-wave counts orders the waves.
 // ---------------------------------------------------------------------------
 constexpr int kRxThreads = 1024;
 constexpr int kRxWaves = kRxThreads / 64;
-constexpr int kRxRowVecs = 9;                               // 16-byte vectors of keys per lane
-constexpr int kRxCandVecs = 5;                              // ... of (key, position) candidates
-constexpr int kRxCap = kRxWaves * 256 * kRxRowVecs;         // 36864 row entries per workgroup
-constexpr int kRxCapPairs = kRxWaves * 256 * kRxCandVecs;   // 20480 candidates per workgroup
+constexpr int kRxRowVecs = 4;                               // 16-byte vectors of keys per lane
+constexpr int kRxCap = kRxWaves * 256 * kRxRowVecs;         // 16384 row entries per workgroup
 
 struct RadixShared {
-  int hist[256];
+  int hist[3][256];  // one per pass, in rotation (as in kth_key)
   int cnt[kRxWaves];
   int fcnt[2][kRxWaves];
   uint32_t red[2][kRxWaves];
-  int digit;
-  int need;
 };
 
-// IN_CAND: the entries are (key, position) candidates [rows, kp] from the
-// segment pass (position -1 = padding; launched with one segment); else the
-// scores of one row at positions [seg * seg_len, (seg + 1) * seg_len).
-// OUT_CAND: write the winners as candidates (kp slots, padded), else their
-// positions to idx (k slots, padded with -1).
-// NV: 16-byte vectors per lane, enough for the launch's longest segment
-// (m <= 4096 NV).
-template <bool IN_CAND, bool OUT_CAND, int NV>
+// NV: 16-byte vectors per lane, enough for the launch's longest row
+// (n <= 4096 NV).
+template <int NV>
 __global__ __launch_bounds__(kRxThreads) void topk_radix_kernel(const int32_t* __restrict__ cu_q,
                                                                 const int32_t* __restrict__ cu_k, int32_t num_seqs,
                                                                 int32_t row_begin, const float* __restrict__ scores,
-                                                                int64_t ld, int32_t k, int32_t seg_len, int32_t kp,
-                                                                uint32_t* __restrict__ ckey,
-                                                                int32_t* __restrict__ cpos,
-                                                                int32_t* __restrict__ idx) {
-  static_assert(NV <= (IN_CAND ? kRxCandVecs : kRxRowVecs), "too many vectors per lane");
+                                                                int64_t ld, int32_t k, int32_t* __restrict__ idx) {
+  static_assert(NV <= kRxRowVecs, "too many vectors per lane");
   __shared__ RadixShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int32_t rl = blockIdx.x, seg = blockIdx.y, nseg = gridDim.y;
+  const int32_t rl = blockIdx.x;
   const RowInfo ri = locate_row_wave(load_seq_table(cu_q, cu_k, num_seqs), cu_q, cu_k, row_begin + rl);
   const int32_t n = ri.pos + 1;
-  if (!IN_CAND && OUT_CAND && n <= k) return;  // the selection pass writes every position directly
-  if (!OUT_CAND && n <= k) {
-    int32_t* out = idx + (int64_t)rl * k;
+  int32_t* out = idx + (int64_t)rl * k;
+  if (n <= k) {
     for (int e = tid; e < k; e += kRxThreads) out[e] = e < n ? e : -1;
     return;
   }
   // ---- load: wave w owns entries [w0, w1), L a multiple of 256
-  int32_t m, lo_pos = 0;
-  if constexpr (IN_CAND) {
-    m = kp;
-  } else {
-    lo_pos = seg * seg_len;  // seg_len is a multiple of 4
-    m = max(0, min(n, lo_pos + seg_len) - lo_pos);
-  }
-  const int L = (m + 256 * kRxWaves - 1) / (256 * kRxWaves) * 256;  // <= 256 * NV
-  const int w0 = min(wave * L, m), w1 = min(w0 + L, m);
+  const int L = (n + 256 * kRxWaves - 1) / (256 * kRxWaves) * 256;  // <= 256 * NV
+  const int w0 = min(wave * L, n), w1 = min(w0 + L, n);
   uint32_t key[NV][4];
   int32_t pos[NV][4];
   {
-    // raw buffer loads over whole 16-byte vectors (they stay in the row:
-    // lo_pos and ld are multiples of 4, candidate lists multiples of 8);
-    // loads past the range read zero, and all are issued before the first use
-    const uint32_t bytes = (uint32_t)((m + 3) / 4 * 16);
-    const void* kbase = IN_CAND ? (const void*)(ckey + (int64_t)rl * kp)
-                                : (const void*)(scores + (int64_t)rl * ld + lo_pos);
-    const auto ks = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, bytes, 0x00020000);
-    i32x4 kv[NV], pv[NV];
+    // raw buffer loads over whole 16-byte vectors (they stay in the row: ld
+    // is a multiple of 4); loads past the range read zero, and all are issued
+    // before the first use
+    const uint32_t bytes = (uint32_t)((n + 3) / 4 * 16);
+    const auto ks = __builtin_amdgcn_make_buffer_rsrc((void*)(scores + (int64_t)rl * ld), 0, bytes, 0x00020000);
+    i32x4 kv[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int e = w0 + 256 * i + 4 * lane;
       const uint32_t off = 256 * i < L ? (uint32_t)e * 4u : 0xfffffff0u;  // outside the wave's range: no access
       kv[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(ks, off, 0, 0));
-      if constexpr (IN_CAND) {
-        const auto ps = __builtin_amdgcn_make_buffer_rsrc((void*)(cpos + (int64_t)rl * kp), 0, bytes, 0x00020000);
-        pv[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(ps, off, 0, 0));
-      }
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int e = w0 + 256 * i + 4 * lane + j;
-        const bool in = 256 * i < L && e < w1;
-        if constexpr (IN_CAND) {
-          pos[i][j] = in ? pv[i][j] : -1;
-          key[i][j] = (uint32_t)kv[i][j];
-        } else {
-          pos[i][j] = in ? lo_pos + e : -1;
-          const int bits = kv[i][j];  // copied out first: a bit_cast of the element expression read element 0
-          key[i][j] = order_key(__int_as_float(bits));
-        }
+        pos[i][j] = 256 * i < L && e < w1 ? e : -1;
+        const int bits = kv[i][j];  // copied out first: a bit_cast of the element expression read element 0
+        key[i][j] = order_key(__int_as_float(bits));
       }
   }
-  // ---- valid entries: count, min and max key
+  // ---- min and max key (n > k >= 1 entries are valid)
   uint32_t mn = 0xffffffffu, mx = 0u;
-  int nv = 0;
 #pragma unroll
   for (int i = 0; i < NV; ++i)
 #pragma unroll
@@ -741,72 +746,64 @@ __global__ __launch_bounds__(kRxThreads) void topk_radix_kernel(const int32_t* _
       if (pos[i][j] >= 0) {
         mn = min(mn, key[i][j]);
         mx = max(mx, key[i][j]);
-        ++nv;
       }
-  for (int o = 32; o >= 1; o >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-    nv += __shfl_xor(nv, o);
-  }
-  if (lane == 0) { sh.red[0][wave] = mn; sh.red[1][wave] = mx; sh.cnt[wave] = nv; }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (lane == 0) { sh.red[0][wave] = mn; sh.red[1][wave] = mx; }
+  if (tid < 256) sh.hist[0][tid] = 0;
   __syncthreads();
   uint32_t lo = sh.red[0][0], hi = sh.red[1][0];
-  int nvalid = sh.cnt[0];
 #pragma unroll
   for (int w = 1; w < kRxWaves; ++w) {
     lo = min(lo, sh.red[0][w]);
     hi = max(hi, sh.red[1][w]);
-    nvalid += sh.cnt[w];
   }
 
   // ---- the k-th key T: entries above it are kept, and `need` of those equal to it (the earliest)
-  const int take = min((int)k, nvalid);
-  int need;
-  if (nvalid > k) {
-    need = k;
-    while (hi > lo) {
-      const uint32_t span = hi - lo;
-      const int bits = 32 - __clz(span);
-      const int shift = bits > 8 ? bits - 8 : 0;
-      const int nbins = (int)(span >> shift) + 1;  // <= 256
-      if (tid < 256) sh.hist[tid] = 0;
-      __syncthreads();
+  int need = k;
+  int hb = 0;
+  while (hi > lo) {
+    const uint32_t span = hi - lo;
+    const int bits = 32 - __clz(span);
+    const int shift = bits > 8 ? bits - 8 : 0;
+    const int nbins = (int)(span >> shift) + 1;  // <= 256
+    int* hist = sh.hist[hb];
 #pragma unroll
-      for (int i = 0; i < NV; ++i)
+    for (int i = 0; i < NV; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t kk = key[i][j];
-          if (pos[i][j] >= 0 && kk >= lo && kk <= hi) atomicAdd(&sh.hist[(kk - lo) >> shift], 1);
-        }
-      __syncthreads();
-      if (wave == 0) {
-        int c[4], sum = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int b = nbins - 1 - 4 * lane - j;
-          c[j] = b >= 0 ? sh.hist[b] : 0;
-          sum += c[j];
-        }
-        const int incl = wave_inclusive_scan(sum);
-        const int excl = incl - sum;
-        if (excl < need && need <= incl) {
-          int run = excl;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (run < need && need <= run + c[j]) { sh.digit = nbins - 1 - 4 * lane - j; sh.need = need - run; }
-            run += c[j];
-          }
-        }
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t kk = key[i][j];
+        if (pos[i][j] >= 0 && kk >= lo && kk <= hi) atomicAdd(&hist[(kk - lo) >> shift], 1);
       }
-      __syncthreads();
-      const uint32_t blo = lo + ((uint32_t)sh.digit << shift);
-      lo = blo;
-      hi = min(hi, blo + ((1u << shift) - 1u));
-      need = sh.need;
+    hb = hb == 2 ? 0 : hb + 1;
+    if (tid < 256) sh.hist[hb][tid] = 0;  // the next pass's histogram, last read two passes ago
+    __syncthreads();
+    int c[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = nbins - 1 - 4 * lane - j;
+      c[j] = b >= 0 ? hist[b] : 0;
+      sum += c[j];
     }
-  } else {
-    lo = 0u;  // every valid entry is kept
-    need = 0x7fffffff;
+    const int incl = (int)wave_scan_dpp((uint32_t)sum, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+    const int excl = incl - sum;
+    const bool mine = excl < need && need <= incl;
+    int digit = 0, rest = 0;
+    if (mine) {
+      int run = excl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (run < need && need <= run + c[j]) { digit = nbins - 1 - 4 * lane - j; rest = need - run; }
+        run += c[j];
+      }
+    }
+    const int owner = (int)__builtin_ctzll(__ballot(mine));
+    digit = __builtin_amdgcn_readlane(digit, owner);
+    rest = __builtin_amdgcn_readlane(rest, owner);
+    const uint32_t blo = lo + ((uint32_t)digit << shift);
+    lo = blo;
+    hi = min(hi, blo + ((1u << shift) - 1u));
+    need = rest;
   }
   const uint32_t T = lo;
 
@@ -837,15 +834,6 @@ __global__ __launch_bounds__(kRxThreads) void topk_radix_kernel(const int32_t* _
       eq_pre += e_w;
     }
   }
-  uint32_t* okey = nullptr;
-  int32_t* opos = nullptr;
-  int32_t* out = nullptr;
-  if constexpr (OUT_CAND) {
-    okey = ckey + ((int64_t)rl * nseg + seg) * kp;
-    opos = cpos + ((int64_t)rl * nseg + seg) * kp;
-  } else {
-    out = idx + (int64_t)rl * k;
-  }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     int eq_l = 0;
@@ -867,23 +855,10 @@ __global__ __launch_bounds__(kRxThreads) void topk_radix_kernel(const int32_t* _
     int o = keeprun + wave_excl_prefix_small<3>(keep_l, keep_tot);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (kept[j]) {
-        if constexpr (OUT_CAND) {
-          okey[o] = key[i][j];
-          opos[o] = pos[i][j];
-        } else {
-          out[o] = pos[i][j];
-        }
-        ++o;
-      }
+      if (kept[j]) out[o++] = pos[i][j];
     }
     eqrun += eq_tot;
     keeprun += keep_tot;
-  }
-  if constexpr (OUT_CAND) {
-    for (int e = take + tid; e < kp; e += kRxThreads) { okey[e] = 0u; opos[e] = -1; }
-  } else {
-    for (int e = take + tid; e < k; e += kRxThreads) out[e] = -1;
   }
 }
 
@@ -932,26 +907,18 @@ TopkPlan topk_plan(int rows, int max_ctx, int k, int num_cus) {
   return p;
 }
 
-template <bool IN_CAND, bool OUT_CAND, int NV>
-hipError_t launch_radix_nv(const TopkLaunch& L, dim3 grid, int32_t seg_len, int32_t kp, uint32_t* ckey,
-                           int32_t* cpos, hipStream_t s) {
-  hipLaunchKernelGGL((topk_radix_kernel<IN_CAND, OUT_CAND, NV>), grid, dim3(kRxThreads), 0, s, L.b.cu_q, L.b.cu_k,
-                     L.b.num_seqs, L.b.row_begin, L.scores, L.ld, L.k, seg_len, kp, ckey, cpos, L.idx);
+template <int NV>
+hipError_t launch_radix_nv(const TopkLaunch& L, int rows, hipStream_t s) {
+  hipLaunchKernelGGL((topk_radix_kernel<NV>), dim3((unsigned)rows), dim3(kRxThreads), 0, s, L.b.cu_q, L.b.cu_k,
+                     L.b.num_seqs, L.b.row_begin, L.scores, L.ld, L.k, L.idx);
   return hipGetLastError();
 }
 
-// m_max: the most entries one workgroup holds (a segment, or a row's candidates)
-template <bool IN_CAND, bool OUT_CAND>
-hipError_t launch_radix(const TopkLaunch& L, dim3 grid, int32_t seg_len, int32_t kp, int32_t m_max, uint32_t* ckey,
-                        int32_t* cpos, hipStream_t s) {
-  const int nv = (m_max + 256 * kRxWaves - 1) / (256 * kRxWaves);
-  if (nv <= 1) return launch_radix_nv<IN_CAND, OUT_CAND, 1>(L, grid, seg_len, kp, ckey, cpos, s);
-  if (nv <= 2) return launch_radix_nv<IN_CAND, OUT_CAND, 2>(L, grid, seg_len, kp, ckey, cpos, s);
-  if (nv <= 3) return launch_radix_nv<IN_CAND, OUT_CAND, 3>(L, grid, seg_len, kp, ckey, cpos, s);
-  if (nv <= 5) return launch_radix_nv<IN_CAND, OUT_CAND, 5>(L, grid, seg_len, kp, ckey, cpos, s);
-  if constexpr (!IN_CAND) {
-    if (nv <= 9) return launch_radix_nv<IN_CAND, OUT_CAND, 9>(L, grid, seg_len, kp, ckey, cpos, s);
-  }
+hipError_t launch_radix(const TopkLaunch& L, int rows, hipStream_t s) {
+  const int nv = (L.b.max_ctx + 256 * kRxWaves - 1) / (256 * kRxWaves);
+  if (nv <= 1) return launch_radix_nv<1>(L, rows, s);
+  if (nv <= 2) return launch_radix_nv<2>(L, rows, s);
+  if (nv <= 4) return launch_radix_nv<4>(L, rows, s);
   return hipErrorInvalidValue;
 }
 
@@ -992,7 +959,7 @@ hipError_t launch_topk(const TopkLaunch& L, hipStream_t s) {
     return hipGetLastError();
   }
   if (p.kind == kRadix)
-    return launch_radix<false, false>(L, dim3((unsigned)rows), kRxCap, 0, L.b.max_ctx, nullptr, nullptr, s);
+    return launch_radix(L, rows, s);
   const SegWorkspace w = seg_workspace(rows, p);
   const int cap = seg_cap(p);
   uint32_t* ckey = (uint32_t*)L.ws;

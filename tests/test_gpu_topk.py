@@ -105,10 +105,12 @@ def test_few_long_rows_use_segments(dsa, k):
 
 @pytest.mark.parametrize("k", [1, 100, 2048])
 def test_few_rows_radix_select(dsa, k):
-    """Few rows that fit the LDS radix path: ties, -0/+0, NaN and a row
-    whose keys nearly all fall in one histogram bin."""
+    """Few rows: ties, -0/+0, NaN, a row whose keys nearly all fall in one
+    histogram bin, keys a few ulps apart.  With k = 2048 every row is shorter
+    than 4k entries and takes one radix workgroup (up to 16383 entries, four
+    vectors per lane); smaller k split the rows into segments."""
     announce("topk radix", k)
-    p = _problem([30000, 36864, 2049, 12000, 500, 36000], [1, 1, 1, 1, 1, 1], k)
+    p = _problem([12000, 16383, 2049, 9000, 500, 15000], [1, 1, 1, 1, 1, 1], k)
     rng = np.random.default_rng(10 + k)
     n = _ld(p)
     s = rng.standard_normal((p.total_q, n)).astype(np.float32)
@@ -116,7 +118,7 @@ def test_few_rows_radix_select(dsa, k):
     s[0][s[0] == 0] = np.where(rng.random((s[0] == 0).sum()) < 0.5, -0.0, 0.0)
     s[1][rng.random(n) < 0.02] = np.nan
     s[3] = 1.0                                                           # one bin holds almost every key
-    s[3, rng.integers(0, 12000, 40)] = rng.standard_normal(40).astype(np.float32)
+    s[3, rng.integers(0, 9000, 40)] = rng.standard_normal(40).astype(np.float32)
     s[5] = np.float32(0.25) + np.float32(1e-7) * np.arange(n, dtype=np.float32)        # keys a few ulps apart
     got, ref = _run(dsa, p, s, k)
     assert np.array_equal(got, ref)

@@ -155,10 +155,14 @@ size_t stage_out_bytes(int64_t rows, int32_t H, const AttnWiden& w) {
   return w.out ? round_up((size_t)rows * H * kVW * 2, 256) : 0;
 }
 
+// key-split partials: bf16 outputs [rows, splits, H, d_v], then fp32 lse
+// [rows, splits, H]
+size_t partial_o_bytes(int32_t rows, int splits, int32_t H, int32_t d_v) {
+  return round_up((size_t)rows * splits * H * d_v * sizeof(uint16_t), 256);
+}
 size_t attention_ws_bytes(int32_t rows, int splits, int32_t H, int32_t d_v) {
   if (splits <= 1) return 0;
-  return round_up((size_t)rows * splits * H * d_v * sizeof(float), 256) +
-         round_up((size_t)rows * splits * H * sizeof(float), 256);
+  return partial_o_bytes(rows, splits, H, d_v) + round_up((size_t)rows * splits * H * sizeof(float), 256);
 }
 
 }  // namespace
@@ -302,8 +306,8 @@ dsa_status run_attention(const dsa_batch* batch, dsa::AttnLaunch L, int32_t d_qk
     return fail(DSA_ERR_WORKSPACE, "%s workspace: need %zu bytes (got %zu)", what, need, ws_bytes);
   char* base = (char*)ws;
   if (L.splits > 1) {
-    L.ws_o = (float*)base;
-    L.ws_lse = (float*)(base + round_up((size_t)rows * L.splits * H * w.d_v * sizeof(float), 256));
+    L.ws_o = (uint16_t*)base;
+    L.ws_lse = (float*)(base + partial_o_bytes(rows, L.splits, H, w.d_v));
   }
   if (w.in) {
     hipError_t e = dsa::launch_copy_rows(L.q, 2 * d_qk, base + part, 2 * kQkW, (int64_t)rows * H, 2 * d_qk, cus, st);
@@ -682,9 +686,8 @@ dsa_status dsa_forward(const dsa_forward_params* p, void* ws, size_t ws_bytes, d
                        p->dtype == DSA_BF16, splits, nullptr, nullptr};
     AL.dense_short = true;  // rows with pos + 1 <= k: the masked mode, same result as their idx = 0 .. pos
     if (splits > 1) {
-      AL.ws_o = (float*)(base + f.off_attn);
-      AL.ws_lse = (float*)(base + f.off_attn +
-                           round_up((size_t)(r1 - r0) * splits * p->H * f.w.d_v * sizeof(float), 256));
+      AL.ws_o = (uint16_t*)(base + f.off_attn);
+      AL.ws_lse = (float*)(base + f.off_attn + partial_o_bytes(r1 - r0, splits, p->H, f.w.d_v));
     }
     e = dsa::launch_attention(AL, st);
     if (e != hipSuccess) return hip_fail(e, "forward attention launch");

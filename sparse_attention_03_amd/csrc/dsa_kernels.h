@@ -66,7 +66,7 @@ struct AttnLaunch {
   float* lse;              // [total_q, H] or null (global rows)
   bool bf16;
   int32_t splits;          // >1: partials in ws, then a merge
-  float* ws_o;             // [rows, splits, H, d_v]
+  uint16_t* ws_o;          // [rows, splits, H, d_v] bf16: each split's normalised output
   float* ws_lse;           // [rows, splits, H]
   bool dense = false;      // every candidate [0, pos] (idx unused; k = max_ctx)
   bool dense_short = false;  // rows with pos + 1 <= k walk [0, pos] without reading idx

@@ -51,7 +51,7 @@ struct MlaArgs {
   int32_t splits, tiles_per_split;
   int32_t dense;        // every candidate [0, pos] instead of idx (k = the longest row's candidate count)
   int32_t dense_short;  // rows with n <= k walk [0, pos] directly (their idx is 0 .. pos)
-  float* ws_o;
+  uint16_t* ws_o;  // bf16 partial outputs, each split's own normalised average
   float* ws_lse;
   const float* lse_in;  // target: the main attention's lse per (row, head)
   float* p_out;         // target: [rows, ld_p]
@@ -336,22 +336,20 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
     const float inv = empty ? 0.0f : 1.0f / l;
     const float lse_v = empty ? -INFINITY : (m_fix[nt] + log2f(l)) * 0.69314718055994531f;
     if (GHOST && h >= a.H) continue;  // a head past H: nothing to store
-    if (a.splits == 1) {
-      uint16_t* orow = a.out + ((int64_t)r * a.H + h) * kDv + 4 * g;
+    // one row of the output, or (key splits) this split's bf16 partial
+    const bool direct = a.splits == 1;
+    const int64_t slot = ((int64_t)rl * a.splits + sp) * a.H + h;
+    uint16_t* orow = (direct ? a.out + ((int64_t)r * a.H + h) * kDv : a.ws_o + slot * kDv) + 4 * g;
 #pragma unroll
-      for (int dt = 0; dt < kDvTiles; ++dt) {
-        const f32x4 o = oacc[dt][nt];
-        const uint32_t lo = (uint32_t)to_bf16_bits(o[0] * inv) | ((uint32_t)to_bf16_bits(o[1] * inv) << 16);
-        const uint32_t hi = (uint32_t)to_bf16_bits(o[2] * inv) | ((uint32_t)to_bf16_bits(o[3] * inv) << 16);
-        *(uint2*)(orow + 16 * dt) = make_uint2(lo, hi);
-      }
-      if (a.lse && g == 0) a.lse[(int64_t)r * a.H + h] = lse_v;
-    } else {
-      const int64_t slot = ((int64_t)rl * a.splits + sp) * a.H + h;
-      float* orow = a.ws_o + slot * kDv + 4 * g;
-#pragma unroll
-      for (int dt = 0; dt < kDvTiles; ++dt) *(f32x4*)(orow + 16 * dt) = oacc[dt][nt] * inv;
-      if (g == 0) a.ws_lse[slot] = lse_v;
+    for (int dt = 0; dt < kDvTiles; ++dt) {
+      const f32x4 o = oacc[dt][nt];
+      const uint32_t lo = (uint32_t)to_bf16_bits(o[0] * inv) | ((uint32_t)to_bf16_bits(o[1] * inv) << 16);
+      const uint32_t hi = (uint32_t)to_bf16_bits(o[2] * inv) | ((uint32_t)to_bf16_bits(o[3] * inv) << 16);
+      *(uint2*)(orow + 16 * dt) = make_uint2(lo, hi);
+    }
+    if (g == 0) {
+      if (!direct) a.ws_lse[slot] = lse_v;
+      else if (a.lse) a.lse[(int64_t)r * a.H + h] = lse_v;
     }
   }
 }
@@ -565,10 +563,19 @@ __global__ __launch_bounds__(128) void merge_kernel(MlaArgs a, int d_v) {
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
   for (int d = 4 * tid; d < d_v; d += 4 * blockDim.x) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < S; ++s) {
-      const float wgt = wsh[s];
-      if (wgt == 0.0f) continue;
-      acc += wgt * *(const f32x4*)(a.ws_o + (slot0 + (int64_t)s * a.H) * d_v + d);
+    // four splits' bf16 partials in flight at a time
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      uint2 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        v[u] = s0 + u < S ? *(const uint2*)(a.ws_o + (slot0 + (int64_t)(s0 + u) * a.H) * d_v + d) : make_uint2(0, 0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wgt = s0 + u < S ? wsh[s0 + u] : 0.0f;
+        if (wgt != 0.0f)
+          acc += wgt * f32x4{__uint_as_float(v[u].x << 16), __uint_as_float(v[u].x & 0xffff0000u),
+                             __uint_as_float(v[u].y << 16), __uint_as_float(v[u].y & 0xffff0000u)};
+      }
     }
     acc *= inv;
     const int64_t oi = ((int64_t)r * a.H + h) * d_v + d;

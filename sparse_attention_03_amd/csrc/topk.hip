@@ -410,10 +410,10 @@ __device__ __forceinline__ int stream_select(TopkShared& sh, const Src& src, typ
   return cnt;
 }
 
-// Long rows start from a sampled threshold: the key of rank ~1.5 k n_s / n
+// Long rows start from a sampled threshold: the key of rank 1.3 k n_s / n + 8
 // among n_s = 4096 entries (four contiguous blocks spread over the row), so
-// that about 1.5 k entries of the row reach it and the stream rarely needs a
-// cut.  The result stays exact: if at least k entries reach the threshold,
+// that about 1.3 k to 1.4 k entries of the row reach it and the stream rarely
+// needs a cut.  The result stays exact: if at least k entries reach the threshold,
 // the k-th best key of the row is at least the threshold and every winner is
 // admitted; otherwise the row is selected again without it.
 constexpr int kSampleBlocks = 4;
@@ -440,7 +440,7 @@ __device__ __forceinline__ uint32_t sampled_threshold(TopkShared& sh, const f32x
 #pragma unroll
     for (int c = 0; c < 4; ++c) kr[4 * b + c] = order_key(v[b][c]);
   constexpr int m = kSampleBlocks * kSampleBlock;
-  const int rank = (int)min((int64_t)m, 3LL * k * m / (2LL * n) + 8);
+  const int rank = (int)min((int64_t)m, 13LL * k * m / (10LL * n) + 8);
   int need;
   return kth_key(sh, kr, kSegMax, rank, need, passes);
 }

@@ -167,7 +167,7 @@ def test_segment_threshold_fallbacks(dsa):
     rng = np.random.default_rng(60)
     s = (0.14 + 0.03 * rng.standard_normal((p.total_q, _ld(p)))).astype(np.float32)
     n = ctx[0]
-    rank = min(4096, 3 * k * 4096 // (2 * n) + 8)
+    rank = min(4096, 13 * k * 4096 // (10 * n) + 8)
     for b in range(4):
         start = (b * (n - 1024) // 3) & ~3
         s[0, start:start + rank // 4 + 1] = 100.0                      # the sample's top ranks: too high
@@ -203,7 +203,7 @@ def test_long_rows_sampled_threshold(dsa):
     s[1::3] = rng.integers(-2, 3, (len(s[1::3]), n_ld)).astype(np.float32)
     for r in range(0, p.total_q, 3):
         n = 40000 - p.total_q + r + 1
-        rank = min(4096, 3 * k * 4096 // (2 * n) + 8)
+        rank = min(4096, 13 * k * 4096 // (10 * n) + 8)
         for b in range(4):
             start = (b * (n - 1024) // 3) & ~3
             s[r, start:start + rank // 4 + 1] = 100.0                  # the sample's top ranks: too high

@@ -529,16 +529,26 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_target_kernel(MlaArgs a) {
 // Combine key-split partials: o = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M).
 // One workgroup per (row, head); each thread owns 4 consecutive value columns.
 // Up to kMaxSplits splits: the weights are formed by the whole workgroup
-// (strided over the splits, then a max and a sum across its two waves).
+// (strided over the splits, then a max and a sum across its two waves).  The
+// first four splits' partials are loaded before the weights are known, so
+// their latency overlaps that of the lse loads.
 template <bool BF16>
-__global__ __launch_bounds__(128) void merge_kernel(MlaArgs a, int d_v) {
+__global__ __launch_bounds__(128) void merge_kernel(MlaArgs a) {
+  static_assert(kDv == 4 * 128, "one thread per four value columns");
   __shared__ float wsh[kMaxSplits];
   __shared__ float red[2][2];
   const int32_t rl = blockIdx.x, r = a.row_begin + rl;
   const int h = blockIdx.y;
   const int S = a.splits;
   const int tid = threadIdx.x, wv = tid >> 6;
+  const int d = 4 * tid;
   const int64_t slot0 = (int64_t)rl * S * a.H + h;  // split s: slot0 + s * H
+  auto load_part = [&](int s) -> uint2 {
+    return s < S ? *(const uint2*)(a.ws_o + (slot0 + (int64_t)s * a.H) * kDv + d) : make_uint2(0, 0);
+  };
+  uint2 v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) v[u] = load_part(u);
   float mloc = -INFINITY;
   for (int s = tid; s < S; s += 128) {
     const float ls = a.ws_lse[slot0 + (int64_t)s * a.H];
@@ -561,31 +571,29 @@ __global__ __launch_bounds__(128) void merge_kernel(MlaArgs a, int d_v) {
   __syncthreads();
   const float den = red[1][0] + red[1][1];
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  for (int d = 4 * tid; d < d_v; d += 4 * blockDim.x) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    // four splits' bf16 partials in flight at a time
-    for (int s0 = 0; s0 < S; s0 += 4) {
-      uint2 v[4];
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  // four splits' bf16 partials in flight at a time
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    if (s0 > 0) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        v[u] = s0 + u < S ? *(const uint2*)(a.ws_o + (slot0 + (int64_t)(s0 + u) * a.H) * d_v + d) : make_uint2(0, 0);
+      for (int u = 0; u < 4; ++u) v[u] = load_part(s0 + u);
+    }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float wgt = s0 + u < S ? wsh[s0 + u] : 0.0f;
-        if (wgt != 0.0f)
-          acc += wgt * f32x4{__uint_as_float(v[u].x << 16), __uint_as_float(v[u].x & 0xffff0000u),
-                             __uint_as_float(v[u].y << 16), __uint_as_float(v[u].y & 0xffff0000u)};
-      }
+    for (int u = 0; u < 4; ++u) {
+      const float wgt = s0 + u < S ? wsh[s0 + u] : 0.0f;
+      if (wgt != 0.0f)
+        acc += wgt * f32x4{__uint_as_float(v[u].x << 16), __uint_as_float(v[u].x & 0xffff0000u),
+                           __uint_as_float(v[u].y << 16), __uint_as_float(v[u].y & 0xffff0000u)};
     }
-    acc *= inv;
-    const int64_t oi = ((int64_t)r * a.H + h) * d_v + d;
-    if constexpr (BF16) {
-      const uint32_t lo = (uint32_t)to_bf16_bits(acc[0]) | ((uint32_t)to_bf16_bits(acc[1]) << 16);
-      const uint32_t hi = (uint32_t)to_bf16_bits(acc[2]) | ((uint32_t)to_bf16_bits(acc[3]) << 16);
-      *(uint2*)(a.out + oi) = make_uint2(lo, hi);
-    } else {
-      *(f32x4*)((float*)a.out + oi) = acc;
-    }
+  }
+  acc *= inv;
+  const int64_t oi = ((int64_t)r * a.H + h) * kDv + d;
+  if constexpr (BF16) {
+    const uint32_t lo = (uint32_t)to_bf16_bits(acc[0]) | ((uint32_t)to_bf16_bits(acc[1]) << 16);
+    const uint32_t hi = (uint32_t)to_bf16_bits(acc[2]) | ((uint32_t)to_bf16_bits(acc[3]) << 16);
+    *(uint2*)(a.out + oi) = make_uint2(lo, hi);
+  } else {
+    *(f32x4*)((float*)a.out + oi) = acc;
   }
   if (tid == 0 && a.lse) a.lse[(int64_t)r * a.H + h] = den > 0.0f ? M + logf(den) : -INFINITY;
 }
@@ -793,7 +801,7 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL((merge_kernel<true>), dim3((unsigned)rows, (unsigned)a.H), dim3(128), 0, s, a, kDv);
+  hipLaunchKernelGGL((merge_kernel<true>), dim3((unsigned)rows, (unsigned)a.H), dim3(128), 0, s, a);
   return hipGetLastError();
 }
 

@@ -62,19 +62,7 @@ struct BwdArgs {
 template <int NW>
 __device__ __forceinline__ void load_selection(const BwdArgs& a, int32_t rl, int ntiles, DSA_LDS int32_t* sel,
                                                DSA_LDS uint32_t* tmask) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int32_t* idx_row = a.idx + (int64_t)rl * a.k;
-  for (int base = wave * 64; base < ntiles * kTile; base += NW * 64) {
-    const int e = base + lane;
-    const bool in = e < ntiles * kTile;
-    const int32_t v = e < a.k ? idx_row[e] : -1;
-    if (in) sel[e] = v;
-    const uint64_t m = __ballot(in && v >= 0);
-    if (lane == 0) {
-      tmask[base / kTile] = (uint32_t)m;
-      tmask[base / kTile + 1] = (uint32_t)(m >> 32);
-    }
-  }
+  stage_selection<NW>(a.idx + (int64_t)rl * a.k, a.k, ntiles, sel, tmask);
 }
 
 template <int HPW, int NW>

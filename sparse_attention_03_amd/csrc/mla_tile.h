@@ -87,5 +87,38 @@ __device__ __forceinline__ void gather_tile(const uint8_t* kv, int32_t kbase, co
   gather_lines<NW, 0, kSegments>(kv, kbase, p, buf);
 }
 
+// The row's selected positions in LDS, -1 padded to whole tiles
+// (sel[0 .. 32 ntiles)), and per tile the mask of its valid entries
+// (tmask[t] bit j: entry 32 t + j is >= 0).  Every load of the wave is issued
+// before the first is used (range-checked buffer loads: entries past k read
+// nothing and become -1), so staging the row costs one load latency rather
+// than one per 64 entries.
+template <int NW>
+__device__ __forceinline__ void stage_selection(const int32_t* idx_row, int32_t k, int ntiles, DSA_LDS int32_t* sel,
+                                                DSA_LDS uint32_t* tmask) {
+  constexpr int kIters = kMaxSel / (NW * 64);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)idx_row, 0, (uint32_t)k * 4u, 0x00020000);
+  int32_t v[kIters];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it)
+    v[it] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)((it * NW + wave) * 64 + lane) * 4u, 0, 0);
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int base = (it * NW + wave) * 64;
+    if (base < ntiles * kTile) {
+      const int e = base + lane;
+      const bool in = e < ntiles * kTile;
+      const int32_t x = e < k ? v[it] : -1;
+      if (in) sel[e] = x;
+      const uint64_t m = __ballot(in && x >= 0);
+      if (lane == 0) {
+        tmask[base / kTile] = (uint32_t)m;
+        tmask[base / kTile + 1] = (uint32_t)(m >> 32);
+      }
+    }
+  }
+}
+
 }  // namespace mla
 }  // namespace dsa

@@ -96,17 +96,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_bf16_kernel(MlaArgs a) {
   // mask of its valid entries (bit j: entry 32 t + j is >= 0)
   DSA_LDS uint32_t* tmask = (DSA_LDS uint32_t*)(sel + kMaxSel);
   const int32_t* idx_row = a.idx + (int64_t)rl * a.k;
-  for (int base = wave * 64; !dense && base < ntiles * kTile; base += NW * 64) {
-    const int e = base + lane;
-    const bool in = e < ntiles * kTile;
-    const int32_t v = e < a.k ? idx_row[e] : -1;
-    if (in) sel[e] = v;
-    const uint64_t m = __ballot(in && v >= 0);
-    if (lane == 0) {
-      tmask[base / kTile] = (uint32_t)m;
-      tmask[base / kTile + 1] = (uint32_t)(m >> 32);
-    }
-  }
+  if (!dense) stage_selection<NW>(idx_row, a.k, ntiles, sel, tmask);
 
   // query fragments: B operand of S^T = K Q^T (lane: head li of column tile nt, d = 32c + 8g .. +7)
   bf16x8 qf[NT][kQkSteps];
@@ -388,17 +378,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_target_kernel(MlaArgs a) {
   const int t0 = sp * a.tiles_per_split;
   const int t1 = min(ntiles, t0 + a.tiles_per_split);
   const int32_t* idx_row = a.idx + (int64_t)rl * a.k;
-  for (int base = wave * 64; !dense && base < ntiles * kTile; base += NW * 64) {
-    const int e = base + lane;
-    const bool in = e < ntiles * kTile;
-    const int32_t v = e < a.k ? idx_row[e] : -1;
-    if (in) sel[e] = v;
-    const uint64_t m = __ballot(in && v >= 0);
-    if (lane == 0) {
-      tmask[base / kTile] = (uint32_t)m;
-      tmask[base / kTile + 1] = (uint32_t)(m >> 32);
-    }
-  }
+  if (!dense) stage_selection<NW>(idx_row, a.k, ntiles, sel, tmask);
   bf16x8 qf[NT][kQkSteps];
   float lse2[NT];
   const int head0 = wave * HPW;

@@ -176,6 +176,25 @@ def test_segment_threshold_fallbacks(dsa):
     assert np.array_equal(got, ref)
 
 
+def test_segment_cut_inside_a_segment(dsa):
+    """40 rows of 131072 entries take segments of 10240 entries (13 per row
+    on 256 CUs).  A hot region of 10240 entries between the sample blocks
+    puts every entry of its segment above the row's threshold, so that
+    segment's buffer overflows and is cut to its k best while streaming; in
+    one row the hot entries all tie (the earliest k win), in another they
+    straddle two segments."""
+    announce("topk segment cut inside a segment")
+    k = 2048
+    p = _problem([131072] * 40, [1] * 40, k)
+    rng = np.random.default_rng(70)
+    s = (0.14 + 0.03 * rng.standard_normal((p.total_q, _ld(p)))).astype(np.float32)
+    s[3, 20480:30720] = (10.0 + rng.standard_normal(10240)).astype(np.float32)
+    s[7, 20480:30720] = 10.0                                             # ties: the earliest k win
+    s[11, 25000:35240] = (10.0 + rng.standard_normal(10240)).astype(np.float32)
+    got, ref = _run(dsa, p, s, k)
+    assert np.array_equal(got, ref)
+
+
 @pytest.mark.parametrize("k", [5, 2048])
 def test_few_short_rows_one_radix_pass(dsa, k):
     """Few rows too short to split: one radix workgroup per row, no workspace."""

@@ -161,7 +161,10 @@ __device__ __forceinline__ int block_excl_scan(int v, int* slot, int& total) {
 // kHistBins equal power-of-two bins, so clustered scores still spread over the
 // bins; at most four passes, none when every key is equal.  After max_passes
 // passes the lower end of the interval is returned instead: a key at most T,
-// with `need` then meaningless.  One barrier per pass: the histograms rotate
+// with `need` then meaningless.  When every entry of the bin holding the
+// rank is kept, the bin's lower end is returned as T (a key at most the k-th
+// best; every entry at or above it is among the k best, `need` = the bin's
+// count) without refining further.  One barrier per pass: the histograms rotate
 // over three buffers (a pass clears the next one, last read two passes
 // before), and every wave scans the histogram itself.
 __device__ uint32_t kth_key(TopkShared& sh, const uint32_t (&kr)[kSegMax], int nv, int k, int& need,
@@ -208,7 +211,7 @@ __device__ uint32_t kth_key(TopkShared& sh, const uint32_t (&kr)[kSegMax], int n
     const int incl = (int)wave_scan_dpp((uint32_t)sum, 0u, [](uint32_t a, uint32_t b) { return a + b; });
     const int excl = incl - sum;
     const bool mine = excl < need && need <= incl;  // exactly one lane: T lies in [lo, hi]
-    int digit = 0, rest = 0;
+    int digit = 0, rest = 0, in_bin = 0;
     if (mine) {
       int run = excl;
 #pragma unroll
@@ -216,6 +219,7 @@ __device__ uint32_t kth_key(TopkShared& sh, const uint32_t (&kr)[kSegMax], int n
         if (run < need && need <= run + c[j]) {
           digit = nbins - 1 - kBinsPerLane * lane - j;
           rest = need - run;
+          in_bin = c[j];
         }
         run += c[j];
       }
@@ -223,11 +227,16 @@ __device__ uint32_t kth_key(TopkShared& sh, const uint32_t (&kr)[kSegMax], int n
     const int owner = (int)__builtin_ctzll(__ballot(mine));
     digit = __builtin_amdgcn_readlane(digit, owner);
     rest = __builtin_amdgcn_readlane(rest, owner);
+    in_bin = __builtin_amdgcn_readlane(in_bin, owner);
     const uint32_t blo = lo + ((uint32_t)digit << shift);
     const uint32_t bhi = blo + ((1u << shift) - 1u);
     lo = blo;
     hi = min(hi, bhi);
     need = rest;
+    // every entry of the bin ranks among the k best: the bin's lower end
+    // serves as T (the entries above it and all those equal to it are the
+    // ones kept), with no further pass
+    if (rest == in_bin) break;
   }
   return lo;
 }
@@ -788,22 +797,24 @@ __global__ __launch_bounds__(kRxThreads) void topk_radix_kernel(const int32_t* _
     const int incl = (int)wave_scan_dpp((uint32_t)sum, 0u, [](uint32_t a, uint32_t b) { return a + b; });
     const int excl = incl - sum;
     const bool mine = excl < need && need <= incl;
-    int digit = 0, rest = 0;
+    int digit = 0, rest = 0, in_bin = 0;
     if (mine) {
       int run = excl;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (run < need && need <= run + c[j]) { digit = nbins - 1 - 4 * lane - j; rest = need - run; }
+        if (run < need && need <= run + c[j]) { digit = nbins - 1 - 4 * lane - j; rest = need - run; in_bin = c[j]; }
         run += c[j];
       }
     }
     const int owner = (int)__builtin_ctzll(__ballot(mine));
     digit = __builtin_amdgcn_readlane(digit, owner);
     rest = __builtin_amdgcn_readlane(rest, owner);
+    in_bin = __builtin_amdgcn_readlane(in_bin, owner);
     const uint32_t blo = lo + ((uint32_t)digit << shift);
     lo = blo;
     hi = min(hi, blo + ((1u << shift) - 1u));
     need = rest;
+    if (rest == in_bin) break;  // the whole bin is kept: its lower end serves as T (as in kth_key)
   }
   const uint32_t T = lo;
 

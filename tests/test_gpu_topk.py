@@ -125,10 +125,12 @@ def test_few_rows_radix_select(dsa, k):
 
 
 @pytest.mark.parametrize("k", [37, 2048])
-def test_radix_segments_and_winner_merge(dsa, k):
-    """Rows longer than one LDS stage: per-segment winners, then a selection
-    over them; ties straddle the segment borders and short rows ride along."""
-    announce("topk radix segments", k)
+def test_long_rows_segments_and_list_merge(dsa, k):
+    """Few long rows: each row's segments keep the entries that reach the
+    row's sampled threshold and the merge cuts their lists; ties straddle the
+    segment borders (2048-entry segments here, 64 per row) and short rows ride
+    along."""
+    announce("topk segments and list merge", k)
     p = _problem([131072, 2000, 73728, 36865, 100000], [1, 1, 1, 1, 1], k)
     rng = np.random.default_rng(20 + k)
     n = _ld(p)

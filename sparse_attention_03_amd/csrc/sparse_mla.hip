@@ -709,14 +709,20 @@ hipError_t launch_bf16(const MlaArgs& a, int rows, hipStream_t s) {
 // Waves of 32 heads per workgroup for H heads (heads past H are masked).
 int attention_waves(int H) { return H <= 32 ? 1 : H <= 64 ? 2 : 4; }
 
+// A workgroup fills a CU (its LDS and one wave per SIMD), so a launch of more
+// workgroups than CUs runs in rounds: the splits are as many as fit beside
+// each other, rows * splits <= num_cus, with the tiles dealt out evenly and no
+// split left empty (40 rows of 64 tiles on 256 CUs: 6 splits of 11 tiles, one
+// round, where 8 splits of 8 would take two).
 int attention_splits(int rows, int k, bool bf16, int num_cus) {
   if (!bf16 || rows <= 0) return 1;
   const int ntiles = (k + kTile - 1) / kTile;
-  int splits = 1;
-  while (splits < ntiles && splits < kMaxSplits && (int64_t)rows * splits < (int64_t)num_cus) splits <<= 1;
-  if (splits > ntiles) splits = ntiles;
-  if (splits > kMaxSplits) splits = kMaxSplits;
-  return splits < 1 ? 1 : splits;
+  int64_t target = (int64_t)num_cus / rows;
+  if (target > ntiles) target = ntiles;
+  if (target > kMaxSplits) target = kMaxSplits;
+  if (target <= 1) return 1;
+  const int tps = (int)((ntiles + target - 1) / target);  // tiles per split
+  return (ntiles + tps - 1) / tps;
 }
 
 hipError_t launch_attention(const AttnLaunch& L, hipStream_t s) {

@@ -80,12 +80,15 @@ __device__ inline RowInfo locate_row(const int32_t* __restrict__ cu_q, const int
 }
 
 // The same lookup for a row that is uniform over the wave, with every lane
-// active.  For batches of at most 63 sequences each lane holds one cu_q / cu_k
-// entry (load_seq_table, one load each for the whole kernel) and a row is
-// located with one ballot; larger batches fall back to the binary search.
+// active.  For batches of at most 127 sequences the lanes hold the cu_q / cu_k
+// entries, lane l entries l and 64 + l (load_seq_table, one load each, a
+// second pair only for 64 sequences or more, for the whole kernel), and a row
+// is located with one ballot per half; larger batches fall back to the
+// binary search.
 struct SeqTable {
-  int32_t q, k;  // cu_q[lane], cu_k[lane] (lane <= num_seqs)
-  int32_t n;     // num_seqs
+  int32_t q, k;    // cu_q[lane], cu_k[lane] (lane <= num_seqs)
+  int32_t q2, k2;  // cu_q[64 + lane], cu_k[64 + lane] (64 + lane <= num_seqs)
+  int32_t n;       // num_seqs
 };
 
 __device__ inline SeqTable load_seq_table(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
@@ -95,23 +98,40 @@ __device__ inline SeqTable load_seq_table(const int32_t* __restrict__ cu_q, cons
   t.n = num_seqs;
   t.q = 0;
   t.k = 0;
-  if (num_seqs < 64) {
+  t.q2 = 0;
+  t.k2 = 0;
+  if (num_seqs < 128) {
     const int i = min(lane, num_seqs);
     t.q = cu_q[i];
     t.k = cu_k[i];
+    if (num_seqs >= 64) {
+      const int i2 = min(64 + lane, num_seqs);
+      t.q2 = cu_q[i2];
+      t.k2 = cu_k[i2];
+    }
   }
   return t;
 }
 
 __device__ inline RowInfo locate_row_wave(const SeqTable& t, const int32_t* __restrict__ cu_q,
                                           const int32_t* __restrict__ cu_k, int32_t r) {
-  if (t.n >= 64) return locate_row(cu_q, cu_k, t.n, r);
+  if (t.n >= 128) return locate_row(cu_q, cu_k, t.n, r);
   const int lane = threadIdx.x & 63;
-  // cu_q[0] = 0 <= r and cu_q is nondecreasing: lanes 1 .. b hold the entries <= r
-  const int b = __popcll(__ballot(lane >= 1 && lane <= t.n && t.q <= r));
-  const int32_t q0 = __builtin_amdgcn_readlane(t.q, b), q1 = __builtin_amdgcn_readlane(t.q, b + 1);
-  const int32_t k0 = __builtin_amdgcn_readlane(t.k, b), k1 = __builtin_amdgcn_readlane(t.k, b + 1);
+  // cu_q[0] = 0 <= r and cu_q is nondecreasing: entries 1 .. b are the ones <= r
+  int b = __popcll(__ballot(lane >= 1 && lane <= t.n && t.q <= r));
   RowInfo ri;
+  if (t.n < 64) {
+    const int32_t q0 = __builtin_amdgcn_readlane(t.q, b), q1 = __builtin_amdgcn_readlane(t.q, b + 1);
+    const int32_t k0 = __builtin_amdgcn_readlane(t.k, b), k1 = __builtin_amdgcn_readlane(t.k, b + 1);
+    ri.pos = (k1 - k0) - (q1 - q0) + (r - q0);
+    ri.kbase = k0;
+    return ri;
+  }
+  b += __popcll(__ballot(64 + lane <= t.n && t.q2 <= r));
+  // entry i: lane i of the first pair (i < 64) or lane i - 64 of the second
+  auto q_at = [&](int i) { return i < 64 ? __builtin_amdgcn_readlane(t.q, i) : __builtin_amdgcn_readlane(t.q2, i - 64); };
+  auto k_at = [&](int i) { return i < 64 ? __builtin_amdgcn_readlane(t.k, i) : __builtin_amdgcn_readlane(t.k2, i - 64); };
+  const int32_t q0 = q_at(b), q1 = q_at(b + 1), k0 = k_at(b), k1 = k_at(b + 1);
   ri.pos = (k1 - k0) - (q1 - q0) + (r - q0);
   ri.kbase = k0;
   return ri;

@@ -507,75 +507,82 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_target_kernel(MlaArgs a) {
 }
 
 // Combine key-split partials: o = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M).
-// One workgroup per (row, head); each thread owns 4 consecutive value columns.
-// Up to kMaxSplits splits: the weights are formed by the whole workgroup
-// (strided over the splits, then a max and a sum across its two waves).  The
-// first four splits' partials are loaded before the weights are known, so
-// their latency overlaps that of the lse loads.
+// One wave per (row, head), lane l owning value columns 8 l .. 8 l + 7, so a
+// split's partial is one 1-KB load of the wave and the reductions need no
+// barrier.  Up to kMaxSplits splits: lane l holds the weights of splits
+// l, l + 64, ...; the accumulation takes them by readlane.  The first four
+// splits' partials are loaded before the weights are known, so their latency
+// overlaps that of the lse loads.
 template <bool BF16>
-__global__ __launch_bounds__(128) void merge_kernel(MlaArgs a) {
-  static_assert(kDv == 4 * 128, "one thread per four value columns");
-  __shared__ float wsh[kMaxSplits];
-  __shared__ float red[2][2];
+__global__ __launch_bounds__(64) void merge_kernel(MlaArgs a) {
+  static_assert(kDv == 8 * 64, "one lane per eight value columns");
+  constexpr int kW = kMaxSplits / 64;  // weights per lane
   const int32_t rl = blockIdx.x, r = a.row_begin + rl;
   const int h = blockIdx.y;
   const int S = a.splits;
-  const int tid = threadIdx.x, wv = tid >> 6;
-  const int d = 4 * tid;
+  const int lane = threadIdx.x;
+  const int d = 8 * lane;
   const int64_t slot0 = (int64_t)rl * S * a.H + h;  // split s: slot0 + s * H
-  auto load_part = [&](int s) -> uint2 {
-    return s < S ? *(const uint2*)(a.ws_o + (slot0 + (int64_t)s * a.H) * kDv + d) : make_uint2(0, 0);
+  auto load_part = [&](int s) -> uint4 {
+    return s < S ? *(const uint4*)(a.ws_o + (slot0 + (int64_t)s * a.H) * kDv + d) : make_uint4(0, 0, 0, 0);
   };
-  uint2 v[4];
+  uint4 v[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) v[u] = load_part(u);
+  float wl[kW];
   float mloc = -INFINITY;
-  for (int s = tid; s < S; s += 128) {
-    const float ls = a.ws_lse[slot0 + (int64_t)s * a.H];
-    wsh[s] = ls;
-    mloc = fmaxf(mloc, ls);
+#pragma unroll
+  for (int j = 0; j < kW; ++j) {
+    const int s = 64 * j + lane;
+    wl[j] = s < S ? a.ws_lse[slot0 + (int64_t)s * a.H] : -INFINITY;
+    mloc = fmaxf(mloc, wl[j]);
   }
-  mloc = wave_max(mloc);
-  if ((tid & 63) == 0) red[0][wv] = mloc;
-  __syncthreads();
-  const float M = fmaxf(red[0][0], red[0][1]);
+  const float M = wave_max(mloc);
   float dloc = 0.0f;
-  for (int s = tid; s < S; s += 128) {
-    const float ls = wsh[s];
-    const float wgt = (M == -INFINITY || ls == -INFINITY) ? 0.0f : expf(ls - M);
-    wsh[s] = wgt;
-    dloc += wgt;
+#pragma unroll
+  for (int j = 0; j < kW; ++j) {
+    wl[j] = (M == -INFINITY || wl[j] == -INFINITY) ? 0.0f : expf(wl[j] - M);
+    dloc += wl[j];
   }
-  dloc = wave_sum(dloc);
-  if ((tid & 63) == 0) red[1][wv] = dloc;
-  __syncthreads();
-  const float den = red[1][0] + red[1][1];
+  const float den = wave_sum(dloc);
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  // four splits' bf16 partials in flight at a time
-  for (int s0 = 0; s0 < S; s0 += 4) {
-    if (s0 > 0) {
+  f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto lo16 = [](uint32_t x) { return __uint_as_float(x << 16); };
+  auto hi16 = [](uint32_t x) { return __uint_as_float(x & 0xffff0000u); };
+  // four splits' bf16 partials in flight at a time; the weights of splits
+  // 64 j .. 64 j + 63 sit in wl[j] of lanes 0 .. 63
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = load_part(s0 + u);
-    }
+  for (int j = 0; j < kW; ++j) {
+    if (64 * j >= S) break;
+    const int s_end = min(S, 64 * j + 64);
+    for (int s0 = 64 * j; s0 < s_end; s0 += 4) {
+      if (s0 > 0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float wgt = s0 + u < S ? wsh[s0 + u] : 0.0f;
-      if (wgt != 0.0f)
-        acc += wgt * f32x4{__uint_as_float(v[u].x << 16), __uint_as_float(v[u].x & 0xffff0000u),
-                           __uint_as_float(v[u].y << 16), __uint_as_float(v[u].y & 0xffff0000u)};
+        for (int u = 0; u < 4; ++u) v[u] = load_part(s0 + u);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s = s0 + u;
+        const float w = s < s_end ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl[j]), s - 64 * j)) : 0.0f;
+        if (w != 0.0f) {
+          acc0 += w * f32x4{lo16(v[u].x), hi16(v[u].x), lo16(v[u].y), hi16(v[u].y)};
+          acc1 += w * f32x4{lo16(v[u].z), hi16(v[u].z), lo16(v[u].w), hi16(v[u].w)};
+        }
+      }
     }
   }
-  acc *= inv;
+  acc0 *= inv;
+  acc1 *= inv;
   const int64_t oi = ((int64_t)r * a.H + h) * kDv + d;
   if constexpr (BF16) {
-    const uint32_t lo = (uint32_t)to_bf16_bits(acc[0]) | ((uint32_t)to_bf16_bits(acc[1]) << 16);
-    const uint32_t hi = (uint32_t)to_bf16_bits(acc[2]) | ((uint32_t)to_bf16_bits(acc[3]) << 16);
-    *(uint2*)(a.out + oi) = make_uint2(lo, hi);
+    auto pack = [](float x, float y) { return (uint32_t)to_bf16_bits(x) | ((uint32_t)to_bf16_bits(y) << 16); };
+    *(uint4*)(a.out + oi) = make_uint4(pack(acc0[0], acc0[1]), pack(acc0[2], acc0[3]), pack(acc1[0], acc1[1]),
+                                       pack(acc1[2], acc1[3]));
   } else {
-    *(f32x4*)((float*)a.out + oi) = acc;
+    *(f32x4*)((float*)a.out + oi) = acc0;
+    *(f32x4*)((float*)a.out + oi + 4) = acc1;
   }
-  if (tid == 0 && a.lse) a.lse[(int64_t)r * a.H + h] = den > 0.0f ? M + logf(den) : -INFINITY;
+  if (lane == 0 && a.lse) a.lse[(int64_t)r * a.H + h] = den > 0.0f ? M + logf(den) : -INFINITY;
 }
 
 // fp32 inputs, alignment target: one workgroup per row, the heads in turn;
@@ -787,7 +794,7 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL((merge_kernel<true>), dim3((unsigned)rows, (unsigned)a.H), dim3(128), 0, s, a);
+  hipLaunchKernelGGL((merge_kernel<true>), dim3((unsigned)rows, (unsigned)a.H), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -209,3 +209,28 @@ def test_forward_narrow_attention_widths(dsa):
     out3, lse3, idx3 = dsa.forward(p, q_block=1000)
     assert torch.equal(idx3, idx)
     assert row_norm_err(out3.float().cpu().numpy(), out.float().cpu().numpy()) <= TOL_ATTN_BF16
+
+
+@pytest.mark.parametrize("nseq,many_q", [(63, False), (64, False), (100, False), (127, False), (128, False),
+                                         (130, False), (100, True)])
+def test_forward_many_sequences(dsa, nseq, many_q):
+    """Batches of 63 to 130 sequences, decode-like (mostly one query each) or
+    prefill-like (8-10 queries each): the kernels locate a row from the batch
+    offsets held one per lane below 64 sequences, two per lane from 64 to 127
+    and by binary search from 128 on.  Every row against the oracle, and the
+    separate calls give the same result bit for bit."""
+    announce("forward many sequences", nseq, many_q)
+    rng = np.random.default_rng(1000 + nseq)
+    ctx = rng.integers(200, 3000, nseq)
+    if many_q:
+        nq = rng.integers(8, 11, nseq)
+    else:
+        nq = np.where(rng.random(nseq) < 0.1, rng.integers(2, 6, nseq), 1)
+    p = gen.make_problem("fwd", ctx.tolist(), nq.tolist(), H_I=64, H=64, k=512, device=DEV,
+                         seed=50 + nseq + int(many_q))
+    out, lse, idx = dsa.forward(p)
+    idx2 = dsa.topk(p, dsa.indexer_scores(p))
+    assert torch.equal(idx, idx2)
+    out2, lse2 = dsa.sparse_mla_attn(p, idx2)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    _check_rows(p, out, idx, np.arange(p.total_q), TOL_ATTN_BF16)

@@ -370,22 +370,12 @@ dsa_status dsa_cache_append(int64_t n, const int32_t* dst_rows, int64_t cache_ro
                             dsa_stream_t stream);
 
 /*
- * The three steps fused in one call, with no host synchronisation.  Query
- * rows are processed in chunks of q_block rows (bounded score workspace).
- * Rows with pos + 1 <= k skip the indexer and the selection: every candidate
- * is selected, which is the masked dense-equivalent mode [P2] 【推理成本评估】
- * describes for short prefill.  The indices equal those of
- * dsa_topk(dsa_indexer_scores(...)) bit for bit.
- * Streams: with more than one chunk and a workspace of the size
- * dsa_forward_workspace_size reports (two score buffers), chunk c + 1's
- * indexer runs on `stream` while chunk c's top-k runs on a second stream the
- * library keeps per device (default priority, created on the first such
- * call); events order the two, and the last launch of the call is on
- * `stream`, so work enqueued on `stream` afterwards sees every output.  With
- * one chunk, or a smaller workspace that holds one score buffer, every launch
- * is on `stream`.  The results are the same either way.  The workspace is
- * the call's until its work is done: calls that share one run in order on
- * one stream.
+ * The three steps fused in one call, on one stream, with no host
+ * synchronisation.  Query rows are processed in chunks of q_block rows
+ * (bounded score workspace).  Rows with pos + 1 <= k skip the indexer and the
+ * selection: every candidate is selected, which is the masked dense-equivalent
+ * mode [P2] 【推理成本评估】 describes for short prefill.  The indices equal
+ * those of dsa_topk(dsa_indexer_scores(...)) bit for bit.
  */
 typedef struct {
   const dsa_batch* batch;
@@ -411,10 +401,9 @@ dsa_status dsa_forward(const dsa_forward_params* p, void* ws, size_t ws_bytes, d
  * workspace is the library's own static device array of 128 MiB (134217728
  * bytes), which each device the library runs on holds until the process
  * ends; the caller still passes every input and output.  The call allocates
- * nothing and enqueues exactly the kernels dsa_forward enqueues, all on
- * `stream` with one score buffer, so the results are identical.  A batch that
- * needs more than 128 MiB of that one-stream workspace gives
- * DSA_ERR_WORKSPACE with nothing enqueued (decode steps of tens
+ * nothing and enqueues exactly the kernels dsa_forward enqueues, so the
+ * results are identical.  A batch whose dsa_forward_workspace_size exceeds
+ * 128 MiB gives DSA_ERR_WORKSPACE with nothing enqueued (decode steps of tens
  * of sequences fit; long prefills need dsa_forward with their own workspace).
  * Nothing in the array needs to start at zero: a call writes every byte it
  * reads.  Every call on one device shares that device's array, so calls that

@@ -541,8 +541,6 @@ struct ForwardPlan {
   bool pad;         // FP8 with d_I < 128: q_I (per chunk) and k_I widened to 128-byte rows
   AttnWiden w;      // BF16 attention shapes other than 576 / 512: q (per chunk), kv, output staging
   int max_splits;
-  bool two;            // two score buffers: chunk c + 1's indexer overlaps chunk c's top-k (a second stream)
-  size_t score_bytes;  // one score buffer
 };
 
 dsa_status check_forward(const dsa_forward_params* p) {
@@ -559,16 +557,14 @@ dsa_status check_forward(const dsa_forward_params* p) {
                          p->lse);
 }
 
-dsa_status plan_forward(const dsa_forward_params* p, int cus, bool two, ForwardPlan* f) {
+dsa_status plan_forward(const dsa_forward_params* p, int cus, ForwardPlan* f) {
   const dsa_batch* b = p->batch;
   f->qb = p->q_block > 0 ? p->q_block : 4096;
   if (f->qb > b->total_q) f->qb = b->total_q > 0 ? b->total_q : 1;
   f->ld = (int64_t)round_up((size_t)b->max_ctx, 64);
-  f->two = two && b->total_q > f->qb;
   size_t off = 0;
   f->off_scores = off;
-  f->score_bytes = round_up((size_t)f->qb * (size_t)f->ld * sizeof(float), 256);
-  off += f->score_bytes * (f->two ? 2 : 1);
+  off += round_up((size_t)f->qb * (size_t)f->ld * sizeof(float), 256);
   f->off_idx = off;
   if (!p->out_idx) off += round_up((size_t)f->qb * p->k * sizeof(int32_t), 256);
   f->off_topk = off;
@@ -607,45 +603,21 @@ dsa_status plan_forward(const dsa_forward_params* p, int cus, bool two, ForwardP
 
 }  // namespace
 
-namespace {
+extern "C" {
 
-// The second stream of dsa_forward on each device (default priority, created
-// on first use): chunk c's top-k runs there while chunk c + 1's indexer runs
-// on the caller's stream.
-constexpr int kMaxSideDevices = 64;
-hipStream_t g_side[kMaxSideDevices];
-std::once_flag g_side_once[kMaxSideDevices];
-
-hipStream_t side_stream() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return nullptr;
-  std::call_once(g_side_once[dev], [dev] {
-    hipStream_t s = nullptr;
-    g_side[dev] = hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess ? s : nullptr;
-  });
-  return g_side[dev];
-}
-
-}  // namespace
-
-namespace dsa {
-
-dsa_status forward_workspace(const dsa_forward_params* p, bool overlap, size_t* bytes) {
+dsa_status dsa_forward_workspace_size(const dsa_forward_params* p, size_t* bytes) {
   g_err[0] = 0;
   if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is NULL");
   if (dsa_status s = check_forward(p)) return s;
   int cus = 0;
   if (dsa_status s = device_cus(&cus)) return s;
   ForwardPlan f;
-  if (dsa_status s = plan_forward(p, cus, overlap, &f)) return s;
+  if (dsa_status s = plan_forward(p, cus, &f)) return s;
   *bytes = f.total;
   return DSA_OK;
 }
 
-// overlap: two score buffers and a second stream when the batch has several
-// chunks and the workspace holds both buffers; otherwise every launch is on
-// the caller's stream.  The results are the same either way (same launches).
-dsa_status forward_run(const dsa_forward_params* p, void* ws, size_t ws_bytes, dsa_stream_t stream, bool overlap) {
+dsa_status dsa_forward(const dsa_forward_params* p, void* ws, size_t ws_bytes, dsa_stream_t stream) {
   g_err[0] = 0;
   if (dsa_status s = check_forward(p)) return s;
   const dsa_batch* b = p->batch;
@@ -653,23 +625,12 @@ dsa_status forward_run(const dsa_forward_params* p, void* ws, size_t ws_bytes, d
   int cus = 0;
   if (dsa_status s = device_cus(&cus)) return s;
   ForwardPlan f;
-  if (dsa_status s = plan_forward(p, cus, overlap, &f)) return s;
-  if (f.two && ws_bytes < f.total) {  // a workspace of the one-stream size
-    if (dsa_status s = plan_forward(p, cus, false, &f)) return s;
-  }
+  if (dsa_status s = plan_forward(p, cus, &f)) return s;
   if (!ws || ws_bytes < f.total || !aligned16(ws))
     return fail(DSA_ERR_WORKSPACE, "forward workspace: need %zu bytes (got %zu)", f.total, ws_bytes);
   hipStream_t st = (hipStream_t)stream;
-  hipStream_t side = f.two ? side_stream() : nullptr;
-  hipEvent_t ev_a = nullptr, ev_b = nullptr;  // last work on the caller's / the second stream
-  if (side && (hipEventCreateWithFlags(&ev_a, hipEventDisableTiming) != hipSuccess ||
-               hipEventCreateWithFlags(&ev_b, hipEventDisableTiming) != hipSuccess))
-    side = nullptr;
-  struct Events {  // released when the call returns (HIP frees them once their work is done)
-    hipEvent_t& a; hipEvent_t& b;
-    ~Events() { if (a) (void)hipEventDestroy(a); if (b) (void)hipEventDestroy(b); }
-  } events{ev_a, ev_b};
   char* base = (char*)ws;
+  float* scores = (float*)(base + f.off_scores);
   const void* k_idx = p->k_idx;
   int32_t d_I = p->d_I;
   const void* kv = p->kv;
@@ -684,20 +645,10 @@ dsa_status forward_run(const dsa_forward_params* p, void* ws, size_t ws_bytes, d
     k_idx = base + f.off_pad_k;
     d_I = 128;
   }
-  const int32_t nchunks = (b->total_q + f.qb - 1) / f.qb;
-  auto rows_of = [&](int32_t c, int32_t* r0, int32_t* r1) {
-    *r0 = c * f.qb;
-    *r1 = *r0 + f.qb < b->total_q ? *r0 + f.qb : b->total_q;
-  };
-  auto scores_of = [&](int32_t c) { return (float*)(base + f.off_scores + (side ? (size_t)(c & 1) * f.score_bytes : 0)); };
-  auto idx_of = [&](int32_t r0) {
-    return p->out_idx ? p->out_idx + (int64_t)r0 * p->k : (int32_t*)(base + f.off_idx);
-  };
-  // chunk c's indexer (and its query widening) on the caller's stream
-  auto indexer = [&](int32_t c) -> dsa_status {
-    int32_t r0, r1;
-    rows_of(c, &r0, &r1);
+  for (int32_t r0 = 0; r0 < b->total_q; r0 += f.qb) {
+    const int32_t r1 = r0 + f.qb < b->total_q ? r0 + f.qb : b->total_q;
     const dsa::BatchView v = view(b, r0, r1);
+    int32_t* idx = p->out_idx ? p->out_idx + (int64_t)r0 * p->k : (int32_t*)(base + f.off_idx);
     const void* q_idx = p->q_idx;
     if (f.pad) {
       // the chunk's query rows widened; the indexer addresses q_I by global row,
@@ -709,29 +660,20 @@ dsa_status forward_run(const dsa_forward_params* p, void* ws, size_t ws_bytes, d
       q_idx = (const void*)((uintptr_t)(base + f.off_pad_q) - (uintptr_t)r0 * row_bytes);
     }
     // rows with pos + 1 <= k select every candidate: their scores are never read
-    dsa::IndexerLaunch IL{v, p->k, q_idx, k_idx, p->w, scores_of(c), f.ld, p->H_I, d_I, (int32_t)p->act,
+    dsa::IndexerLaunch IL{v, p->k, q_idx, k_idx, p->w, scores, f.ld, p->H_I, d_I, (int32_t)p->act,
                           p->idx_dtype == DSA_FP8_E4M3, cus, base + f.off_lin};
     IL.k_scale = p->k_idx_scale;
     IL.batch_rows = b->total_q;  // every chunk scores its rows as the whole batch does
     hipError_t e = dsa::launch_indexer(IL, st);
-    return e == hipSuccess ? DSA_OK : hip_fail(e, "forward indexer launch");
-  };
-  auto topk = [&](int32_t c, hipStream_t s) -> dsa_status {
-    int32_t r0, r1;
-    rows_of(c, &r0, &r1);
-    dsa::TopkLaunch TL{view(b, r0, r1), scores_of(c), f.ld, p->k, idx_of(r0), base + f.off_topk, cus};
-    hipError_t e = dsa::launch_topk(TL, s);
-    return e == hipSuccess ? DSA_OK : hip_fail(e, "forward topk launch");
-  };
-  auto attention = [&](int32_t c) -> dsa_status {
-    int32_t r0, r1;
-    rows_of(c, &r0, &r1);
+    if (e != hipSuccess) return hip_fail(e, "forward indexer launch");
+    dsa::TopkLaunch TL{v, scores, f.ld, p->k, idx, base + f.off_topk, cus};
+    e = dsa::launch_topk(TL, st);
+    if (e != hipSuccess) return hip_fail(e, "forward topk launch");
     const int splits = dsa::attention_splits(r1 - r0, p->k, p->dtype == DSA_BF16, cus);
     // q and out are addressed by global row: widened / staged copies of this
     // chunk's rows are passed as their buffer's address less r0 rows
     const void* q = p->q;
     void* out = p->out;
-    hipError_t e;
     if (f.w.in) {
       const size_t row = (size_t)p->H * kQkW * 2;
       e = dsa::launch_copy_rows((const char*)p->q + (size_t)r0 * p->H * p->d_qk * 2, 2 * p->d_qk, base + f.off_wq,
@@ -740,8 +682,8 @@ dsa_status forward_run(const dsa_forward_params* p, void* ws, size_t ws_bytes, d
       q = (const void*)((uintptr_t)(base + f.off_wq) - (uintptr_t)r0 * row);
     }
     if (f.w.out) out = (void*)((uintptr_t)(base + f.off_stage) - (uintptr_t)r0 * ((size_t)p->H * kVW * 2));
-    dsa::AttnLaunch AL{view(b, r0, r1), q, kv, idx_of(r0), p->k, p->H, f.w.d_qk, f.w.d_v, p->softmax_scale, out,
-                       p->lse, p->dtype == DSA_BF16, splits, nullptr, nullptr};
+    dsa::AttnLaunch AL{v, q, kv, idx, p->k, p->H, f.w.d_qk, f.w.d_v, p->softmax_scale, out, p->lse,
+                       p->dtype == DSA_BF16, splits, nullptr, nullptr};
     AL.dense_short = true;  // rows with pos + 1 <= k: the masked mode, same result as their idx = 0 .. pos
     if (splits > 1) {
       AL.ws_o = (uint16_t*)(base + f.off_attn);
@@ -754,48 +696,8 @@ dsa_status forward_run(const dsa_forward_params* p, void* ws, size_t ws_bytes, d
                                 2 * p->d_v, (int64_t)(r1 - r0) * p->H, 2 * p->d_v, cus, st);
       if (e != hipSuccess) return hip_fail(e, "forward output narrowing");
     }
-    return DSA_OK;
-  };
-  if (!side) {
-    for (int32_t c = 0; c < nchunks; ++c) {
-      if (dsa_status s = indexer(c)) return s;
-      if (dsa_status s = topk(c, st)) return s;
-      if (dsa_status s = attention(c)) return s;
-    }
-    return DSA_OK;
-  }
-  // Caller's stream: I(0), I(1), A(0), I(2), A(1), ...; second stream: T(0),
-  // T(1), ...  T(c) waits for the caller's stream up to I(c) and A(c - 1)
-  // (A(c - 1) read the index buffer and follows I(c)); A(c) waits for T(c).
-  // I(c + 2) rewrites the score buffer T(c) read, after A(c), so after T(c).
-  // The caller's stream ends after A(n - 1), which waited for the last top-k.
-  auto wait_on = [&](hipEvent_t ev, hipStream_t from, hipStream_t to, const char* what) -> dsa_status {
-    hipError_t e = hipEventRecord(ev, from);
-    if (e == hipSuccess) e = hipStreamWaitEvent(to, ev, 0);
-    return e == hipSuccess ? DSA_OK : hip_fail(e, what);
-  };
-  if (dsa_status s = indexer(0)) return s;
-  for (int32_t c = 0; c < nchunks; ++c) {
-    if (dsa_status s = wait_on(ev_a, st, side, "forward: second stream wait")) return s;
-    if (dsa_status s = topk(c, side)) return s;
-    if (c + 1 < nchunks)
-      if (dsa_status s = indexer(c + 1)) return s;
-    if (dsa_status s = wait_on(ev_b, side, st, "forward: caller stream wait")) return s;
-    if (dsa_status s = attention(c)) return s;
   }
   return DSA_OK;
-}
-
-}  // namespace dsa
-
-extern "C" {
-
-dsa_status dsa_forward_workspace_size(const dsa_forward_params* p, size_t* bytes) {
-  return dsa::forward_workspace(p, true, bytes);
-}
-
-dsa_status dsa_forward(const dsa_forward_params* p, void* ws, size_t ws_bytes, dsa_stream_t stream) {
-  return dsa::forward_run(p, ws, ws_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -5,8 +5,8 @@
 // until the process ends.  Its device address is taken once per device with
 // hipGetSymbolAddress and kept; host code only ever passes that address on
 // (the array's own name in host code is a host-side stand-in, not a device
-// address).  The call enqueues the same kernels as dsa_forward, all on the
-// caller's stream with a single score buffer, so the results are identical.
+// address).  The call enqueues the same kernels as dsa_forward, so the
+// results are identical.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -16,11 +16,6 @@
 namespace dsa {
 // api.hip: record the thread's last error and return the status
 dsa_status report_error(dsa_status s, const char* fmt, ...);
-// api.hip: dsa_forward's workspace plan and run; overlap = false keeps every
-// launch on the caller's stream with one score buffer (no second stream, no
-// events)
-dsa_status forward_workspace(const dsa_forward_params* p, bool overlap, size_t* bytes);
-dsa_status forward_run(const dsa_forward_params* p, void* ws, size_t ws_bytes, dsa_stream_t stream, bool overlap);
 }  // namespace dsa
 
 namespace {
@@ -39,7 +34,7 @@ std::once_flag g_scratch_once[kMaxDevices];
 extern "C" dsa_status dsa_forward_noalloc(const dsa_forward_params* p, dsa_stream_t stream) {
   size_t need = 0;
   // argument checks and the workspace plan of dsa_forward (host only)
-  if (dsa_status s = dsa::forward_workspace(p, false, &need)) return s;
+  if (dsa_status s = dsa_forward_workspace_size(p, &need)) return s;
   if (need > kScratchBytes)
     return dsa::report_error(DSA_ERR_WORKSPACE,
                              "dsa_forward_noalloc: this batch needs %zu bytes of workspace, the static scratch "
@@ -59,5 +54,5 @@ extern "C" dsa_status dsa_forward_noalloc(const dsa_forward_params* p, dsa_strea
   if (g_scratch_err[dev] != hipSuccess || !g_scratch[dev])
     return dsa::report_error(DSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
                              hipGetErrorString(g_scratch_err[dev]));
-  return dsa::forward_run(p, g_scratch[dev], kScratchBytes, stream, false);
+  return dsa_forward(p, g_scratch[dev], kScratchBytes, stream);
 }

@@ -235,25 +235,3 @@ def test_forward_many_sequences(dsa, nseq, many_q):
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
     _check_rows(p, out, idx, np.arange(p.total_q), TOL_ATTN_BF16)
 
-
-def test_forward_one_stream_workspace_same_result(dsa):
-    """Several chunks: with the reported workspace (two score buffers) chunk
-    c + 1's indexer overlaps chunk c's top-k on a second stream; a workspace
-    one score buffer smaller runs every launch on the caller's stream.  Both
-    give the same outputs bit for bit, and so does the one-chunk call."""
-    from sparse_attention_03_amd import libdsa as L
-    announce("forward one-stream workspace")
-    p = gen.make_problem("fwd", [3000, 2600], [3000, 1], H_I=64, H=128, k=512, device=DEV, seed=31)
-    qb = 512
-    f = dsa.Forward(p, q_block=qb)
-    f()
-    out2, lse2, idx2 = f.out.clone(), f.lse.clone(), f.idx.clone()
-    one_buffer = -(-(qb * (-(-p.max_ctx // 64) * 64) * 4) // 256) * 256
-    ws1 = torch.empty(f.ws.numel() - one_buffer, dtype=torch.uint8, device=DEV)
-    f.out.zero_(); f.lse.zero_(); f.idx.zero_()
-    L.dsa_forward(f.params, ws1)
-    assert torch.equal(f.idx, idx2) and torch.equal(f.out, out2) and torch.equal(f.lse, lse2)
-    with pytest.raises(RuntimeError):
-        L.dsa_forward(f.params, ws1[:ws1.numel() - 256])  # below the one-stream size: refused
-    out3, lse3, idx3 = dsa.forward(p, q_block=p.total_q)
-    assert torch.equal(idx3, idx2) and torch.equal(out3, out2) and torch.equal(lse3, lse2)
